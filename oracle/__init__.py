@@ -1,0 +1,263 @@
+"""CPU oracle for the binary XNOR-popcount path (numpy front end).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline may import this package; the product package never does.  It shares
+no code with the HIP library.
+
+The arithmetic lives in ``oracle.c`` (plain C, built with gcc into
+``liboracle.so``); this module only marshals numpy arrays.  Each wrapper names
+the passage of the source pages it follows (page title and section/equation):
+
+* "First Principles: Why Binary Ops Can Be Exponentially Faster", section
+  "1. Arithmetic: MAC -> XNOR + popcount": bit 0 encodes +1, bit 1 encodes -1,
+  pad bits encode +1, and the dot identity <w,x> = N - 2 popcount(w xor x).
+* "Extreme Quantization: Binary, Ternary & 1-bit LLMs": Notation (sign),
+  eq. (1) (alpha = mean |w|), eq. (4)-(6) (XNOR-Net).
+* "Binary Neural Network (BNN)" glossary: scaling factors and BatchNorm.
+* "Perfected Concept", "What is binary vs not": FP first/last layers and FP
+  residual streams; "State of the Art Survey", Bi-Real Net: FP shortcut.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` with gcc (never hipcc) into ``liboracle.so``."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O3", "-fopenmp", "-fPIC", "-shared",
+           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
+           _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        sigs = {
+            "oracle_sign": [_p, _i64, _i64, _i64, _p],
+            "oracle_pack_signs": [_p, _i64, _i64, _p, _i64],
+            "oracle_unpack_signs": [_p, _i64, _i64, _i64, _p],
+            "oracle_alpha": [_p, _i64, _i64, _i64, _p],
+            "oracle_dot": [_p, _p, _i64, _i64, _i64, _p],
+            "oracle_scale": [_p, _p, _i64, _i64, _p],
+            "oracle_scale_residual": [_p, _p, _p, _i64, _i64, _i64, _p],
+            "oracle_bn_fold": [_p, _p, _p, _p, ctypes.c_float, _p, _i64, _p, _p],
+            "oracle_threshold_signs": [_p, _p, _p, _i64, _i64, _p],
+            "oracle_im2col_signs": [_p, _i64, _i64, _i64, _i64, _p],
+            "oracle_dense_f64": [_p, _i64, _p, _i64, _i64, _i64, _i64, _p],
+            "oracle_dense_pm1_f32out": [_p, _p, _i64, _i64, _i64, _i64, _p],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = None
+        _lib = L
+    return _lib
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def sign(x: np.ndarray) -> np.ndarray:
+    """sign(x) = +1 for x >= 0, -1 otherwise, as int8 (Notation, page
+    "Extreme Quantization")."""
+    x = _c(x, np.float32)
+    x2 = x.reshape(-1, x.shape[-1]) if x.ndim > 1 else x.reshape(1, -1)
+    s = np.empty(x2.shape, dtype=np.int8)
+    lib().oracle_sign(_ptr(x2), x2.shape[0], x2.shape[1], x2.shape[1], _ptr(s))
+    return s.reshape(x.shape)
+
+
+def pack_signs(s: np.ndarray, ld: int | None = None) -> np.ndarray:
+    """Pack a [rows, K] matrix of +1/-1 into uint32 words [rows, ld]
+    (bit 0 = +1, bit 1 = -1, LSB first, pad bits and pad words 0)."""
+    s = _c(s, np.int8)
+    rows, K = s.shape
+    kw = (K + 31) // 32
+    ld = kw if ld is None else ld
+    assert ld >= kw
+    out = np.empty((rows, ld), dtype=np.uint32)
+    lib().oracle_pack_signs(_ptr(s), rows, K, _ptr(out), ld)
+    return out
+
+
+def unpack_signs(words: np.ndarray, K: int) -> np.ndarray:
+    words = _c(words, np.uint32)
+    rows, ld = words.shape
+    s = np.empty((rows, K), dtype=np.int8)
+    lib().oracle_unpack_signs(_ptr(words), rows, K, ld, _ptr(s))
+    return s
+
+
+def alpha(W: np.ndarray) -> np.ndarray:
+    """alpha_n = mean_k |W[n, k]| (eq. (1)), double sum, one rounding."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    out = np.empty(N, dtype=np.float32)
+    lib().oracle_alpha(_ptr(W), N, K, K, _ptr(out))
+    return out
+
+
+def dot(xs: np.ndarray, ws: np.ndarray) -> np.ndarray:
+    """D[m, n] = sum_k xs[m, k] * ws[n, k] over +1/-1 int8 (eq. (6))."""
+    xs = _c(xs, np.int8)
+    ws = _c(ws, np.int8)
+    M, K = xs.shape
+    N, K2 = ws.shape
+    assert K == K2
+    D = np.empty((M, N), dtype=np.int32)
+    lib().oracle_dot(_ptr(xs), _ptr(ws), M, N, K, _ptr(D))
+    return D
+
+
+def scale(D: np.ndarray, a: np.ndarray) -> np.ndarray:
+    """Y = alpha_n * D (eq. (1)), one rounded single multiply."""
+    D = _c(D, np.int32)
+    a = _c(a, np.float32)
+    M, N = D.shape
+    Y = np.empty((M, N), dtype=np.float32)
+    lib().oracle_scale(_ptr(D), _ptr(a), M, N, _ptr(Y))
+    return Y
+
+
+def scale_residual(D: np.ndarray, a: np.ndarray, R: np.ndarray) -> np.ndarray:
+    """Y = fl(fl(alpha_n * D) + R) (FP shortcut of Bi-Real Net)."""
+    D = _c(D, np.int32)
+    a = _c(a, np.float32)
+    R = _c(R, np.float32)
+    M, N = D.shape
+    assert R.shape == (M, N)
+    Y = np.empty((M, N), dtype=np.float32)
+    lib().oracle_scale_residual(_ptr(D), _ptr(a), _ptr(R), N, M, N, _ptr(Y))
+    return Y
+
+
+def bn_fold(gamma, beta, mean, var, eps, a):
+    """Fold inference BatchNorm of alpha*D followed by sign into (tau, dir)."""
+    gamma, beta, mean, var, a = (_c(v, np.float32) for v in (gamma, beta, mean, var, a))
+    N = a.shape[0]
+    tau = np.empty(N, dtype=np.float32)
+    d = np.empty(N, dtype=np.int8)
+    lib().oracle_bn_fold(_ptr(gamma), _ptr(beta), _ptr(mean), _ptr(var),
+                         ctypes.c_float(float(eps)), _ptr(a), N, _ptr(tau), _ptr(d))
+    return tau, d
+
+
+def threshold_signs(D: np.ndarray, tau: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Next-layer signs: +1 iff (float)(dir_n * D) >= tau_n."""
+    D = _c(D, np.int32)
+    tau = _c(tau, np.float32)
+    d = _c(d, np.int8)
+    M, N = D.shape
+    s = np.empty((M, N), dtype=np.int8)
+    lib().oracle_threshold_signs(_ptr(D), _ptr(tau), _ptr(d), M, N, _ptr(s))
+    return s
+
+
+def im2col_signs(X: np.ndarray) -> np.ndarray:
+    """[B*H*W, 9*C] signs of a 3x3/stride-1/pad-1 im2col of NHWC X, pad = +1."""
+    X = _c(X, np.float32)
+    B, H, W, C = X.shape
+    cols = np.empty((B * H * W, 9 * C), dtype=np.int8)
+    lib().oracle_im2col_signs(_ptr(X), B, H, W, C, _ptr(cols))
+    return cols
+
+
+def dense_f64(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """H = X W^T accumulated in double (first FP layer)."""
+    X = _c(X, np.float32)
+    W = _c(W, np.float32)
+    M, K = X.shape
+    N, K2 = W.shape
+    assert K == K2
+    H = np.empty((M, N), dtype=np.float64)
+    lib().oracle_dense_f64(_ptr(X), K, _ptr(W), K, M, N, K, _ptr(H))
+    return H
+
+
+def dense_pm1_f32out(s: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Y = fl32(sum_k s[m,k] W[n,k]) with a double sum (last FP layer)."""
+    s = _c(s, np.int8)
+    W = _c(W, np.float32)
+    M, K = s.shape
+    N, K2 = W.shape
+    assert K == K2
+    Y = np.empty((M, N), dtype=np.float32)
+    lib().oracle_dense_pm1_f32out(_ptr(s), _ptr(W), K, M, N, K, _ptr(Y))
+    return Y
+
+
+# ---------------------------------------------------------------------------
+# Whole-workload chains, each composed only of the routines above.
+# ---------------------------------------------------------------------------
+
+def binary_linear(X: np.ndarray, W: np.ndarray):
+    """Single binary linear layer: returns (D int32, Y = alpha*D fp32, alpha)."""
+    a = alpha(W)
+    D = dot(sign(X), sign(W))
+    return D, scale(D, a), a
+
+
+def binary_mlp(X, W1, hidden, W5):
+    """Binary MLP: FP first layer (double accumulate) -> sign -> binary hidden
+    layers with folded BatchNorm and sign -> FP last layer on the +1/-1 output.
+
+    ``hidden`` is a list of (W, gamma, beta, mean, var, eps).  Returns a dict
+    with the first-layer pre-activations, per-layer signs, alphas, thresholds,
+    integer dots and the logits.
+    """
+    h1 = dense_f64(X, W1)
+    s = np.where(h1 >= 0.0, 1, -1).astype(np.int8)
+    out = dict(h1=h1, signs=[s], alphas=[], taus=[], dirs=[], dots=[])
+    for (W, g, b, mu, var, eps) in hidden:
+        a = alpha(W)
+        tau, d = bn_fold(g, b, mu, var, eps, a)
+        D = dot(s, sign(W))
+        s = threshold_signs(D, tau, d)
+        out["alphas"].append(a)
+        out["taus"].append(tau)
+        out["dirs"].append(d)
+        out["dots"].append(D)
+        out["signs"].append(s)
+    out["logits"] = dense_pm1_f32out(s, W5)
+    return out
+
+
+def conv_block(X: np.ndarray, W_ohwi: np.ndarray):
+    """Binary 3x3 conv (stride 1, pad 1, pad pixels +1) + alpha + FP residual.
+
+    X is NHWC [B, H, W, C]; W_ohwi is [Cout, 3, 3, C]; the residual is X
+    itself (Cout == C).  Returns (D [B*H*W, Cout], Y, alpha)."""
+    B, H, Wd, C = X.shape
+    Cout = W_ohwi.shape[0]
+    Wf = np.ascontiguousarray(W_ohwi.reshape(Cout, 9 * C))
+    a = alpha(Wf)
+    D = dot(im2col_signs(X), sign(Wf))
+    R = X.reshape(B * H * Wd, C)
+    return D, scale_residual(D, a, R), a

@@ -1,0 +1,226 @@
+/*
+ * CPU oracle for the binary (XNOR-popcount) inference path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the benchmark's CPU
+ * baseline use it.  It shares no source, header, table or helper with the HIP
+ * library; the two meet only through the seeded inputs.
+ *
+ * Every routine is the plain definition written out: signs are stored
+ * unpacked as int8 (+1 / -1) and a binary dot product is an integer
+ * multiply-add over them.  Floating point uses IEEE single/double arithmetic
+ * as written in C (built without fast-math and without FMA contraction).
+ * Loops over independent outputs run under OpenMP; no loop is blocked, fused
+ * or reordered.
+ *
+ * Sources (page title, section / equation):
+ *  [P2] "First Principles: Why Binary Ops Can Be Exponentially Faster",
+ *       section "1. Arithmetic: MAC -> XNOR + popcount" (encoding bit0 -> +1,
+ *       bit1 -> -1; dot identity; pad bits encode +1; 64 bits per word).
+ *  [P5] "Extreme Quantization: Binary, Ternary & 1-bit LLMs": "Notation"
+ *       (sign(x) = +1 for x >= 0, -1 for x < 0), "Binary Neural Networks"
+ *       eq. (1) (alpha = mean |w|, y = alpha * w_b^T x), "XNOR-Net" eq. (4)-(6).
+ *  [P1] "Binary Neural Network (BNN)" glossary: per-filter scaling factors and
+ *       BatchNorm around the binarized layers.
+ *  [P3] "Perfected Concept", table "What is binary vs not": first/last layers
+ *       and BatchNorm scales stay in higher precision; residual streams stay FP.
+ *  [P4] "State of the Art Survey", Bi-Real Net row: FP residual shortcut.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#define API __attribute__((visibility("default")))
+
+/* [P5] Notation: sign(x) = +1 if x >= 0, else -1.  The comparison is the IEEE
+ * one: -0.0 >= 0 holds (+1); NaN compares false (-1); denormals compare by
+ * value.  Output s is dense [rows, cols]. */
+API void oracle_sign(const float* x, int64_t rows, int64_t cols, int64_t ldx, int8_t* s)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            s[r * cols + c] = (x[r * ldx + c] >= 0.0f) ? (int8_t)1 : (int8_t)-1;
+}
+
+/* [P2] encoding: a sign of +1 is bit value 0, a sign of -1 is bit value 1.
+ * Element k of a row sits in word k / 32 at bit k % 32 (least significant
+ * bit first).  Bits at positions k >= K and words from ceil(K/32) up to ld-1
+ * are written as 0, i.e. they encode +1 as [P2] requires of pad bits. */
+API void oracle_pack_signs(const int8_t* s, int64_t rows, int64_t K, uint32_t* words, int64_t ld)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t w = 0; w < ld; ++w) words[r * ld + w] = 0u;
+        for (int64_t k = 0; k < K; ++k) {
+            if (s[r * K + k] == -1)
+                words[r * ld + k / 32] |= (uint32_t)1u << (k % 32);
+        }
+    }
+}
+
+/* Inverse of oracle_pack_signs over the first K positions. */
+API void oracle_unpack_signs(const uint32_t* words, int64_t rows, int64_t K, int64_t ld, int8_t* s)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k)
+            s[r * K + k] = ((words[r * ld + k / 32] >> (k % 32)) & 1u) ? (int8_t)-1 : (int8_t)1;
+}
+
+/* [P5] eq. (1): alpha = (1/n) * sum_i |w_i|, one value per output row (per
+ * filter, [P1]).  n is the real row length K.  The sum runs in double in
+ * index order, is divided by K in double and rounded once to float. */
+API void oracle_alpha(const float* W, int64_t N, int64_t K, int64_t ldw, float* alpha)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double sum = 0.0;
+        for (int64_t k = 0; k < K; ++k) sum += fabs((double)W[n * ldw + k]);
+        alpha[n] = (float)(sum / (double)K);
+    }
+}
+
+/* [P5] eq. (4)-(6): the binary dot product w_b^T x_b, computed here as the
+ * plain integer multiply-add of the +1/-1 values.  xs is [M, K], ws is
+ * [N, K] (both dense), D is [M, N]. */
+API void oracle_dot(const int8_t* xs, const int8_t* ws, int64_t M, int64_t N, int64_t K, int32_t* D)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (int32_t)xs[m * K + k] * (int32_t)ws[n * K + k];
+            D[m * N + n] = acc;
+        }
+    }
+}
+
+/* [P5] eq. (1): y = alpha * (w_b^T x_b), one rounded single multiply. */
+API void oracle_scale(const int32_t* D, const float* alpha, int64_t M, int64_t N, float* Y)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            Y[m * N + n] = alpha[n] * (float)D[m * N + n];
+}
+
+/* [P4] Bi-Real Net row and [P3] "residual streams stay FP": the scaled binary
+ * output plus the fp32 shortcut, as two rounded single operations (scale,
+ * then add).  R is [M, N] with leading dimension ldr. */
+API void oracle_scale_residual(const int32_t* D, const float* alpha, const float* R, int64_t ldr,
+                               int64_t M, int64_t N, float* Y)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float z = alpha[n] * (float)D[m * N + n];
+            Y[m * N + n] = z + R[m * ldr + n];
+        }
+}
+
+/* [P1] BatchNorm follows the scaled binary output, and the next binary layer
+ * takes its sign ([P5] eq. (4)).  Inference BatchNorm of z = alpha * D is
+ *     BN(z) = gamma * (z - mean) / sqrt(var + eps) + beta,
+ * and the next sign is +1 iff BN(z) >= 0.  Writing sd = sqrt(var + eps) > 0
+ * and c = gamma * alpha, BN(z) >= 0 is  c * D >= gamma * mean - beta * sd.
+ *   c > 0:  D >= t  with  t = (gamma * mean - beta * sd) / c   -> dir = +1, tau = t
+ *   c < 0:  D <= t                                         -> dir = -1, tau = -t
+ *   c = 0:  the sign is that of BN(0) = beta - gamma * mean / sd, a constant:
+ *           dir = 0, tau = 0 when that constant is >= 0 (sign +1), else 1.
+ * With these, the next sign is +1 iff (float)(dir * D) >= tau (see
+ * oracle_threshold_signs).  Computed in double, tau rounded once to float. */
+API void oracle_bn_fold(const float* gamma, const float* beta, const float* mean, const float* var,
+                        float eps, const float* alpha, int64_t N, float* tau, int8_t* dir)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        double sd = sqrt((double)var[n] + (double)eps);
+        double c = (double)gamma[n] * (double)alpha[n];
+        double rhs = (double)gamma[n] * (double)mean[n] - (double)beta[n] * sd;
+        if (c > 0.0) {
+            dir[n] = 1;
+            tau[n] = (float)(rhs / c);
+        } else if (c < 0.0) {
+            dir[n] = -1;
+            tau[n] = (float)(-(rhs / c));
+        } else {
+            double bn0 = (double)beta[n] - (double)gamma[n] * (double)mean[n] / sd;
+            dir[n] = 0;
+            tau[n] = (bn0 >= 0.0) ? 0.0f : 1.0f;
+        }
+    }
+}
+
+/* The folded BatchNorm decision: s_out = +1 iff (float)(dir * D) >= tau, else
+ * -1.  D is exact as a float for |D| <= 2^24, so the comparison is exact. */
+API void oracle_threshold_signs(const int32_t* D, const float* tau, const int8_t* dir,
+                                int64_t M, int64_t N, int8_t* s_out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float v = (float)((int32_t)dir[n] * D[m * N + n]);
+            s_out[m * N + n] = (v >= tau[n]) ? (int8_t)1 : (int8_t)-1;
+        }
+}
+
+/* im2col of the signs of an NHWC input for a 3x3 convolution with stride 1
+ * and padding 1.  Output row p = (b * H + oh) * W + ow; column
+ * k = (kh * 3 + kw) * C + c (tap-major, channel-minor).  A tap that falls
+ * outside the image contributes +1 for every channel (pad pixels encode +1,
+ * the pad-bit rule of [P2] applied to the spatial border).  Inside the image
+ * the entry is sign(X[b, oh - 1 + kh, ow - 1 + kw, c]) per [P5] Notation. */
+API void oracle_im2col_signs(const float* X, int64_t B, int64_t H, int64_t W, int64_t C, int8_t* cols)
+{
+    const int64_t K = 9 * C;
+    #pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < B * H * W; ++p) {
+        int64_t b = p / (H * W);
+        int64_t oh = (p / W) % H;
+        int64_t ow = p % W;
+        for (int64_t kh = 0; kh < 3; ++kh)
+            for (int64_t kw = 0; kw < 3; ++kw) {
+                int64_t ih = oh - 1 + kh, iw = ow - 1 + kw;
+                int inside = (ih >= 0 && ih < H && iw >= 0 && iw < W);
+                for (int64_t c = 0; c < C; ++c) {
+                    int8_t v = 1;
+                    if (inside)
+                        v = (X[((b * H + ih) * W + iw) * C + c] >= 0.0f) ? (int8_t)1 : (int8_t)-1;
+                    cols[p * K + (kh * 3 + kw) * C + c] = v;
+                }
+            }
+    }
+}
+
+/* [P3] "What is binary vs not": the first layer stays in floating point.
+ * H[m, n] = sum_k X[m, k] * W[n, k] accumulated in double in index order
+ * (each product of two floats is exact in double). */
+API void oracle_dense_f64(const float* X, int64_t ldx, const float* W, int64_t ldw,
+                          int64_t M, int64_t N, int64_t K, double* H)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (double)X[m * ldx + k] * (double)W[n * ldw + k];
+            H[m * N + n] = acc;
+        }
+}
+
+/* [P3]: the last layer stays in floating point and reads the +1/-1 outputs
+ * of the last binary layer.  Y[m, n] = (float)(sum_k s[m, k] * W[n, k]) with
+ * the sum in double in index order, rounded once to float. */
+API void oracle_dense_pm1_f32out(const int8_t* s, const float* W, int64_t ldw,
+                                 int64_t M, int64_t N, int64_t K, float* Y)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (double)s[m * K + k] * (double)W[n * ldw + k];
+            Y[m * N + n] = (float)acc;
+        }
+}

@@ -1,0 +1,400 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+None of these checks re-types an oracle formula: each compares the oracle with
+a different formulation (the XOR-popcount identity on packed words, a numpy
+float64 matmul, exact rational arithmetic, torch's conv2d, values derived by
+hand from a worked example) or with an invariant.  Sources are cited by page
+title and section/equation.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from exact_math import round_to_f32, f32_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_kv(path):
+    out = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split("=", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def _popcount_identity(xw: np.ndarray, ww: np.ndarray, K: int) -> np.ndarray:
+    """K - 2 * sum popcount(x xor w) over packed rows (page "First Principles",
+    section "1. Arithmetic"; page "Extreme Quantization" eq. (6)), computed with
+    numpy's bit count on uint32 words."""
+    x = xw[:, None, :] ^ ww[None, :, :]
+    return (K - 2 * np.bitwise_count(x).sum(axis=-1, dtype=np.int64)).astype(np.int64)
+
+
+def _rand_signs(rng, shape):
+    return np.where(rng.random(shape) < 0.5, 1, -1).astype(np.int8)
+
+
+# ---------------------------------------------------------------- worked example
+def test_exercise1_worked_example():
+    g = _read_kv(os.path.join(GOLDEN, "exercise1.txt"))
+    w = np.array([int(t) for t in g["w_b"].split()], dtype=np.float32)[None, :]
+    x = np.array([int(t) for t in g["x_b"].split()], dtype=np.float32)[None, :]
+    ws, xs = oracle.sign(w), oracle.sign(x)
+    wp, xp = oracle.pack_signs(ws), oracle.pack_signs(xs)
+    assert int(wp[0, 0]) == int(g["w_word"])
+    assert int(xp[0, 0]) == int(g["x_word"])
+    assert bin(int(wp[0, 0]) ^ int(xp[0, 0])).count("1") == int(g["xor_popcount"])
+    assert int(oracle.dot(xs, ws)[0, 0]) == int(g["dot"])
+
+
+# ---------------------------------------------------------------- sign
+def test_sign_edge_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "sign_table.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                h, s, *_ = line.split()
+                rows.append((int(h, 16), int(s)))
+    bits = np.array([r[0] for r in rows], dtype=np.uint32)
+    want = np.array([r[1] for r in rows], dtype=np.int8)
+    got = oracle.sign(bits.view(np.float32)[None, :])[0]
+    np.testing.assert_array_equal(got, want)
+
+
+def test_sign_random_values_match_definition_by_bits():
+    # sign by the IEEE ordering of the bit pattern: x >= 0 iff (non-NaN and the
+    # sign bit clear) or x is -0.0.
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2**32, size=200000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    nonneg = ((bits <= 0x7F800000) | (bits == 0x80000000))
+    want = np.where(nonneg, 1, -1).astype(np.int8)
+    np.testing.assert_array_equal(oracle.sign(x[None, :])[0], want)
+
+
+# ---------------------------------------------------------------- packing
+def test_pack_layout_bit_order_and_pads():
+    # element k -> word k//32, bit k%32; -1 is bit 1; pad bits/words are 0.
+    K = 70
+    s = np.ones((3, K), dtype=np.int8)
+    s[0, 0] = -1
+    s[1, 33] = -1
+    s[2, 69] = -1
+    p = oracle.pack_signs(s, ld=5)
+    assert p.shape == (3, 5)
+    assert p[0].tolist() == [1, 0, 0, 0, 0]
+    assert p[1].tolist() == [0, 2, 0, 0, 0]
+    assert p[2].tolist() == [0, 0, 1 << 5, 0, 0]
+    allneg = -np.ones((1, K), dtype=np.int8)
+    q = oracle.pack_signs(allneg, ld=4)
+    assert q[0].tolist() == [0xFFFFFFFF, 0xFFFFFFFF, 0x3F, 0]   # 6 live bits in word 2
+
+
+def test_pack_unpack_roundtrip():
+    rng = np.random.default_rng(3)
+    for K in (1, 31, 32, 33, 63, 64, 65, 1000):
+        s = _rand_signs(rng, (5, K))
+        p = oracle.pack_signs(s, ld=(K + 31) // 32 + 3)
+        np.testing.assert_array_equal(oracle.unpack_signs(p, K), s)
+
+
+def test_packed_bytes_match_page_formula():
+    # page "First Principles", "Bandwidth math": binary packed weights take
+    # M*N/8 bytes (1/8 byte per weight, 32 binary values per 32-bit word).
+    for (N, K) in ((11008, 4096), (4096, 11008)):
+        p = oracle.pack_signs(np.ones((4, K), dtype=np.int8))
+        assert p.shape[1] * 4 * N == N * K // 8
+
+
+# ---------------------------------------------------------------- the dot identity
+def test_identity_exhaustive_small_K():
+    for K in range(1, 9):
+        S = np.array(list(itertools.product([1, -1], repeat=K)), dtype=np.int8)
+        D = oracle.dot(S, S)
+        P = oracle.pack_signs(S)
+        np.testing.assert_array_equal(D.astype(np.int64), _popcount_identity(P, P, K))
+
+
+@pytest.mark.parametrize("K", list(range(1, 131)) + [576, 1000, 2304, 4096, 11008])
+def test_identity_random_K(K):
+    rng = np.random.default_rng(K)
+    xs, ws = _rand_signs(rng, (6, K)), _rand_signs(rng, (5, K))
+    D = oracle.dot(xs, ws)
+    np.testing.assert_array_equal(
+        D.astype(np.int64), _popcount_identity(oracle.pack_signs(xs), oracle.pack_signs(ws), K))
+
+
+def test_dot_matches_float64_matmul():
+    rng = np.random.default_rng(11)
+    for (M, N, K) in ((64, 256, 1000), (7, 9, 4096), (33, 17, 11008)):
+        xs, ws = _rand_signs(rng, (M, K)), _rand_signs(rng, (N, K))
+        ref = xs.astype(np.float64) @ ws.astype(np.float64).T
+        np.testing.assert_array_equal(oracle.dot(xs, ws), ref.astype(np.int32))
+
+
+def test_dot_invariants():
+    rng = np.random.default_rng(5)
+    K = 1000
+    xs, ws = _rand_signs(rng, (20, K)), _rand_signs(rng, (30, K))
+    D = oracle.dot(xs, ws).astype(np.int64)
+    assert np.all((D - K) % 2 == 0)
+    assert np.all(np.abs(D) <= K)
+    np.testing.assert_array_equal(np.diag(oracle.dot(xs, xs)), np.full(20, K))
+    np.testing.assert_array_equal(np.diag(oracle.dot(xs, -xs)), np.full(20, -K))
+    ws2 = ws.copy()
+    ws2[4] = -ws2[4]
+    D2 = oracle.dot(xs, ws2).astype(np.int64)
+    np.testing.assert_array_equal(D2[:, 4], -D[:, 4])
+    np.testing.assert_array_equal(np.delete(D2, 4, axis=1), np.delete(D, 4, axis=1))
+
+
+def test_pad_bit_invariance_and_negative_control():
+    # page "First Principles": pad bits must encode +1 so they do not add to the
+    # disagreement count d.  Equal pad bits on both sides leave the identity's
+    # value unchanged; mismatched pad bits lower it by 2 per mismatch.
+    rng = np.random.default_rng(9)
+    for K in (1, 5, 31, 33, 1000):
+        xs, ws = _rand_signs(rng, (4, K)), _rand_signs(rng, (3, K))
+        D = oracle.dot(xs, ws).astype(np.int64)
+        xp, wp = oracle.pack_signs(xs), oracle.pack_signs(ws)
+        live = K % 32
+        if live == 0:
+            continue
+        padmask = np.uint32((0xFFFFFFFF << live) & 0xFFFFFFFF)
+        pat = np.uint32(rng.integers(1, 2**32, dtype=np.uint64)) & padmask
+        xq, wq = xp.copy(), wp.copy()
+        xq[:, -1] |= pat
+        wq[:, -1] |= pat
+        np.testing.assert_array_equal(_popcount_identity(xq, wq, K), D)
+        xr = xp.copy()
+        xr[:, -1] |= pat
+        mism = bin(int(pat)).count("1")
+        np.testing.assert_array_equal(_popcount_identity(xr, wp, K), D - 2 * mism)
+
+
+# ---------------------------------------------------------------- alpha
+def test_alpha_equals_exact_rational_mean():
+    # page "Extreme Quantization" eq. (1): alpha = (1/n) sum |w_i|.  The exact
+    # rational mean, rounded once to fp32, must equal the oracle's value.
+    for K in (576, 1000, 2304, 4096, 11008, 16384):
+        W = workloads.normal_f32(90000 + K, (6, K))
+        a = oracle.alpha(W)
+        for n in range(W.shape[0]):
+            exact = sum((Fraction(float(abs(v))) for v in W[n]), Fraction(0)) / K
+            assert f32_bits(a[n]) == f32_bits(round_to_f32(exact)), (K, n)
+
+
+def test_alpha_closed_forms():
+    rng = np.random.default_rng(1)
+    K = 1000
+    W = (0.75 * _rand_signs(rng, (4, K))).astype(np.float32)
+    np.testing.assert_array_equal(oracle.alpha(W), np.full(4, 0.75, np.float32))
+    assert oracle.alpha(np.zeros((1, 33), np.float32))[0] == 0.0
+    # mean of |1..K| = (K+1)/2
+    W = np.arange(1, K + 1, dtype=np.float32)[None, :] * np.where(np.arange(K) % 3, 1, -1)
+    assert oracle.alpha(W.astype(np.float32))[0] == np.float32((K + 1) / 2)
+
+
+# ---------------------------------------------------------------- scaling epilogues
+def test_scale_is_one_rounded_multiply():
+    rng = np.random.default_rng(2)
+    a = (rng.random(50) * 3).astype(np.float32)
+    D = rng.integers(-2**24, 2**24 + 1, size=(40, 50)).astype(np.int32)
+    D[0, :] = 0
+    Y = oracle.scale(D, a)
+    for m in range(0, 40, 3):
+        for n in range(50):
+            want = round_to_f32(Fraction(float(a[n])) * int(D[m, n]))
+            assert f32_bits(Y[m, n]) == f32_bits(want)
+
+
+def test_scale_residual_two_roundings():
+    rng = np.random.default_rng(4)
+    a = (rng.random(30) * 2).astype(np.float32)
+    D = rng.integers(-5000, 5001, size=(20, 30)).astype(np.int32)
+    R = workloads.normal_f32(44, (20, 30)) * np.float32(1e3)
+    R[0, :5] = np.float32(1e-30)     # very different exponents
+    Y = oracle.scale_residual(D, a, R)
+    for m in range(20):
+        for n in range(30):
+            z = round_to_f32(Fraction(float(a[n])) * int(D[m, n]))
+            want = round_to_f32(Fraction(float(z)) + Fraction(float(R[m, n])))
+            assert f32_bits(Y[m, n]) == f32_bits(want)
+
+
+# ---------------------------------------------------------------- BatchNorm fold
+def _exact_bn_sign(D, a, g, b, mu, var, eps):
+    """sign(BN(alpha*D)) decided exactly: BN >= 0  iff  g*(a*D - mu) >= -b*sd,
+    sd = sqrt(var + eps), decided by squaring with sign cases."""
+    a, g, b, mu = (Fraction(float(v)) for v in (a, g, b, mu))
+    v2 = Fraction(float(var)) + Fraction(float(eps))
+    L = g * (a * D - mu)
+    R0 = -b          # right side is R0 * sd, sd > 0
+    if R0 <= 0 and L >= 0:
+        return 1
+    if R0 >= 0 and L < 0:
+        return -1
+    if R0 > 0:       # L >= 0: L >= R0*sd  iff  L^2 >= R0^2 v2
+        return 1 if L * L >= R0 * R0 * v2 else -1
+    # R0 < 0, L < 0: L >= R0*sd  iff  |L| <= |R0| sd  iff  L^2 <= R0^2 v2
+    return 1 if L * L <= R0 * R0 * v2 else -1
+
+
+def test_bn_fold_exact_ties_and_directions():
+    one = np.ones(1, np.float32)
+    zero = np.zeros(1, np.float32)
+    # gamma=1, alpha=0.5, beta=-1, mean=0, var=1, eps=0: BN = 0.5 D - 1, tie at D=2
+    tau, d = oracle.bn_fold(one, -one, zero, one, 0.0, 0.5 * one)
+    assert d[0] == 1 and tau[0] == 2.0
+    D = np.array([[1], [2], [3]], np.int32)          # M=3 rows, one channel
+    np.testing.assert_array_equal(oracle.threshold_signs(D, tau, d)[:, 0], [-1, 1, 1])
+    # gamma=-1: BN = -0.5 D - 1 >= 0 iff D <= -2 (tie at -2 -> +1)
+    tau, d = oracle.bn_fold(-one, -one, zero, one, 0.0, 0.5 * one)
+    assert d[0] == -1
+    D = np.array([[-3], [-2], [-1]], np.int32)
+    np.testing.assert_array_equal(oracle.threshold_signs(D, tau, d)[:, 0], [1, 1, -1])
+    # gamma=0: constant sign of beta
+    for beta, want in ((0.3, 1), (-0.3, -1), (0.0, 1)):
+        tau, d = oracle.bn_fold(zero, beta * one, zero, one, 1e-5, 0.5 * one)
+        assert d[0] == 0
+        got = oracle.threshold_signs(np.array([[-7], [0], [9]], np.int32), tau, d)[:, 0]
+        np.testing.assert_array_equal(got, [want] * 3)
+    # alpha=0 (all-zero weight row): BN(0) = beta - gamma*mean/sd
+    tau, d = oracle.bn_fold(one, 0.2 * one, one, one, 0.0, zero)
+    assert d[0] == 0
+    assert oracle.threshold_signs(np.array([[5]], np.int32), tau, d)[0, 0] == -1
+
+
+def test_bn_fold_decisions_match_exact_rational():
+    rng = np.random.default_rng(12)
+    N = 64
+    g, b, mu, var, eps = workloads.bn_params(2001, N)
+    g = g * np.where(np.arange(N) % 5 == 0, -1, 1).astype(np.float32)   # both directions
+    mu = (rng.normal(0, 3, N)).astype(np.float32)
+    var = (rng.random(N) * 2 + 0.1).astype(np.float32)
+    a = (rng.random(N) + 0.2).astype(np.float32)
+    tau, d = oracle.bn_fold(g, b, mu, var, eps, a)
+    # D values around every threshold, both parities
+    Dn = np.rint(tau.astype(np.float64) * d).astype(np.int64)
+    D = (Dn[None, :] + np.arange(-3, 4)[:, None]).astype(np.int32)
+    s = oracle.threshold_signs(D, tau, d)
+    for i in range(D.shape[0]):
+        for n in range(N):
+            assert s[i, n] == _exact_bn_sign(int(D[i, n]), a[n], g[n], b[n], mu[n], var[n], eps), (i, n)
+
+
+# ---------------------------------------------------------------- conv im2col
+def _direct_conv_pm1(xs_nhwc: np.ndarray, ws_ohwi: np.ndarray) -> np.ndarray:
+    """3x3, stride 1, pad 1 with pad value +1, as direct loops over the
+    padded +1/-1 image (no im2col)."""
+    B, H, W, C = xs_nhwc.shape
+    Co = ws_ohwi.shape[0]
+    P = np.ones((B, H + 2, W + 2, C), dtype=np.int64)
+    P[:, 1:-1, 1:-1, :] = xs_nhwc
+    out = np.zeros((B, H, W, Co), dtype=np.int64)
+    for b in range(B):
+        for oh in range(H):
+            for ow in range(W):
+                for o in range(Co):
+                    acc = 0
+                    for kh in range(3):
+                        for kw in range(3):
+                            acc += int(np.dot(P[b, oh + kh, ow + kw, :], ws_ohwi[o, kh, kw, :].astype(np.int64)))
+                    out[b, oh, ow, o] = acc
+    return out
+
+
+def test_im2col_dot_matches_direct_conv_and_torch():
+    import torch
+    import torch.nn.functional as F
+    X = workloads.normal_f32(5100, (2, 5, 4, 3))
+    Wt = workloads.normal_f32(5101, (4, 3, 3, 3))
+    D = oracle.dot(oracle.im2col_signs(X), oracle.sign(Wt.reshape(4, 27)))
+    xs = oracle.sign(X.reshape(-1, 3)).reshape(X.shape)
+    ws = oracle.sign(Wt.reshape(-1, 3)).reshape(Wt.shape)
+    direct = _direct_conv_pm1(xs, ws).reshape(-1, 4)
+    np.testing.assert_array_equal(D.astype(np.int64), direct)
+    xt = torch.from_numpy(xs.astype(np.float64)).permute(0, 3, 1, 2)
+    wt = torch.from_numpy(ws.astype(np.float64)).permute(0, 3, 1, 2)
+    ref = F.conv2d(F.pad(xt, (1, 1, 1, 1), value=1.0), wt)
+    np.testing.assert_array_equal(D.astype(np.int64),
+                                  ref.permute(0, 2, 3, 1).reshape(-1, 4).numpy().astype(np.int64))
+
+
+def test_im2col_border_taps_are_plus_one():
+    X = -np.ones((1, 2, 2, 2), dtype=np.float32)     # every in-image sign is -1
+    cols = oracle.im2col_signs(X)
+    # output pixel (0,0): taps with kh==0 or kw==0 are outside -> +1
+    row = cols[0].reshape(3, 3, 2)
+    for kh in range(3):
+        for kw in range(3):
+            want = 1 if (kh == 0 or kw == 0) else -1
+            assert np.all(row[kh, kw] == want), (kh, kw)
+
+
+def test_conv_block_residual_layout():
+    X = workloads.normal_f32(5200, (1, 3, 3, 4))
+    Wt = workloads.normal_f32(5201, (4, 3, 3, 4))
+    D, Y, a = oracle.conv_block(X, Wt)
+    np.testing.assert_array_equal(Y, oracle.scale_residual(D, a, X.reshape(9, 4)))
+
+
+# ---------------------------------------------------------------- FP first/last layers
+def test_dense_f64_matches_numpy_and_exact():
+    X = workloads.uniform01_f32(2000, (8, 784))
+    W = workloads.normal_f32(2001, (16, 784))
+    H = oracle.dense_f64(X, W)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    bound = 784 * 2.0**-52 * (np.abs(X).astype(np.float64) @ np.abs(W).astype(np.float64).T)
+    assert np.all(np.abs(H - ref) <= 2 * bound)
+    for (m, n) in ((0, 0), (3, 7), (7, 15)):
+        exact = sum((Fraction(float(X[m, k])) * Fraction(float(W[n, k])) for k in range(784)), Fraction(0))
+        assert abs(Fraction(H[m, n]) - exact) <= Fraction(float(bound[m, n]))
+
+
+def test_dense_pm1_f32out_is_rounded_exact_sum():
+    rng = np.random.default_rng(8)
+    s = _rand_signs(rng, (4, 300))
+    W = workloads.normal_f32(2005, (3, 300))
+    Y = oracle.dense_pm1_f32out(s, W)
+    for m in range(4):
+        for n in range(3):
+            exact = sum((int(s[m, k]) * Fraction(float(W[n, k])) for k in range(300)), Fraction(0))
+            # double accumulation error is far below half an fp32 ulp here
+            assert abs(float(Y[m, n]) - float(exact)) <= abs(float(exact)) * 2.0**-23 + 1e-30
+            assert f32_bits(Y[m, n]) == f32_bits(round_to_f32(exact))
+
+
+def test_mlp_chain_small_composition():
+    X = workloads.uniform01_f32(2100, (16, 40))
+    W1 = workloads.normal_f32(2101, (64, 40))
+    hidden = []
+    for i in range(3):
+        Wh = workloads.normal_f32(2110 + i, (64, 64))
+        hidden.append((Wh,) + workloads.bn_params(2120 + i, 64))
+    W5 = workloads.normal_f32(2130, (10, 64))
+    r = oracle.binary_mlp(X, W1, hidden, W5)
+    s = r["signs"][0]
+    np.testing.assert_array_equal(s, np.where(X.astype(np.float64) @ W1.astype(np.float64).T >= 0, 1, -1))
+    for i, (Wh, g, b, mu, var, eps) in enumerate(hidden):
+        D = (s.astype(np.int64) @ np.where(Wh >= 0, 1, -1).T)
+        np.testing.assert_array_equal(r["dots"][i], D)
+        for m in range(0, 16, 5):
+            for n in range(64):
+                want = _exact_bn_sign(int(D[m, n]), r["alphas"][i][n], g[n], b[n], mu[n], var[n], eps)
+                assert r["signs"][i + 1][m, n] == want
+        s = r["signs"][i + 1]
+    assert r["logits"].shape == (16, 10)
