@@ -1,0 +1,208 @@
+/*
+ * bnn.h - C ABI of libbnn.so, the MI355X (gfx950) binary-neural-network
+ * inference path: sign + bit-pack, XNOR-popcount GEMM / GEMV, and fused
+ * epilogues (alpha scale, fp32 residual, folded-BatchNorm threshold with
+ * re-sign and re-pack).
+ *
+ * Sources (page title, section / equation):
+ *  [P2] "First Principles: Why Binary Ops Can Be Exponentially Faster",
+ *       section "1. Arithmetic: MAC -> XNOR + popcount": bit 0 encodes +1,
+ *       bit 1 encodes -1; <w,x> = N - 2 popcount(w_bit xor x_bit); pad bits
+ *       encode +1; pack bits into machine words.  Section "Bandwidth math":
+ *       batch-1 y = Wx moves about MN/8 bytes of packed weights.
+ *  [P5] "Extreme Quantization: Binary, Ternary & 1-bit LLMs": "Notation"
+ *       (sign(x) = +1 for x >= 0, else -1), "Binary Neural Networks" eq. (1)
+ *       (y = alpha * w_b^T x, alpha = mean |w|), "XNOR-Net" eq. (4)-(6).
+ *  [P1] "Binary Neural Network (BNN)" glossary: activations are binarized
+ *       before each binary layer; per-filter scaling factors; BatchNorm.
+ *  [P3] "Perfected Concept", "What is binary vs not": first/last layers and
+ *       BatchNorm scales stay FP; residual streams stay FP.
+ *  [P4] "State of the Art Survey", Bi-Real Net row: FP residual shortcut.
+ *
+ * Conventions (all entry points):
+ *  - Data pointers are DEVICE pointers unless the name ends in _host.  The
+ *    caller owns every buffer; the library never allocates, frees or
+ *    synchronizes.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Argument structs are host memory, read during the call only.
+ *  - Arguments are validated before anything is launched.  A non-OK status
+ *    means nothing was launched and no memory was touched.  BNN_ERR_HIP means
+ *    the HIP runtime refused a launch.  Faults inside kernels surface at the
+ *    caller's next synchronization.
+ *  - No global mutable state: calls may be issued from several host threads.
+ *  - Sizes: 1 <= K <= 2^24 (so every dot product is exact as an fp32 and an
+ *    int32).  M == 0 or N == 0 is a valid empty call (nothing launched).
+ *
+ * Packed layout (the "packed operand" of every call):
+ *  - A packed matrix [rows, ld] of uint32 words holds row r's element k at
+ *    word r*ld + k/32, bit k%32 (least significant bit first); bit value 0
+ *    is +1 and 1 is -1 [P2].  Kw = ceil(K/32) words carry data.
+ *  - Pad bits (k >= K in word Kw-1) and pad words (Kw .. ld-1) hold 0, i.e.
+ *    +1 [P2]; the pack calls always write them.  The GEMM/GEMV read words
+ *    0..Kw-1 only and need the pad bits of the two operands to be equal.
+ *  - Packed operands: base pointer 16-byte aligned and ld a multiple of 4
+ *    (rows are read in 16-byte units), else BNN_ERR_ALIGN.
+ */
+#ifndef BNN_H
+#define BNN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* bnn_stream_t; /* a hipStream_t; NULL selects the null stream */
+
+typedef enum bnn_status {
+    BNN_OK = 0,
+    BNN_ERR_NULL = 1,        /* a required pointer is NULL */
+    BNN_ERR_SHAPE = 2,       /* a size is negative or out of range */
+    BNN_ERR_LD = 3,          /* a leading dimension is smaller than the row */
+    BNN_ERR_ALIGN = 4,       /* a packed operand is misaligned */
+    BNN_ERR_UNSUPPORTED = 5, /* unknown flag, flag combination or geometry */
+    BNN_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} bnn_status;
+
+#define BNN_MAX_K ((int64_t)1 << 24)
+
+/* Epilogue flags of bnn_linear_fused (OR them together). */
+#define BNN_EPI_DOT_I32      1u /* D[m,n] = K - 2*popcount(...)  (int32)              */
+#define BNN_EPI_SCALE_F32    2u /* Y[m,n] = fl32(alpha[n] * D[m,n])  [P5] eq. (1)       */
+#define BNN_EPI_RESIDUAL_F32 4u /* Y[m,n] = fl32(fl32(alpha[n]*D) + R[m,n])  [P4], [P3]  */
+#define BNN_EPI_THRESH_PACK  8u /* Op bit (m,n) = ((float)(dir[n]*D) >= tau[n]) ? 0 : 1  */
+
+/* Geometry of a binary 3x3 convolution lowered to a GEMM by im2col.
+ * Input NHWC [B, H, W, C] fp32, contiguous.  Only R = S = 3, stride 1,
+ * pad 1 is supported; the pad pixels encode +1 (bit 0), the pad-bit rule of
+ * [P2] applied to the image border.  The im2col row of output pixel
+ * p = (b*H + oh)*W + ow has K = 9*C entries, k = (kh*3 + kw)*C + c. */
+typedef struct bnn_conv_geom {
+    int64_t B, H, W, C;
+    int64_t R, S;        /* kernel height, width: must be 3, 3 */
+    int64_t stride, pad; /* must be 1, 1 */
+} bnn_conv_geom;
+
+/* Arguments of bnn_linear_fused.  Host struct; every pointer is device
+ * memory.  Pointers an epilogue does not use may be NULL. */
+typedef struct bnn_fused_args {
+    const uint32_t* Xp; int64_t ldXp; /* packed activations [M, ldXp]           */
+    const uint32_t* Wp; int64_t ldWp; /* packed weights     [N, ldWp]           */
+    int64_t M, N, K;
+    uint32_t epilogue;                /* OR of BNN_EPI_* (at least one)         */
+    int32_t* D; int64_t ldD;          /* DOT_I32: int32 [M, ldD], ldD >= N      */
+    const float* alpha;               /* SCALE/RESIDUAL: fp32 [N]               */
+    float* Y; int64_t ldY;            /* SCALE/RESIDUAL: fp32 [M, ldY]          */
+    const float* R; int64_t ldR;      /* RESIDUAL: fp32 [M, ldR]; may not alias Y
+                                         unless R == Y and ldR == ldY           */
+    const float* tau;                 /* THRESH_PACK: fp32 [N]                  */
+    const int8_t* dir;                /* THRESH_PACK: int8 [N] in {+1, -1, 0}   */
+    uint32_t* Op; int64_t ldOp;       /* THRESH_PACK: packed [M, ldOp],
+                                         ldOp >= ceil(N/32); pad bits/words 0   */
+} bnn_fused_args;
+
+/* Number of 32-bit words that carry K packed bits: ceil(K/32); -1 if K < 0. */
+int64_t bnn_packed_words(int64_t K);
+
+/* Static, human-readable name of a status code. */
+const char* bnn_status_string(bnn_status status);
+
+/* Binarize and pack weights, and compute the per-output-row scale.
+ * [P1] weights are binarized once for inference; [P5] Notation for sign;
+ * [P2] encoding; [P5] eq. (1) alpha = (1/K) sum_k |W[n,k]| per output row.
+ *  W     fp32 [N, ldW] (row-major, ldW >= K, 4-byte aligned).
+ *  Wp    packed [N, ldWp] output (16-byte aligned, ldWp % 4 == 0,
+ *        ldWp >= Kw); bits, pad bits and pad words are all written.
+ *  alpha fp32 [N] output, or NULL to skip.  The sum of |W| runs in double
+ *        and is rounded once to fp32 after the division by K.
+ * sign(x) is decided on the bit pattern: +1 for +0.0, -0.0 and every x > 0
+ * including +inf and positive denormals; -1 for x < 0 and for NaN. */
+bnn_status bnn_pack_weights(const float* W, int64_t N, int64_t K, int64_t ldW,
+                            uint32_t* Wp, int64_t ldWp, float* alpha,
+                            bnn_stream_t stream);
+
+/* Binarize and pack activations.  [P1] each layer's activations are
+ * binarized before the next binary layer; [P5] eq. (4) x_b = sign(x).
+ *  geom == NULL: X is fp32 [M, ldX] (ldX >= K), packed row by row.
+ *  geom != NULL: X is the NHWC image of *geom; the call writes its packed
+ *        im2col matrix (see bnn_conv_geom).  M must equal B*H*W and K must
+ *        equal 9*C; ldX is ignored.
+ *  Xp    packed [M, ldXp] output (16-byte aligned, ldXp % 4 == 0,
+ *        ldXp >= Kw); pad bits and pad words written as 0. */
+bnn_status bnn_pack_activations(const float* X, int64_t M, int64_t K, int64_t ldX,
+                                const bnn_conv_geom* geom,
+                                uint32_t* Xp, int64_t ldXp, bnn_stream_t stream);
+
+/* XNOR-popcount binary matrix multiply [P2], [P5] eq. (6):
+ *     D[m,n] = K - 2 * sum_{w < Kw} popcount(Xp[m,w] xor Wp[n,w])
+ *     Y[m,n] = fl32(alpha[n] * (float)D[m,n])          ([P5] eq. (1))
+ *  Xp [M, ldXp], Wp [N, ldWp]: packed operands (see the layout above).
+ *  D  int32 [M, ldD] (ldD >= N) or NULL; Y fp32 [M, ldY] (ldY >= N) or NULL;
+ *  alpha fp32 [N], required when Y is given.  At least one of D, Y.
+ *  Small M (M <= 4, the batch-1 decode case of [P2] "Bandwidth math") runs
+ *  an HBM-streaming GEMV kernel; larger M the register-blocked GEMM. */
+bnn_status bnn_xnor_gemm(const uint32_t* Xp, int64_t ldXp,
+                         const uint32_t* Wp, int64_t ldWp,
+                         int64_t M, int64_t N, int64_t K,
+                         int32_t* D, int64_t ldD,
+                         const float* alpha, float* Y, int64_t ldY,
+                         bnn_stream_t stream);
+
+/* The XNOR-popcount GEMM with a fused epilogue (see BNN_EPI_*):
+ *  DOT_I32      D as in bnn_xnor_gemm.
+ *  SCALE_F32    Y = fl32(alpha[n] * D)                               [P5] eq. (1)
+ *  RESIDUAL_F32 with SCALE_F32: Y = fl32(fl32(alpha[n] * D) + R[m,n]), two
+ *               rounded operations, no fused multiply-add      [P4] Bi-Real, [P3]
+ *  THRESH_PACK  folded BatchNorm followed by sign [P1], [P5] eq. (4): the
+ *               output bit of (m,n) is 0 (+1) iff (float)(dir[n]*D) >= tau[n],
+ *               else 1 (-1); packed along n (bit n%32 of word n/32 of row m),
+ *               so Op is the packed activation matrix of the next binary
+ *               layer (its K is N).  Bits n >= N and words ceil(N/32)..ldOp-1
+ *               are written as 0.  tau/dir come from
+ *               bnn_fold_bn_thresholds_host.
+ * Errors: RESIDUAL without SCALE, no flag, or unknown flag bits ->
+ * BNN_ERR_UNSUPPORTED. */
+bnn_status bnn_linear_fused(const bnn_fused_args* args, bnn_stream_t stream);
+
+/* Fold inference BatchNorm of z = alpha[n] * D followed by sign into the
+ * (tau, dir) pair consumed by BNN_EPI_THRESH_PACK.  [P1] BatchNorm around
+ * binary layers; [P3] BatchNorm scales stay FP.  HOST memory, synchronous.
+ *   BN(z) = gamma (z - mean) / sqrt(var + eps) + beta ; next sign = +1 iff BN >= 0.
+ * With sd = sqrt(var + eps) and c = gamma*alpha (double):
+ *   c > 0: dir = +1, tau = fl32((gamma*mean - beta*sd) / c)      (D >= tau)
+ *   c < 0: dir = -1, tau = fl32(-(gamma*mean - beta*sd) / c)     (-D >= tau)
+ *   c = 0: dir =  0, tau = 0 if beta - gamma*mean/sd >= 0 else 1 (constant)
+ * Errors: NULL pointer -> BNN_ERR_NULL; N < 0 -> BNN_ERR_SHAPE. */
+bnn_status bnn_fold_bn_thresholds_host(const float* gamma, const float* beta,
+                                       const float* mean, const float* var, float eps,
+                                       const float* alpha, int64_t N,
+                                       float* tau, int8_t* dir);
+
+/* First FP layer of a binary network [P3] ("first / last layers stay higher
+ * precision"), fused with the sign + pack of its output [P5] eq. (4):
+ *     h[m,n] = sum_k X[m,k] * W[n,k]   (products exact, accumulated in double)
+ *     Op bit (m,n) = (h >= 0) ? 0 : 1, packed along n as in THRESH_PACK.
+ *  X fp32 [M, ldX], W fp32 [N, ldW] (ldX, ldW >= K; 4-byte aligned);
+ *  Op packed [M, ldOp], ldOp >= ceil(N/32), pad bits/words written 0.
+ *  K may exceed 2^24 here only up to 2^31-1 (no exactness claim on h). */
+bnn_status bnn_dense_f32_sign_pack(const float* X, int64_t ldX,
+                                   const float* W, int64_t ldW,
+                                   int64_t M, int64_t N, int64_t K,
+                                   uint32_t* Op, int64_t ldOp, bnn_stream_t stream);
+
+/* Last FP layer of a binary network [P3], reading the +1/-1 outputs of the
+ * last binary layer in packed form:
+ *     Y[m,n] = fl32( sum_k s(m,k) * W[n,k] ),  s = +1 for bit 0, -1 for bit 1,
+ *  the sum in double (exact terms), rounded once.
+ *  Xp packed [M, ldXp] (16-byte aligned, ldXp % 4 == 0, ldXp >= Kw);
+ *  W fp32 [N, ldW] (ldW >= K); Y fp32 [M, ldY] (ldY >= N). */
+bnn_status bnn_dense_binact_f32(const uint32_t* Xp, int64_t ldXp,
+                                const float* W, int64_t ldW,
+                                int64_t M, int64_t N, int64_t K,
+                                float* Y, int64_t ldY, bnn_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BNN_H */

@@ -1,0 +1,171 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point the header declares, rejects bad arguments before any launch, and its
+host-side BatchNorm fold agrees bit for bit with the oracle's."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bnn.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_LD, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = range(7)
+
+# Fake device addresses: validation never dereferences them, and every case
+# below fails validation, so nothing is launched.
+A16 = 0x10000          # 16-byte aligned
+A4 = 0x10004           # 4-byte aligned, not 16
+A2 = 0x10002           # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    import xnor_popcount_gemm_amd as bnn
+    return bnn.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bnn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(L):
+    names = declared_functions()
+    assert {"bnn_pack_weights", "bnn_pack_activations", "bnn_xnor_gemm", "bnn_linear_fused"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/bnn.h but not exported"
+
+
+def test_packed_words_and_status_strings(L):
+    assert [L.bnn_packed_words(k) for k in (0, 1, 31, 32, 33, 1000, 16384)] == [0, 1, 1, 1, 2, 32, 512]
+    assert L.bnn_packed_words(-1) == -1
+    for s in range(7):
+        assert L.bnn_status_string(s).startswith(b"BNN_")
+
+
+@pytest.mark.parametrize("args,want", [
+    # (W, N, K, ldW, Wp, ldWp, alpha)
+    ((0, 4, 64, 64, A16, 4, None), ERR_NULL),
+    ((A16, 4, 64, 64, 0, 4, None), ERR_NULL),
+    ((A16, 4, 0, 64, A16, 4, None), ERR_SHAPE),
+    ((A16, 4, (1 << 24) + 1, (1 << 24) + 1, A16, 1 << 19, None), ERR_SHAPE),
+    ((A16, -1, 64, 64, A16, 4, None), ERR_SHAPE),
+    ((A16, 4, 64, 63, A16, 4, None), ERR_LD),
+    ((A16, 4, 1000, 1000, A16, 28, None), ERR_LD),
+    ((A16, 4, 64, 64, A4, 4, None), ERR_ALIGN),
+    ((A16, 4, 64, 64, A16, 6, None), ERR_ALIGN),
+    ((A2, 4, 64, 64, A16, 4, None), ERR_ALIGN),
+    ((A16, 4, 64, 64, A16, 4, A2), ERR_ALIGN),
+])
+def test_pack_weights_validation(L, args, want):
+    W, N, K, ldW, Wp, ldWp, a = args
+    assert L.bnn_pack_weights(W, N, K, ldW, Wp, ldWp, a, None) == want
+
+
+def test_pack_activations_validation(L):
+    import xnor_popcount_gemm_amd as bnn
+    bad = bnn._ConvGeom(2, 5, 5, 8, 3, 3, 2, 1)       # stride 2: unsupported
+    assert L.bnn_pack_activations(A16, 50, 72, 8, ctypes.byref(bad), A16, 4, None) == ERR_UNSUPPORTED
+    g2 = bnn._ConvGeom(2, 5, 5, 8, 3, 3, 1, 1)
+    assert L.bnn_pack_activations(A16, 49, 72, 8, ctypes.byref(g2), A16, 4, None) == ERR_SHAPE   # M != B*H*W
+    assert L.bnn_pack_activations(A16, 50, 71, 8, ctypes.byref(g2), A16, 4, None) == ERR_SHAPE   # K != 9*C
+    assert L.bnn_pack_activations(0, 4, 64, 64, None, A16, 4, None) == ERR_NULL
+    assert L.bnn_pack_activations(A16, 4, 64, 60, None, A16, 4, None) == ERR_LD
+    assert L.bnn_pack_activations(A16, 4, 64, 64, None, A16 + 4, 4, None) == ERR_ALIGN
+
+
+def test_conv_geom_struct_layout():
+    import xnor_popcount_gemm_amd as bnn
+    assert ctypes.sizeof(bnn._ConvGeom) == 8 * 8
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Xp=0), ERR_NULL),
+    (dict(Wp=0), ERR_NULL),
+    (dict(D=0, Y=0), ERR_NULL),
+    (dict(K=0), ERR_SHAPE),
+    (dict(M=-1), ERR_SHAPE),
+    (dict(ldXp=1), ERR_LD),
+    (dict(ldWp=0), ERR_LD),
+    (dict(ldD=7), ERR_LD),
+    (dict(Xp=A4), ERR_ALIGN),
+    (dict(ldWp=6), ERR_ALIGN),
+    (dict(D=A2), ERR_ALIGN),
+    (dict(Y=A16, alpha=0), ERR_NULL),
+    (dict(D=0, Y=A16, alpha=A16, ldY=3), ERR_LD),
+])
+def test_xnor_gemm_validation(L, kw, want):
+    a = dict(Xp=A16, ldXp=4, Wp=A16, ldWp=4, M=3, N=8, K=100, D=A16, ldD=8, alpha=None, Y=None, ldY=0)
+    a.update(kw)
+    st = L.bnn_xnor_gemm(a["Xp"], a["ldXp"], a["Wp"], a["ldWp"], a["M"], a["N"], a["K"],
+                         a["D"], a["ldD"], a["alpha"], a["Y"], a["ldY"], None)
+    assert st == want
+
+
+def _fused(**kw):
+    import xnor_popcount_gemm_amd as bnn
+    a = bnn._FusedArgs()
+    base = dict(Xp=A16, ldXp=4, Wp=A16, ldWp=4, M=3, N=40, K=100, epilogue=bnn.EPI_DOT_I32,
+                D=A16, ldD=40)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(epilogue=0), ERR_UNSUPPORTED),
+    (dict(epilogue=16), ERR_UNSUPPORTED),
+    (dict(epilogue=4, Y=A16, ldY=40, R=A16, ldR=40, alpha=A16), ERR_UNSUPPORTED),   # residual without scale
+    (dict(epilogue=8), ERR_NULL),                                                 # thresh without tau/dir/Op
+    (dict(epilogue=8, tau=A16, dir=A16, Op=A16, ldOp=1), ERR_LD),                 # ldOp < ceil(40/32)
+    (dict(epilogue=6, Y=A16, ldY=40, alpha=A16), ERR_NULL),                       # residual without R
+    (dict(epilogue=6, Y=A16, ldY=40, alpha=A16, R=A16 + 64, ldR=40), ERR_UNSUPPORTED),  # R, Y overlap
+    (dict(M=(1 << 31)), ERR_SHAPE),
+])
+def test_linear_fused_validation(L, kw, want):
+    a = _fused(**kw)
+    assert L.bnn_linear_fused(ctypes.byref(a), None) == want
+    assert L.bnn_linear_fused(None, None) == ERR_NULL
+
+
+def test_dense_support_validation(L):
+    assert L.bnn_dense_f32_sign_pack(0, 784, A16, 784, 4, 64, 784, A16, 4, None) == ERR_NULL
+    assert L.bnn_dense_f32_sign_pack(A16, 783, A16, 784, 4, 64, 784, A16, 4, None) == ERR_LD
+    assert L.bnn_dense_f32_sign_pack(A16, 784, A16, 784, 4, 64, 784, A16, 1, None) == ERR_LD
+    assert L.bnn_dense_binact_f32(A4, 128, A16, 4096, 4, 10, 4096, A16, 10, None) == ERR_ALIGN
+    assert L.bnn_dense_binact_f32(A16, 128, A16, 4096, 4, 10, 4096, A16, 9, None) == ERR_LD
+
+
+def test_empty_calls_launch_nothing(L):
+    # M == 0 or N == 0 is a valid empty call that returns before any launch.
+    assert L.bnn_xnor_gemm(A16, 4, A16, 4, 0, 8, 100, A16, 8, None, None, 0, None) == OK
+    assert L.bnn_xnor_gemm(A16, 4, A16, 4, 3, 0, 100, A16, 8, None, None, 0, None) == OK
+    assert L.bnn_pack_weights(A16, 0, 64, 64, A16, 4, None, None) == OK
+    assert L.bnn_pack_activations(A16, 0, 64, 64, None, A16, 4, None) == OK
+
+
+def test_fold_bn_thresholds_matches_oracle_bit_exact():
+    import xnor_popcount_gemm_amd as bnn
+    for seed in (2001, 2002, 2003):
+        N = 4096
+        g, b, mu, var, eps = workloads.bn_params(seed, N)
+        rng = np.random.default_rng(seed)
+        g = g * np.where(rng.random(N) < 0.1, -1, 1).astype(np.float32)
+        g[:3] = 0.0
+        mu = rng.normal(0, 2, N).astype(np.float32)
+        var = (rng.random(N) * 3 + 0.01).astype(np.float32)
+        a = (rng.random(N) + 0.1).astype(np.float32)
+        a[5] = 0.0
+        t1, d1 = bnn.fold_bn_thresholds(g, b, mu, var, eps, a)
+        t2, d2 = oracle.bn_fold(g, b, mu, var, eps, a)
+        np.testing.assert_array_equal(d1, d2)
+        np.testing.assert_array_equal(t1.view(np.uint32), t2.view(np.uint32))

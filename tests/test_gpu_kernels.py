@@ -1,0 +1,264 @@
+"""GPU parity of each kernel family against the CPU oracle, at sizes the
+oracle finishes in seconds that still span several tiles and ragged tails.
+
+Bar: packed words (including pad bits and pad words) and int32 dot products
+bit-exact; alpha and alpha-scaled fp32 within 1e-6 relative (the sum of |w|
+may round differently in its last fp64 bits, at most one fp32 ulp in alpha);
+the residual sum within 1e-6 of the operands' magnitude.  All calls go through
+the C ABI (the ctypes binding)."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import (require_gpu, banner, dev, host, host_u32, assert_f32_close,
+                      exact_fraction)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bnn():
+    require_gpu()
+    import xnor_popcount_gemm_amd as m
+    m.lib()
+    return m
+
+
+def _signs_with_edges(seed, shape, frac=0.02):
+    x = workloads.normal_f32(seed, shape)
+    return workloads.inject_edge_values(x, seed + 7, frac)
+
+
+# ---------------------------------------------------------------- pack
+@pytest.mark.parametrize("N,K", [(256, 1000), (7, 1), (9, 31), (33, 32), (5, 33), (64, 65),
+                                 (300, 4096), (3, 11008), (129, 2304), (17, 257)])
+def test_pack_weights_bits_and_alpha(bnn, N, K):
+    W = _signs_with_edges(100 + K, (N, K))
+    W[0, :] = np.abs(W[0, :])                   # a row with no NaN, finite alpha
+    W[0, :][~np.isfinite(W[0, :])] = 1.0
+    banner(f"pack_weights N={N} K={K}")
+    Wp, a = bnn.pack_weights(dev(W))
+    torch.cuda.synchronize()
+    ld = Wp.shape[1]
+    np.testing.assert_array_equal(host_u32(Wp), oracle.pack_signs(oracle.sign(W), ld=ld))
+    a_ref = oracle.alpha(W)
+    assert_f32_close(host(a), a_ref, what="alpha")
+
+
+@pytest.mark.parametrize("M,K,extra_ld", [(64, 1000, 0), (3, 70, 12), (1, 4096, 0), (1, 11008, 0),
+                                          (100, 129, 4), (2, 5, 0)])
+def test_pack_activations_dense(bnn, M, K, extra_ld):
+    X = _signs_with_edges(200 + K, (M, K))
+    ld = bnn.padded_ld(K) + extra_ld
+    out = torch.full((M, ld), -1, dtype=torch.int32, device="cuda")   # pads must be overwritten
+    banner(f"pack_activations dense M={M} K={K} ld={ld}")
+    bnn.pack_activations(dev(X), out=out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u32(out), oracle.pack_signs(oracle.sign(X), ld=ld))
+
+
+def test_pack_unaligned_source_rows(bnn):
+    # ld of the fp32 source not a multiple of 4 -> the scalar-load path
+    M, K = 37, 301
+    big = workloads.normal_f32(250, (M, K + 3))
+    Xt = dev(big)[:, :K]
+    assert Xt.stride(0) == K + 3
+    banner("pack_activations scalar path")
+    Xp = bnn.pack_activations(Xt)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u32(Xp), oracle.pack_signs(oracle.sign(big[:, :K]), ld=Xp.shape[1]))
+
+
+@pytest.mark.parametrize("B,H,W,C", [(2, 5, 4, 8), (1, 3, 3, 64), (2, 6, 7, 64), (1, 4, 4, 256),
+                                     (2, 3, 5, 3), (1, 2, 2, 36), (3, 1, 1, 32)])
+def test_pack_im2col3x3(bnn, B, H, W, C):
+    X = _signs_with_edges(300 + C, (B, H, W, C))
+    banner(f"pack im2col B={B} H={H} W={W} C={C}")
+    Xp = bnn.pack_activations(dev(X), conv3x3=True)
+    torch.cuda.synchronize()
+    want = oracle.pack_signs(oracle.im2col_signs(X), ld=Xp.shape[1])
+    np.testing.assert_array_equal(host_u32(Xp), want)
+
+
+# ---------------------------------------------------------------- GEMM / GEMV
+def _packed_pair(M, N, K, seed):
+    X = workloads.normal_f32(seed, (M, K))
+    W = workloads.normal_f32(seed + 1, (N, K))
+    return X, W
+
+
+GEMM_SHAPES = [(64, 256, 1000), (300, 100, 777), (257, 129, 1100), (5, 70, 4096), (1, 7, 33),
+               (2, 300, 11008), (4, 33, 64), (512, 64, 576), (70, 1, 32), (1, 1, 1), (65, 96, 16),
+               (256, 512, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_xnor_gemm_dot_and_scale(bnn, M, N, K):
+    X, W = _packed_pair(M, N, K, 400 + M + N + K)
+    banner(f"xnor_gemm M={M} N={N} K={K}")
+    Wp, a = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    D, Y = bnn.xnor_gemm(Xp, Wp, K, alpha=a, want_dot=True, want_scaled=True)
+    torch.cuda.synchronize()
+    D_ref, Y_ref, a_ref = oracle.binary_linear(X, W)
+    np.testing.assert_array_equal(host(D), D_ref)
+    assert_f32_close(host(a), a_ref, what="alpha")
+    assert_f32_close(host(Y), Y_ref, what="Y")
+    # Y must be exactly alpha * D with the GPU's own alpha (one rounding)
+    np.testing.assert_array_equal(host(Y), (host(a)[None, :] * host(D).astype(np.float32)).astype(np.float32))
+
+
+@pytest.mark.parametrize("tn", ["16", "32", "64"])
+@pytest.mark.parametrize("M,N,K", [(300, 100, 777), (257, 129, 1100), (600, 200, 2304)])
+def test_xnor_gemm_every_column_tile(bnn, tn, M, N, K):
+    X, W = _packed_pair(M, N, K, 500 + M)
+    old = os.environ.get("BNN_GEMM_TN")
+    os.environ["BNN_GEMM_TN"] = tn
+    try:
+        banner(f"xnor_gemm TN={tn} M={M} N={N} K={K}")
+        Wp, a = bnn.pack_weights(dev(W))
+        Xp = bnn.pack_activations(dev(X))
+        D, _ = bnn.xnor_gemm(Xp, Wp, K)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            os.environ.pop("BNN_GEMM_TN", None)
+        else:
+            os.environ["BNN_GEMM_TN"] = old
+    np.testing.assert_array_equal(host(D), oracle.dot(oracle.sign(X), oracle.sign(W)))
+
+
+def test_xnor_gemm_strided_outputs(bnn):
+    M, N, K = 130, 70, 500
+    X, W = _packed_pair(M, N, K, 600)
+    Wp, a = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    Dbig = torch.full((M, N + 5), 7, dtype=torch.int32, device="cuda")
+    Ybig = torch.full((M, N + 3), 7.0, dtype=torch.float32, device="cuda")
+    banner("xnor_gemm strided outputs")
+    bnn.xnor_gemm(Xp, Wp, K, alpha=a, want_scaled=True, D=Dbig[:, :N], Y=Ybig[:, :N])
+    torch.cuda.synchronize()
+    D_ref, Y_ref, _ = oracle.binary_linear(X, W)
+    np.testing.assert_array_equal(host(Dbig)[:, :N], D_ref)
+    assert np.all(host(Dbig)[:, N:] == 7), "write outside the output columns"
+    assert np.all(host(Ybig)[:, N:] == 7.0), "write outside the output columns"
+    assert_f32_close(host(Ybig)[:, :N], Y_ref, what="Y")
+
+
+def test_gemm_extreme_values(bnn):
+    # all +1 against all -1 and identical rows: D = -K and +K exactly
+    K = 1000
+    X = np.ones((3, K), np.float32)
+    W = np.stack([np.ones(K, np.float32), -np.ones(K, np.float32), np.zeros(K, np.float32)])
+    Wp, a = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    D, Y = bnn.xnor_gemm(Xp, Wp, K, alpha=a, want_scaled=True)
+    torch.cuda.synchronize()
+    assert host(D).tolist() == [[K, -K, K]] * 3
+    assert host(a).tolist() == [1.0, 1.0, 0.0]
+    assert host(Y).tolist() == [[K, -K, 0.0]] * 3
+
+
+# ---------------------------------------------------------------- fused epilogues
+@pytest.mark.parametrize("M,N,K", [(64, 256, 1000), (300, 100, 777), (3, 40, 64), (1, 33, 4096),
+                                   (257, 4096, 4096), (100, 31, 100)])
+def test_fused_threshold_pack(bnn, M, N, K):
+    X, W = _packed_pair(M, N, K, 700 + N)
+    g, b, mu, var, eps = workloads.bn_params(701 + N, N)
+    banner(f"fused thresh-pack M={M} N={N} K={K}")
+    Wp, a = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    a_ref = oracle.alpha(W)
+    tau, d = oracle.bn_fold(g, b, mu, var, eps, a_ref)   # the same tau/dir feed both sides
+    ldo = bnn.padded_ld(N) + 4
+    Op = torch.full((M, ldo), -1, dtype=torch.int32, device="cuda")
+    out = bnn.linear_fused(Xp, Wp, K, bnn.EPI_THRESH_PACK | bnn.EPI_DOT_I32,
+                           tau=dev(tau), dir=dev(d), Op=Op)
+    torch.cuda.synchronize()
+    D_ref = oracle.dot(oracle.sign(X), oracle.sign(W))
+    np.testing.assert_array_equal(host(out["D"]), D_ref)
+    want = oracle.pack_signs(oracle.threshold_signs(D_ref, tau, d), ld=ldo)
+    np.testing.assert_array_equal(host_u32(Op), want)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 64, 576), (50, 256, 2304), (2, 64, 576), (129, 70, 333)])
+def test_fused_scale_residual(bnn, M, N, K):
+    X, W = _packed_pair(M, N, K, 800 + K)
+    R = workloads.normal_f32(802 + K, (M, N))
+    banner(f"fused residual M={M} N={N} K={K}")
+    Wp, a = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    out = bnn.linear_fused(Xp, Wp, K, bnn.EPI_SCALE_F32 | bnn.EPI_RESIDUAL_F32 | bnn.EPI_DOT_I32,
+                           alpha=a, R=dev(R))
+    torch.cuda.synchronize()
+    D_ref = oracle.dot(oracle.sign(X), oracle.sign(W))
+    np.testing.assert_array_equal(host(out["D"]), D_ref)
+    a_ref = oracle.alpha(W)
+    Y_ref = oracle.scale_residual(D_ref, a_ref, R)
+    scale = np.abs(a_ref[None, :] * D_ref) + np.abs(R)
+    assert_f32_close(host(out["Y"]), Y_ref, scale=scale, what="Y residual")
+    # with the GPU's own alpha the result is exact
+    np.testing.assert_array_equal(host(out["Y"]), oracle.scale_residual(D_ref, host(a), R))
+
+
+def test_fused_residual_in_place(bnn):
+    M, N, K = 257, 64, 576
+    X, W = _packed_pair(M, N, K, 900)
+    R = workloads.normal_f32(901, (M, N))
+    Wp, a = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    Rd = dev(R)
+    banner("fused residual in place")
+    bnn.linear_fused(Xp, Wp, K, bnn.EPI_SCALE_F32 | bnn.EPI_RESIDUAL_F32, alpha=a, R=Rd, Y=Rd)
+    torch.cuda.synchronize()
+    D_ref = oracle.dot(oracle.sign(X), oracle.sign(W))
+    np.testing.assert_array_equal(host(Rd), oracle.scale_residual(D_ref, host(a), R))
+
+
+# ---------------------------------------------------------------- FP first / last layers
+@pytest.mark.parametrize("M,N,K", [(64, 128, 784), (100, 70, 33), (1, 32, 1), (130, 4096, 784)])
+def test_dense_f32_sign_pack(bnn, M, N, K):
+    X = workloads.uniform01_f32(1000 + K, (M, K))
+    W = workloads.normal_f32(1001 + K, (N, K))
+    banner(f"dense sign-pack M={M} N={N} K={K}")
+    Op = bnn.dense_f32_sign_pack(dev(X), dev(W))
+    torch.cuda.synchronize()
+    H = oracle.dense_f64(X, W)
+    s = np.where(H >= 0.0, 1, -1).astype(np.int8)
+    np.testing.assert_array_equal(host_u32(Op), oracle.pack_signs(s, ld=Op.shape[1]))
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 10, 4096), (7, 3, 33), (130, 17, 1000)])
+def test_dense_binact_f32(bnn, M, N, K):
+    rng = np.random.default_rng(1100 + K)
+    s = np.where(rng.random((M, K)) < 0.5, 1, -1).astype(np.int8)
+    W = workloads.normal_f32(1101 + K, (N, K))
+    Xp = dev(oracle.pack_signs(s, ld=bnn.padded_ld(K)).view(np.int32))
+    banner(f"dense binact M={M} N={N} K={K}")
+    Y = bnn.dense_binact_f32(Xp, dev(W), K)
+    torch.cuda.synchronize()
+    Y_ref = oracle.dense_pm1_f32out(s, W)
+    # double sums in another order differ by <= ~2K * 2^-53 * sum|W|; after the
+    # fp32 rounding that is within 1e-6 relative, or 1e-9 * sum|W| absolute
+    assert_f32_close(host(Y), Y_ref, scale=1e-3 * np.abs(W).sum(axis=1)[None, :], what="logits")
+
+
+def test_deterministic_repeat(bnn):
+    M, N, K = 300, 200, 1000
+    X, W = _packed_pair(M, N, K, 1200)
+    Wd, Xd = dev(W), dev(X)
+    outs = []
+    for _ in range(2):
+        Wp, a = bnn.pack_weights(Wd)
+        Xp = bnn.pack_activations(Xd)
+        D, Y = bnn.xnor_gemm(Xp, Wp, K, alpha=a, want_scaled=True)
+        torch.cuda.synchronize()
+        outs.append((host_u32(Wp), host(a), host(D), host(Y)))
+    for u, v in zip(outs[0], outs[1]):
+        np.testing.assert_array_equal(u, v)

@@ -1,0 +1,286 @@
+"""Python binding of libbnn.so, the MI355X (gfx950) binary-network hot path.
+
+Argument marshalling only: every step of the path (sign + bit-pack,
+XNOR-popcount GEMM/GEMV, alpha / residual / folded-BatchNorm epilogues, the FP
+first and last layers) runs in the HIP kernels behind the C ABI declared in
+``include/bnn.h``.  PyTorch provides device memory and the current stream;
+there is no CPU or PyTorch fallback: if the library is missing, importing the
+binding's calls raises.
+
+The functions keep the C names without the ``bnn_`` prefix.  Tensors passed
+in must live on a HIP device; outputs are allocated here (or given with
+``out=`` style arguments) with the layouts the C ABI documents:
+packed matrices are uint32 ``[rows, ld]`` stored as ``torch.int32`` (same
+bits), ``ld`` a multiple of 4, bit 0 = +1, bit 1 = -1, pad bits and words 0.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BnnError", "lib", "packed_words", "padded_ld", "pack_weights", "pack_activations",
+    "xnor_gemm", "linear_fused", "fold_bn_thresholds", "dense_f32_sign_pack",
+    "dense_binact_f32", "EPI_DOT_I32", "EPI_SCALE_F32", "EPI_RESIDUAL_F32",
+    "EPI_THRESH_PACK", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbnn.so")
+
+EPI_DOT_I32 = 1
+EPI_SCALE_F32 = 2
+EPI_RESIDUAL_F32 = 4
+EPI_THRESH_PACK = 8
+
+_STATUS = {
+    0: "BNN_OK", 1: "BNN_ERR_NULL", 2: "BNN_ERR_SHAPE", 3: "BNN_ERR_LD",
+    4: "BNN_ERR_ALIGN", 5: "BNN_ERR_UNSUPPORTED", 6: "BNN_ERR_HIP",
+}
+
+
+class BnnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)}")
+
+
+class _ConvGeom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("B", "H", "W", "C", "R", "S", "stride", "pad")]
+
+
+class _FusedArgs(ctypes.Structure):
+    _fields_ = [
+        ("Xp", ctypes.c_void_p), ("ldXp", ctypes.c_int64),
+        ("Wp", ctypes.c_void_p), ("ldWp", ctypes.c_int64),
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("epilogue", ctypes.c_uint32),
+        ("D", ctypes.c_void_p), ("ldD", ctypes.c_int64),
+        ("alpha", ctypes.c_void_p),
+        ("Y", ctypes.c_void_p), ("ldY", ctypes.c_int64),
+        ("R", ctypes.c_void_p), ("ldR", ctypes.c_int64),
+        ("tau", ctypes.c_void_p), ("dir", ctypes.c_void_p),
+        ("Op", ctypes.c_void_p), ("ldOp", ctypes.c_int64),
+    ]
+
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbnn.so (built in-tree by ``xnor_popcount_gemm_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m xnor_popcount_gemm_amd.build` "
+                "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.bnn_packed_words.argtypes = [_i64]
+        L.bnn_packed_words.restype = _i64
+        L.bnn_status_string.argtypes = [ctypes.c_int]
+        L.bnn_status_string.restype = ctypes.c_char_p
+        sigs = {
+            "bnn_pack_weights": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
+            "bnn_pack_activations": [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp],
+            "bnn_xnor_gemm": [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp],
+            "bnn_linear_fused": [ctypes.POINTER(_FusedArgs), _vp],
+            "bnn_fold_bn_thresholds_host": [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _vp, _vp],
+            "bnn_dense_f32_sign_pack": [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp],
+            "bnn_dense_binact_f32": [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise BnnError(status, where)
+
+
+def packed_words(K: int) -> int:
+    """ceil(K / 32)."""
+    return int(lib().bnn_packed_words(int(K)))
+
+
+def padded_ld(K: int) -> int:
+    """Smallest valid leading dimension of a packed matrix: ceil(K/32) rounded
+    up to a multiple of 4 words (16-byte rows)."""
+    kw = (int(K) + 31) // 32
+    return (kw + 3) // 4 * 4
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return t
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _packed_empty(rows: int, K: int, device, ld: int | None = None) -> torch.Tensor:
+    ld = padded_ld(K) if ld is None else ld
+    return torch.empty((rows, ld), dtype=torch.int32, device=device)
+
+
+def pack_weights(W: torch.Tensor, *, alpha: bool = True, out: torch.Tensor | None = None,
+                 alpha_out: torch.Tensor | None = None):
+    """Sign + bit-pack fp32 weights [N, K]; returns (Wp [N, ld], alpha [N] or None)."""
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    Wp = _packed_empty(N, K, W.device) if out is None else out
+    a = None
+    if alpha:
+        a = torch.empty(N, dtype=torch.float32, device=W.device) if alpha_out is None else alpha_out
+    _check(lib().bnn_pack_weights(_ptr(W), N, K, _ld(W), _ptr(Wp), _ld(Wp), _ptr(a),
+                                  _stream(W.device)), "bnn_pack_weights")
+    return Wp, a
+
+
+def pack_activations(X: torch.Tensor, *, conv3x3: bool = False, out: torch.Tensor | None = None):
+    """Sign + bit-pack activations.
+
+    Dense: X fp32 [M, K] -> packed [M, ld].  ``conv3x3=True``: X is an NHWC
+    fp32 image [B, H, W, C] (contiguous) and the result is its packed 3x3 /
+    stride 1 / pad 1 im2col matrix [B*H*W, ld] with K = 9*C, pad pixels +1.
+    """
+    _dev(X, torch.float32, "X")
+    if conv3x3:
+        if X.dim() != 4 or not X.is_contiguous():
+            raise ValueError("conv3x3 input must be a contiguous NHWC tensor")
+        B, H, Wd, C = X.shape
+        M, K = B * H * Wd, 9 * C
+        g = _ConvGeom(B, H, Wd, C, 3, 3, 1, 1)
+        Xp = _packed_empty(M, K, X.device) if out is None else out
+        _check(lib().bnn_pack_activations(_ptr(X), M, K, C, ctypes.byref(g), _ptr(Xp), _ld(Xp),
+                                          _stream(X.device)), "bnn_pack_activations")
+        return Xp
+    M, K = X.shape
+    Xp = _packed_empty(M, K, X.device) if out is None else out
+    _check(lib().bnn_pack_activations(_ptr(X), M, K, _ld(X), None, _ptr(Xp), _ld(Xp),
+                                      _stream(X.device)), "bnn_pack_activations")
+    return Xp
+
+
+def xnor_gemm(Xp: torch.Tensor, Wp: torch.Tensor, K: int, *, alpha: torch.Tensor | None = None,
+              want_dot: bool = True, want_scaled: bool = False,
+              D: torch.Tensor | None = None, Y: torch.Tensor | None = None):
+    """D = K - 2 popcount(Xp xor Wp) (int32 [M, N]) and/or Y = alpha * D (fp32)."""
+    _dev(Xp, torch.int32, "Xp")
+    _dev(Wp, torch.int32, "Wp")
+    M, N = Xp.shape[0], Wp.shape[0]
+    if want_dot and D is None:
+        D = torch.empty((M, N), dtype=torch.int32, device=Xp.device)
+    if want_scaled and Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=Xp.device)
+    if not want_dot:
+        D = None
+    if not want_scaled:
+        Y = None
+    _check(lib().bnn_xnor_gemm(_ptr(Xp), _ld(Xp), _ptr(Wp), _ld(Wp), M, N, int(K),
+                               _ptr(D), _ld(D) if D is not None else 0, _ptr(alpha),
+                               _ptr(Y), _ld(Y) if Y is not None else 0,
+                               _stream(Xp.device)), "bnn_xnor_gemm")
+    return D, Y
+
+
+def linear_fused(Xp: torch.Tensor, Wp: torch.Tensor, K: int, epilogue: int, *,
+                 alpha=None, R=None, tau=None, dir=None, D=None, Y=None, Op=None,
+                 M: int | None = None):
+    """XNOR-popcount GEMM with a fused epilogue (OR of EPI_* flags).
+
+    Returns a dict with the outputs the flags ask for: ``D`` (int32 [M, N]),
+    ``Y`` (fp32 [M, N]), ``Op`` (packed [M, ld] of the output signs).
+    """
+    _dev(Xp, torch.int32, "Xp")
+    _dev(Wp, torch.int32, "Wp")
+    M = Xp.shape[0] if M is None else M
+    N = Wp.shape[0]
+    dev = Xp.device
+    if epilogue & EPI_DOT_I32 and D is None:
+        D = torch.empty((M, N), dtype=torch.int32, device=dev)
+    if epilogue & (EPI_SCALE_F32 | EPI_RESIDUAL_F32) and Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    if epilogue & EPI_THRESH_PACK and Op is None:
+        Op = _packed_empty(M, N, dev)
+    a = _FusedArgs()
+    a.Xp, a.ldXp = Xp.data_ptr(), _ld(Xp)
+    a.Wp, a.ldWp = Wp.data_ptr(), _ld(Wp)
+    a.M, a.N, a.K = M, N, int(K)
+    a.epilogue = int(epilogue)
+    if D is not None:
+        a.D, a.ldD = D.data_ptr(), _ld(D)
+    if alpha is not None:
+        a.alpha = alpha.data_ptr()
+    if Y is not None:
+        a.Y, a.ldY = Y.data_ptr(), _ld(Y)
+    if R is not None:
+        a.R, a.ldR = R.data_ptr(), _ld(R)
+    if tau is not None:
+        a.tau = tau.data_ptr()
+    if dir is not None:
+        a.dir = dir.data_ptr()
+    if Op is not None:
+        a.Op, a.ldOp = Op.data_ptr(), _ld(Op)
+    _check(lib().bnn_linear_fused(ctypes.byref(a), _stream(dev)), "bnn_linear_fused")
+    return {"D": D, "Y": Y, "Op": Op}
+
+
+def fold_bn_thresholds(gamma, beta, mean, var, eps, alpha):
+    """Host-side BatchNorm fold -> (tau fp32 [N], dir int8 [N]) as numpy arrays."""
+    import numpy as np
+    g, b, mu, v, a = (np.ascontiguousarray(x, dtype=np.float32) for x in (gamma, beta, mean, var, alpha))
+    N = a.shape[0]
+    tau = np.empty(N, dtype=np.float32)
+    d = np.empty(N, dtype=np.int8)
+    P = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+    _check(lib().bnn_fold_bn_thresholds_host(P(g), P(b), P(mu), P(v), ctypes.c_float(float(eps)),
+                                             P(a), N, P(tau), P(d)), "bnn_fold_bn_thresholds_host")
+    return tau, d
+
+
+def dense_f32_sign_pack(X: torch.Tensor, W: torch.Tensor, *, out: torch.Tensor | None = None):
+    """FP first layer: packed signs of X W^T (double accumulation)."""
+    _dev(X, torch.float32, "X")
+    _dev(W, torch.float32, "W")
+    M, K = X.shape
+    N = W.shape[0]
+    Op = _packed_empty(M, N, X.device) if out is None else out
+    _check(lib().bnn_dense_f32_sign_pack(_ptr(X), _ld(X), _ptr(W), _ld(W), M, N, K,
+                                         _ptr(Op), _ld(Op), _stream(X.device)),
+           "bnn_dense_f32_sign_pack")
+    return Op
+
+
+def dense_binact_f32(Xp: torch.Tensor, W: torch.Tensor, K: int, *, out: torch.Tensor | None = None):
+    """FP last layer on packed +1/-1 activations: fp32 [M, N]."""
+    _dev(Xp, torch.int32, "Xp")
+    _dev(W, torch.float32, "W")
+    M, N = Xp.shape[0], W.shape[0]
+    Y = torch.empty((M, N), dtype=torch.float32, device=Xp.device) if out is None else out
+    _check(lib().bnn_dense_binact_f32(_ptr(Xp), _ld(Xp), _ptr(W), _ld(W), M, N, int(K),
+                                      _ptr(Y), _ld(Y), _stream(Xp.device)), "bnn_dense_binact_f32")
+    return Y

@@ -1,0 +1,241 @@
+// C ABI of libbnn: argument validation and dispatch to the gfx950 kernels.
+// Every check runs before anything is launched; a failed check returns a
+// status and touches nothing.  The semantics of each entry point are
+// documented (with their sources on the pages) in include/bnn.h.
+#include <math.h>
+
+#include "bnn.h"
+#include "bnn_launch.hpp"
+
+namespace {
+
+using bnn::Epilogue;
+
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
+
+int64_t words_of(int64_t K) { return (K + 31) / 32; }
+
+hipStream_t as_stream(bnn_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+bnn_status from_hip(hipError_t e) { return e == hipSuccess ? BNN_OK : BNN_ERR_HIP; }
+
+// Common checks of a packed operand [rows, ld] holding K bits per row.
+bnn_status check_packed(const uint32_t* p, int64_t K, int64_t ld) {
+    if (!p) return BNN_ERR_NULL;
+    if (ld < words_of(K)) return BNN_ERR_LD;
+    if (misaligned16(p) || (ld % 4) != 0) return BNN_ERR_ALIGN;
+    return BNN_OK;
+}
+
+bnn_status check_k(int64_t K) {
+    return (K < 1 || K > BNN_MAX_K) ? BNN_ERR_SHAPE : BNN_OK;
+}
+
+// Shapes are kept within int32 index arithmetic inside the kernels.
+bnn_status check_rows(int64_t rows) {
+    return (rows < 0 || rows > ((int64_t)1 << 31) - 1) ? BNN_ERR_SHAPE : BNN_OK;
+}
+
+bnn_status validate_fused(const bnn_fused_args* a) {
+    if (!a) return BNN_ERR_NULL;
+    bnn_status st;
+    if ((st = check_rows(a->M)) != BNN_OK) return st;
+    if ((st = check_rows(a->N)) != BNN_OK) return st;
+    if ((st = check_k(a->K)) != BNN_OK) return st;
+    // the GEMM grid (256-row x 16-column tiles) must fit one launch dimension
+    if (((a->M + 255) / 256) * ((a->N + 15) / 16) > ((int64_t)1 << 31) - 1) return BNN_ERR_SHAPE;
+    const uint32_t f = a->epilogue;
+    const uint32_t known = BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32 | BNN_EPI_RESIDUAL_F32 | BNN_EPI_THRESH_PACK;
+    if (f == 0 || (f & ~known) != 0) return BNN_ERR_UNSUPPORTED;
+    if ((f & BNN_EPI_RESIDUAL_F32) && !(f & BNN_EPI_SCALE_F32)) return BNN_ERR_UNSUPPORTED;
+    if ((st = check_packed(a->Xp, a->K, a->ldXp)) != BNN_OK) return st;
+    if ((st = check_packed(a->Wp, a->K, a->ldWp)) != BNN_OK) return st;
+    if (f & BNN_EPI_DOT_I32) {
+        if (!a->D) return BNN_ERR_NULL;
+        if (a->ldD < a->N) return BNN_ERR_LD;
+        if (misaligned4(a->D)) return BNN_ERR_ALIGN;
+    }
+    if (f & BNN_EPI_SCALE_F32) {
+        if (!a->Y || !a->alpha) return BNN_ERR_NULL;
+        if (a->ldY < a->N) return BNN_ERR_LD;
+        if (misaligned4(a->Y) || misaligned4(a->alpha)) return BNN_ERR_ALIGN;
+    }
+    if (f & BNN_EPI_RESIDUAL_F32) {
+        if (!a->R) return BNN_ERR_NULL;
+        if (a->ldR < a->N) return BNN_ERR_LD;
+        if (misaligned4(a->R)) return BNN_ERR_ALIGN;
+        if (a->R != a->Y && a->ldR == a->ldY) {
+            // partial overlap of R and Y would make the result order-dependent
+            const char* r0 = reinterpret_cast<const char*>(a->R);
+            const char* y0 = reinterpret_cast<const char*>(a->Y);
+            const int64_t span = (a->M > 0 ? (a->M - 1) * a->ldY + a->N : 0) * (int64_t)sizeof(float);
+            if (span > 0 && r0 < y0 + span && y0 < r0 + span) return BNN_ERR_UNSUPPORTED;
+        }
+    }
+    if (f & BNN_EPI_THRESH_PACK) {
+        if (!a->tau || !a->dir || !a->Op) return BNN_ERR_NULL;
+        if (a->ldOp < words_of(a->N)) return BNN_ERR_LD;
+        if (misaligned4(a->Op) || misaligned4(a->tau)) return BNN_ERR_ALIGN;
+    }
+    return BNN_OK;
+}
+
+bnn_status run_fused(const bnn_fused_args* a, hipStream_t s) {
+    if (a->M == 0 || a->N == 0) return BNN_OK;
+    Epilogue e;
+    e.flags = a->epilogue;
+    e.D = a->D; e.ldD = a->ldD;
+    e.alpha = a->alpha;
+    e.Y = a->Y; e.ldY = a->ldY;
+    e.R = a->R; e.ldR = a->ldR;
+    e.tau = a->tau; e.dir = a->dir;
+    e.Op = a->Op; e.ldOp = a->ldOp;
+    if (bnn::gemv_eligible(a->M, a->K, e.flags))
+        return from_hip(bnn::launch_xnor_gemv(a->Xp, a->ldXp, a->Wp, a->ldWp, a->M, a->N, a->K, e, s));
+    return from_hip(bnn::launch_xnor_gemm(a->Xp, a->ldXp, a->Wp, a->ldWp, a->M, a->N, a->K, e, s));
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int64_t bnn_packed_words(int64_t K) { return K < 0 ? -1 : words_of(K); }
+
+const char* bnn_status_string(bnn_status status) {
+    switch (status) {
+        case BNN_OK: return "BNN_OK";
+        case BNN_ERR_NULL: return "BNN_ERR_NULL: a required pointer is NULL";
+        case BNN_ERR_SHAPE: return "BNN_ERR_SHAPE: a size is negative or out of range";
+        case BNN_ERR_LD: return "BNN_ERR_LD: a leading dimension is smaller than the row";
+        case BNN_ERR_ALIGN: return "BNN_ERR_ALIGN: a packed operand is misaligned";
+        case BNN_ERR_UNSUPPORTED: return "BNN_ERR_UNSUPPORTED: unsupported flags or geometry";
+        case BNN_ERR_HIP: return "BNN_ERR_HIP: the HIP runtime reported a launch error";
+    }
+    return "unknown bnn_status";
+}
+
+bnn_status bnn_pack_weights(const float* W, int64_t N, int64_t K, int64_t ldW,
+                            uint32_t* Wp, int64_t ldWp, float* alpha, bnn_stream_t stream)
+{
+    bnn_status st;
+    if ((st = check_rows(N)) != BNN_OK) return st;
+    if ((st = check_k(K)) != BNN_OK) return st;
+    if (!W) return BNN_ERR_NULL;
+    if (ldW < K) return BNN_ERR_LD;
+    if (misaligned4(W)) return BNN_ERR_ALIGN;
+    if ((st = check_packed(Wp, K, ldWp)) != BNN_OK) return st;
+    if (alpha && misaligned4(alpha)) return BNN_ERR_ALIGN;
+    if (N == 0) return BNN_OK;
+    return from_hip(bnn::launch_pack_dense(W, N, K, ldW, Wp, ldWp, alpha, as_stream(stream)));
+}
+
+bnn_status bnn_pack_activations(const float* X, int64_t M, int64_t K, int64_t ldX,
+                                const bnn_conv_geom* geom, uint32_t* Xp, int64_t ldXp,
+                                bnn_stream_t stream)
+{
+    bnn_status st;
+    if ((st = check_rows(M)) != BNN_OK) return st;
+    if ((st = check_k(K)) != BNN_OK) return st;
+    if (!X) return BNN_ERR_NULL;
+    if (misaligned4(X)) return BNN_ERR_ALIGN;
+    if ((st = check_packed(Xp, K, ldXp)) != BNN_OK) return st;
+    if (geom) {
+        if (geom->R != 3 || geom->S != 3 || geom->stride != 1 || geom->pad != 1) return BNN_ERR_UNSUPPORTED;
+        if (geom->B < 0 || geom->H < 1 || geom->W < 1 || geom->C < 1) return BNN_ERR_SHAPE;
+        if (geom->H > 65535 || geom->W > 65535) return BNN_ERR_SHAPE;
+        if (geom->B * geom->H * geom->W != M || 9 * geom->C != K) return BNN_ERR_SHAPE;
+        if (geom->B * geom->H * geom->W * geom->C > ((int64_t)1 << 40)) return BNN_ERR_SHAPE;
+        if (M == 0) return BNN_OK;
+        return from_hip(bnn::launch_pack_im2col3x3(X, geom->B, geom->H, geom->W, geom->C,
+                                                   Xp, ldXp, as_stream(stream)));
+    }
+    if (ldX < K) return BNN_ERR_LD;
+    if (M == 0) return BNN_OK;
+    return from_hip(bnn::launch_pack_dense(X, M, K, ldX, Xp, ldXp, nullptr, as_stream(stream)));
+}
+
+bnn_status bnn_xnor_gemm(const uint32_t* Xp, int64_t ldXp, const uint32_t* Wp, int64_t ldWp,
+                         int64_t M, int64_t N, int64_t K,
+                         int32_t* D, int64_t ldD, const float* alpha, float* Y, int64_t ldY,
+                         bnn_stream_t stream)
+{
+    if (!D && !Y) return BNN_ERR_NULL;
+    bnn_fused_args a = {};
+    a.Xp = Xp; a.ldXp = ldXp; a.Wp = Wp; a.ldWp = ldWp;
+    a.M = M; a.N = N; a.K = K;
+    a.epilogue = (D ? BNN_EPI_DOT_I32 : 0u) | (Y ? BNN_EPI_SCALE_F32 : 0u);
+    a.D = D; a.ldD = ldD; a.alpha = alpha; a.Y = Y; a.ldY = ldY;
+    const bnn_status st = validate_fused(&a);
+    if (st != BNN_OK) return st;
+    return run_fused(&a, as_stream(stream));
+}
+
+bnn_status bnn_linear_fused(const bnn_fused_args* args, bnn_stream_t stream)
+{
+    const bnn_status st = validate_fused(args);
+    if (st != BNN_OK) return st;
+    return run_fused(args, as_stream(stream));
+}
+
+bnn_status bnn_fold_bn_thresholds_host(const float* gamma, const float* beta,
+                                       const float* mean, const float* var, float eps,
+                                       const float* alpha, int64_t N, float* tau, int8_t* dir)
+{
+    if (N < 0) return BNN_ERR_SHAPE;
+    if (N == 0) return BNN_OK;
+    if (!gamma || !beta || !mean || !var || !alpha || !tau || !dir) return BNN_ERR_NULL;
+    for (int64_t n = 0; n < N; ++n) {
+        const double sd = sqrt((double)var[n] + (double)eps);
+        const double c = (double)gamma[n] * (double)alpha[n];
+        const double rhs = (double)gamma[n] * (double)mean[n] - (double)beta[n] * sd;
+        if (c > 0.0) {
+            dir[n] = 1;
+            tau[n] = (float)(rhs / c);
+        } else if (c < 0.0) {
+            dir[n] = -1;
+            tau[n] = (float)(-(rhs / c));
+        } else {
+            const double bn0 = (double)beta[n] - (double)gamma[n] * (double)mean[n] / sd;
+            dir[n] = 0;
+            tau[n] = bn0 >= 0.0 ? 0.0f : 1.0f;
+        }
+    }
+    return BNN_OK;
+}
+
+bnn_status bnn_dense_f32_sign_pack(const float* X, int64_t ldX, const float* W, int64_t ldW,
+                                   int64_t M, int64_t N, int64_t K,
+                                   uint32_t* Op, int64_t ldOp, bnn_stream_t stream)
+{
+    bnn_status st;
+    if ((st = check_rows(M)) != BNN_OK) return st;
+    if ((st = check_rows(N)) != BNN_OK) return st;
+    if ((st = check_k(K)) != BNN_OK) return st;
+    if (!X || !W || !Op) return BNN_ERR_NULL;
+    if (ldX < K || ldW < K || ldOp < words_of(N)) return BNN_ERR_LD;
+    if (misaligned4(X) || misaligned4(W) || misaligned4(Op)) return BNN_ERR_ALIGN;
+    if (M == 0) return BNN_OK;
+    if (N == 0) return BNN_ERR_SHAPE;   // a packed output row needs at least one column
+    return from_hip(bnn::launch_dense_f32_sign_pack(X, ldX, W, ldW, M, N, K, Op, ldOp, as_stream(stream)));
+}
+
+bnn_status bnn_dense_binact_f32(const uint32_t* Xp, int64_t ldXp, const float* W, int64_t ldW,
+                                int64_t M, int64_t N, int64_t K,
+                                float* Y, int64_t ldY, bnn_stream_t stream)
+{
+    bnn_status st;
+    if ((st = check_rows(M)) != BNN_OK) return st;
+    if ((st = check_rows(N)) != BNN_OK) return st;
+    if ((st = check_k(K)) != BNN_OK) return st;
+    if ((st = check_packed(Xp, K, ldXp)) != BNN_OK) return st;
+    if (!W || !Y) return BNN_ERR_NULL;
+    if (ldW < K || ldY < N) return BNN_ERR_LD;
+    if (misaligned4(W) || misaligned4(Y)) return BNN_ERR_ALIGN;
+    if (M == 0 || N == 0) return BNN_OK;
+    return from_hip(bnn::launch_dense_binact_f32(Xp, ldXp, W, ldW, M, N, K, Y, ldY, as_stream(stream)));
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,57 @@
+// Device-side helpers shared by the gfx950 kernels of libbnn.
+//
+// Encoding (page "First Principles: Why Binary Ops Can Be Exponentially
+// Faster", section "1. Arithmetic: MAC -> XNOR + popcount"): bit value 0 is
+// +1 and 1 is -1; element k of a row sits in word k/32 at bit k%32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bnn {
+
+// A pointer into the constant address space: uniform loads through it become
+// scalar (s_load_*) loads, so a weight row is broadcast to all 64 lanes from
+// SGPRs instead of being replicated in VGPRs.
+typedef const __attribute__((address_space(4))) uint32_t* cptr_u32;
+typedef const __attribute__((address_space(4))) float* cptr_f32;
+typedef const __attribute__((address_space(4))) int8_t* cptr_i8;
+
+// popcount(x) + acc as the single VALU op v_bcnt_u32_b32.  Written as asm so
+// the compiler cannot re-associate a chain of accumulations into
+// bcnt(x, 0) + v_add3 trees (one extra VALU op per two words).
+__device__ __forceinline__ uint32_t popc_acc(uint32_t x, uint32_t acc) {
+    uint32_t r;
+    asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(acc));
+    return r;
+}
+
+// Sign bit of an fp32 given by its bit pattern u, per the Notation of page
+// "Extreme Quantization: Binary, Ternary & 1-bit LLMs": sign(x) = +1 for
+// x >= 0, else -1; returned as the packed bit (0 for +1, 1 for -1).
+// x >= 0 holds exactly for u in [0, 0x7F800000] (+0, positive finite incl.
+// denormals, +inf) and u == 0x80000000 (-0.0); everything else (negative
+// values, -inf, every NaN) is -1.  An integer test keeps the result
+// independent of any denormal flushing mode of the float compare.
+__device__ __forceinline__ uint32_t neg_bit(uint32_t u) {
+    return (u > 0x7F800000u && u != 0x80000000u) ? 1u : 0u;
+}
+
+// OR of a 32-bit value over each aligned group of 8 consecutive lanes; the
+// result is complete in the last lane of each group (lane % 8 == 7).  DPP
+// row_shr with bound_ctrl reads 0 across a 16-lane row boundary, and the
+// groups never straddle one.
+__device__ __forceinline__ uint32_t or_reduce8_to_last(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+    return v;
+}
+
+}  // namespace bnn

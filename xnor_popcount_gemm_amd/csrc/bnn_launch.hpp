@@ -1,0 +1,48 @@
+// Host-side launchers of the gfx950 kernels (internal to libbnn).  The C ABI
+// in bnn_api.hip validates every argument before calling these; the
+// launchers assume valid, non-empty shapes and report only launch errors.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bnn {
+
+// Epilogue parameters of the XNOR-popcount GEMM / GEMV.
+struct Epilogue {
+    uint32_t flags;          // BNN_EPI_* bits
+    int32_t* D; int64_t ldD;
+    const float* alpha;
+    float* Y; int64_t ldY;
+    const float* R; int64_t ldR;
+    const float* tau; const int8_t* dir;
+    uint32_t* Op; int64_t ldOp;
+};
+
+enum : uint32_t { EPI_DOT = 1u, EPI_SCALE = 2u, EPI_RESIDUAL = 4u, EPI_THRESH = 8u };
+
+hipError_t launch_pack_dense(const float* X, int64_t rows, int64_t K, int64_t ldX,
+                             uint32_t* P, int64_t ldP, float* alpha, hipStream_t s);
+
+hipError_t launch_pack_im2col3x3(const float* X, int64_t B, int64_t H, int64_t W, int64_t C,
+                                 uint32_t* P, int64_t ldP, hipStream_t s);
+
+hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
+                            int64_t M, int64_t N, int64_t K, const Epilogue& e, hipStream_t s);
+
+// True when the streaming GEMV kernel serves this call (small M, no
+// THRESH_PACK, row length within its register budget).
+bool gemv_eligible(int64_t M, int64_t K, uint32_t flags);
+
+hipError_t launch_xnor_gemv(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
+                            int64_t M, int64_t N, int64_t K, const Epilogue& e, hipStream_t s);
+
+hipError_t launch_dense_f32_sign_pack(const float* X, int64_t ldX, const float* W, int64_t ldW,
+                                      int64_t M, int64_t N, int64_t K,
+                                      uint32_t* Op, int64_t ldOp, hipStream_t s);
+
+hipError_t launch_dense_binact_f32(const uint32_t* Xp, int64_t ldXp, const float* W, int64_t ldW,
+                                   int64_t M, int64_t N, int64_t K,
+                                   float* Y, int64_t ldY, hipStream_t s);
+
+}  // namespace bnn

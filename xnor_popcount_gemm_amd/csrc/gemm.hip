@@ -1,0 +1,373 @@
+// XNOR-popcount GEMM and streaming GEMV for gfx950, with fused epilogues.
+//
+// Method (cited by page title and section / equation):
+//  - <w,x> = N - 2 popcount(w_bit xor x_bit) with bit 0 = +1, bit 1 = -1 and
+//    pad bits +1: "First Principles: Why Binary Ops Can Be Exponentially
+//    Faster", section "1. Arithmetic: MAC -> XNOR + popcount"; the same
+//    identity is eq. (6) of "Extreme Quantization: Binary, Ternary & 1-bit
+//    LLMs" (section "XNOR-Net").
+//  - y = alpha * (w_b^T x): "Extreme Quantization", eq. (1).
+//  - batch-1 inference is bound by fetching the packed weights (about MN/8
+//    bytes): "First Principles", sections "The cost of a neural network
+//    step" and "Bandwidth math".
+//  - BatchNorm followed by the next layer's sign: "Binary Neural Network
+//    (BNN)" glossary, eq. (4) of "Extreme Quantization"; FP residual
+//    shortcut: "State of the Art Survey", Bi-Real Net row.
+//
+// GEMM design (CDNA4, wave64, no MFMA -- the contraction is over bits):
+//  - One lane owns one output row m; a wave owns 64 rows, a 256-thread
+//    workgroup 256 rows x TN output columns.  Each lane keeps TN int32
+//    popcount accumulators.
+//  - The activation row is read K-chunk by K-chunk into VGPRs (KC words,
+//    16-byte vector loads).  The TN weight rows of the tile are uniform
+//    across the wave, so they are read with scalar loads (s_load_dwordx16)
+//    into SGPRs and broadcast to all 64 lanes by the VALU's scalar operand:
+//    each output word costs exactly v_xor_b32 (SGPR ^ VGPR) + v_bcnt_u32_b32
+//    (popcount + accumulate), 2 VALU ops per 32 binary MACs, with no LDS
+//    traffic and no barriers.  Scalar loads of the next column are issued
+//    before the current column's 2*KC VALU ops (double-buffered SGPRs).
+//  - Epilogue per lane: D = K - 2*acc, alpha scale, residual, or the folded
+//    BatchNorm threshold with the output bits packed along n in registers
+//    (TN/32 words per lane, no cross-lane traffic).
+// GEMV design (M <= 4): G lanes (a power of two covering the row's 16-byte
+// granules) share one weight row, 64/G rows per wave step; several steps'
+// 16-byte loads are in flight before the XOR-popcount and the G-lane
+// butterfly reduction.  HBM streaming of the packed weights dominates.
+#include <stdlib.h>
+
+#include "bnn_device.hpp"
+#include "bnn_launch.hpp"
+
+namespace bnn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = 256;   // 4 waves x 64 rows
+
+__device__ __forceinline__ void load_granules(uint32_t* a, const uint32_t* __restrict__ src, int n4) {
+#pragma unroll
+    for (int q = 0; q < n4; ++q) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * q);
+        a[4 * q] = v.x; a[4 * q + 1] = v.y; a[4 * q + 2] = v.z; a[4 * q + 3] = v.w;
+    }
+}
+
+// One K-chunk of KCC words for all TN columns.  MASK: only the first nvalid
+// words are live (the K tail); the rest are zeroed on both sides so they add
+// nothing.  FULLN: every column of the tile exists; otherwise columns past
+// nlast re-read the last weight row (their results are discarded).
+template <int TN, int KCC, bool FULLN, bool MASK>
+__device__ __forceinline__ void xnor_chunk(uint32_t (&acc)[TN], const uint32_t* __restrict__ xrow,
+                                           const uint32_t* __restrict__ wbase, int k0, int nvalid,
+                                           int64_t ldW, int nlast)
+{
+    uint32_t a[KCC];
+    load_granules(a, xrow + k0, KCC / 4);
+    if (MASK) {
+#pragma unroll
+        for (int kk = 0; kk < KCC; ++kk) a[kk] = (kk < nvalid) ? a[kk] : 0u;
+    }
+    int64_t ldw = ldW;
+    asm volatile("" : "+s"(ldw));   // keep the TN row offsets out of the loop preheader
+    cptr_u32 p = (cptr_u32)(wbase + k0);
+    uint32_t wc[KCC];
+#pragma unroll
+    for (int kk = 0; kk < KCC; ++kk) wc[kk] = (!MASK || kk < nvalid) ? p[kk] : 0u;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        uint32_t wn[KCC];
+        if (j + 1 < TN) {
+            if (FULLN) p += ldw;
+            else p = (j < nlast) ? p + ldw : p;
+#pragma unroll
+            for (int kk = 0; kk < KCC; ++kk) wn[kk] = (!MASK || kk < nvalid) ? p[kk] : 0u;
+        }
+#pragma unroll
+        for (int kk = 0; kk < KCC; ++kk) acc[j] = popc_acc(a[kk] ^ wc[kk], acc[j]);
+        if (j + 1 < TN) {
+#pragma unroll
+            for (int kk = 0; kk < KCC; ++kk) wc[kk] = wn[kk];
+        }
+    }
+}
+
+template <int TN, int KC, bool FULLN>
+__device__ __forceinline__ void xnor_mainloop(uint32_t (&acc)[TN], const uint32_t* __restrict__ xrow,
+                                              const uint32_t* __restrict__ wbase, int Kw,
+                                              int64_t ldW, int nlast)
+{
+    const int kfull = (Kw / KC) * KC;
+    for (int k0 = 0; k0 < kfull; k0 += KC)
+        xnor_chunk<TN, KC, FULLN, false>(acc, xrow, wbase, k0, KC, ldW, nlast);
+    for (int k0 = kfull; k0 < Kw; k0 += 4)       // 16-byte granules; rows hold ld >= roundup(Kw,4) words
+        xnor_chunk<TN, 4, FULLN, true>(acc, xrow, wbase, k0, min(4, Kw - k0), ldW, nlast);
+}
+
+__device__ __forceinline__ bool aligned16(const void* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+template <int TN, int KC>
+__global__ __launch_bounds__(kThreads) void k_xnor_gemm(
+    const uint32_t* __restrict__ Xp, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
+    int M, int N, int K, int tiles_n, Epilogue e)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int tn = blockIdx.x % tiles_n;
+    const int tm = blockIdx.x / tiles_n;
+    const int wrow0 = tm * kRowsPerBlock + wave * 64;
+    if (wrow0 >= M) return;                       // whole wave past the last row
+    const int m = wrow0 + lane;
+    const int n0 = tn * TN;
+    const int Kw = (K + 31) >> 5;
+    const int nlast = N - 1 - n0;                 // last live column of this tile
+    const uint32_t* __restrict__ xrow = Xp + (int64_t)min(m, M - 1) * ldX;
+    const uint32_t* __restrict__ wbase = Wp + (int64_t)n0 * ldW;
+
+    uint32_t acc[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[j] = 0u;
+    if (n0 + TN <= N) xnor_mainloop<TN, KC, true>(acc, xrow, wbase, Kw, ldW, nlast);
+    else              xnor_mainloop<TN, KC, false>(acc, xrow, wbase, Kw, ldW, nlast);
+
+    if (m >= M) return;
+    const int ncols = min(TN, N - n0);
+    const bool full = (ncols == TN);
+    // Epilogue in groups of 4 columns to keep live ranges short (16-byte
+    // stores when the row segment is aligned and complete).
+    const bool vecD = full && aligned16(e.D) && (e.ldD % 4 == 0);
+    const bool vecY = full && aligned16(e.Y) && (e.ldY % 4 == 0);
+    const bool vecR = full && aligned16(e.R) && (e.ldR % 4 == 0);
+    int32_t* drow = e.D + (int64_t)m * e.ldD + n0;
+    float* yrow = e.Y + (int64_t)m * e.ldY + n0;
+    const float* rrow = e.R + (int64_t)m * e.ldR + n0;
+    cptr_f32 al = (cptr_f32)(e.alpha + n0);
+#pragma unroll
+    for (int q = 0; q < TN / 4; ++q) {
+        int32_t d[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] = K - 2 * (int32_t)acc[4 * q + i];
+        if (e.flags & EPI_DOT) {
+            if (vecD) *reinterpret_cast<int4*>(drow + 4 * q) = make_int4(d[0], d[1], d[2], d[3]);
+            else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) if (4 * q + i < ncols) drow[4 * q + i] = d[i];
+            }
+        }
+        if (e.flags & EPI_SCALE) {
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = al[min(4 * q + i, ncols - 1)] * (float)d[i];
+            if (e.flags & EPI_RESIDUAL) {
+                if (vecR) {
+                    const float4 rv = *reinterpret_cast<const float4*>(rrow + 4 * q);
+                    y[0] = y[0] + rv.x; y[1] = y[1] + rv.y; y[2] = y[2] + rv.z; y[3] = y[3] + rv.w;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) if (4 * q + i < ncols) y[i] = y[i] + rrow[4 * q + i];
+                }
+            }
+            if (vecY) *reinterpret_cast<float4*>(yrow + 4 * q) = make_float4(y[0], y[1], y[2], y[3]);
+            else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) if (4 * q + i < ncols) yrow[4 * q + i] = y[i];
+            }
+        }
+    }
+    if (TN % 32 == 0 && (e.flags & EPI_THRESH)) {
+        cptr_f32 tau = (cptr_f32)(e.tau + n0);
+        const int8_t* dir = e.dir + n0;
+        uint32_t* orow = e.Op + (int64_t)m * e.ldOp;
+        const int nw = (N + 31) >> 5;
+#pragma unroll
+        for (int q = 0; q < TN / 32; ++q) {
+            uint32_t word = 0u;
+#pragma unroll
+            for (int b = 0; b < 32; ++b) {
+                const int j = 32 * q + b;
+                const int jj = min(j, ncols - 1);
+                const float v = (float)((int32_t)dir[jj] * (K - 2 * (int32_t)acc[j]));
+                const uint32_t bit = (j < ncols && !(v >= tau[jj])) ? 1u : 0u;
+                word |= bit << b;
+            }
+            const int widx = (n0 >> 5) + q;
+            if (widx < nw) orow[widx] = word;
+        }
+        if (tn == tiles_n - 1)
+            for (int64_t w = nw; w < e.ldOp; ++w) orow[w] = 0u;
+    }
+}
+
+// ---------------------------------------------------------------- GEMV
+template <int MR, int CPL, int U>
+__global__ __launch_bounds__(kThreads) void k_xnor_gemv(
+    const uint32_t* __restrict__ Xp, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
+    int N, int K, int glog2, Epilogue e)
+{
+    const int lane = threadIdx.x & 63;
+    const int G = 1 << glog2;
+    const int RPS = 64 >> glog2;                  // rows per wave step
+    const int gl = lane & (G - 1);
+    const int go = lane >> glog2;
+    const int Kw = (K + 31) >> 5;
+    const int Kw4 = (Kw + 3) >> 2;
+    const bool ragged = (Kw & 3) != 0;
+
+    // activation granules c = gl + G*i, words >= Kw zeroed
+    uint4 xg[MR][CPL];
+    uint4 wm[CPL];                                // word masks (all ones except pad words)
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = gl + G * i;
+        wm[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (c < Kw4) {
+            wm[i].x = (4 * c + 0 < Kw) ? ~0u : 0u;
+            wm[i].y = (4 * c + 1 < Kw) ? ~0u : 0u;
+            wm[i].z = (4 * c + 2 < Kw) ? ~0u : 0u;
+            wm[i].w = (4 * c + 3 < Kw) ? ~0u : 0u;
+        }
+#pragma unroll
+        for (int mr = 0; mr < MR; ++mr) {
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (c < Kw4) v = *reinterpret_cast<const uint4*>(Xp + (int64_t)mr * ldX + 4 * c);
+            xg[mr][i] = make_uint4(v.x & wm[i].x, v.y & wm[i].y, v.z & wm[i].z, v.w & wm[i].w);
+        }
+    }
+
+    const int64_t nsteps = ((int64_t)N + RPS - 1) / RPS;
+    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+    for (int64_t s0 = wave * U; s0 < nsteps; s0 += nwaves * U) {
+        uint4 wv[U][CPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = (s0 + u) * RPS + go;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = gl + G * i;
+                wv[u][i] = make_uint4(0u, 0u, 0u, 0u);
+                if (row < N && c < Kw4)
+                    wv[u][i] = *reinterpret_cast<const uint4*>(Wp + row * ldW + 4 * c);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = (s0 + u) * RPS + go;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                if (ragged) {
+                    wv[u][i].x &= wm[i].x; wv[u][i].y &= wm[i].y;
+                    wv[u][i].z &= wm[i].z; wv[u][i].w &= wm[i].w;
+                }
+            }
+#pragma unroll
+            for (int mr = 0; mr < MR; ++mr) {
+                uint32_t pc = 0u;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    pc = popc_acc(xg[mr][i].x ^ wv[u][i].x, pc);
+                    pc = popc_acc(xg[mr][i].y ^ wv[u][i].y, pc);
+                    pc = popc_acc(xg[mr][i].z ^ wv[u][i].z, pc);
+                    pc = popc_acc(xg[mr][i].w ^ wv[u][i].w, pc);
+                }
+                for (int o = G >> 1; o >= 1; o >>= 1) pc += __shfl_xor(pc, o, 64);
+                if (gl == 0 && row < N) {
+                    const int32_t d = K - 2 * (int32_t)pc;
+                    if (e.flags & EPI_DOT) e.D[(int64_t)mr * e.ldD + row] = d;
+                    if (e.flags & EPI_SCALE) {
+                        float y = e.alpha[row] * (float)d;
+                        if (e.flags & EPI_RESIDUAL) y = y + e.R[(int64_t)mr * e.ldR + row];
+                        e.Y[(int64_t)mr * e.ldY + row] = y;
+                    }
+                }
+            }
+        }
+    }
+}
+
+int tile_cols_from_env() {
+    const char* v = getenv("BNN_GEMM_TN");
+    if (!v) return 0;
+    const int t = atoi(v);
+    return (t == 16 || t == 32 || t == 64) ? t : 0;
+}
+
+int num_cus() {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    return cus;
+}
+
+}  // namespace
+
+hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
+                            int64_t M, int64_t N, int64_t K, const Epilogue& e, hipStream_t s)
+{
+    // Column tile: wide tiles reuse each activation chunk over more columns;
+    // narrow tiles give more waves (a full chip needs several rounds of
+    // 256 CUs x 4 SIMDs x ~8 waves) and a smaller last round.
+    const int64_t row_tiles = (M + kRowsPerBlock - 1) / kRowsPerBlock;
+    int tn = tile_cols_from_env();
+    if (tn == 0) {
+        const int64_t waves_wanted = (int64_t)num_cus() * 4 * 8 * 6;
+        const int64_t waves64 = ((M + 63) / 64) * ((N + 63) / 64);
+        const int64_t waves32 = ((M + 63) / 64) * ((N + 31) / 32);
+        tn = (waves64 >= waves_wanted) ? 64 : (waves32 >= waves_wanted ? 32 : 16);
+    }
+    if ((e.flags & EPI_THRESH) && tn < 32) tn = 32;   // packed output words need 32 columns per lane
+    const int tiles_n = (int)((N + tn - 1) / tn);
+    const dim3 grid((unsigned)(row_tiles * tiles_n)), block(kThreads);
+    const int m = (int)M, n = (int)N, k = (int)K;
+    switch (tn) {
+        case 64: hipLaunchKernelGGL((k_xnor_gemm<64, 16>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e); break;
+        case 32: hipLaunchKernelGGL((k_xnor_gemm<32, 16>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e); break;
+        default: hipLaunchKernelGGL((k_xnor_gemm<16, 16>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e); break;
+    }
+    return hipGetLastError();
+}
+
+bool gemv_eligible(int64_t M, int64_t K, uint32_t flags) {
+    const int64_t kw4 = ((K + 31) / 32 + 3) / 4;
+    return M >= 1 && M <= 4 && !(flags & EPI_THRESH) && kw4 <= 64 * 8;
+}
+
+hipError_t launch_xnor_gemv(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
+                            int64_t M, int64_t N, int64_t K, const Epilogue& e, hipStream_t s)
+{
+    const int64_t kw4 = ((K + 31) / 32 + 3) / 4;
+    int glog2 = 0;
+    while ((1 << glog2) < kw4 && glog2 < 6) ++glog2;
+    const int G = 1 << glog2;
+    const int cpl_needed = (int)((kw4 + G - 1) / G);
+    const int cpl = cpl_needed <= 1 ? 1 : cpl_needed <= 2 ? 2 : cpl_needed <= 4 ? 4 : 8;
+    const int U = 8 / cpl;
+    const int rps = 64 / G;
+    const int64_t steps = (N + rps - 1) / rps;
+    const int64_t waves = (steps + U - 1) / U;
+    int64_t blocks = (waves + 3) / 4;
+    const int64_t cap = (int64_t)num_cus() * 16;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    const int n = (int)N, k = (int)K;
+#define BNN_GEMV(MR, CPL, UU) hipLaunchKernelGGL((k_xnor_gemv<MR, CPL, UU>), grid, block, 0, s, Xp, ldX, Wp, ldW, n, k, glog2, e)
+#define BNN_GEMV_MR(CPL, UU) \
+    switch (M) { case 1: BNN_GEMV(1, CPL, UU); break; case 2: BNN_GEMV(2, CPL, UU); break; \
+                 case 3: BNN_GEMV(3, CPL, UU); break; default: BNN_GEMV(4, CPL, UU); break; }
+    switch (cpl) {
+        case 1: BNN_GEMV_MR(1, 8); break;
+        case 2: BNN_GEMV_MR(2, 4); break;
+        case 4: BNN_GEMV_MR(4, 2); break;
+        default: BNN_GEMV_MR(8, 1); break;
+    }
+#undef BNN_GEMV_MR
+#undef BNN_GEMV
+    (void)U;
+    return hipGetLastError();
+}
+
+}  // namespace bnn

@@ -1,0 +1,219 @@
+// Sign + bit-pack kernels for gfx950 (weights with per-row alpha, dense
+// activations, and the 3x3 im2col of an NHWC image).
+//
+// Method (cited by page title and section / equation):
+//  - sign(x) = +1 for x >= 0, -1 otherwise: "Extreme Quantization: Binary,
+//    Ternary & 1-bit LLMs", Notation; weights binarized once, activations
+//    before each binary layer: "Binary Neural Network (BNN)" glossary and
+//    eq. (4) of the "Extreme Quantization" page.
+//  - encoding bit 0 = +1, bit 1 = -1, pad bits +1, bits packed into words:
+//    "First Principles: Why Binary Ops Can Be Exponentially Faster",
+//    section "1. Arithmetic: MAC -> XNOR + popcount".
+//  - alpha = (1/n) sum |w_i| per output row: "Extreme Quantization", eq. (1).
+//
+// Mapping: one wavefront owns one output row at a time (grid-stride over
+// rows).  Per step the 64 lanes read 64 x 16 B of consecutive source floats
+// (1 KiB, fully coalesced; the im2col variant gathers the 16-B pieces of the
+// neighbouring pixels) and each aligned group of 8 lanes folds its 32 sign
+// bits into one word with three DPP row shifts; the last lane of the group
+// stores the word.  Four steps are issued before any is consumed, so a wave
+// keeps 4 KiB of loads in flight.  alpha's |w| sum stays in the wave (fp64
+// per lane, then a fixed-order butterfly), so it needs no LDS and no atomics
+// and is the same on every run.
+#include "bnn_device.hpp"
+#include "bnn_launch.hpp"
+
+namespace bnn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSteps = 4;      // 8-word steps issued back to back per wave
+
+struct Frag {                  // four consecutive source elements as bit patterns
+    uint32_t u[4];
+};
+
+__device__ __forceinline__ uint32_t nibble(const Frag& f) {
+    return neg_bit(f.u[0]) | (neg_bit(f.u[1]) << 1) | (neg_bit(f.u[2]) << 2) | (neg_bit(f.u[3]) << 3);
+}
+
+__device__ __forceinline__ double abs_sum4(const Frag& f, double acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += (double)__uint_as_float(f.u[i] & 0x7FFFFFFFu);
+    return acc;
+}
+
+// Elements k .. k+3 of a row; positions >= K read as +0.0 (bit 0, |x| = 0).
+template <bool VEC>
+__device__ __forceinline__ Frag load_frag(const float* __restrict__ row, int k, int K) {
+    Frag f;
+    if (VEC && k + 4 <= K) {
+        const uint4 v = *reinterpret_cast<const uint4*>(row + k);
+        f.u[0] = v.x; f.u[1] = v.y; f.u[2] = v.z; f.u[3] = v.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            f.u[i] = (k + i < K) ? __float_as_uint(row[k + i]) : 0u;
+    }
+    return f;
+}
+
+template <bool VEC, bool ALPHA>
+__global__ __launch_bounds__(kThreads) void k_pack_dense(
+    const float* __restrict__ X, int64_t rows, int K, int64_t ldX,
+    uint32_t* __restrict__ P, int64_t ldP, float* __restrict__ alpha)
+{
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & 7;
+    const int grp = lane >> 3;
+    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+    const int ldp = (int)ldP;
+
+    for (int64_t r = wave; r < rows; r += nwaves) {
+        const float* __restrict__ xr = X + r * ldX;
+        uint32_t* __restrict__ pr = P + r * ldP;
+        double asum = 0.0;
+        for (int w0 = 0; w0 < ldp; w0 += 8 * kSteps) {
+            Frag f[kSteps];
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u)
+                f[u] = load_frag<VEC>(xr, 32 * (w0 + 8 * u + grp) + 4 * sub, K);
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const int w = w0 + 8 * u + grp;
+                const uint32_t word = or_reduce8_to_last(nibble(f[u]) << (4 * sub));
+                if (sub == 7 && w < ldp) pr[w] = word;
+                if (ALPHA) asum = abs_sum4(f[u], asum);
+            }
+        }
+        if (ALPHA) {
+            asum = wave_sum_f64(asum);
+            if (lane == 0) alpha[r] = (float)(asum / (double)K);
+        }
+    }
+}
+
+// im2col of a 3x3 / stride 1 / pad 1 convolution over NHWC input, packed.
+// Output row p = (b*H + oh)*W + ow; element k = (kh*3 + kw)*C + c.  Taps
+// outside the image are +1 (bit 0).  CT is C when fixed at compile time
+// (cheap tap / channel split), 0 for a runtime C.
+template <bool VEC, int CT>
+__global__ __launch_bounds__(kThreads) void k_pack_im2col3x3(
+    const float* __restrict__ X, int B, int H, int W, int Crt,
+    uint32_t* __restrict__ P, int64_t ldP)
+{
+    const int C = CT > 0 ? CT : Crt;
+    const int K = 9 * C;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & 7;
+    const int grp = lane >> 3;
+    const int64_t rows = (int64_t)B * H * W;
+    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+    const int ldp = (int)ldP;
+
+    for (int64_t p = wave; p < rows; p += nwaves) {
+        const int ow = (int)(p % W);
+        const int64_t t = p / W;
+        const int oh = (int)(t % H);
+        const int64_t b = t / H;
+        uint32_t* __restrict__ pr = P + p * ldP;
+        for (int w0 = 0; w0 < ldp; w0 += 8 * kSteps) {
+            Frag f[kSteps];
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const int k = 32 * (w0 + 8 * u + grp) + 4 * sub;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) f[u].u[i] = 0u;
+                if (VEC) {
+                    if (k < K) {                 // C % 4 == 0: k..k+3 share one tap
+                        const int tap = k / C;
+                        const int c = k - tap * C;
+                        const int kh = tap / 3, kw = tap - 3 * (tap / 3);
+                        const int ih = oh - 1 + kh, iw = ow - 1 + kw;
+                        if (ih >= 0 && ih < H && iw >= 0 && iw < W) {
+                            const uint4 v = *reinterpret_cast<const uint4*>(
+                                X + ((b * H + ih) * W + iw) * C + c);
+                            f[u].u[0] = v.x; f[u].u[1] = v.y; f[u].u[2] = v.z; f[u].u[3] = v.w;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kk = k + i;
+                        if (kk < K) {
+                            const int tap = kk / C;
+                            const int c = kk - tap * C;
+                            const int kh = tap / 3, kw = tap - 3 * (tap / 3);
+                            const int ih = oh - 1 + kh, iw = ow - 1 + kw;
+                            if (ih >= 0 && ih < H && iw >= 0 && iw < W)
+                                f[u].u[i] = __float_as_uint(X[((b * H + ih) * W + iw) * C + c]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const int w = w0 + 8 * u + grp;
+                const uint32_t word = or_reduce8_to_last(nibble(f[u]) << (4 * sub));
+                if (sub == 7 && w < ldp) pr[w] = word;
+            }
+        }
+    }
+}
+
+int grid_for_rows(int64_t rows) {
+    const int64_t waves_per_block = kThreads / 64;
+    int64_t blocks = (rows + waves_per_block - 1) / waves_per_block;
+    const int64_t cap = 256 * 32;   // 32 blocks per CU of a 256-CU device
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    return (int)blocks;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+hipError_t launch_pack_dense(const float* X, int64_t rows, int64_t K, int64_t ldX,
+                             uint32_t* P, int64_t ldP, float* alpha, hipStream_t s)
+{
+    const bool vec = aligned16(X) && (ldX % 4 == 0);
+    const dim3 grid(grid_for_rows(rows)), block(kThreads);
+    const int k = (int)K;
+    if (alpha) {
+        if (vec) hipLaunchKernelGGL((k_pack_dense<true, true>), grid, block, 0, s, X, rows, k, ldX, P, ldP, alpha);
+        else     hipLaunchKernelGGL((k_pack_dense<false, true>), grid, block, 0, s, X, rows, k, ldX, P, ldP, alpha);
+    } else {
+        if (vec) hipLaunchKernelGGL((k_pack_dense<true, false>), grid, block, 0, s, X, rows, k, ldX, P, ldP, alpha);
+        else     hipLaunchKernelGGL((k_pack_dense<false, false>), grid, block, 0, s, X, rows, k, ldX, P, ldP, alpha);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_im2col3x3(const float* X, int64_t B, int64_t H, int64_t W, int64_t C,
+                                 uint32_t* P, int64_t ldP, hipStream_t s)
+{
+    const int64_t rows = B * H * W;
+    const bool vec = aligned16(X) && (C % 4 == 0);
+    const dim3 grid(grid_for_rows(rows)), block(kThreads);
+    const int b = (int)B, h = (int)H, w = (int)W, c = (int)C;
+#define BNN_IM2COL(VEC, CT) hipLaunchKernelGGL((k_pack_im2col3x3<VEC, CT>), grid, block, 0, s, X, b, h, w, c, P, ldP)
+    if (vec) {
+        switch (C) {
+            case 32: BNN_IM2COL(true, 32); break;
+            case 64: BNN_IM2COL(true, 64); break;
+            case 128: BNN_IM2COL(true, 128); break;
+            case 256: BNN_IM2COL(true, 256); break;
+            case 512: BNN_IM2COL(true, 512); break;
+            default: BNN_IM2COL(true, 0); break;
+        }
+    } else {
+        BNN_IM2COL(false, 0);
+    }
+#undef BNN_IM2COL
+    return hipGetLastError();
+}
+
+}  // namespace bnn
