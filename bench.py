@@ -1,0 +1,458 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X binary (XNOR-popcount) inference path.
+
+Default workload (the metric's large-GEMM configuration): M = N = K = 16384.
+One step = pack the fp32 activations + pack the fp32 weights with their
+alpha + the XNOR-popcount GEMM writing int32 D and alpha-scaled fp32 Y, on
+inputs already resident in HBM.  ``value`` is binary ops per second over the
+whole step (one binary MAC = 2 ops, 2*M*N*K per step).
+
+Printed as ONE JSON line on stdout; progress goes to stderr.  Besides the
+headline it carries:
+  roofline      the GEMM kernel against the integer-VALU peak (HIP-event
+                durations of every timed launch; algorithmic lane-ops =
+                2 * M * N * ceil(K/32): one v_xor + one v_bcnt per word/output)
+  cpu_baseline  the CPU oracle timed on a bounded row sample of the same
+                workload, extrapolated to the full step
+  secondary     the batch-1 GEMV (streaming over 191 stacked weight copies,
+                and exact-shape cold calls), the 8192^3 GEMM, the binary MLP
+                and the binary conv blocks, each with its own roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+NUM_CU = 256
+CLOCK_HZ = 2.4e9
+VALU_LANES = 64
+PEAK_INT_OPS = NUM_CU * CLOCK_HZ * VALU_LANES        # 39.32e12 int32 lane-ops/s
+PEAK_HBM = 8.0e12                                    # bytes/s
+METRIC = "binary GEMM ops/s (TOPS, % int-VALU peak) + batch-1 GEMV HBM GB/s"
+GEMV_COPIES = 191
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--size", type=int, default=16384, help="M = N = K of the headline GEMM step")
+    p.add_argument("--no-secondary", action="store_true", help="skip the GEMV / MLP / conv / 8192 runs")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv"], default=None,
+                   help="run one workload only (for profiler runs); prints its JSON")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------- timing helpers
+class Ev:
+    """A HIP event pair recorded on the current stream (the library launches
+    on that stream)."""
+
+    def __init__(self):
+        import torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record()
+
+    def stop(self):
+        self.b.record()
+
+    def ms(self) -> float:
+        return self.a.elapsed_time(self.b)
+
+
+def median(xs):
+    return statistics.median(xs) if xs else float("nan")
+
+
+def source_digest(*relpaths) -> str:
+    h = hashlib.sha256()
+    for r in relpaths:
+        with open(os.path.join(ROOT, r), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_key: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            parts = dict(kv.split("=", 1) for kv in line.split())
+            if parts.get("kernel") == kernel_key and parts.get("source") == digest:
+                return float(parts["hbm_bytes_per_launch"])
+    return None
+
+
+# ---------------------------------------------------------------- workloads
+def gemm_step_bench(bnn, torch, M, N, K, steps, warmup, seed_base):
+    import workloads
+    log(f"gemm {M}x{N}x{K}: generating inputs")
+    X = torch.from_numpy(workloads.normal_f32(workloads.seed_for(4, 0) + seed_base, (M, K))).cuda()
+    W = torch.from_numpy(workloads.normal_f32(workloads.seed_for(4, 1) + seed_base, (N, K))).cuda()
+    ld = bnn.padded_ld(K)
+    Xp = torch.empty((M, ld), dtype=torch.int32, device="cuda")
+    Wp = torch.empty((N, ld), dtype=torch.int32, device="cuda")
+    a = torch.empty(N, dtype=torch.float32, device="cuda")
+    D = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    evs = {k: [] for k in ("pack_x", "pack_w", "gemm")}
+
+    def step(record):
+        e = {k: Ev() for k in evs} if record else None
+        if record: e["pack_x"].start()
+        bnn.pack_activations(X, out=Xp)
+        if record: e["pack_x"].stop(); e["pack_w"].start()
+        bnn.pack_weights(W, out=Wp, alpha_out=a)
+        if record: e["pack_w"].stop(); e["gemm"].start()
+        bnn.xnor_gemm(Xp, Wp, K, alpha=a, want_scaled=True, D=D, Y=Y)
+        if record: e["gemm"].stop()
+        return e
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"gemm {M}^3: timing {steps} steps")
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        recs.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for r in recs:
+        for k in evs:
+            evs[k].append(r[k].ms())
+    kw = (K + 31) // 32
+    binops = 2.0 * M * N * K
+    gemm_ms = statistics.mean(evs["gemm"])
+    lane_ops = 2.0 * M * N * kw
+    pack_bytes_x = 4.0 * M * K + 4.0 * M * ld
+    pack_bytes_w = 4.0 * N * K + 4.0 * N * ld + 4.0 * N
+    out = dict(
+        M=M, N=N, K=K, wall_s=wall, ms_per_step=1e3 * wall / steps,
+        binops_per_step=binops,
+        gemm_ms_mean=gemm_ms, gemm_ms_median=median(evs["gemm"]),
+        gemm_lane_ops=lane_ops,
+        gemm_int_ops_per_s=lane_ops / (gemm_ms * 1e-3),
+        gemm_binary_tops=binops / (gemm_ms * 1e-3) / 1e12,
+        pack_x_ms=median(evs["pack_x"]), pack_w_ms=median(evs["pack_w"]),
+        pack_x_GBps=pack_bytes_x / (median(evs["pack_x"]) * 1e-3) / 1e9,
+        pack_w_GBps=pack_bytes_w / (median(evs["pack_w"]) * 1e-3) / 1e9,
+    )
+    del X, W, Xp, Wp, a, D, Y
+    torch.cuda.empty_cache()
+    return out
+
+
+def gemv_bench(bnn, torch, N, K, reps=20):
+    import workloads
+    log(f"gemv N={N} K={K}: {GEMV_COPIES} stacked copies")
+    W = torch.from_numpy(workloads.normal_f32(workloads.seed_for(3, 0) + K, (N, K))).cuda()
+    x = torch.from_numpy(workloads.normal_f32(workloads.seed_for(3, 1) + K, (1, K))).cuda()
+    Wp, a = bnn.pack_weights(W)
+    del W
+    xp = bnn.pack_activations(x)
+    G = GEMV_COPIES
+    Wst = Wp.repeat(G, 1)
+    ast = a.repeat(G)
+    Nt = G * N
+    Y = torch.empty((1, Nt), dtype=torch.float32, device="cuda")
+    kw = (K + 31) // 32
+    # G2: one launch over all copies (streams > 1 GiB, past the 256 MB MALL)
+    for _ in range(3):
+        bnn.xnor_gemm(xp, Wst, K, alpha=ast, want_dot=False, want_scaled=True, Y=Y)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e = Ev(); e.start()
+        bnn.xnor_gemm(xp, Wst, K, alpha=ast, want_dot=False, want_scaled=True, Y=Y)
+        e.stop(); ts.append(e)
+    torch.cuda.synchronize()
+    ms = [e.ms() for e in ts]
+    bytes_stream = 4.0 * Nt * kw + 4.0 * kw + 4.0 * Nt + 4.0 * Nt
+    t_stream = statistics.mean(ms) * 1e-3
+    # G1: exact-shape single calls, each on a copy not touched for 190 calls
+    ys = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    cold = []
+    for i in range(2 * G):
+        g = (i * 37) % G
+        e = Ev(); e.start()
+        bnn.xnor_gemm(xp, Wst[g * N:(g + 1) * N], K, alpha=ast[g * N:(g + 1) * N],
+                      want_dot=False, want_scaled=True, Y=ys)
+        e.stop(); cold.append(e)
+    torch.cuda.synchronize()
+    cold_ms = [e.ms() for e in cold[G:]]
+    bytes_one = 4.0 * N * kw + 4.0 * kw + 8.0 * N
+    res = dict(
+        N=N, K=K, copies=G, stream_ms_mean=statistics.mean(ms), stream_ms_median=median(ms),
+        stream_bytes=bytes_stream, stream_GBps=bytes_stream / t_stream / 1e9,
+        stream_frac_hbm=bytes_stream / t_stream / PEAK_HBM,
+        exact_shape_cold_us_median=1e3 * median(cold_ms),
+        exact_shape_cold_GBps=bytes_one / (median(cold_ms) * 1e-3) / 1e9,
+    )
+    del Wst, ast, Wp, a, Y
+    torch.cuda.empty_cache()
+    return res
+
+
+def mlp_bench(bnn, torch, reps=20, warmup=3):
+    import workloads
+    c = workloads.WORKLOADS[2]
+    B, d_in, h, d_out = c["batch"], c["d_in"], c["hidden"], c["d_out"]
+    log("binary MLP batch 1024: preparing")
+    X = torch.from_numpy(workloads.uniform01_f32(workloads.seed_for(2, 0), (B, d_in))).cuda()
+    W1 = torch.from_numpy(workloads.normal_f32(workloads.seed_for(2, 1), (h, d_in))).cuda()
+    layers = []
+    for i in range(c["n_hidden"]):
+        Wh = torch.from_numpy(workloads.normal_f32(workloads.seed_for(2, 2 + i), (h, h))).cuda()
+        g, b, mu, var, eps = workloads.bn_params(workloads.seed_for(2, 10 + i), h)
+        Wp, a = bnn.pack_weights(Wh)
+        tau, d = bnn.fold_bn_thresholds(g, b, mu, var, eps, a.cpu().numpy())
+        layers.append((Wp, torch.from_numpy(tau).cuda(), torch.from_numpy(d).cuda()))
+    W5 = torch.from_numpy(workloads.normal_f32(workloads.seed_for(2, 20), (d_out, h))).cuda()
+    ld = bnn.padded_ld(h)
+    acts = [torch.empty((B, ld), dtype=torch.int32, device="cuda") for _ in range(4)]
+    logits = torch.empty((B, d_out), dtype=torch.float32, device="cuda")
+
+    def step(record):
+        e = [Ev() for _ in range(5)] if record else None
+        if record: e[0].start()
+        bnn.dense_f32_sign_pack(X, W1, out=acts[0])
+        if record: e[0].stop()
+        for i, (Wp, tau, d) in enumerate(layers):
+            if record: e[i + 1].start()
+            bnn.linear_fused(acts[i], Wp, h, bnn.EPI_THRESH_PACK, tau=tau, dir=d, Op=acts[i + 1])
+            if record: e[i + 1].stop()
+        if record: e[4].start()
+        bnn.dense_binact_f32(acts[3], W5, h, out=logits)
+        if record: e[4].stop()
+        return e
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        recs.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [[r[i].ms() for r in recs] for i in range(5)]
+    kw = (h + 31) // 32
+    hidden_ops = 2.0 * B * h * kw
+    hid_ms = [median(per[i]) for i in (1, 2, 3)]
+    return dict(
+        batch=B, step_ms=1e3 * wall / reps, images_per_s=B * reps / wall,
+        first_layer_ms=median(per[0]),
+        first_layer_f64_frac=(2.0 * B * h * d_in) / (median(per[0]) * 1e-3) / 78.6e12,
+        hidden_layer_ms=hid_ms,
+        hidden_layer_int_valu_frac=[hidden_ops / (t * 1e-3) / PEAK_INT_OPS for t in hid_ms],
+        last_layer_ms=median(per[4]),
+    )
+
+
+def conv_bench(bnn, torch, shape, reps=10, warmup=2):
+    import workloads
+    B, H, Wd, C, Co = shape["B"], shape["H"], shape["W"], shape["C"], shape["Cout"]
+    K = 9 * C
+    log(f"conv block {H}x{Wd}x{C}: preparing")
+    X = torch.from_numpy(workloads.normal_f32(workloads.seed_for(5, 0) + C, (B, H, Wd, C))).cuda()
+    Wt = torch.from_numpy(workloads.normal_f32(workloads.seed_for(5, 1) + C, (Co, K))).cuda()
+    Wp, a = bnn.pack_weights(Wt)
+    M = B * H * Wd
+    ld = bnn.padded_ld(K)
+    Xp = torch.empty((M, ld), dtype=torch.int32, device="cuda")
+    Y = torch.empty((M, Co), dtype=torch.float32, device="cuda")
+    R = X.reshape(M, C)
+
+    def step(record):
+        e = [Ev(), Ev()] if record else None
+        if record: e[0].start()
+        bnn.pack_activations(X, conv3x3=True, out=Xp)
+        if record: e[0].stop(); e[1].start()
+        bnn.linear_fused(Xp, Wp, K, bnn.EPI_SCALE_F32 | bnn.EPI_RESIDUAL_F32, alpha=a, R=R, Y=Y)
+        if record: e[1].stop()
+        return e
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    recs = [step(True) for _ in range(reps)]
+    torch.cuda.synchronize()
+    pack_ms = median([r[0].ms() for r in recs])
+    gemm_ms = median([r[1].ms() for r in recs])
+    kw = (K + 31) // 32
+    lane_ops = 2.0 * M * Co * kw
+    in_bytes = 4.0 * M * C
+    packed = 4.0 * M * ld
+    block_bytes = in_bytes + packed + 4.0 * M * kw + 4.0 * M * Co + 4.0 * M * Co
+    block_ms = pack_ms + gemm_ms
+    ideal_ms = 1e3 * max(block_bytes / PEAK_HBM, lane_ops / PEAK_INT_OPS)
+    return dict(
+        B=B, H=H, W=Wd, C=C, Cout=Co, M=M, K=K,
+        pack_ms=pack_ms, pack_GBps=(in_bytes + packed) / (pack_ms * 1e-3) / 1e9,
+        gemm_ms=gemm_ms, gemm_int_valu_frac=lane_ops / (gemm_ms * 1e-3) / PEAK_INT_OPS,
+        gemm_GBps=(4.0 * M * kw + 8.0 * M * Co) / (gemm_ms * 1e-3) / 1e9,
+        block_ms=block_ms, block_bytes=block_bytes, block_ideal_ms=ideal_ms,
+        block_frac_of_bound=ideal_ms / block_ms,
+    )
+
+
+def cpu_baseline(M, N, K, target_s):
+    """The oracle (unchanged) on a row sample of the same GEMM step: the
+    weight-side work (sign and alpha of all N rows) once, the per-row chain
+    (sign of the sampled activation rows, integer +1/-1 multiply-add against
+    all N weight rows, alpha scaling) on R rows; the full step's time is
+    extrapolated as t_weights + (M / R) * t_rows."""
+    import numpy as np
+    import oracle
+    import workloads
+    log("cpu baseline: oracle on a row sample")
+    W = workloads.normal_f32(workloads.seed_for(4, 1) + M, (N, K))
+    t0 = time.perf_counter()
+    ws = oracle.sign(W)
+    a = oracle.alpha(W)
+    t_w = time.perf_counter() - t0
+    del W
+
+    def rows_time(R):
+        X = workloads.normal_f32(workloads.seed_for(4, 0) + M + 17, (R, K))
+        t = time.perf_counter()
+        D = oracle.dot(oracle.sign(X), ws)
+        oracle.scale(D, a)
+        return time.perf_counter() - t
+
+    r0 = 4
+    t0r = rows_time(r0)
+    R = int(max(r0, min(M, r0 * max(1.0, (target_s - t_w) / max(t0r, 1e-6)))))
+    t_rows = rows_time(R)
+    full_s = t_w + (M / R) * t_rows
+    value = 2.0 * M * N * K / full_s / 1e12
+    return dict(value=value, unit="TOPS", cores=oracle.num_threads(), kind="oracle",
+                sample=(f"{R} of {M} activation rows x all {N} weight rows, K={K} "
+                        f"(sign, +1/-1 int multiply-add, alpha scale) in {t_rows:.1f} s, plus sign+alpha "
+                        f"of all weights in {t_w:.1f} s; step time extrapolated to {full_s:.1f} s"))
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding of "
+              "this path is a design note, not a built path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import xnor_popcount_gemm_amd as bnn
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    bnn.lib()
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name}, {props.multi_processor_count} CUs")
+
+    if args.only and args.only != "gemm":
+        import workloads
+        if args.only == "gemv":
+            r = [gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]]
+        elif args.only == "mlp":
+            r = mlp_bench(bnn, torch)
+        else:
+            r = [conv_bench(bnn, torch, s) for s in workloads.WORKLOADS[5]["shapes"]]
+        print(json.dumps({"only": args.only, "result": r}))
+        return
+
+    S = args.size
+    g = gemm_step_bench(bnn, torch, S, S, S, args.steps, args.warmup, seed_base=S)
+    value = g["binops_per_step"] / (g["ms_per_step"] * 1e-3) / 1e12
+    digest = source_digest("xnor_popcount_gemm_amd/csrc/gemm.hip", "xnor_popcount_gemm_amd/csrc/bnn_device.hpp")
+    traffic = read_traffic(f"xnor_gemm_M{S}", digest)
+    achieved = g["gemm_int_ops_per_s"] / 1e12
+    peak = PEAK_INT_OPS / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(g["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"large binary GEMM M=N=K={S}: sign+pack fp32 activations, sign+pack fp32 "
+                         "weights with alpha=mean|w|, XNOR-popcount GEMM with int32 D and "
+                         "alpha-scaled fp32 Y outputs"),
+            "M": S, "N": S, "K": S,
+            "inputs": "fp32 N(0,1), numpy PCG64 seeded, resident in HBM before timing",
+        },
+        "roofline": {
+            "bound": "alu",
+            "kernel": "k_xnor_gemm",
+            "achieved": round(achieved, 3),
+            "peak": round(peak, 3),
+            "unit": "T int32 lane-ops/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "algorithmic_per_launch": g["gemm_lane_ops"],
+            "launch_ms_mean": round(g["gemm_ms_mean"], 4),
+            "binary_tops": round(g["gemm_binary_tops"], 2),
+        },
+        "step_breakdown_ms": {"pack_activations": round(g["pack_x_ms"], 4),
+                              "pack_weights_alpha": round(g["pack_w_ms"], 4),
+                              "xnor_gemm": round(g["gemm_ms_median"], 4)},
+        "pack_GBps": {"activations": round(g["pack_x_GBps"], 1), "weights": round(g["pack_w_GBps"], 1)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(S, S, S, args.cpu_seconds)
+    if not args.no_secondary:
+        import workloads
+        sec = {}
+        gv = [gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]]
+        sec["gemv_batch1"] = {
+            "metric": "batch-1 GEMV HBM GB/s (191 stacked weight copies, one launch)",
+            "value": round(min(r["stream_GBps"] for r in gv), 1),
+            "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(min(r["stream_GBps"] for r in gv), 1),
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": round(min(r["stream_frac_hbm"] for r in gv), 4)},
+            "shapes": gv,
+        }
+        g8 = gemm_step_bench(bnn, torch, 8192, 8192, 8192, max(5, args.steps // 2), 2, seed_base=8192)
+        sec["gemm_8192"] = {
+            "binary_tops_step": round(g8["binops_per_step"] / (g8["ms_per_step"] * 1e-3) / 1e12, 2),
+            "gemm_int_valu_frac": round(g8["gemm_int_ops_per_s"] / PEAK_INT_OPS, 4),
+            "gemm_ms": round(g8["gemm_ms_median"], 4), "ms_per_step": round(g8["ms_per_step"], 4),
+        }
+        sec["binary_mlp_batch1024"] = mlp_bench(bnn, torch)
+        sec["conv_block"] = [conv_bench(bnn, torch, s) for s in workloads.WORKLOADS[5]["shapes"]]
+        line["secondary"] = sec
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -72,8 +72,15 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = None
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int(lib().oracle_num_threads())
 
 
 def _c(a, dtype):

@@ -27,6 +27,7 @@
  *  [P4] "State of the Art Survey", Bi-Real Net row: FP residual shortcut.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -224,3 +225,6 @@ API void oracle_dense_pm1_f32out(const int8_t* s, const float* W, int64_t ldw,
             Y[m * N + n] = (float)acc;
         }
 }
+
+/* Number of OpenMP threads the routines above use (for reporting). */
+API int oracle_num_threads(void) { return omp_get_max_threads(); }
