@@ -9,9 +9,11 @@ whole step (one binary MAC = 2 ops, 2*M*N*K per step).
 
 Printed as ONE JSON line on stdout; progress goes to stderr.  Besides the
 headline it carries:
-  roofline      the GEMM kernel against the integer-VALU peak (HIP-event
-                durations of every timed launch; algorithmic lane-ops =
-                2 * M * N * ceil(K/32): one v_xor + one v_bcnt per word/output)
+  roofline      the GEMM kernel against the integer-VALU peak of its op mix
+                (256 CUs x 2.4 GHz x 85.33 lane-ops/clk: v_xor at 128 and
+                v_bcnt at 64 lanes/clk/CU; HIP-event durations of every timed
+                launch; algorithmic lane-ops = 2 * M * N * ceil(K/32), one
+                v_xor + one v_bcnt per packed word and output)
   cpu_baseline  the CPU oracle timed on a bounded row sample of the same
                 workload, extrapolated to the full step
   secondary     the batch-1 GEMV (streaming over 191 stacked weight copies,
@@ -34,8 +36,13 @@ if ROOT not in sys.path:
 
 NUM_CU = 256
 CLOCK_HZ = 2.4e9
-VALU_LANES = 64
-PEAK_INT_OPS = NUM_CU * CLOCK_HZ * VALU_LANES        # 39.32e12 int32 lane-ops/s
+# Issue rates of the two VALU ops of one packed word per output, per CU per
+# clock: v_xor_b32 (VOP2) dual-issues at 128 lanes, v_bcnt_u32_b32 (VOP3 only)
+# runs at 64 lanes.  One word-output costs 1/128 + 1/64 = 3/128 CU-clocks, so
+# the XOR-popcount roofline is 2 ops per 3/128 clk = 85.33 lane-ops/clk/CU.
+XOR_LANES, BCNT_LANES = 128, 64
+MIX_LANE_OPS_PER_CLK = 2.0 / (1.0 / XOR_LANES + 1.0 / BCNT_LANES)
+PEAK_INT_OPS = NUM_CU * CLOCK_HZ * MIX_LANE_OPS_PER_CLK   # 52.43e12 lane-ops/s
 PEAK_HBM = 8.0e12                                    # bytes/s
 METRIC = "binary GEMM ops/s (TOPS, % int-VALU peak) + batch-1 GEMV HBM GB/s"
 GEMV_COPIES = 191
@@ -120,9 +127,10 @@ def gemm_step_bench(bnn, torch, M, N, K, steps, warmup, seed_base):
     D = torch.empty((M, N), dtype=torch.int32, device="cuda")
     Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     evs = {k: [] for k in ("pack_x", "pack_w", "gemm")}
+    pool = [{k: Ev() for k in evs} for _ in range(steps)]     # created before timing
 
-    def step(record):
-        e = {k: Ev() for k in evs} if record else None
+    def step(e):
+        record = e is not None
         if record: e["pack_x"].start()
         bnn.pack_activations(X, out=Xp)
         if record: e["pack_x"].stop(); e["pack_w"].start()
@@ -133,13 +141,13 @@ def gemm_step_bench(bnn, torch, M, N, K, steps, warmup, seed_base):
         return e
 
     for _ in range(warmup):
-        step(False)
+        step(None)
     torch.cuda.synchronize()
     log(f"gemm {M}^3: timing {steps} steps")
     recs = []
     t0 = time.perf_counter()
-    for _ in range(steps):
-        recs.append(step(True))
+    for i in range(steps):
+        recs.append(step(pool[i]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for r in recs:
@@ -181,39 +189,52 @@ def gemv_bench(bnn, torch, N, K, reps=20):
     Nt = G * N
     Y = torch.empty((1, Nt), dtype=torch.float32, device="cuda")
     kw = (K + 31) // 32
-    # G2: one launch over all copies (streams > 1 GiB, past the 256 MB MALL)
+    # G2: one launch over all copies (streams > 1 GiB, past the 256 MB MALL);
+    # launches back to back, events created beforehand
     for _ in range(3):
         bnn.xnor_gemm(xp, Wst, K, alpha=ast, want_dot=False, want_scaled=True, Y=Y)
+    ts = [Ev() for _ in range(reps)]
     torch.cuda.synchronize()
-    ts = []
-    for _ in range(reps):
-        e = Ev(); e.start()
+    for e in ts:
+        e.start()
         bnn.xnor_gemm(xp, Wst, K, alpha=ast, want_dot=False, want_scaled=True, Y=Y)
-        e.stop(); ts.append(e)
+        e.stop()
     torch.cuda.synchronize()
     ms = [e.ms() for e in ts]
     bytes_stream = 4.0 * Nt * kw + 4.0 * kw + 4.0 * Nt + 4.0 * Nt
     t_stream = statistics.mean(ms) * 1e-3
-    # G1: exact-shape single calls, each on a copy not touched for 190 calls
+    # G1/G3: exact-shape calls, each on a copy untouched for the previous 190
+    # calls, replayed back to back from a HIP graph (a decode sequence of
+    # 2 x 191 projections); per-call time = replay time / calls.
     ys = torch.empty((1, N), dtype=torch.float32, device="cuda")
-    cold = []
-    for i in range(2 * G):
-        g = (i * 37) % G
-        e = Ev(); e.start()
-        bnn.xnor_gemm(xp, Wst[g * N:(g + 1) * N], K, alpha=ast[g * N:(g + 1) * N],
-                      want_dot=False, want_scaled=True, Y=ys)
-        e.stop(); cold.append(e)
+    order = [(i * 37) % G for i in range(2 * G)]
+
+    def seq():
+        for g in order:
+            bnn.xnor_gemm(xp, Wst[g * N:(g + 1) * N], K, alpha=ast[g * N:(g + 1) * N],
+                          want_dot=False, want_scaled=True, Y=ys)
+    seq()
     torch.cuda.synchronize()
-    cold_ms = [e.ms() for e in cold[G:]]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        seq()
+    graph.replay()
+    torch.cuda.synchronize()
+    e = Ev()
+    e.start()
+    graph.replay()
+    e.stop()
+    torch.cuda.synchronize()
+    per_call_ms = e.ms() / len(order)
     bytes_one = 4.0 * N * kw + 4.0 * kw + 8.0 * N
     res = dict(
         N=N, K=K, copies=G, stream_ms_mean=statistics.mean(ms), stream_ms_median=median(ms),
         stream_bytes=bytes_stream, stream_GBps=bytes_stream / t_stream / 1e9,
         stream_frac_hbm=bytes_stream / t_stream / PEAK_HBM,
-        exact_shape_cold_us_median=1e3 * median(cold_ms),
-        exact_shape_cold_GBps=bytes_one / (median(cold_ms) * 1e-3) / 1e9,
+        exact_shape_cold_us_per_call=1e3 * per_call_ms,
+        exact_shape_cold_GBps=bytes_one / (per_call_ms * 1e-3) / 1e9,
     )
-    del Wst, ast, Wp, a, Y
+    del Wst, ast, Wp, a, Y, graph
     torch.cuda.empty_cache()
     return res
 
@@ -237,8 +258,8 @@ def mlp_bench(bnn, torch, reps=20, warmup=3):
     acts = [torch.empty((B, ld), dtype=torch.int32, device="cuda") for _ in range(4)]
     logits = torch.empty((B, d_out), dtype=torch.float32, device="cuda")
 
-    def step(record):
-        e = [Ev() for _ in range(5)] if record else None
+    def step(e):
+        record = e is not None
         if record: e[0].start()
         bnn.dense_f32_sign_pack(X, W1, out=acts[0])
         if record: e[0].stop()
@@ -252,12 +273,13 @@ def mlp_bench(bnn, torch, reps=20, warmup=3):
         return e
 
     for _ in range(warmup):
-        step(False)
+        step(None)
+    pool = [[Ev() for _ in range(5)] for _ in range(reps)]
     torch.cuda.synchronize()
     recs = []
     t0 = time.perf_counter()
-    for _ in range(reps):
-        recs.append(step(True))
+    for i in range(reps):
+        recs.append(step(pool[i]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [[r[i].ms() for r in recs] for i in range(5)]
@@ -288,8 +310,8 @@ def conv_bench(bnn, torch, shape, reps=10, warmup=2):
     Y = torch.empty((M, Co), dtype=torch.float32, device="cuda")
     R = X.reshape(M, C)
 
-    def step(record):
-        e = [Ev(), Ev()] if record else None
+    def step(e):
+        record = e is not None
         if record: e[0].start()
         bnn.pack_activations(X, conv3x3=True, out=Xp)
         if record: e[0].stop(); e[1].start()
@@ -298,9 +320,10 @@ def conv_bench(bnn, torch, shape, reps=10, warmup=2):
         return e
 
     for _ in range(warmup):
-        step(False)
+        step(None)
+    pool = [[Ev(), Ev()] for _ in range(reps)]
     torch.cuda.synchronize()
-    recs = [step(True) for _ in range(reps)]
+    recs = [step(pool[i]) for i in range(reps)]
     torch.cuda.synchronize()
     pack_ms = median([r[0].ms() for r in recs])
     gemm_ms = median([r[1].ms() for r in recs])

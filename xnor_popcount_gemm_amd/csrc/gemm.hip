@@ -200,6 +200,14 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemm(
 }
 
 // ---------------------------------------------------------------- GEMV
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming load of one 16-byte weight granule: the weights are read once per
+// call, so the load is marked nontemporal and does not displace cached data.
+__device__ __forceinline__ u32x4 load_stream(const uint32_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 template <int MR, int CPL, int U>
 __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
     const uint32_t* __restrict__ Xp, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
@@ -215,12 +223,12 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
     const bool ragged = (Kw & 3) != 0;
 
     // activation granules c = gl + G*i, words >= Kw zeroed
-    uint4 xg[MR][CPL];
-    uint4 wm[CPL];                                // word masks (all ones except pad words)
+    u32x4 xg[MR][CPL];
+    u32x4 wm[CPL];                                // word masks (all ones except pad words)
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = gl + G * i;
-        wm[i] = make_uint4(0u, 0u, 0u, 0u);
+        wm[i] = (u32x4){0u, 0u, 0u, 0u};
         if (c < Kw4) {
             wm[i].x = (4 * c + 0 < Kw) ? ~0u : 0u;
             wm[i].y = (4 * c + 1 < Kw) ? ~0u : 0u;
@@ -229,9 +237,9 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
         }
 #pragma unroll
         for (int mr = 0; mr < MR; ++mr) {
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (c < Kw4) v = *reinterpret_cast<const uint4*>(Xp + (int64_t)mr * ldX + 4 * c);
-            xg[mr][i] = make_uint4(v.x & wm[i].x, v.y & wm[i].y, v.z & wm[i].z, v.w & wm[i].w);
+            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+            if (c < Kw4) v = *reinterpret_cast<const u32x4*>(Xp + (int64_t)mr * ldX + 4 * c);
+            xg[mr][i] = v & wm[i];
         }
     }
 
@@ -239,37 +247,34 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
     const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
     const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
     for (int64_t s0 = wave * U; s0 < nsteps; s0 += nwaves * U) {
-        uint4 wv[U][CPL];
+        u32x4 wv[U][CPL];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = (s0 + u) * RPS + go;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = gl + G * i;
-                wv[u][i] = make_uint4(0u, 0u, 0u, 0u);
-                if (row < N && c < Kw4)
-                    wv[u][i] = *reinterpret_cast<const uint4*>(Wp + row * ldW + 4 * c);
+                wv[u][i] = (u32x4){0u, 0u, 0u, 0u};
+                if (row < N && c < Kw4) wv[u][i] = load_stream(Wp + row * ldW + 4 * c);
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = (s0 + u) * RPS + go;
+            if (ragged) {
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                if (ragged) {
-                    wv[u][i].x &= wm[i].x; wv[u][i].y &= wm[i].y;
-                    wv[u][i].z &= wm[i].z; wv[u][i].w &= wm[i].w;
-                }
+                for (int i = 0; i < CPL; ++i) wv[u][i] &= wm[i];
             }
 #pragma unroll
             for (int mr = 0; mr < MR; ++mr) {
                 uint32_t pc = 0u;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
-                    pc = popc_acc(xg[mr][i].x ^ wv[u][i].x, pc);
-                    pc = popc_acc(xg[mr][i].y ^ wv[u][i].y, pc);
-                    pc = popc_acc(xg[mr][i].z ^ wv[u][i].z, pc);
-                    pc = popc_acc(xg[mr][i].w ^ wv[u][i].w, pc);
+                    const u32x4 t = xg[mr][i] ^ wv[u][i];
+                    pc = popc_acc(t.x, pc);
+                    pc = popc_acc(t.y, pc);
+                    pc = popc_acc(t.z, pc);
+                    pc = popc_acc(t.w, pc);
                 }
                 for (int o = G >> 1; o >= 1; o >>= 1) pc += __shfl_xor(pc, o, 64);
                 if (gl == 0 && row < N) {
@@ -338,18 +343,26 @@ bool gemv_eligible(int64_t M, int64_t K, uint32_t flags) {
 hipError_t launch_xnor_gemv(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
                             int64_t M, int64_t N, int64_t K, const Epilogue& e, hipStream_t s)
 {
+    // G lanes per weight row: the smallest power of two covering its 16-byte
+    // granules (at most 64); CPL granules per lane.  Large calls unroll U
+    // row-steps per wave (8 KiB of loads in flight per wave at CPL = 1);
+    // calls too small to fill the chip keep U = 1 for more waves.
     const int64_t kw4 = ((K + 31) / 32 + 3) / 4;
     int glog2 = 0;
     while ((1 << glog2) < kw4 && glog2 < 6) ++glog2;
     const int G = 1 << glog2;
     const int cpl_needed = (int)((kw4 + G - 1) / G);
     const int cpl = cpl_needed <= 1 ? 1 : cpl_needed <= 2 ? 2 : cpl_needed <= 4 ? 4 : 8;
-    const int U = 8 / cpl;
+    const int umax = 8 / cpl;
     const int rps = 64 / G;
     const int64_t steps = (N + rps - 1) / rps;
+    const int cus = num_cus();
+    const int64_t full_chip_waves = (int64_t)cus * 4 * 8;
+    const bool unroll = umax > 1 && steps >= full_chip_waves * umax;
+    const int U = unroll ? umax : 1;
     const int64_t waves = (steps + U - 1) / U;
     int64_t blocks = (waves + 3) / 4;
-    const int64_t cap = (int64_t)num_cus() * 16;
+    const int64_t cap = (int64_t)cus * 64;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     const dim3 grid((unsigned)blocks), block(kThreads);
@@ -358,15 +371,22 @@ hipError_t launch_xnor_gemv(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
 #define BNN_GEMV_MR(CPL, UU) \
     switch (M) { case 1: BNN_GEMV(1, CPL, UU); break; case 2: BNN_GEMV(2, CPL, UU); break; \
                  case 3: BNN_GEMV(3, CPL, UU); break; default: BNN_GEMV(4, CPL, UU); break; }
-    switch (cpl) {
-        case 1: BNN_GEMV_MR(1, 8); break;
-        case 2: BNN_GEMV_MR(2, 4); break;
-        case 4: BNN_GEMV_MR(4, 2); break;
-        default: BNN_GEMV_MR(8, 1); break;
+    if (unroll) {
+        switch (cpl) {
+            case 1: BNN_GEMV_MR(1, 8); break;
+            case 2: BNN_GEMV_MR(2, 4); break;
+            default: BNN_GEMV_MR(4, 2); break;
+        }
+    } else {
+        switch (cpl) {
+            case 1: BNN_GEMV_MR(1, 1); break;
+            case 2: BNN_GEMV_MR(2, 1); break;
+            case 4: BNN_GEMV_MR(4, 1); break;
+            default: BNN_GEMV_MR(8, 1); break;
+        }
     }
 #undef BNN_GEMV_MR
 #undef BNN_GEMV
-    (void)U;
     return hipGetLastError();
 }
 
