@@ -75,7 +75,7 @@ def test_pack_unaligned_source_rows(bnn):
     np.testing.assert_array_equal(host_u32(Xp), oracle.pack_signs(oracle.sign(big[:, :K]), ld=Xp.shape[1]))
 
 
-@pytest.mark.parametrize("B,H,W,C", [(2, 5, 4, 8), (1, 3, 3, 64), (2, 6, 7, 64), (1, 4, 4, 256),
+@pytest.mark.parametrize("B,H,W,C", [(2, 5, 4, 8), (1, 3, 3, 64), (2, 6, 7, 64), (1, 4, 4, 256), (2, 3, 4, 128), (1, 2, 3, 512), (1, 1, 5, 64),
                                      (2, 3, 5, 3), (1, 2, 2, 36), (3, 1, 1, 32)])
 def test_pack_im2col3x3(bnn, B, H, W, C):
     X = _signs_with_edges(300 + C, (B, H, W, C))
@@ -185,6 +185,56 @@ def test_fused_threshold_pack(bnn, M, N, K):
     np.testing.assert_array_equal(host(out["D"]), D_ref)
     want = oracle.pack_signs(oracle.threshold_signs(D_ref, tau, d), ld=ldo)
     np.testing.assert_array_equal(host_u32(Op), want)
+
+
+@pytest.mark.parametrize("tn", ["8", "16", "32", "64"])
+@pytest.mark.parametrize("M,N,K", [(300, 100, 777), (130, 20, 64), (70, 40, 4096), (257, 96, 200)])
+def test_fused_threshold_pack_every_column_tile(bnn, tn, M, N, K):
+    X, W = _packed_pair(M, N, K, 750 + N + int(tn))
+    g, b, mu, var, eps = workloads.bn_params(751 + N, N)
+    Wp, a = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    tau, d = oracle.bn_fold(g, b, mu, var, eps, oracle.alpha(W))
+    ldo = bnn.padded_ld(N) + 4
+    Op = torch.full((M, ldo), -1, dtype=torch.int32, device="cuda")
+    old = os.environ.get("BNN_GEMM_TN")
+    os.environ["BNN_GEMM_TN"] = tn
+    try:
+        banner(f"fused thresh-pack TN={tn} M={M} N={N} K={K}")
+        bnn.linear_fused(Xp, Wp, K, bnn.EPI_THRESH_PACK, tau=dev(tau), dir=dev(d), Op=Op)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            os.environ.pop("BNN_GEMM_TN", None)
+        else:
+            os.environ["BNN_GEMM_TN"] = old
+    D_ref = oracle.dot(oracle.sign(X), oracle.sign(W))
+    np.testing.assert_array_equal(host_u32(Op), oracle.pack_signs(oracle.threshold_signs(D_ref, tau, d), ld=ldo))
+
+
+@pytest.mark.parametrize("tn", ["8", "16", "32", "64"])
+@pytest.mark.parametrize("M,N,K", [(300, 64, 576), (257, 128, 2304), (65, 96, 100)])
+def test_fused_epilogue_every_column_tile(bnn, tn, M, N, K):
+    """DOT + SCALE + RESIDUAL through the staged (LDS) epilogue for small K."""
+    X, W = _packed_pair(M, N, K, 850 + N + int(tn))
+    R = workloads.normal_f32(852 + K, (M, N))
+    Wp, a = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    old = os.environ.get("BNN_GEMM_TN")
+    os.environ["BNN_GEMM_TN"] = tn
+    try:
+        banner(f"fused residual TN={tn} M={M} N={N} K={K}")
+        out = bnn.linear_fused(Xp, Wp, K, bnn.EPI_SCALE_F32 | bnn.EPI_RESIDUAL_F32 | bnn.EPI_DOT_I32,
+                               alpha=a, R=dev(R))
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            os.environ.pop("BNN_GEMM_TN", None)
+        else:
+            os.environ["BNN_GEMM_TN"] = old
+    D_ref = oracle.dot(oracle.sign(X), oracle.sign(W))
+    np.testing.assert_array_equal(host(out["D"]), D_ref)
+    np.testing.assert_array_equal(host(out["Y"]), oracle.scale_residual(D_ref, host(a), R))
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 64, 576), (50, 256, 2304), (2, 64, 576), (129, 70, 333)])

@@ -107,11 +107,61 @@ __device__ __forceinline__ bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-template <int TN, int KC>
+// Epilogue through LDS for outputs that are HBM-heavy relative to their
+// K loop (small K, e.g. the conv blocks).  Each lane owns one row, so a
+// direct store instruction would touch 64 rows at once.  Instead the wave
+// stages CH columns of its 64 x TN tile in LDS (row stride CH+1 words: the
+// writes are bank-conflict free) and reads them back transposed: in each
+// pass, CH/4 consecutive lanes cover one row's CH columns as 16-byte pieces,
+// so every store (and residual load) instruction covers 64*16/(CH*4) whole
+// row segments of CH*4 bytes.  Only full, 16-byte aligned tiles use it; LDS
+// is private to the wave (no workgroup barrier).
+template <int TN>
+__device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t* __restrict__ lds,
+                                             int wrow0, int M, int n0, int K, const Epilogue& e)
+{
+    constexpr int CH = TN < 32 ? TN : 32;
+    constexpr int G4 = CH / 4;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int c0 = 0; c0 < TN; c0 += CH) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) lds[lane * (CH + 1) + j] = (uint32_t)(K - 2 * (int32_t)acc[c0 + j]);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < G4; ++q) {
+            const int idx = q * 64 + lane;
+            const int r = idx / G4, cg = idx - (idx / G4) * G4;
+            int32_t d[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] = (int32_t)lds[r * (CH + 1) + 4 * cg + i];
+            const int m = wrow0 + r;
+            if (m < M) {
+                const int n = n0 + c0 + 4 * cg;
+                if (e.flags & EPI_DOT)
+                    *reinterpret_cast<int4*>(e.D + (int64_t)m * e.ldD + n) = make_int4(d[0], d[1], d[2], d[3]);
+                if (e.flags & EPI_SCALE) {
+                    const float4 a = *reinterpret_cast<const float4*>(e.alpha + n);
+                    float4 y = make_float4(a.x * (float)d[0], a.y * (float)d[1], a.z * (float)d[2], a.w * (float)d[3]);
+                    if (e.flags & EPI_RESIDUAL) {
+                        const float4 rv = *reinterpret_cast<const float4*>(e.R + (int64_t)m * e.ldR + n);
+                        y.x = y.x + rv.x; y.y = y.y + rv.y; y.z = y.z + rv.z; y.w = y.w + rv.w;
+                    }
+                    *reinterpret_cast<float4*>(e.Y + (int64_t)m * e.ldY + n) = y;
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+template <int TN, int KC, bool EPI_LDS>
 __global__ __launch_bounds__(kThreads) void k_xnor_gemm(
     const uint32_t* __restrict__ Xp, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
     int M, int N, int K, int tiles_n, Epilogue e)
 {
+    constexpr int kLdsWords = 64 * ((TN < 32 ? TN : 32) + 1);
+    __shared__ uint32_t lds_epi[EPI_LDS ? 4 * kLdsWords : 1];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int tn = blockIdx.x % tiles_n;
@@ -131,9 +181,16 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemm(
     if (n0 + TN <= N) xnor_mainloop<TN, KC, true>(acc, xrow, wbase, Kw, ldW, nlast);
     else              xnor_mainloop<TN, KC, false>(acc, xrow, wbase, Kw, ldW, nlast);
 
-    if (m >= M) return;
     const int ncols = min(TN, N - n0);
     const bool full = (ncols == TN);
+    if (EPI_LDS && full && !(e.flags & EPI_THRESH) &&
+        (!(e.flags & EPI_DOT) || (aligned16(e.D) && e.ldD % 4 == 0)) &&
+        (!(e.flags & EPI_SCALE) || (aligned16(e.Y) && e.ldY % 4 == 0 && aligned16(e.alpha))) &&
+        (!(e.flags & EPI_RESIDUAL) || (aligned16(e.R) && e.ldR % 4 == 0))) {
+        epilogue_lds<TN>(acc, lds_epi + wave * kLdsWords, wrow0, M, n0, K, e);
+        return;
+    }
+    if (m >= M) return;
     // Epilogue in groups of 4 columns to keep live ranges short (16-byte
     // stores when the row segment is aligned and complete).
     const bool vecD = full && aligned16(e.D) && (e.ldD % 4 == 0);
@@ -175,27 +232,41 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemm(
             }
         }
     }
-    if (TN % 32 == 0 && (e.flags & EPI_THRESH)) {
+    if (e.flags & EPI_THRESH) {
+        // Output bits of this lane's row, packed along n: bit (n % 32) of word
+        // n / 32.  A tile owns TN/8 whole bytes of the row (n0 is a multiple
+        // of TN), so tiles never share a byte.
         cptr_f32 tau = (cptr_f32)(e.tau + n0);
         const int8_t* dir = e.dir + n0;
         uint32_t* orow = e.Op + (int64_t)m * e.ldOp;
-        const int nw = (N + 31) >> 5;
+        constexpr int WB = TN < 32 ? TN : 32;          // bits per store
 #pragma unroll
-        for (int q = 0; q < TN / 32; ++q) {
+        for (int q = 0; q < TN / WB; ++q) {
             uint32_t word = 0u;
 #pragma unroll
-            for (int b = 0; b < 32; ++b) {
-                const int j = 32 * q + b;
+            for (int b = 0; b < WB; ++b) {
+                const int j = WB * q + b;
                 const int jj = min(j, ncols - 1);
                 const float v = (float)((int32_t)dir[jj] * (K - 2 * (int32_t)acc[j]));
                 const uint32_t bit = (j < ncols && !(v >= tau[jj])) ? 1u : 0u;
                 word |= bit << b;
             }
-            const int widx = (n0 >> 5) + q;
-            if (widx < nw) orow[widx] = word;
+            const int nb = n0 + WB * q;                // first column of this store
+            if (nb < N) {
+                if (WB == 32) orow[nb >> 5] = word;
+                else if (WB == 16) reinterpret_cast<uint16_t*>(orow)[nb >> 4] = (uint16_t)word;
+                else reinterpret_cast<uint8_t*>(orow)[nb >> 3] = (uint8_t)word;
+            }
         }
-        if (tn == tiles_n - 1)
-            for (int64_t w = nw; w < e.ldOp; ++w) orow[w] = 0u;
+        if (tn == tiles_n - 1) {
+            // zero the rest of the row: bytes after this tile (pad bits of the
+            // last word, if the tile is narrower than a word) and the pad words
+            uint8_t* ob = reinterpret_cast<uint8_t*>(orow);
+            const int64_t first = (int64_t)(n0 + WB * ((ncols + WB - 1) / WB)) / 8;   // after the last store
+            const int64_t wfirst = (first + 3) / 4;
+            for (int64_t b = first; b < wfirst * 4 && b < e.ldOp * 4; ++b) ob[b] = 0u;
+            for (int64_t w = wfirst; w < e.ldOp; ++w) orow[w] = 0u;
+        }
     }
 }
 
@@ -295,7 +366,7 @@ int tile_cols_from_env() {
     const char* v = getenv("BNN_GEMM_TN");
     if (!v) return 0;
     const int t = atoi(v);
-    return (t == 16 || t == 32 || t == 64) ? t : 0;
+    return (t == 8 || t == 16 || t == 32 || t == 64) ? t : 0;
 }
 
 int num_cus() {
@@ -316,22 +387,38 @@ hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
     // narrow tiles give more waves (a full chip needs several rounds of
     // 256 CUs x 4 SIMDs x ~8 waves) and a smaller last round.
     const int64_t row_tiles = (M + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int64_t row_waves = (M + 63) / 64;
     int tn = tile_cols_from_env();
     if (tn == 0) {
         const int64_t waves_wanted = (int64_t)num_cus() * 4 * 8 * 6;
-        const int64_t waves64 = ((M + 63) / 64) * ((N + 63) / 64);
-        const int64_t waves32 = ((M + 63) / 64) * ((N + 31) / 32);
-        tn = (waves64 >= waves_wanted) ? 64 : (waves32 >= waves_wanted ? 32 : 16);
+        tn = 8;
+        for (int t = 64; t >= 16; t >>= 1)
+            if (row_waves * ((N + t - 1) / t) >= waves_wanted) { tn = t; break; }
     }
-    if ((e.flags & EPI_THRESH) && tn < 32) tn = 32;   // packed output words need 32 columns per lane
+    // HBM-heavy epilogue (short K loop, float or int32 outputs): stage
+    // through LDS so stores cover whole row segments.
+    const int64_t kw = (K + 31) / 32;
+    const bool lds = kw <= 128 && (e.flags & (EPI_DOT | EPI_SCALE)) && !(e.flags & EPI_THRESH);
     const int tiles_n = (int)((N + tn - 1) / tn);
     const dim3 grid((unsigned)(row_tiles * tiles_n)), block(kThreads);
     const int m = (int)M, n = (int)N, k = (int)K;
-    switch (tn) {
-        case 64: hipLaunchKernelGGL((k_xnor_gemm<64, 16>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e); break;
-        case 32: hipLaunchKernelGGL((k_xnor_gemm<32, 16>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e); break;
-        default: hipLaunchKernelGGL((k_xnor_gemm<16, 16>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e); break;
+#define BNN_GEMM(T, L) hipLaunchKernelGGL((k_xnor_gemm<T, 16, L>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e)
+    if (lds) {
+        switch (tn) {
+            case 64: BNN_GEMM(64, true); break;
+            case 32: BNN_GEMM(32, true); break;
+            case 16: BNN_GEMM(16, true); break;
+            default: BNN_GEMM(8, true); break;
+        }
+    } else {
+        switch (tn) {
+            case 64: BNN_GEMM(64, false); break;
+            case 32: BNN_GEMM(32, false); break;
+            case 16: BNN_GEMM(16, false); break;
+            default: BNN_GEMM(8, false); break;
+        }
     }
+#undef BNN_GEMM
     return hipGetLastError();
 }
 

@@ -63,6 +63,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_dense(
     const float* __restrict__ X, int64_t rows, int K, int64_t ldX,
     uint32_t* __restrict__ P, int64_t ldP, float* __restrict__ alpha)
 {
+    // Each row writes words 0 .. ldP-1: its ceil(K/32) data words and its pad words.
     const int lane = threadIdx.x & 63;
     const int sub = lane & 7;
     const int grp = lane >> 3;
@@ -163,6 +164,82 @@ __global__ __launch_bounds__(kThreads) void k_pack_im2col3x3(
     }
 }
 
+// Two-phase im2col for C % 32 == 0 (every tap is CW = C/32 whole words).
+// Phase 1 packs each input pixel once, from a fully coalesced stream of the
+// NHWC image, into the centre-tap slot (tap 4 = (kh,kw) = (1,1)) of the
+// output row of the same pixel: that slot of output row p IS pixel p.
+// Phase 2 fills the other eight tap slots of every output row from the
+// centre slots of its neighbours (or 0 = +1 outside the image) and zeroes
+// the pad words.  Phase 2 reads only centre slots and writes only other
+// slots, so the two phases need no buffer besides the output.
+template <int CWLOG2>
+__global__ __launch_bounds__(kThreads) void k_im2col_center(
+    const float* __restrict__ X, int64_t pixels, uint32_t* __restrict__ P, int64_t ldP)
+{
+    constexpr int CW = 1 << CWLOG2;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & 7;
+    const int grp = lane >> 3;
+    const int64_t nwords = pixels * CW;
+    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+    // word g covers floats [32g, 32g+32) of the image (pixel g/CW, word g%CW)
+    for (int64_t g0 = wave * 8 * kSteps; g0 < nwords; g0 += nwaves * 8 * kSteps) {
+        Frag f[kSteps];
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const int64_t g = g0 + 8 * u + grp;
+            if (g < nwords) {
+                const uint4 v = *reinterpret_cast<const uint4*>(X + 32 * g + 4 * sub);
+                f[u].u[0] = v.x; f[u].u[1] = v.y; f[u].u[2] = v.z; f[u].u[3] = v.w;
+            } else {
+                f[u].u[0] = f[u].u[1] = f[u].u[2] = f[u].u[3] = 0u;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const int64_t g = g0 + 8 * u + grp;
+            const uint32_t word = or_reduce8_to_last(nibble(f[u]) << (4 * sub));
+            if (sub == 7 && g < nwords)
+                P[(g >> CWLOG2) * ldP + 4 * CW + (g & (CW - 1))] = word;
+        }
+    }
+}
+
+// One thread per (output pixel, task): tasks 0..8 are the taps in k order
+// (task 4, the centre, is already written), task 9 zeroes the pad words.
+template <int CWLOG2>
+__global__ __launch_bounds__(kThreads) void k_im2col_taps(
+    int B, int H, int W, uint32_t* __restrict__ P, int64_t ldP)
+{
+    constexpr int CW = 1 << CWLOG2;
+    const int64_t pixels = (int64_t)B * H * W;
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t p = t / 10;
+    const int task = (int)(t - p * 10);
+    if (p >= pixels || task == 4) return;
+    uint32_t* __restrict__ row = P + p * ldP;
+    if (task == 9) {
+        for (int64_t w = 9 * CW; w < ldP; ++w) row[w] = 0u;
+        return;
+    }
+    const int ow = (int)(p % W);
+    const int oh = (int)((p / W) % H);
+    const int kh = task / 3, kw = task - 3 * (task / 3);
+    const int dh = kh - 1, dw = kw - 1;
+    uint32_t v[CW];
+    if (oh + dh >= 0 && oh + dh < H && ow + dw >= 0 && ow + dw < W) {
+        const uint32_t* __restrict__ src = P + (p + (int64_t)dh * W + dw) * ldP + 4 * CW;
+#pragma unroll
+        for (int j = 0; j < CW; ++j) v[j] = src[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < CW; ++j) v[j] = 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < CW; ++j) row[task * CW + j] = v[j];
+}
+
 int grid_for_rows(int64_t rows) {
     const int64_t waves_per_block = kThreads / 64;
     int64_t blocks = (rows + waves_per_block - 1) / waves_per_block;
@@ -196,6 +273,28 @@ hipError_t launch_pack_im2col3x3(const float* X, int64_t B, int64_t H, int64_t W
                                  uint32_t* P, int64_t ldP, hipStream_t s)
 {
     const int64_t rows = B * H * W;
+    const int64_t cw = C / 32;
+    if (C % 32 == 0 && aligned16(X) && (cw & (cw - 1)) == 0 && cw <= 16) {
+        int cwlog2 = 0;
+        while ((1 << cwlog2) < cw) ++cwlog2;
+        const int64_t nwords = rows * cw;
+        int64_t b1 = (nwords + 8 * kSteps * 4 - 1) / (8 * kSteps * 4);
+        if (b1 > 256 * 32) b1 = 256 * 32;
+        const int64_t b2 = (rows * 10 + kThreads - 1) / kThreads;
+        const int bb = (int)B, hh = (int)H, ww = (int)W;
+#define BNN_IM2COL2(L) do { \
+        hipLaunchKernelGGL((k_im2col_center<L>), dim3((unsigned)b1), dim3(kThreads), 0, s, X, rows, P, ldP); \
+        hipLaunchKernelGGL((k_im2col_taps<L>), dim3((unsigned)b2), dim3(kThreads), 0, s, bb, hh, ww, P, ldP); } while (0)
+        switch (cwlog2) {
+            case 0: BNN_IM2COL2(0); break;
+            case 1: BNN_IM2COL2(1); break;
+            case 2: BNN_IM2COL2(2); break;
+            case 3: BNN_IM2COL2(3); break;
+            default: BNN_IM2COL2(4); break;
+        }
+#undef BNN_IM2COL2
+        return hipGetLastError();
+    }
     const bool vec = aligned16(X) && (C % 4 == 0);
     const dim3 grid(grid_for_rows(rows)), block(kThreads);
     const int b = (int)B, h = (int)H, w = (int)W, c = (int)C;
