@@ -52,41 +52,60 @@ __device__ __forceinline__ void load_granules(uint32_t* a, const uint32_t* __res
     }
 }
 
-// One K-chunk of KCC words for all TN columns.  MASK: only the first nvalid
-// words are live (the K tail); the rest are zeroed on both sides so they add
-// nothing.  FULLN: every column of the tile exists; otherwise columns past
-// nlast re-read the last weight row (their results are discarded).
-template <int TN, int KCC, bool FULLN, bool MASK>
-__device__ __forceinline__ void xnor_chunk(uint32_t (&acc)[TN], const uint32_t* __restrict__ xrow,
+// Scalar loads of the KCC words of CP consecutive weight rows starting at p
+// (rows past the last live column re-read it).  MASK zeroes words >= nvalid.
+template <int CP, int KCC, bool FULLN, bool MASK>
+__device__ __forceinline__ void load_w(uint32_t (&w)[CP][KCC], cptr_u32 p, int64_t ldw, int j0, int nlast,
+                                       int nvalid)
+{
+#pragma unroll
+    for (int c = 0; c < CP; ++c) {
+        const cptr_u32 q = FULLN ? p + c * ldw : p + (int64_t)min(j0 + c, nlast) * ldw;
+#pragma unroll
+        for (int kk = 0; kk < KCC; ++kk) w[c][kk] = (!MASK || kk < nvalid) ? q[kk] : 0u;
+    }
+}
+
+// One K-chunk of KCC words for all TN columns.  The activation words a[] are
+// already in VGPRs.  Weight rows are scalar-loaded CP columns per step into
+// one of two SGPR sets: the loads of step s+1 are issued (and pinned there
+// by a scheduling barrier) before the 2*CP*KCC VALU ops of step s, so each
+// wait on the scalar counter (which must be lgkmcnt(0): scalar loads return
+// out of order) comes a full step after its loads were issued.
+// MASK: only the first nvalid words are live (the K tail).  FULLN: every
+// column of the tile exists; otherwise columns past nlast re-read the last
+// weight row (their results are discarded).
+template <int TN, int KCC, int CP, bool FULLN, bool MASK>
+__device__ __forceinline__ void xnor_chunk(uint32_t (&acc)[TN], const uint32_t (&a)[KCC],
                                            const uint32_t* __restrict__ wbase, int k0, int nvalid,
                                            int64_t ldW, int nlast)
 {
-    uint32_t a[KCC];
-    load_granules(a, xrow + k0, KCC / 4);
-    if (MASK) {
-#pragma unroll
-        for (int kk = 0; kk < KCC; ++kk) a[kk] = (kk < nvalid) ? a[kk] : 0u;
-    }
     int64_t ldw = ldW;
     asm volatile("" : "+s"(ldw));   // keep the TN row offsets out of the loop preheader
-    cptr_u32 p = (cptr_u32)(wbase + k0);
-    uint32_t wc[KCC];
+    const cptr_u32 p0 = (cptr_u32)(wbase + k0);
+    uint32_t wc[CP][KCC];
+    load_w<CP, KCC, FULLN, MASK>(wc, p0, ldw, 0, nlast, nvalid);
 #pragma unroll
-    for (int kk = 0; kk < KCC; ++kk) wc[kk] = (!MASK || kk < nvalid) ? p[kk] : 0u;
+    for (int j = 0; j < TN; j += CP) {
+        // Consume the current set's scalar loads here (the counter wait lands
+        // before the next loads are issued, not after them).
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        uint32_t wn[KCC];
-        if (j + 1 < TN) {
-            if (FULLN) p += ldw;
-            else p = (j < nlast) ? p + ldw : p;
+        for (int c = 0; c < CP; ++c)
 #pragma unroll
-            for (int kk = 0; kk < KCC; ++kk) wn[kk] = (!MASK || kk < nvalid) ? p[kk] : 0u;
-        }
+            for (int kk = 0; kk < KCC; ++kk) asm volatile("" : : "s"(wc[c][kk]));
+        uint32_t wn[CP][KCC];
+        if (j + CP < TN)
+            load_w<CP, KCC, FULLN, MASK>(wn, p0 + (FULLN ? (int64_t)(j + CP) * ldw : 0), ldw, j + CP, nlast, nvalid);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kk = 0; kk < KCC; ++kk) acc[j] = popc_acc(a[kk] ^ wc[kk], acc[j]);
-        if (j + 1 < TN) {
+        for (int c = 0; c < CP; ++c)
 #pragma unroll
-            for (int kk = 0; kk < KCC; ++kk) wc[kk] = wn[kk];
+            for (int kk = 0; kk < KCC; ++kk) acc[j + c] = popc_acc(a[kk] ^ wc[c][kk], acc[j + c]);
+        if (j + CP < TN) {
+#pragma unroll
+            for (int c = 0; c < CP; ++c)
+#pragma unroll
+                for (int kk = 0; kk < KCC; ++kk) wc[c][kk] = wn[c][kk];
         }
     }
 }
@@ -96,11 +115,30 @@ __device__ __forceinline__ void xnor_mainloop(uint32_t (&acc)[TN], const uint32_
                                               const uint32_t* __restrict__ wbase, int Kw,
                                               int64_t ldW, int nlast)
 {
+    constexpr int CP = (TN >= 2) ? 2 : 1;
     const int kfull = (Kw / KC) * KC;
-    for (int k0 = 0; k0 < kfull; k0 += KC)
-        xnor_chunk<TN, KC, FULLN, false>(acc, xrow, wbase, k0, KC, ldW, nlast);
-    for (int k0 = kfull; k0 < Kw; k0 += 4)       // 16-byte granules; rows hold ld >= roundup(Kw,4) words
-        xnor_chunk<TN, 4, FULLN, true>(acc, xrow, wbase, k0, min(4, Kw - k0), ldW, nlast);
+    // activation chunk double-buffered: the next chunk's vector loads are in
+    // flight during this chunk's VALU work
+    uint32_t a[KC], an[KC];
+    if (kfull > 0) load_granules(an, xrow, KC / 4);
+    for (int k0 = 0; k0 < kfull; k0 += KC) {
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) a[kk] = an[kk];
+        // take delivery of this chunk (issued one chunk ago) before the next
+        // chunk's loads go out, so no wait ever covers a fresh prefetch
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) asm volatile("" : : "v"(a[kk]));
+        if (k0 + KC < kfull) load_granules(an, xrow + k0 + KC, KC / 4);
+        xnor_chunk<TN, KC, CP, FULLN, false>(acc, a, wbase, k0, KC, ldW, nlast);
+    }
+    for (int k0 = kfull; k0 < Kw; k0 += 4) {     // 16-byte granules; rows hold ld >= roundup(Kw,4) words
+        const int nvalid = min(4, Kw - k0);
+        uint32_t t[4];
+        load_granules(t, xrow + k0, 1);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) t[kk] = (kk < nvalid) ? t[kk] : 0u;
+        xnor_chunk<TN, 4, CP, FULLN, true>(acc, t, wbase, k0, nvalid, ldW, nlast);
+    }
 }
 
 __device__ __forceinline__ bool aligned16(const void* p) {
@@ -390,10 +428,14 @@ hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
     const int64_t row_waves = (M + 63) / 64;
     int tn = tile_cols_from_env();
     if (tn == 0) {
-        const int64_t waves_wanted = (int64_t)num_cus() * 4 * 8 * 6;
-        tn = 8;
-        for (int t = 64; t >= 16; t >>= 1)
-            if (row_waves * ((N + t - 1) / t) >= waves_wanted) { tn = t; break; }
+        // Measured on MI355X: 64-wide tiles once the launch has >= 6 rounds
+        // of 8 waves per SIMD, 32-wide at >= 3 rounds, else 16-wide (8-wide
+        // tiles reload each activation chunk too often to pay off unless
+        // N itself is that narrow).
+        const int64_t rounds_wave = (int64_t)num_cus() * 4 * 8;
+        if (row_waves * ((N + 63) / 64) >= 6 * rounds_wave) tn = 64;
+        else if (row_waves * ((N + 31) / 32) >= 3 * rounds_wave) tn = 32;
+        else tn = N <= 8 ? 8 : 16;
     }
     // HBM-heavy epilogue (short K loop, float or int32 outputs): stage
     // through LDS so stores cover whole row segments.
