@@ -63,7 +63,22 @@ def parse_args():
     p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv"], default=None,
                    help="run one workload only (for profiler runs); prints its JSON")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="also run a plain 1 GiB device copy (torch copy_) three times, the known-size "
+                        "kernel that scales the profiler's FETCH_SIZE / WRITE_SIZE readings")
     return p.parse_args()
+
+
+def copy_calibration(torch):
+    """Three launches of a plain device copy: 1 GiB read + 1 GiB written each."""
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 x (1 GiB read + 1 GiB write) done")
+    del src, dst
 
 
 # ---------------------------------------------------------------- timing helpers
@@ -395,7 +410,13 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name}, {props.multi_processor_count} CUs")
 
-    if args.only and args.only != "gemm":
+    if args.only == "gemm":
+        g = gemm_step_bench(bnn, torch, args.size, args.size, args.size, args.steps, args.warmup, seed_base=args.size)
+        if args.copy_calib:
+            copy_calibration(torch)
+        print(json.dumps({"only": "gemm", "result": g}))
+        return
+    if args.only:
         import workloads
         if args.only == "gemv":
             r = [gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]]
@@ -403,6 +424,8 @@ def main():
             r = mlp_bench(bnn, torch)
         else:
             r = [conv_bench(bnn, torch, s) for s in workloads.WORKLOADS[5]["shapes"]]
+        if args.copy_calib:
+            copy_calibration(torch)
         print(json.dumps({"only": args.only, "result": r}))
         return
 
