@@ -48,6 +48,23 @@ __device__ __forceinline__ uint32_t or_reduce8_to_last(uint32_t v) {
     return v;
 }
 
+// Sum of a 32-bit value over each aligned group of 2^glog2 lanes (glog2 <=
+// 6, wave-uniform); the total is complete in the last lane of each group.
+// DPP row shifts accumulate inclusive sums inside 16-lane rows (bound_ctrl
+// reads 0 before a row start; groups never straddle a row below 16 lanes);
+// row_bcast15 / row_bcast31 carry row totals across rows for 32 / 64.
+__device__ __forceinline__ uint32_t sum_reduce_to_last(uint32_t v, int glog2) {
+    // branch-free: every step runs, steps beyond glog2 add 0
+    uint32_t t;
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true); v += glog2 >= 1 ? t : 0u;  // row_shr:1
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true); v += glog2 >= 2 ? t : 0u;  // row_shr:2
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true); v += glog2 >= 3 ? t : 0u;  // row_shr:4
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true); v += glog2 >= 4 ? t : 0u;  // row_shr:8
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); v += glog2 >= 5 ? t : 0u; // row_bcast:15 -> rows 1,3
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); v += glog2 >= 6 ? t : 0u; // row_bcast:31 -> rows 2,3
+    return v;
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);

@@ -14,9 +14,8 @@
 // sum as a plain sequential loop.  The signs of each row's 32-column groups
 // are folded into packed words with DPP row shifts, as in the pack kernels.
 //
-// Last layer: one wave per activation row; lanes split K in 4-element
-// slices, every lane keeps one double accumulator per output column, and a
-// fixed-order butterfly reduces them (deterministic on every run).
+// Last layer: one workgroup per activation row, K split over its waves,
+// double accumulators, fixed-order reductions (deterministic on every run).
 #include "bnn_device.hpp"
 #include "bnn_launch.hpp"
 
@@ -89,20 +88,25 @@ __global__ __launch_bounds__(kThreads) void k_dense_f32_sign_pack(
     }
 }
 
-template <int NB>
+// Last layer: one workgroup per activation row; its 4 waves take interleaved
+// 256-element slices of K (lane: 4 consecutive k), every lane keeps one
+// double per output column (NB per pass), each wave reduces with a
+// fixed-order butterfly and wave 0 adds the 4 wave sums in order.
+template <int NB, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_dense_binact_f32(
     const uint32_t* __restrict__ Xp, int64_t ldXp, const float* __restrict__ W, int64_t ldW,
     int M, int N, int K, float* __restrict__ Y, int64_t ldY)
 {
+    __shared__ double part[4][NB];
     const int lane = threadIdx.x & 63;
-    const int64_t m = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-    if (m >= M) return;
+    const int wave = threadIdx.x >> 6;
+    const int64_t m = blockIdx.x;
     const uint32_t* __restrict__ xr = Xp + m * ldXp;
     for (int n0 = 0; n0 < N; n0 += NB) {
         double acc[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[j] = 0.0;
-        for (int kb = 0; kb < K; kb += 256) {
+        for (int kb = 256 * wave; kb < K; kb += 1024) {
             const int k = kb + 4 * lane;
             if (k < K) {
                 const uint32_t bits = xr[k >> 5] >> (k & 31);
@@ -110,12 +114,18 @@ __global__ __launch_bounds__(kThreads) void k_dense_binact_f32(
                 for (int j = 0; j < NB; ++j) {
                     if (n0 + j < N) {
                         const float* wr = W + (int64_t)(n0 + j) * ldW + k;
+                        float w[4];
+                        if (VEC && k + 4 <= K) {
+                            const float4 v = *reinterpret_cast<const float4*>(wr);
+                            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) w[i] = (k + i < K) ? wr[i] : 0.0f;
+                        }
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            if (k + i < K) {
-                                const double w = (double)wr[i];
-                                acc[j] = ((bits >> i) & 1u) ? acc[j] - w : acc[j] + w;
-                            }
+                            const double d = (double)w[i];
+                            acc[j] = ((bits >> i) & 1u) ? acc[j] - d : acc[j] + d;
                         }
                     }
                 }
@@ -124,8 +134,14 @@ __global__ __launch_bounds__(kThreads) void k_dense_binact_f32(
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const double tot = wave_sum_f64(acc[j]);
-            if (lane == 0 && n0 + j < N) Y[m * ldY + n0 + j] = (float)tot;
+            if (lane == 0) part[wave][j] = tot;
         }
+        __syncthreads();
+        if (threadIdx.x < NB && n0 + (int)threadIdx.x < N) {
+            const int j = threadIdx.x;
+            Y[m * ldY + n0 + j] = (float)(((part[0][j] + part[1][j]) + part[2][j]) + part[3][j]);
+        }
+        __syncthreads();
     }
 }
 
@@ -147,9 +163,12 @@ hipError_t launch_dense_binact_f32(const uint32_t* Xp, int64_t ldXp, const float
                                    int64_t M, int64_t N, int64_t K,
                                    float* Y, int64_t ldY, hipStream_t s)
 {
-    const dim3 grid((unsigned)((M + 3) / 4)), block(kThreads);
-    hipLaunchKernelGGL((k_dense_binact_f32<8>), grid, block, 0, s, Xp, ldXp, W, ldW,
-                       (int)M, (int)N, (int)K, Y, ldY);
+    const dim3 grid((unsigned)M), block(kThreads);
+    const bool vec = (reinterpret_cast<uintptr_t>(W) & 15u) == 0 && ldW % 4 == 0;
+    if (vec) hipLaunchKernelGGL((k_dense_binact_f32<16, true>), grid, block, 0, s, Xp, ldXp, W, ldW,
+                                (int)M, (int)N, (int)K, Y, ldY);
+    else     hipLaunchKernelGGL((k_dense_binact_f32<16, false>), grid, block, 0, s, Xp, ldXp, W, ldW,
+                                (int)M, (int)N, (int)K, Y, ldY);
     return hipGetLastError();
 }
 

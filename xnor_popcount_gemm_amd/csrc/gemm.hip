@@ -1,4 +1,4 @@
-// XNOR-popcount GEMM and streaming GEMV for gfx950, with fused epilogues.
+// XNOR-popcount GEMM for gfx950, with fused epilogues.
 //
 // Method (cited by page title and section / equation):
 //  - <w,x> = N - 2 popcount(w_bit xor x_bit) with bit 0 = +1, bit 1 = -1 and
@@ -29,10 +29,6 @@
 //  - Epilogue per lane: D = K - 2*acc, alpha scale, residual, or the folded
 //    BatchNorm threshold with the output bits packed along n in registers
 //    (TN/32 words per lane, no cross-lane traffic).
-// GEMV design (M <= 4): G lanes (a power of two covering the row's 16-byte
-// granules) share one weight row, 64/G rows per wave step; several steps'
-// 16-byte loads are in flight before the XOR-popcount and the G-lane
-// butterfly reduction.  HBM streaming of the packed weights dominates.
 #include <stdlib.h>
 
 #include "bnn_device.hpp"
@@ -43,6 +39,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = 256;   // 4 waves x 64 rows
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void load_granules(uint32_t* a, const uint32_t* __restrict__ src, int n4) {
 #pragma unroll
@@ -165,6 +163,20 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
     for (int c0 = 0; c0 < TN; c0 += CH) {
 #pragma unroll
         for (int j = 0; j < CH; ++j) lds[lane * (CH + 1) + j] = (uint32_t)(K - 2 * (int32_t)acc[c0 + j]);
+        // The residual and alpha pieces of all passes are requested before
+        // any is used, so their latencies overlap instead of adding up.
+        f32x4 rv[G4];
+        float4 av[G4];
+#pragma unroll
+        for (int q = 0; q < G4; ++q) {
+            const int idx = q * 64 + lane;
+            const int r = idx / G4, cg = idx - (idx / G4) * G4;
+            const int m = min(wrow0 + r, M - 1);
+            const int n = n0 + c0 + 4 * cg;
+            if (e.flags & EPI_SCALE) av[q] = *reinterpret_cast<const float4*>(e.alpha + n);
+            if (e.flags & EPI_RESIDUAL)
+                rv[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(e.R + (int64_t)m * e.ldR + n));
+        }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int q = 0; q < G4; ++q) {
@@ -179,13 +191,10 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
                 if (e.flags & EPI_DOT)
                     *reinterpret_cast<int4*>(e.D + (int64_t)m * e.ldD + n) = make_int4(d[0], d[1], d[2], d[3]);
                 if (e.flags & EPI_SCALE) {
-                    const float4 a = *reinterpret_cast<const float4*>(e.alpha + n);
-                    float4 y = make_float4(a.x * (float)d[0], a.y * (float)d[1], a.z * (float)d[2], a.w * (float)d[3]);
-                    if (e.flags & EPI_RESIDUAL) {
-                        const float4 rv = *reinterpret_cast<const float4*>(e.R + (int64_t)m * e.ldR + n);
-                        y.x = y.x + rv.x; y.y = y.y + rv.y; y.z = y.z + rv.z; y.w = y.w + rv.w;
-                    }
-                    *reinterpret_cast<float4*>(e.Y + (int64_t)m * e.ldY + n) = y;
+                    const float4 a = av[q];
+                    f32x4 y = {a.x * (float)d[0], a.y * (float)d[1], a.z * (float)d[2], a.w * (float)d[3]};
+                    if (e.flags & EPI_RESIDUAL) y = y + rv[q];
+                    __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(e.Y + (int64_t)m * e.ldY + n));
                 }
             }
         }
@@ -308,98 +317,6 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemm(
     }
 }
 
-// ---------------------------------------------------------------- GEMV
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Streaming load of one 16-byte weight granule: the weights are read once per
-// call, so the load is marked nontemporal and does not displace cached data.
-__device__ __forceinline__ u32x4 load_stream(const uint32_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
-template <int MR, int CPL, int U>
-__global__ __launch_bounds__(kThreads) void k_xnor_gemv(
-    const uint32_t* __restrict__ Xp, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
-    int N, int K, int glog2, Epilogue e)
-{
-    const int lane = threadIdx.x & 63;
-    const int G = 1 << glog2;
-    const int RPS = 64 >> glog2;                  // rows per wave step
-    const int gl = lane & (G - 1);
-    const int go = lane >> glog2;
-    const int Kw = (K + 31) >> 5;
-    const int Kw4 = (Kw + 3) >> 2;
-    const bool ragged = (Kw & 3) != 0;
-
-    // activation granules c = gl + G*i, words >= Kw zeroed
-    u32x4 xg[MR][CPL];
-    u32x4 wm[CPL];                                // word masks (all ones except pad words)
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = gl + G * i;
-        wm[i] = (u32x4){0u, 0u, 0u, 0u};
-        if (c < Kw4) {
-            wm[i].x = (4 * c + 0 < Kw) ? ~0u : 0u;
-            wm[i].y = (4 * c + 1 < Kw) ? ~0u : 0u;
-            wm[i].z = (4 * c + 2 < Kw) ? ~0u : 0u;
-            wm[i].w = (4 * c + 3 < Kw) ? ~0u : 0u;
-        }
-#pragma unroll
-        for (int mr = 0; mr < MR; ++mr) {
-            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-            if (c < Kw4) v = *reinterpret_cast<const u32x4*>(Xp + (int64_t)mr * ldX + 4 * c);
-            xg[mr][i] = v & wm[i];
-        }
-    }
-
-    const int64_t nsteps = ((int64_t)N + RPS - 1) / RPS;
-    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
-    for (int64_t s0 = wave * U; s0 < nsteps; s0 += nwaves * U) {
-        u32x4 wv[U][CPL];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = (s0 + u) * RPS + go;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = gl + G * i;
-                wv[u][i] = (u32x4){0u, 0u, 0u, 0u};
-                if (row < N && c < Kw4) wv[u][i] = load_stream(Wp + row * ldW + 4 * c);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = (s0 + u) * RPS + go;
-            if (ragged) {
-#pragma unroll
-                for (int i = 0; i < CPL; ++i) wv[u][i] &= wm[i];
-            }
-#pragma unroll
-            for (int mr = 0; mr < MR; ++mr) {
-                uint32_t pc = 0u;
-#pragma unroll
-                for (int i = 0; i < CPL; ++i) {
-                    const u32x4 t = xg[mr][i] ^ wv[u][i];
-                    pc = popc_acc(t.x, pc);
-                    pc = popc_acc(t.y, pc);
-                    pc = popc_acc(t.z, pc);
-                    pc = popc_acc(t.w, pc);
-                }
-                for (int o = G >> 1; o >= 1; o >>= 1) pc += __shfl_xor(pc, o, 64);
-                if (gl == 0 && row < N) {
-                    const int32_t d = K - 2 * (int32_t)pc;
-                    if (e.flags & EPI_DOT) e.D[(int64_t)mr * e.ldD + row] = d;
-                    if (e.flags & EPI_SCALE) {
-                        float y = e.alpha[row] * (float)d;
-                        if (e.flags & EPI_RESIDUAL) y = y + e.R[(int64_t)mr * e.ldR + row];
-                        e.Y[(int64_t)mr * e.ldY + row] = y;
-                    }
-                }
-            }
-        }
-    }
-}
-
 int tile_cols_from_env() {
     const char* v = getenv("BNN_GEMM_TN");
     if (!v) return 0;
@@ -461,61 +378,6 @@ hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
         }
     }
 #undef BNN_GEMM
-    return hipGetLastError();
-}
-
-bool gemv_eligible(int64_t M, int64_t K, uint32_t flags) {
-    const int64_t kw4 = ((K + 31) / 32 + 3) / 4;
-    return M >= 1 && M <= 4 && !(flags & EPI_THRESH) && kw4 <= 64 * 8;
-}
-
-hipError_t launch_xnor_gemv(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
-                            int64_t M, int64_t N, int64_t K, const Epilogue& e, hipStream_t s)
-{
-    // G lanes per weight row: the smallest power of two covering its 16-byte
-    // granules (at most 64); CPL granules per lane.  Large calls unroll U
-    // row-steps per wave (8 KiB of loads in flight per wave at CPL = 1);
-    // calls too small to fill the chip keep U = 1 for more waves.
-    const int64_t kw4 = ((K + 31) / 32 + 3) / 4;
-    int glog2 = 0;
-    while ((1 << glog2) < kw4 && glog2 < 6) ++glog2;
-    const int G = 1 << glog2;
-    const int cpl_needed = (int)((kw4 + G - 1) / G);
-    const int cpl = cpl_needed <= 1 ? 1 : cpl_needed <= 2 ? 2 : cpl_needed <= 4 ? 4 : 8;
-    const int umax = 8 / cpl;
-    const int rps = 64 / G;
-    const int64_t steps = (N + rps - 1) / rps;
-    const int cus = num_cus();
-    const int64_t full_chip_waves = (int64_t)cus * 4 * 8;
-    const bool unroll = umax > 1 && steps >= full_chip_waves * umax;
-    const int U = unroll ? umax : 1;
-    const int64_t waves = (steps + U - 1) / U;
-    int64_t blocks = (waves + 3) / 4;
-    const int64_t cap = (int64_t)cus * 64;
-    if (blocks > cap) blocks = cap;
-    if (blocks < 1) blocks = 1;
-    const dim3 grid((unsigned)blocks), block(kThreads);
-    const int n = (int)N, k = (int)K;
-#define BNN_GEMV(MR, CPL, UU) hipLaunchKernelGGL((k_xnor_gemv<MR, CPL, UU>), grid, block, 0, s, Xp, ldX, Wp, ldW, n, k, glog2, e)
-#define BNN_GEMV_MR(CPL, UU) \
-    switch (M) { case 1: BNN_GEMV(1, CPL, UU); break; case 2: BNN_GEMV(2, CPL, UU); break; \
-                 case 3: BNN_GEMV(3, CPL, UU); break; default: BNN_GEMV(4, CPL, UU); break; }
-    if (unroll) {
-        switch (cpl) {
-            case 1: BNN_GEMV_MR(1, 8); break;
-            case 2: BNN_GEMV_MR(2, 4); break;
-            default: BNN_GEMV_MR(4, 2); break;
-        }
-    } else {
-        switch (cpl) {
-            case 1: BNN_GEMV_MR(1, 1); break;
-            case 2: BNN_GEMV_MR(2, 1); break;
-            case 4: BNN_GEMV_MR(4, 1); break;
-            default: BNN_GEMV_MR(8, 1); break;
-        }
-    }
-#undef BNN_GEMV_MR
-#undef BNN_GEMV
     return hipGetLastError();
 }
 

@@ -164,80 +164,75 @@ __global__ __launch_bounds__(kThreads) void k_pack_im2col3x3(
     }
 }
 
-// Two-phase im2col for C % 32 == 0 (every tap is CW = C/32 whole words).
-// Phase 1 packs each input pixel once, from a fully coalesced stream of the
-// NHWC image, into the centre-tap slot (tap 4 = (kh,kw) = (1,1)) of the
-// output row of the same pixel: that slot of output row p IS pixel p.
-// Phase 2 fills the other eight tap slots of every output row from the
-// centre slots of its neighbours (or 0 = +1 outside the image) and zeroes
-// the pad words.  Phase 2 reads only centre slots and writes only other
-// slots, so the two phases need no buffer besides the output.
+// Banded im2col for C % 32 == 0 (every tap is CW = C/32 whole words).
+// One workgroup owns R consecutive output rows (oh0 .. oh0+R-1) of one
+// image.  Phase 1 packs the input rows oh0-1 .. oh0+R they need -- a
+// contiguous stretch of the NHWC image, read as one coalesced stream -- into
+// LDS (rows outside the image are 0, i.e. +1).  Phase 2 writes the R*W
+// output rows, ld words each, in 16-byte pieces: word w < 9*CW is tap w/CW,
+// read from LDS (0 for columns outside the image); words from 9*CW are pad.
 template <int CWLOG2>
-__global__ __launch_bounds__(kThreads) void k_im2col_center(
-    const float* __restrict__ X, int64_t pixels, uint32_t* __restrict__ P, int64_t ldP)
+__global__ __launch_bounds__(kThreads) void k_im2col_band(
+    const float* __restrict__ X, int H, int W, int R, int bands,
+    uint32_t* __restrict__ P, int ldP)
 {
     constexpr int CW = 1 << CWLOG2;
-    const int lane = threadIdx.x & 63;
-    const int sub = lane & 7;
-    const int grp = lane >> 3;
-    const int64_t nwords = pixels * CW;
-    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
-    // word g covers floats [32g, 32g+32) of the image (pixel g/CW, word g%CW)
-    for (int64_t g0 = wave * 8 * kSteps; g0 < nwords; g0 += nwaves * 8 * kSteps) {
+    extern __shared__ uint32_t band[];                  // (R+2) x W x CW words
+    const int b = blockIdx.x / bands;
+    const int oh0 = (blockIdx.x - b * bands) * R;
+    const int rows_out = min(R, H - oh0);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane & 7, grp = lane >> 3;
+
+    // phase 1: words g of band rows 0 .. rows_out+1 (input row oh0-1+i)
+    const int nwords = (rows_out + 2) * W * CW;
+    const int row_words = W * CW;
+    for (int g0 = wave * 8 * kSteps; g0 < nwords; g0 += 4 * 8 * kSteps) {
         Frag f[kSteps];
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
-            const int64_t g = g0 + 8 * u + grp;
-            if (g < nwords) {
-                const uint4 v = *reinterpret_cast<const uint4*>(X + 32 * g + 4 * sub);
+            const int g = g0 + 8 * u + grp;
+            const int i = g / row_words;
+            const int ih = oh0 - 1 + i;
+            f[u].u[0] = f[u].u[1] = f[u].u[2] = f[u].u[3] = 0u;
+            if (g < nwords && ih >= 0 && ih < H) {
+                const int64_t e = ((int64_t)b * H + ih) * W * (32 * CW) + (int64_t)(g - i * row_words) * 32 + 4 * sub;
+                const uint4 v = *reinterpret_cast<const uint4*>(X + e);
                 f[u].u[0] = v.x; f[u].u[1] = v.y; f[u].u[2] = v.z; f[u].u[3] = v.w;
-            } else {
-                f[u].u[0] = f[u].u[1] = f[u].u[2] = f[u].u[3] = 0u;
             }
         }
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
-            const int64_t g = g0 + 8 * u + grp;
+            const int g = g0 + 8 * u + grp;
             const uint32_t word = or_reduce8_to_last(nibble(f[u]) << (4 * sub));
-            if (sub == 7 && g < nwords)
-                P[(g >> CWLOG2) * ldP + 4 * CW + (g & (CW - 1))] = word;
+            if (sub == 7 && g < nwords) band[g] = word;
         }
     }
-}
+    __syncthreads();
 
-// One thread per (output pixel, task): tasks 0..8 are the taps in k order
-// (task 4, the centre, is already written), task 9 zeroes the pad words.
-template <int CWLOG2>
-__global__ __launch_bounds__(kThreads) void k_im2col_taps(
-    int B, int H, int W, uint32_t* __restrict__ P, int64_t ldP)
-{
-    constexpr int CW = 1 << CWLOG2;
-    const int64_t pixels = (int64_t)B * H * W;
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t p = t / 10;
-    const int task = (int)(t - p * 10);
-    if (p >= pixels || task == 4) return;
-    uint32_t* __restrict__ row = P + p * ldP;
-    if (task == 9) {
-        for (int64_t w = 9 * CW; w < ldP; ++w) row[w] = 0u;
-        return;
+    // phase 2: the output rows of this band, 4 words per thread and step
+    const int quads = ldP >> 2;                          // ldP % 4 == 0
+    const int total = rows_out * W * quads;
+    uint32_t* __restrict__ out = P + ((int64_t)b * H + oh0) * W * ldP;
+    for (int t = threadIdx.x; t < total; t += kThreads) {
+        const int px = t / quads;                        // pixel within the band
+        const int w0 = (t - px * quads) * 4;
+        const int r = px / W, ow = px - (px / W) * W;
+        uint32_t v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int w = w0 + i;
+            uint32_t x = 0u;
+            if (w < 9 * CW) {
+                const int tap = w >> CWLOG2, j = w & (CW - 1);
+                const int kh = tap / 3, kw = tap - 3 * (tap / 3);
+                const int iw = ow - 1 + kw;
+                if (iw >= 0 && iw < W) x = band[((r + kh) * W + iw) * CW + j];
+            }
+            v[i] = x;
+        }
+        *reinterpret_cast<uint4*>(out + (int64_t)px * ldP + w0) = make_uint4(v[0], v[1], v[2], v[3]);
     }
-    const int ow = (int)(p % W);
-    const int oh = (int)((p / W) % H);
-    const int kh = task / 3, kw = task - 3 * (task / 3);
-    const int dh = kh - 1, dw = kw - 1;
-    uint32_t v[CW];
-    if (oh + dh >= 0 && oh + dh < H && ow + dw >= 0 && ow + dw < W) {
-        const uint32_t* __restrict__ src = P + (p + (int64_t)dh * W + dw) * ldP + 4 * CW;
-#pragma unroll
-        for (int j = 0; j < CW; ++j) v[j] = src[j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < CW; ++j) v[j] = 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < CW; ++j) row[task * CW + j] = v[j];
 }
 
 int grid_for_rows(int64_t rows) {
@@ -274,25 +269,31 @@ hipError_t launch_pack_im2col3x3(const float* X, int64_t B, int64_t H, int64_t W
 {
     const int64_t rows = B * H * W;
     const int64_t cw = C / 32;
-    if (C % 32 == 0 && aligned16(X) && (cw & (cw - 1)) == 0 && cw <= 16) {
+    // banded path: whole-word taps, 16-byte rows, band in <= 32 KiB of LDS
+    if (C % 32 == 0 && aligned16(X) && aligned16(P) && ldP % 4 == 0 && (cw & (cw - 1)) == 0 && cw <= 16 &&
+        W * cw * 3 <= 8192 && ldP < ((int64_t)1 << 20) && W * ldP < ((int64_t)1 << 24)) {
         int cwlog2 = 0;
         while ((1 << cwlog2) < cw) ++cwlog2;
-        const int64_t nwords = rows * cw;
-        int64_t b1 = (nwords + 8 * kSteps * 4 - 1) / (8 * kSteps * 4);
-        if (b1 > 256 * 32) b1 = 256 * 32;
-        const int64_t b2 = (rows * 10 + kThreads - 1) / kThreads;
-        const int bb = (int)B, hh = (int)H, ww = (int)W;
-#define BNN_IM2COL2(L) do { \
-        hipLaunchKernelGGL((k_im2col_center<L>), dim3((unsigned)b1), dim3(kThreads), 0, s, X, rows, P, ldP); \
-        hipLaunchKernelGGL((k_im2col_taps<L>), dim3((unsigned)b2), dim3(kThreads), 0, s, bb, hh, ww, P, ldP); } while (0)
+        // rows per band: enough bands for ~1024 workgroups (4 per CU), within
+        // the LDS budget; each band re-reads 2 input rows, so taller is cheaper
+        const int64_t r_lds = 8192 / (W * cw) - 2;
+        int64_t R = (B * H + 1023) / 1024;
+        if (R < 1) R = 1;
+        if (R > r_lds) R = r_lds;
+        if (R > H) R = H;
+        const int64_t bands = (H + R - 1) / R;
+        const size_t lds = (size_t)(R + 2) * W * cw * sizeof(uint32_t);
+        const dim3 grid((unsigned)(B * bands)), block(kThreads);
+        const int hh = (int)H, ww = (int)W, rr = (int)R, nb = (int)bands, ldp = (int)ldP;
+#define BNN_BAND(L) hipLaunchKernelGGL((k_im2col_band<L>), grid, block, lds, s, X, hh, ww, rr, nb, P, ldp)
         switch (cwlog2) {
-            case 0: BNN_IM2COL2(0); break;
-            case 1: BNN_IM2COL2(1); break;
-            case 2: BNN_IM2COL2(2); break;
-            case 3: BNN_IM2COL2(3); break;
-            default: BNN_IM2COL2(4); break;
+            case 0: BNN_BAND(0); break;
+            case 1: BNN_BAND(1); break;
+            case 2: BNN_BAND(2); break;
+            case 3: BNN_BAND(3); break;
+            default: BNN_BAND(4); break;
         }
-#undef BNN_IM2COL2
+#undef BNN_BAND
         return hipGetLastError();
     }
     const bool vec = aligned16(X) && (C % 4 == 0);
