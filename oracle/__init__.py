@@ -35,17 +35,31 @@ _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
 
 
-def build(force: bool = True) -> str:
+GCC_FLAGS = ["-std=c11", "-O3", "-fopenmp", "-fPIC", "-shared",
+             "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
     """Compile ``oracle.c`` with gcc (never hipcc) into ``liboracle.so``."""
-    if not force and os.path.exists(_LIB):
-        return _LIB
-    tmp = _LIB + ".tmp"
-    cmd = ["gcc", "-std=c11", "-O3", "-fopenmp", "-fPIC", "-shared",
-           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
-           _SRC, "-o", tmp, "-lm"]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    if not force and os.path.exists(out):
+        return out
+    tmp = out + ".tmp"
+    subprocess.run(["gcc"] + GCC_FLAGS + [src, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _load(path: str):
+    L = ctypes.CDLL(path)
+    return L
+
+
+def use_library(path: str | None):
+    """Point the wrappers at another build of oracle.c (the mutation test
+    compiles deliberately broken copies to check that the pins catch them);
+    None restores the default library."""
+    global _lib
+    _lib = None if path is None else _configure(_load(path))
 
 
 def lib():
@@ -53,29 +67,33 @@ def lib():
     if _lib is None:
         if not os.path.exists(_LIB):
             build()
-        L = ctypes.CDLL(_LIB)
-        sigs = {
-            "oracle_sign": [_p, _i64, _i64, _i64, _p],
-            "oracle_pack_signs": [_p, _i64, _i64, _p, _i64],
-            "oracle_unpack_signs": [_p, _i64, _i64, _i64, _p],
-            "oracle_alpha": [_p, _i64, _i64, _i64, _p],
-            "oracle_dot": [_p, _p, _i64, _i64, _i64, _p],
-            "oracle_scale": [_p, _p, _i64, _i64, _p],
-            "oracle_scale_residual": [_p, _p, _p, _i64, _i64, _i64, _p],
-            "oracle_bn_fold": [_p, _p, _p, _p, ctypes.c_float, _p, _i64, _p, _p],
-            "oracle_threshold_signs": [_p, _p, _p, _i64, _i64, _p],
-            "oracle_im2col_signs": [_p, _i64, _i64, _i64, _i64, _p],
-            "oracle_dense_f64": [_p, _i64, _p, _i64, _i64, _i64, _i64, _p],
-            "oracle_dense_pm1_f32out": [_p, _p, _i64, _i64, _i64, _i64, _p],
-        }
-        for name, args in sigs.items():
-            fn = getattr(L, name)
-            fn.argtypes = args
-            fn.restype = None
-        L.oracle_num_threads.argtypes = []
-        L.oracle_num_threads.restype = ctypes.c_int
-        _lib = L
+        _lib = _configure(_load(_LIB))
     return _lib
+
+
+def _configure(L):
+    """Declare the C signatures on a loaded oracle library."""
+    sigs = {
+        "oracle_sign": [_p, _i64, _i64, _i64, _p],
+        "oracle_pack_signs": [_p, _i64, _i64, _p, _i64],
+        "oracle_unpack_signs": [_p, _i64, _i64, _i64, _p],
+        "oracle_alpha": [_p, _i64, _i64, _i64, _p],
+        "oracle_dot": [_p, _p, _i64, _i64, _i64, _p],
+        "oracle_scale": [_p, _p, _i64, _i64, _p],
+        "oracle_scale_residual": [_p, _p, _p, _i64, _i64, _i64, _p],
+        "oracle_bn_fold": [_p, _p, _p, _p, ctypes.c_float, _p, _i64, _p, _p],
+        "oracle_threshold_signs": [_p, _p, _p, _i64, _i64, _p],
+        "oracle_im2col_signs": [_p, _i64, _i64, _i64, _i64, _p],
+        "oracle_dense_f64": [_p, _i64, _p, _i64, _i64, _i64, _i64, _p],
+        "oracle_dense_pm1_f32out": [_p, _p, _i64, _i64, _i64, _i64, _p],
+    }
+    for name, args in sigs.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = None
+    L.oracle_num_threads.argtypes = []
+    L.oracle_num_threads.restype = ctypes.c_int
+    return L
 
 
 def num_threads() -> int:

@@ -1,0 +1,128 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each case plants one plausible mistake in a copy of ``oracle/oracle.c`` (a
+wrong comparison, a dropped term, a transposed index, a wrong divisor, a
+missing rounding, a flipped sign, ...), builds it with gcc into a temporary
+library, points the oracle at it, and runs the pin suite of
+``test_oracle_pins.py``: at least one pin must fail.  A mutant that every pin
+accepts would mean the pins do not constrain that part of the oracle.
+"""
+from __future__ import annotations
+
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
+
+MUTATIONS = [
+    ("sign: zero maps to -1",
+     "(x[r * ldx + c] >= 0.0f)", "(x[r * ldx + c] > 0.0f)"),
+    ("pack: bit 1 encodes +1",
+     "if (s[r * K + k] == -1)", "if (s[r * K + k] == 1)"),
+    ("pack: most significant bit first",
+     "|= (uint32_t)1u << (k % 32);", "|= (uint32_t)1u << (31 - k % 32);"),
+    ("pack: pad words left as ones",
+     "for (int64_t w = 0; w < ld; ++w) words[r * ld + w] = 0u;",
+     "for (int64_t w = 0; w < ld; ++w) words[r * ld + w] = (w * 32 >= K) ? ~0u : 0u;"),
+    ("dot: last term dropped",
+     "for (int64_t k = 0; k < K; ++k)\n                acc += (int32_t)xs",
+     "for (int64_t k = 0; k + 1 < K; ++k)\n                acc += (int32_t)xs"),
+    ("dot: operands paired in reverse order",
+     "(int32_t)ws[n * K + k];", "(int32_t)ws[n * K + (K - 1 - k)];"),
+    ("alpha: divided by K + 1",
+     "alpha[n] = (float)(sum / (double)K);", "alpha[n] = (float)(sum / (double)(K + 1));"),
+    ("alpha: summed in single precision",
+     "double sum = 0.0;\n        for (int64_t k = 0; k < K; ++k) sum += fabs((double)W[n * ldw + k]);",
+     "float sum = 0.0f;\n        for (int64_t k = 0; k < K; ++k) sum += fabsf(W[n * ldw + k]);"),
+    ("alpha: signed mean",
+     "sum += fabs((double)W[n * ldw + k]);", "sum += (double)W[n * ldw + k];"),
+    ("scale: alpha indexed by row",
+     "Y[m * N + n] = alpha[n] * (float)D[m * N + n];", "Y[m * N + n] = alpha[m % N] * (float)D[m * N + n];"),
+    ("residual: fused multiply-add",
+     "float z = alpha[n] * (float)D[m * N + n];\n            Y[m * N + n] = z + R[m * ldr + n];",
+     "Y[m * N + n] = fmaf(alpha[n], (float)D[m * N + n], R[m * ldr + n]);"),
+    ("bn fold: sign of beta flipped",
+     "double rhs = (double)gamma[n] * (double)mean[n] - (double)beta[n] * sd;",
+     "double rhs = (double)gamma[n] * (double)mean[n] + (double)beta[n] * sd;"),
+    ("bn fold: negative direction not flipped",
+     "tau[n] = (float)(-(rhs / c));", "tau[n] = (float)(rhs / c);"),
+    ("bn fold: eps ignored",
+     "double sd = sqrt((double)var[n] + (double)eps);", "double sd = sqrt((double)var[n]);"),
+    ("threshold: strict comparison at the tie",
+     "s_out[m * N + n] = (v >= tau[n])", "s_out[m * N + n] = (v > tau[n])"),
+    ("im2col: pad pixels encode -1",
+     "int8_t v = 1;\n                    if (inside)", "int8_t v = -1;\n                    if (inside)"),
+    ("im2col: tap order transposed",
+     "cols[p * K + (kh * 3 + kw) * C + c] = v;", "cols[p * K + (kw * 3 + kh) * C + c] = v;"),
+    ("im2col: window not centred",
+     "int64_t ih = oh - 1 + kh, iw = ow - 1 + kw;", "int64_t ih = oh + kh, iw = ow - 1 + kw;"),
+    ("first FP layer: single-precision accumulation",
+     "acc += (double)X[m * ldx + k] * (double)W[n * ldw + k];", "acc += (double)(X[m * ldx + k] * W[n * ldw + k]);"),
+    ("last FP layer: activation signs ignored",
+     "acc += (double)s[m * K + k] * (double)W[n * ldw + k];", "acc += (double)W[n * ldw + k];"),
+    ("last FP layer: no final rounding to single",
+     "Y[m * N + n] = (float)acc;", "Y[m * N + n] = (float)(acc * (1.0 + 1e-6));"),
+]
+
+
+def _pin_calls():
+    """The pin suite; parametrized pins run with their own parameter lists
+    (the random-K identity with a representative subset)."""
+    calls = []
+    for name in sorted(dir(pins)):
+        fn = getattr(pins, name)
+        if not (name.startswith("test_") and callable(fn)):
+            continue
+        marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+        if not marks:
+            calls.append((name, fn))
+            continue
+        argnames, values = marks[0].args[0], marks[0].args[1]
+        if name == "test_identity_random_K":
+            values = [1, 5, 31, 32, 33, 64, 100, 1000]
+        keys = [a.strip() for a in argnames.split(",")]
+        for v in values:
+            args = v if len(keys) > 1 else (v,)
+            calls.append((f"{name}{list(args)}", lambda fn=fn, args=args: fn(*args)))
+    return calls
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    with tempfile.TemporaryDirectory(prefix="oracle_mut_") as d:
+        yield d
+
+
+def test_pins_pass_on_the_real_oracle():
+    oracle.use_library(None)
+    for name, call in _pin_calls():
+        call()
+
+
+@pytest.mark.parametrize("label,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_each_planted_mistake_fails_a_pin(workdir, label, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique or missing: {label}"
+    mutated = src.replace(old, new)
+    tag = "".join(ch if ch.isalnum() else "_" for ch in label)
+    csrc = os.path.join(workdir, f"{tag}.c")
+    lib = os.path.join(workdir, f"{tag}.so")
+    with open(csrc, "w") as f:
+        f.write(mutated)
+    oracle.build(src=csrc, out=lib)
+    failed = []
+    try:
+        oracle.use_library(lib)
+        for name, call in _pin_calls():
+            try:
+                call()
+            except Exception:        # AssertionError, or a numpy comparison error
+                failed.append(name)
+    finally:
+        oracle.use_library(None)
+    assert failed, f"no pin caught the planted mistake: {label}"

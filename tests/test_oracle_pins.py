@@ -276,12 +276,19 @@ def test_bn_fold_exact_ties_and_directions():
     tau, d = oracle.bn_fold(one, 0.2 * one, one, one, 0.0, zero)
     assert d[0] == 0
     assert oracle.threshold_signs(np.array([[5]], np.int32), tau, d)[0, 0] == -1
+    # eps enters sd = sqrt(var + eps): var=0, eps=4 -> sd=2, BN = 0.5 D - 2, tie at D=4
+    tau, d = oracle.bn_fold(one, -one, zero, zero, 4.0, 0.5 * one)
+    assert d[0] == 1 and tau[0] == 4.0
+    D = np.array([[2], [3], [4], [5]], np.int32)
+    np.testing.assert_array_equal(oracle.threshold_signs(D, tau, d)[:, 0], [-1, -1, 1, 1])
 
 
-def test_bn_fold_decisions_match_exact_rational():
+@pytest.mark.parametrize("eps_scale", [1.0, 1e4])
+def test_bn_fold_decisions_match_exact_rational(eps_scale):
     rng = np.random.default_rng(12)
     N = 64
     g, b, mu, var, eps = workloads.bn_params(2001, N)
+    eps = np.float32(eps * eps_scale)        # 1e-5, and 0.1 where eps moves the thresholds
     g = g * np.where(np.arange(N) % 5 == 0, -1, 1).astype(np.float32)   # both directions
     mu = (rng.normal(0, 3, N)).astype(np.float32)
     var = (rng.random(N) * 2 + 0.1).astype(np.float32)

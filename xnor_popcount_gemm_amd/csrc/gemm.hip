@@ -38,7 +38,6 @@ namespace bnn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = 256;   // 4 waves x 64 rows
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -95,10 +94,11 @@ __device__ __forceinline__ void xnor_chunk(uint32_t (&acc)[TN], const uint32_t (
         if (j + CP < TN)
             load_w<CP, KCC, FULLN, MASK>(wn, p0 + (FULLN ? (int64_t)(j + CP) * ldw : 0), ldw, j + CP, nlast, nvalid);
         __builtin_amdgcn_sched_barrier(0);
+        // word-outer, column-inner: CP independent accumulator chains interleave
 #pragma unroll
-        for (int c = 0; c < CP; ++c)
+        for (int kk = 0; kk < KCC; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < KCC; ++kk) acc[j + c] = popc_acc(a[kk] ^ wc[c][kk], acc[j + c]);
+            for (int c = 0; c < CP; ++c) acc[j + c] = popc_acc(a[kk] ^ wc[c][kk], acc[j + c]);
         if (j + CP < TN) {
 #pragma unroll
             for (int c = 0; c < CP; ++c)
@@ -202,18 +202,18 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
     }
 }
 
-template <int TN, int KC, bool EPI_LDS>
-__global__ __launch_bounds__(kThreads) void k_xnor_gemm(
+template <int TN, int KC, bool EPI_LDS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
     const uint32_t* __restrict__ Xp, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
     int M, int N, int K, int tiles_n, Epilogue e)
 {
     constexpr int kLdsWords = 64 * ((TN < 32 ? TN : 32) + 1);
-    __shared__ uint32_t lds_epi[EPI_LDS ? 4 * kLdsWords : 1];
+    __shared__ uint32_t lds_epi[EPI_LDS ? WAVES * kLdsWords : 1];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int tn = blockIdx.x % tiles_n;
     const int tm = blockIdx.x / tiles_n;
-    const int wrow0 = tm * kRowsPerBlock + wave * 64;
+    const int wrow0 = tm * (WAVES * 64) + wave * 64;
     if (wrow0 >= M) return;                       // whole wave past the last row
     const int m = wrow0 + lane;
     const int n0 = tn * TN;
@@ -341,7 +341,6 @@ hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
     // Column tile: wide tiles reuse each activation chunk over more columns;
     // narrow tiles give more waves (a full chip needs several rounds of
     // 256 CUs x 4 SIMDs x ~8 waves) and a smaller last round.
-    const int64_t row_tiles = (M + kRowsPerBlock - 1) / kRowsPerBlock;
     const int64_t row_waves = (M + 63) / 64;
     int tn = tile_cols_from_env();
     if (tn == 0) {
@@ -358,25 +357,36 @@ hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
     // through LDS so stores cover whole row segments.
     const int64_t kw = (K + 31) / 32;
     const bool lds = kw <= 128 && (e.flags & (EPI_DOT | EPI_SCALE)) && !(e.flags & EPI_THRESH);
+    // Waves per workgroup: all waves of a workgroup read the same TN weight
+    // rows through the CU's scalar cache, so bigger workgroups put fewer
+    // distinct weight streams on a CU.
+    int waves = 4;
+    if (const char* v = getenv("BNN_GEMM_WAVES")) {       // tuning override: 4, 8 or 16
+        const int w = atoi(v);
+        if (w == 4 || w == 8 || w == 16) waves = w;
+    }
+    const int64_t row_tiles = (M + waves * 64 - 1) / (waves * 64);
     const int tiles_n = (int)((N + tn - 1) / tn);
-    const dim3 grid((unsigned)(row_tiles * tiles_n)), block(kThreads);
+    const dim3 grid((unsigned)(row_tiles * tiles_n)), block(waves * 64);
     const int m = (int)M, n = (int)N, k = (int)K;
-#define BNN_GEMM(T, L) hipLaunchKernelGGL((k_xnor_gemm<T, 16, L>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e)
+#define BNN_GEMM(T, L, WV) hipLaunchKernelGGL((k_xnor_gemm<T, 16, L, WV>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e)
+#define BNN_GEMM_W(T, L) switch (waves) { case 8: BNN_GEMM(T, L, 8); break; case 16: BNN_GEMM(T, L, 16); break; default: BNN_GEMM(T, L, 4); break; }
     if (lds) {
         switch (tn) {
-            case 64: BNN_GEMM(64, true); break;
-            case 32: BNN_GEMM(32, true); break;
-            case 16: BNN_GEMM(16, true); break;
-            default: BNN_GEMM(8, true); break;
+            case 64: BNN_GEMM_W(64, true); break;
+            case 32: BNN_GEMM_W(32, true); break;
+            case 16: BNN_GEMM_W(16, true); break;
+            default: BNN_GEMM_W(8, true); break;
         }
     } else {
         switch (tn) {
-            case 64: BNN_GEMM(64, false); break;
-            case 32: BNN_GEMM(32, false); break;
-            case 16: BNN_GEMM(16, false); break;
-            default: BNN_GEMM(8, false); break;
+            case 64: BNN_GEMM_W(64, false); break;
+            case 32: BNN_GEMM_W(32, false); break;
+            case 16: BNN_GEMM_W(16, false); break;
+            default: BNN_GEMM_W(8, false); break;
         }
     }
+#undef BNN_GEMM_W
 #undef BNN_GEMM
     return hipGetLastError();
 }
