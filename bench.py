@@ -479,6 +479,9 @@ def main():
         import workloads
         sec = {}
         gv = [gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]]
+        gdig = source_digest("xnor_popcount_gemm_amd/csrc/gemv.hip", "xnor_popcount_gemm_amd/csrc/bnn_device.hpp")
+        for r in gv:
+            r["traffic"] = read_traffic(f"xnor_gemv_N{r['N']}_K{r['K']}_stack{GEMV_COPIES}", gdig)
         sec["gemv_batch1"] = {
             "metric": "batch-1 GEMV HBM GB/s (191 stacked weight copies, one launch)",
             "value": round(min(r["stream_GBps"] for r in gv), 1),
