@@ -86,11 +86,18 @@ def _configure(L):
         "oracle_im2col_signs": [_p, _i64, _i64, _i64, _i64, _p],
         "oracle_dense_f64": [_p, _i64, _p, _i64, _i64, _i64, _i64, _p],
         "oracle_dense_pm1_f32out": [_p, _p, _i64, _i64, _i64, _i64, _p],
+        "oracle_dot_i8": [_p, _p, _i64, _i64, _i64, _p],
+        "oracle_quantize_absmax_i8": [_p, _i64, _i64, _i64, _p, _p],
+        "oracle_pack_planes_i8": [_p, _i64, _i64, _p, _i64, _p],
+        "oracle_scale_i8": [_p, _p, _i64, _p, _i64, _i64, _p],
+        "oracle_scale_bias_residual": [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = None
+    L.oracle_alpha_tensor.argtypes = [_p, _i64, _i64, _i64]
+    L.oracle_alpha_tensor.restype = ctypes.c_float
     L.oracle_num_threads.argtypes = []
     L.oracle_num_threads.restype = ctypes.c_int
     return L
@@ -159,6 +166,96 @@ def dot(xs: np.ndarray, ws: np.ndarray) -> np.ndarray:
     D = np.empty((M, N), dtype=np.int32)
     lib().oracle_dot(_ptr(xs), _ptr(ws), M, N, K, _ptr(D))
     return D
+
+
+def dot_i8(xq: np.ndarray, ws: np.ndarray) -> np.ndarray:
+    """D[m, n] = sum_k xq[m, k] * ws[n, k]: int8 activations times +1/-1
+    weights ("Extreme Quantization" eq. (1)-(2); INT8 activations of its
+    BitNet section)."""
+    xq = _c(xq, np.int8)
+    ws = _c(ws, np.int8)
+    M, K = xq.shape
+    N, K2 = ws.shape
+    assert K == K2
+    D = np.empty((M, N), dtype=np.int32)
+    lib().oracle_dot_i8(_ptr(xq), _ptr(ws), M, N, K, _ptr(D))
+    return D
+
+
+def quantize_absmax_i8(X: np.ndarray):
+    """Per-row symmetric absmax INT8 quantization (BitNet item 2; the
+    quantizer itself is this module's reading): returns (Q int8 [M, K],
+    scale fp32 [M]) with X ~= scale * Q."""
+    X = _c(X, np.float32)
+    M, K = X.shape
+    Q = np.empty((M, K), dtype=np.int8)
+    sc = np.empty(M, dtype=np.float32)
+    lib().oracle_quantize_absmax_i8(_ptr(X), M, K, K, _ptr(Q), _ptr(sc))
+    return Q, sc
+
+
+def pack_planes_i8(Q: np.ndarray, ld: int | None = None):
+    """Bit planes of int8 rows: words [M, 8, ld] (plane b = bit b of each
+    two's-complement byte, packed LSB first along K, pads 0) and xsum [M]."""
+    Q = _c(Q, np.int8)
+    M, K = Q.shape
+    kw = (K + 31) // 32
+    ld = kw if ld is None else ld
+    assert ld >= kw
+    words = np.empty((M, 8, ld), dtype=np.uint32)
+    xsum = np.empty(M, dtype=np.int32)
+    lib().oracle_pack_planes_i8(_ptr(Q), M, K, _ptr(words), ld, _ptr(xsum))
+    return words, xsum
+
+
+def alpha_tensor(W: np.ndarray) -> np.float32:
+    """One scale for the whole matrix, ||W||_1 / (N K) (eq. (8))."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    return np.float32(lib().oracle_alpha_tensor(_ptr(W), N, K, K))
+
+
+def scale_i8(D: np.ndarray, a: np.ndarray, xscale: np.ndarray) -> np.ndarray:
+    """Y = fl(fl(alpha * D) * xscale_m); a of length N (per row) or 1 (per
+    tensor)."""
+    D = _c(D, np.int32)
+    a = _c(np.atleast_1d(a), np.float32)
+    xscale = _c(xscale, np.float32)
+    M, N = D.shape
+    stride = 0 if a.shape[0] == 1 else 1
+    assert stride == 0 or a.shape[0] == N
+    Y = np.empty((M, N), dtype=np.float32)
+    lib().oracle_scale_i8(_ptr(D), _ptr(a), stride, _ptr(xscale), M, N, _ptr(Y))
+    return Y
+
+
+def scale_bias_residual(D: np.ndarray, a: np.ndarray, bias: np.ndarray,
+                        R: np.ndarray | None = None) -> np.ndarray:
+    """Y = fl(fl(fl(alpha * D) + b_n) + R) (bias of "y = Wx + b"; R optional);
+    a of length N (per row) or 1 (per tensor, eq. (8))."""
+    D = _c(D, np.int32)
+    a = _c(np.atleast_1d(a), np.float32)
+    bias = _c(bias, np.float32)
+    M, N = D.shape
+    stride = 0 if a.shape[0] == 1 else 1
+    assert stride == 0 or a.shape[0] == N
+    Y = np.empty((M, N), dtype=np.float32)
+    if R is None:
+        lib().oracle_scale_bias_residual(_ptr(D), _ptr(a), stride, _ptr(bias), None, 0, M, N, _ptr(Y))
+    else:
+        R = _c(R, np.float32)
+        assert R.shape == (M, N)
+        lib().oracle_scale_bias_residual(_ptr(D), _ptr(a), stride, _ptr(bias), _ptr(R), N, M, N, _ptr(Y))
+    return Y
+
+
+def binary_weight_linear_i8(X: np.ndarray, W: np.ndarray, per_tensor: bool = False):
+    """fp32 activations X [M, K] quantized to INT8, times binary weights W
+    [N, K]: returns (Q, xscale, D int32, Y fp32, alpha)."""
+    Q, xs = quantize_absmax_i8(X)
+    a = np.atleast_1d(alpha_tensor(W)) if per_tensor else alpha(W)
+    D = dot_i8(Q, sign(W))
+    return Q, xs, D, scale_i8(D, a, xs), a
 
 
 def scale(D: np.ndarray, a: np.ndarray) -> np.ndarray:

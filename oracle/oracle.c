@@ -25,6 +25,8 @@
  *  [P3] "Perfected Concept", table "What is binary vs not": first/last layers
  *       and BatchNorm scales stay in higher precision; residual streams stay FP.
  *  [P4] "State of the Art Survey", Bi-Real Net row: FP residual shortcut.
+ *  [P5] "BitNet: 1-bit Transformer": activations kept at INT8 next to binary
+ *       weights; eq. (8) (one mean-|W| scale for the whole matrix).
  */
 #include <math.h>
 #include <omp.h>
@@ -223,6 +225,124 @@ API void oracle_dense_pm1_f32out(const int8_t* s, const float* W, int64_t ldw,
             for (int64_t k = 0; k < K; ++k)
                 acc += (double)s[m * K + k] * (double)W[n * ldw + k];
             Y[m * N + n] = (float)acc;
+        }
+}
+
+/* [P5] "Binary Neural Networks" eq. (1)-(2) (binary weights times real
+ * activations: only additions and subtractions) with the activations
+ * quantized to 8-bit integers as in the BitNet section of [P5]:
+ * D[m, n] = sum_k x[m, k] * s[n, k] for int8 x and +1/-1 signs s, an exact
+ * integer multiply-add (|D| <= 128 K fits int32 for K <= 2^24).  xq is
+ * [M, K] (dense), ws is [N, K] (+1/-1), D is [M, N]. */
+API void oracle_dot_i8(const int8_t* xq, const int8_t* ws, int64_t M, int64_t N, int64_t K, int32_t* D)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (int64_t)xq[m * K + k] * (int64_t)ws[n * K + k];
+            D[m * N + n] = (int32_t)acc;
+        }
+}
+
+/* [P5] "BitNet: 1-bit Transformer", item 2 (activations quantized to INT8).
+ * The page names no quantizer; the reading taken is symmetric per-row absmax:
+ *   amax = max_k |x[m,k]| (NaN elements skipped),
+ *   inv  = fl32(127 / amax)  (0 when amax is 0),
+ *   q    = rint(fl32(x * inv)) clamped to [-127, 127]  (round half to even;
+ *          NaN products give 0),
+ *   scale[m] = fl32(amax / 127), so x ~= scale * q.
+ * All arithmetic is IEEE single precision as written (one rounding per op).
+ * Q is dense [M, K]. */
+API void oracle_quantize_absmax_i8(const float* X, int64_t M, int64_t K, int64_t ldx,
+                                   int8_t* Q, float* scale)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(X[m * ldx + k]);
+            if (a > amax) amax = a;
+        }
+        float inv = (amax > 0.0f) ? 127.0f / amax : 0.0f;
+        scale[m] = amax / 127.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = X[m * ldx + k] * inv;
+            float r = rintf(v);
+            int8_t q;
+            if (isnan(r)) q = 0;
+            else if (r > 127.0f) q = 127;
+            else if (r < -127.0f) q = -127;
+            else q = (int8_t)r;
+            Q[m * K + k] = q;
+        }
+    }
+}
+
+/* Bit-plane layout of int8 activations (a storage convention, not stated by
+ * the pages): plane b (0..7) of row m holds bit b of the two's-complement
+ * byte of Q[m,k], packed like a sign row (element k in word k / 32 at bit
+ * k % 32); plane b of row m starts at words + (m * 8 + b) * ld.  Pad bits and
+ * pad words are 0, i.e. the value 0.  xsum[m] = sum_k Q[m,k]. */
+API void oracle_pack_planes_i8(const int8_t* Q, int64_t M, int64_t K, uint32_t* words, int64_t ld,
+                               int32_t* xsum)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t total = 0;
+        for (int64_t b = 0; b < 8; ++b)
+            for (int64_t w = 0; w < ld; ++w) words[(m * 8 + b) * ld + w] = 0u;
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = (uint8_t)Q[m * K + k];
+            total += Q[m * K + k];
+            for (int64_t b = 0; b < 8; ++b)
+                if ((byte >> b) & 1u)
+                    words[(m * 8 + b) * ld + k / 32] |= (uint32_t)1u << (k % 32);
+        }
+        xsum[m] = (int32_t)total;
+    }
+}
+
+/* [P5] eq. (8): one scale for the whole matrix, the mean magnitude over all
+ * N * K weights (||W||_1 / (nm)), summed in double in index order and
+ * rounded once to float. */
+API float oracle_alpha_tensor(const float* W, int64_t N, int64_t K, int64_t ldw)
+{
+    double total = 0.0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) total += fabs((double)W[n * ldw + k]);
+    return (float)(total / ((double)N * (double)K));
+}
+
+/* Dequantized output of binary weights times absmax-int8 activations:
+ * Y[m,n] = fl32(fl32(alpha[n] * (float)D[m,n]) * xscale[m]), two rounded
+ * multiplies, no FMA.  alpha_stride 1: one scale per output row n; 0: one
+ * scale for the whole matrix (alpha[0]). */
+API void oracle_scale_i8(const int32_t* D, const float* alpha, int64_t alpha_stride,
+                         const float* xscale, int64_t M, int64_t N, float* Y)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float z = alpha[n * alpha_stride] * (float)D[m * N + n];
+            Y[m * N + n] = z * xscale[m];
+        }
+}
+
+/* [P2] "y = Wx + b": the layer's bias after the alpha scale, then the
+ * optional residual: Y = fl32(fl32(fl32(alpha * D) + b[n]) + R[m,n]), each
+ * step one rounded op, no FMA.  alpha_stride as above; R may be NULL. */
+API void oracle_scale_bias_residual(const int32_t* D, const float* alpha, int64_t alpha_stride,
+                                    const float* bias, const float* R, int64_t ldr,
+                                    int64_t M, int64_t N, float* Y)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float z = alpha[n * alpha_stride] * (float)D[m * N + n];
+            float zb = z + bias[n];
+            Y[m * N + n] = R ? zb + R[m * ldr + n] : zb;
         }
 }
 

@@ -25,7 +25,11 @@ MUTATIONS = [
     ("pack: bit 1 encodes +1",
      "if (s[r * K + k] == -1)", "if (s[r * K + k] == 1)"),
     ("pack: most significant bit first",
-     "|= (uint32_t)1u << (k % 32);", "|= (uint32_t)1u << (31 - k % 32);"),
+     "words[r * ld + k / 32] |= (uint32_t)1u << (k % 32);",
+     "words[r * ld + k / 32] |= (uint32_t)1u << (31 - k % 32);"),
+    ("planes: most significant bit first",
+     "words[(m * 8 + b) * ld + k / 32] |= (uint32_t)1u << (k % 32);",
+     "words[(m * 8 + b) * ld + k / 32] |= (uint32_t)1u << (31 - k % 32);"),
     ("pack: pad words left as ones",
      "for (int64_t w = 0; w < ld; ++w) words[r * ld + w] = 0u;",
      "for (int64_t w = 0; w < ld; ++w) words[r * ld + w] = (w * 32 >= K) ? ~0u : 0u;"),
@@ -67,6 +71,37 @@ MUTATIONS = [
      "acc += (double)s[m * K + k] * (double)W[n * ldw + k];", "acc += (double)W[n * ldw + k];"),
     ("last FP layer: no final rounding to single",
      "Y[m * N + n] = (float)acc;", "Y[m * N + n] = (float)(acc * (1.0 + 1e-6));"),
+    ("int8 dot: activations read as unsigned",
+     "acc += (int64_t)xq[m * K + k] * (int64_t)ws[n * K + k];",
+     "acc += (int64_t)(uint8_t)xq[m * K + k] * (int64_t)ws[n * K + k];"),
+    ("int8 dot: weight sign ignored",
+     "acc += (int64_t)xq[m * K + k] * (int64_t)ws[n * K + k];",
+     "acc += (int64_t)xq[m * K + k];"),
+    ("quantize: 128 levels instead of 127",
+     "float inv = (amax > 0.0f) ? 127.0f / amax : 0.0f;",
+     "float inv = (amax > 0.0f) ? 128.0f / amax : 0.0f;"),
+    ("quantize: truncation instead of rounding",
+     "float r = rintf(v);", "float r = truncf(v);"),
+    ("quantize: ties rounded away from zero",
+     "float r = rintf(v);", "float r = roundf(v);"),
+    ("quantize: scale inverted",
+     "scale[m] = amax / 127.0f;", "scale[m] = 127.0f / amax;"),
+    ("quantize: NaN taken as the maximum",
+     "if (a > amax) amax = a;", "if (!(a <= amax)) amax = a;"),
+    ("planes: sign plane dropped",
+     "for (int64_t b = 0; b < 8; ++b)\n                if", "for (int64_t b = 0; b < 7; ++b)\n                if"),
+    ("planes: sum of magnitudes",
+     "total += Q[m * K + k];", "total += Q[m * K + k] < 0 ? -Q[m * K + k] : Q[m * K + k];"),
+    ("per-tensor alpha: divided by K only",
+     "return (float)(total / ((double)N * (double)K));", "return (float)(total / (double)K);"),
+    ("per-tensor alpha: signed sum",
+     "total += fabs((double)W[n * ldw + k]);", "total += (double)W[n * ldw + k];"),
+    ("int8 dequant: activation scale ignored",
+     "Y[m * N + n] = z * xscale[m];", "Y[m * N + n] = z;"),
+    ("bias: added before the alpha scale",
+     "float zb = z + bias[n];", "float zb = alpha[n * alpha_stride] * ((float)D[m * N + n] + bias[n]);"),
+    ("bias: indexed by activation row",
+     "float zb = z + bias[n];", "float zb = z + bias[m % N];"),
 ]
 
 

@@ -405,3 +405,196 @@ def test_mlp_chain_small_composition():
                 assert r["signs"][i + 1][m, n] == want
         s = r["signs"][i + 1]
     assert r["logits"].shape == (16, 10)
+
+
+# ---------------------------------------------------------------- binary weights x INT8 activations
+# Page "Extreme Quantization", "Binary Neural Networks" eq. (1)-(2): with
+# +1/-1 weights a dot product only adds or subtracts activations; its "BitNet"
+# section keeps the activations at INT8.
+def test_dot_i8_matches_int64_matmul():
+    rng = np.random.default_rng(70)
+    for K in (1, 7, 31, 32, 33, 100, 1000, 4096):
+        xq = rng.integers(-128, 128, size=(5, K)).astype(np.int8)
+        ws = _rand_signs(rng, (9, K))
+        want = xq.astype(np.int64) @ ws.astype(np.int64).T
+        np.testing.assert_array_equal(oracle.dot_i8(xq, ws).astype(np.int64), want)
+
+
+def test_dot_i8_add_subtract_reading():
+    # eq. (2): each weight either adds (+1) or subtracts (-1) its activation
+    rng = np.random.default_rng(71)
+    xq = rng.integers(-128, 128, size=(3, 37)).astype(np.int8)
+    ws = _rand_signs(rng, (4, 37))
+    D = oracle.dot_i8(xq, ws)
+    for m in range(3):
+        for n in range(4):
+            acc = 0
+            for k in range(37):
+                if ws[n, k] == 1:
+                    acc += int(xq[m, k])
+                else:
+                    acc -= int(xq[m, k])
+            assert int(D[m, n]) == acc
+
+
+def test_dot_i8_extremes_and_invariants():
+    K = 1000
+    lo = np.full((1, K), -128, np.int8)
+    hi = np.full((1, K), 127, np.int8)
+    plus = np.ones((1, K), np.int8)
+    minus = -plus
+    assert int(oracle.dot_i8(lo, minus)[0, 0]) == 128 * K
+    assert int(oracle.dot_i8(lo, plus)[0, 0]) == -128 * K
+    assert int(oracle.dot_i8(hi, minus)[0, 0]) == -127 * K
+    rng = np.random.default_rng(72)
+    xq = rng.integers(-128, 128, size=(4, 333)).astype(np.int8)
+    ws = _rand_signs(rng, (6, 333))
+    D = oracle.dot_i8(xq, ws)
+    np.testing.assert_array_equal(oracle.dot_i8(xq, -ws), -D)          # negate weights
+    np.testing.assert_array_equal(oracle.dot_i8(xq, ws[::-1]), D[:, ::-1])  # row n -> column n
+
+
+def test_planes_layout_hand_example():
+    # q = [1, -1, -128, 127, 0]; bytes 0x01, 0xFF, 0x80, 0x7F, 0x00.
+    # plane 0 holds elements 0, 1, 3 -> 0b1011 = 11; planes 1..6 hold
+    # elements 1, 3 -> 0b1010 = 10; plane 7 holds elements 1, 2 -> 0b110 = 6.
+    words, xsum = oracle.pack_planes_i8(np.array([[1, -1, -128, 127, 0]], np.int8), ld=2)
+    assert words.shape == (1, 8, 2)
+    assert [int(v) for v in words[0, :, 0]] == [11, 10, 10, 10, 10, 10, 10, 6]
+    assert not words[0, :, 1].any()
+    assert int(xsum[0]) == -1
+
+
+def test_planes_reconstruct_values_and_pads():
+    rng = np.random.default_rng(73)
+    for K in (1, 31, 32, 33, 1000):
+        Q = rng.integers(-128, 128, size=(3, K)).astype(np.int8)
+        words, xsum = oracle.pack_planes_i8(Q, ld=(K + 31) // 32 + 2)
+        bits = (words[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1   # [M, 8, ld, 32]
+        bits = bits.reshape(3, 8, -1).astype(np.int64)
+        weight = np.array([1, 2, 4, 8, 16, 32, 64, -128], np.int64)      # two's complement
+        vals = np.einsum("mbk,b->mk", bits, weight)
+        np.testing.assert_array_equal(vals[:, :K], Q.astype(np.int64))
+        assert not bits[:, :, K:].any()                                    # pads hold 0
+        np.testing.assert_array_equal(xsum.astype(np.int64), Q.astype(np.int64).sum(axis=1))
+
+
+def test_planes_popcount_identity_equals_dot_i8():
+    # With weight bit 1 = -1: sum_k s_k x_k = sum_k x_k - 2 sum_{k: bit_k = 1} x_k,
+    # and sum_{bit=1} x = sum_b c_b popcount(plane_b AND wbits), c_b = 2^b
+    # (b < 7), c_7 = -128.
+    rng = np.random.default_rng(74)
+    for K in (5, 64, 1000, 4096):
+        Q = rng.integers(-128, 128, size=(4, K)).astype(np.int8)
+        ws = _rand_signs(rng, (7, K))
+        planes, xsum = oracle.pack_planes_i8(Q)
+        wp = oracle.pack_signs(ws)
+        cnt = np.bitwise_count(planes[:, None, :, :] & wp[None, :, None, :]).sum(axis=-1, dtype=np.int64)
+        weight = np.array([1, 2, 4, 8, 16, 32, 64, -128], np.int64)
+        neg = (cnt * weight).sum(axis=-1)
+        np.testing.assert_array_equal(xsum[:, None].astype(np.int64) - 2 * neg,
+                                      oracle.dot_i8(Q, ws).astype(np.int64))
+
+
+def test_quantize_integer_grid_is_exact():
+    x = np.arange(-127, 128, dtype=np.float32)[None, :]
+    Q, sc = oracle.quantize_absmax_i8(x)
+    np.testing.assert_array_equal(Q[0].astype(np.int64), np.arange(-127, 128))
+    assert sc[0] == np.float32(1.0)
+
+
+def test_quantize_half_even_ties():
+    # amax = 254 -> 127/254 = 0.5 exactly; x * 0.5 lands on .5 for odd x
+    x = np.array([[254.0, 5.0, 7.0, -5.0, -7.0, 1.0, 3.0, -254.0]], np.float32)
+    Q, sc = oracle.quantize_absmax_i8(x)
+    assert Q[0].tolist() == [127, 2, 4, -2, -4, 0, 2, -127]
+    assert sc[0] == np.float32(2.0)
+
+
+def test_quantize_matches_exact_rounding_away_from_ties():
+    # q is the integer nearest to x * 127 / amax; the single-precision
+    # evaluation may differ from exact only within a few ulps of a .5 tie.
+    rng = np.random.default_rng(75)
+    X = workloads.normal_f32(75000, (6, 700)) * np.float32(3.0)
+    X[1] *= np.float32(1e-30)                  # tiny magnitudes
+    X[2] *= np.float32(1e30)
+    Q, sc = oracle.quantize_absmax_i8(X)
+    for m in range(X.shape[0]):
+        amax = Fraction(float(np.abs(X[m]).max()))
+        assert f32_bits(sc[m]) == f32_bits(round_to_f32(amax / 127))
+        for k in range(X.shape[1]):
+            t = Fraction(float(X[m, k])) * 127 / amax
+            fl = math.floor(t)
+            frac = t - fl
+            if abs(frac - Fraction(1, 2)) > Fraction(1, 10000):
+                assert int(Q[m, k]) == (fl + 1 if frac > Fraction(1, 2) else fl), (m, k)
+            else:
+                assert int(Q[m, k]) in (fl, fl + 1)
+    # the largest magnitude always maps to +-127; the map is odd
+    for m in range(X.shape[0]):
+        k = int(np.abs(X[m]).argmax())
+        assert abs(int(Q[m, k])) == 127
+    Qn, scn = oracle.quantize_absmax_i8(-X)
+    np.testing.assert_array_equal(Qn, -Q)
+    np.testing.assert_array_equal(scn, sc)
+    del rng
+
+
+def test_quantize_special_rows():
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    X = np.array([[0.0, -0.0, 0.0, 0.0],
+                  [nan, 2.0, -1.0, nan],
+                  [inf, 1.0, -3.0, 0.0]], np.float32)
+    Q, sc = oracle.quantize_absmax_i8(X)
+    assert Q[0].tolist() == [0, 0, 0, 0] and sc[0] == 0.0
+    assert Q[1].tolist() == [0, 127, -64, 0] and sc[1] == np.float32(2.0 / 127.0)
+    assert Q[2].tolist() == [0, 0, 0, 0] and np.isinf(sc[2])
+
+
+def test_alpha_tensor_equals_exact_rational_mean():
+    # page "Extreme Quantization" eq. (8): ||W||_1 / (nm), one scale
+    for shape in ((3, 1000), (16, 576), (7, 33)):
+        W = workloads.normal_f32(76000 + shape[1], shape)
+        exact = sum((Fraction(float(abs(v))) for v in W.ravel()), Fraction(0)) / (shape[0] * shape[1])
+        assert f32_bits(oracle.alpha_tensor(W)) == f32_bits(round_to_f32(exact))
+    W = np.full((5, 40), -0.25, np.float32)
+    assert oracle.alpha_tensor(W) == np.float32(0.25)
+    # per-tensor scale differs from the per-row one when the rows differ
+    W = np.vstack([np.full((1, 8), 1.0, np.float32), np.full((1, 8), 3.0, np.float32)])
+    assert oracle.alpha_tensor(W) == np.float32(2.0)
+    assert oracle.alpha(W).tolist() == [1.0, 3.0]
+
+
+def test_scale_i8_two_roundings():
+    rng = np.random.default_rng(77)
+    D = rng.integers(-128 * 4096, 128 * 4096, size=(6, 20)).astype(np.int32)
+    a = (rng.random(20) * 2).astype(np.float32)
+    xs = (rng.random(6) * 0.1).astype(np.float32)
+    for aa in (a, a[:1]):
+        Y = oracle.scale_i8(D, aa, xs)
+        for m in range(6):
+            for n in range(20):
+                an = aa[n] if aa.shape[0] > 1 else aa[0]
+                z = round_to_f32(Fraction(float(an)) * int(D[m, n]))
+                want = round_to_f32(Fraction(float(z)) * Fraction(float(xs[m])))
+                assert f32_bits(Y[m, n]) == f32_bits(want)
+
+
+def test_scale_bias_residual_roundings():
+    rng = np.random.default_rng(78)
+    D = rng.integers(-5000, 5001, size=(8, 12)).astype(np.int32)
+    a = (rng.random(12) * 2).astype(np.float32)
+    b = workloads.normal_f32(78001, (12,)) * np.float32(100.0)
+    R = workloads.normal_f32(78002, (8, 12)) * np.float32(1e3)
+    R[0, :3] = np.float32(1e-30)
+    for aa in (a, a[:1]):
+        for RR in (None, R):
+            Y = oracle.scale_bias_residual(D, aa, b, RR)
+            for m in range(8):
+                for n in range(12):
+                    an = aa[n] if aa.shape[0] > 1 else aa[0]
+                    z = round_to_f32(Fraction(float(an)) * int(D[m, n]))
+                    z = round_to_f32(Fraction(float(z)) + Fraction(float(b[n])))
+                    if RR is not None:
+                        z = round_to_f32(Fraction(float(z)) + Fraction(float(RR[m, n])))
+                    assert f32_bits(Y[m, n]) == f32_bits(z)
