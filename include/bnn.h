@@ -18,6 +18,8 @@
  *  [P3] "Perfected Concept", "What is binary vs not": first/last layers and
  *       BatchNorm scales stay FP; residual streams stay FP.
  *  [P4] "State of the Art Survey", Bi-Real Net row: FP residual shortcut.
+ *  [P5] "BitNet: 1-bit Transformer": binary weights next to INT8
+ *       activations; eq. (8) one mean-|W| scale for the whole matrix.
  *
  * Conventions (all entry points):
  *  - Data pointers are DEVICE pointers unless the name ends in _host.  The
@@ -71,6 +73,11 @@ typedef enum bnn_status {
 #define BNN_EPI_SCALE_F32    2u /* Y[m,n] = fl32(alpha[n] * D[m,n])  [P5] eq. (1)       */
 #define BNN_EPI_RESIDUAL_F32 4u /* Y[m,n] = fl32(fl32(alpha[n]*D) + R[m,n])  [P4], [P3]  */
 #define BNN_EPI_THRESH_PACK  8u /* Op bit (m,n) = ((float)(dir[n]*D) >= tau[n]) ? 0 : 1  */
+#define BNN_EPI_ALPHA_TENSOR 16u /* with SCALE: one scale alpha[0] for every n  [P5] eq. (8) */
+#define BNN_EPI_BIAS_F32     32u /* with SCALE: + bias[n] after the scale, before R  [P2]  */
+
+/* Longest row of the INT8-activation calls: |D| <= 128 K stays exact in fp32. */
+#define BNN_MAX_K_I8 ((int64_t)1 << 17)
 
 /* Geometry of a binary 3x3 convolution lowered to a GEMM by im2col.
  * Input NHWC [B, H, W, C] fp32, contiguous.  Only R = S = 3, stride 1,
@@ -99,7 +106,28 @@ typedef struct bnn_fused_args {
     const int8_t* dir;                /* THRESH_PACK: int8 [N] in {+1, -1, 0}   */
     uint32_t* Op; int64_t ldOp;       /* THRESH_PACK: packed [M, ldOp],
                                          ldOp >= ceil(N/32); pad bits/words 0   */
+    const float* bias;                /* BIAS_F32: fp32 [N]                     */
 } bnn_fused_args;
+
+/* Arguments of bnn_bwn_i8_linear (binary weights x INT8 activations).  Host
+ * struct; every pointer is device memory.  The activations come in either
+ * (or both) of two forms written by bnn_quantize_act_i8 / bnn_pack_act_i8:
+ *   bit planes  Xb [M, 8, ldXb] + xsum [M]  (read by the bit-plane GEMV);
+ *   int8 rows   Xq [M, ldXq]                (read by the MFMA GEMM). */
+typedef struct bnn_i8_args {
+    const uint32_t* Xb; int64_t ldXb; /* planes: 16-byte aligned, ldXb % 4 == 0,
+                                         ldXb >= ceil(K/32); plane pad bits 0  */
+    const int32_t* xsum;              /* [M] row sums of the int8 values        */
+    const int8_t* Xq; int64_t ldXq;   /* int8 rows: 16-byte aligned, ldXq % 16
+                                         == 0, ldXq >= K                        */
+    const float* xscale;              /* [M] activation scales, or NULL (1.0)   */
+    const uint32_t* Wp; int64_t ldWp; /* packed weights [N, ldWp] (packed layout) */
+    int64_t M, N, K;                  /* 1 <= K <= BNN_MAX_K_I8                 */
+    uint32_t epilogue;                /* DOT_I32 | SCALE_F32 [| ALPHA_TENSOR]   */
+    int32_t* D; int64_t ldD;          /* DOT_I32: int32 [M, ldD], ldD >= N      */
+    const float* alpha;               /* SCALE: fp32 [N] (or [1], ALPHA_TENSOR) */
+    float* Y; int64_t ldY;            /* SCALE: fp32 [M, ldY], ldY >= N         */
+} bnn_i8_args;
 
 /* Number of 32-bit words that carry K packed bits: ceil(K/32); -1 if K < 0. */
 int64_t bnn_packed_words(int64_t K);
@@ -160,9 +188,65 @@ bnn_status bnn_xnor_gemm(const uint32_t* Xp, int64_t ldXp,
  *               layer (its K is N).  Bits n >= N and words ceil(N/32)..ldOp-1
  *               are written as 0.  tau/dir come from
  *               bnn_fold_bn_thresholds_host.
- * Errors: RESIDUAL without SCALE, no flag, or unknown flag bits ->
- * BNN_ERR_UNSUPPORTED. */
+ *  ALPHA_TENSOR with SCALE_F32: alpha[0] scales every column, the single
+ *               scale ||W||_1 / (nm) of [P5] eq. (8) (bnn_weight_scale_tensor)
+ *  BIAS_F32     with SCALE_F32: Y = fl32(fl32(alpha * D) + bias[n]), then
+ *               the residual (if any) is added: the "y = Wx + b" of [P2]
+ *               section "The cost of a neural network step"
+ * Errors: RESIDUAL, BIAS or ALPHA_TENSOR without SCALE, no flag, or unknown
+ * flag bits -> BNN_ERR_UNSUPPORTED. */
 bnn_status bnn_linear_fused(const bnn_fused_args* args, bnn_stream_t stream);
+
+/* One scale for the whole weight matrix, [P5] eq. (8):
+ *     alpha[0] = fl32( (sum_{n,k} |W[n,k]|) / (N*K) )
+ *  the sums in fp64 (per row, then over rows in a fixed order; the same on
+ *  every run), one rounding to fp32 at the end.
+ *  W fp32 [N, ldW] (ldW >= K, 4-byte aligned); work: device scratch of N
+ *  doubles owned by the caller (8-byte aligned); alpha: device fp32 [1].
+ *  N >= 1.  Errors: NULL -> BNN_ERR_NULL; sizes -> BNN_ERR_SHAPE / _LD. */
+bnn_status bnn_weight_scale_tensor(const float* W, int64_t N, int64_t K, int64_t ldW,
+                                   double* work, float* alpha, bnn_stream_t stream);
+
+/* Quantize fp32 activations to INT8, one scale per row, [P5] "BitNet"
+ * item 2 (activations at INT8; the quantizer is not given there, this is
+ * symmetric absmax):
+ *     amax = max_k |X[m,k]|  (NaN skipped);  inv = fl32(127 / amax), 0 if amax == 0
+ *     q[m,k] = rint(fl32(X[m,k] * inv)) clamped to [-127, 127] (ties to even;
+ *              a NaN product gives 0);       xscale[m] = fl32(amax / 127)
+ *  so X ~= xscale * q.  Outputs (any of Xq, Xb may be NULL, not both):
+ *  Xq    int8 [M, ldXq] (ldXq >= K);
+ *  Xb    bit planes [M, 8, ldXb]: plane b of row m starts at word
+ *        (m*8 + b)*ldXb and holds bit b of each two's-complement byte q[m,k]
+ *        at word k/32, bit k%32; pad bits and pad words are written 0;
+ *        16-byte aligned, ldXb % 4 == 0, ldXb >= ceil(K/32);
+ *  xsum  int32 [M] = sum_k q[m,k] (required with Xb, else ignored);
+ *  xscale fp32 [M] (required).
+ *  X fp32 [M, ldX], ldX >= K.  1 <= K <= BNN_MAX_K_I8. */
+bnn_status bnn_quantize_act_i8(const float* X, int64_t M, int64_t K, int64_t ldX,
+                               int8_t* Xq, int64_t ldXq,
+                               uint32_t* Xb, int64_t ldXb, int32_t* xsum,
+                               float* xscale, bnn_stream_t stream);
+
+/* Bit planes (and row sums) of int8 activations that are already quantized;
+ * the same plane layout and xsum as bnn_quantize_act_i8.
+ *  Xq int8 [M, ldXq] (ldXq >= K); Xb, ldXb, xsum as above (all required). */
+bnn_status bnn_pack_act_i8(const int8_t* Xq, int64_t M, int64_t K, int64_t ldXq,
+                           uint32_t* Xb, int64_t ldXb, int32_t* xsum, bnn_stream_t stream);
+
+/* Binary weights x INT8 activations, [P5] eq. (1)-(2) (each +1/-1 weight
+ * adds or subtracts its activation) with the INT8 activations of [P5]
+ * "BitNet":
+ *     D[m,n] = sum_k q[m,k] * s(n,k)     (exact int32; s = +1 for bit 0)
+ *     Y[m,n] = fl32( fl32(alpha_n * (float)D) * xscale[m] )   (xscale given)
+ *            = fl32( alpha_n * (float)D )                      (xscale NULL)
+ *  alpha_n = alpha[n], or alpha[0] with BNN_EPI_ALPHA_TENSOR.
+ *  Path: M <= 2 with Xb and xsum given, and ceil(ceil(K/32)/4) <= 256/M
+ *  (K <= 32768 for one row, 16384 for two): the bit-plane streaming
+ *  GEMV (the batch-1 decode case of [P2] "Bandwidth math"); otherwise the
+ *  int8 MFMA GEMM, which needs Xq.  Flags other than DOT_I32, SCALE_F32 and
+ *  ALPHA_TENSOR -> BNN_ERR_UNSUPPORTED; neither usable activation form ->
+ *  BNN_ERR_NULL. */
+bnn_status bnn_bwn_i8_linear(const bnn_i8_args* args, bnn_stream_t stream);
 
 /* Fold inference BatchNorm of z = alpha[n] * D followed by sign into the
  * (tau, dir) pair consumed by BNN_EPI_THRESH_PACK.  [P1] BatchNorm around

@@ -130,6 +130,11 @@ def _fused(**kw):
     (dict(epilogue=6, Y=A16, ldY=40, alpha=A16), ERR_NULL),                       # residual without R
     (dict(epilogue=6, Y=A16, ldY=40, alpha=A16, R=A16 + 64, ldR=40), ERR_UNSUPPORTED),  # R, Y overlap
     (dict(M=(1 << 31)), ERR_SHAPE),
+    (dict(epilogue=32), ERR_UNSUPPORTED),                                          # bias without scale
+    (dict(epilogue=64), ERR_UNSUPPORTED),                                          # unknown flag
+    (dict(epilogue=34, Y=A16, ldY=40, alpha=A16), ERR_NULL),                       # bias pointer missing
+    (dict(epilogue=34, Y=A16, ldY=40, alpha=A16, bias=A2), ERR_ALIGN),
+    (dict(epilogue=18, Y=A16, ldY=40, alpha=A2), ERR_ALIGN),                       # per-tensor alpha, misaligned
 ])
 def test_linear_fused_validation(L, kw, want):
     a = _fused(**kw)
@@ -143,6 +148,70 @@ def test_dense_support_validation(L):
     assert L.bnn_dense_f32_sign_pack(A16, 784, A16, 784, 4, 64, 784, A16, 1, None) == ERR_LD
     assert L.bnn_dense_binact_f32(A4, 128, A16, 4096, 4, 10, 4096, A16, 10, None) == ERR_ALIGN
     assert L.bnn_dense_binact_f32(A16, 128, A16, 4096, 4, 10, 4096, A16, 9, None) == ERR_LD
+
+
+def _i8(**kw):
+    import xnor_popcount_gemm_amd as bnn
+    a = bnn._I8Args()
+    base = dict(Xb=A16, ldXb=4, xsum=A16, Wp=A16, ldWp=4, M=1, N=40, K=100,
+                epilogue=bnn.EPI_DOT_I32, D=A16, ldD=40)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), OK),                                                   # valid: validation passes, M=0 below
+    (dict(Xb=0), ERR_NULL),                                         # no activation form
+    (dict(Xb=0, Xq=A16, ldXq=112), OK),                             # int8 rows (GEMM path)
+    (dict(Xb=0, Xq=A16, ldXq=100), ERR_ALIGN),                      # ldXq % 16
+    (dict(Xb=0, Xq=A16 + 4, ldXq=112), ERR_ALIGN),
+    (dict(Xb=0, Xq=A16, ldXq=96), ERR_LD),
+    (dict(M=3), ERR_NULL),                                          # planes serve M <= 2 only
+    (dict(K=(1 << 17) + 1), ERR_SHAPE),
+    (dict(K=0), ERR_SHAPE),
+    (dict(ldXb=3), ERR_LD),
+    (dict(Xb=A4), ERR_ALIGN),
+    (dict(xsum=A2), ERR_ALIGN),
+    (dict(epilogue=4), ERR_UNSUPPORTED),                            # residual is not offered here
+    (dict(epilogue=16), ERR_UNSUPPORTED),                           # per-tensor alpha without scale
+    (dict(epilogue=2), ERR_NULL),                                   # scale without Y / alpha
+    (dict(epilogue=18, Y=A16, ldY=40, alpha=A16), OK),
+    (dict(epilogue=2, Y=A16, ldY=39, alpha=A16), ERR_LD),
+    (dict(xscale=A2), ERR_ALIGN),
+])
+def test_bwn_i8_validation(L, kw, want):
+    a = _i8(**kw)
+    if want == OK:
+        a.M = 0                      # nothing is launched on this host
+    assert L.bnn_bwn_i8_linear(ctypes.byref(a), None) == want
+    assert L.bnn_bwn_i8_linear(None, None) == ERR_NULL
+
+
+def test_i8_activation_writers_validation(L):
+    # quantize: X, M, K, ldX, Xq, ldXq, Xb, ldXb, xsum, xscale
+    q = L.bnn_quantize_act_i8
+    assert q(A16, 0, 100, 100, A16, 112, A16, 4, A16, A16, None) == OK
+    assert q(0, 1, 100, 100, A16, 112, A16, 4, A16, A16, None) == ERR_NULL
+    assert q(A16, 1, 100, 100, 0, 0, 0, 0, 0, A16, None) == ERR_NULL       # no output form
+    assert q(A16, 1, 100, 100, A16, 112, A16, 4, A16, 0, None) == ERR_NULL  # xscale required
+    assert q(A16, 1, 100, 100, 0, 0, A16, 4, 0, A16, None) == ERR_NULL      # planes need xsum
+    assert q(A16, 1, 100, 99, A16, 112, 0, 0, 0, A16, None) == ERR_LD
+    assert q(A16, 1, 100, 100, A16, 99, 0, 0, 0, A16, None) == ERR_LD
+    assert q(A16, 1, 100, 100, 0, 0, A16, 6, A16, A16, None) == ERR_ALIGN
+    assert q(A16, 1, (1 << 17) + 1, 1 << 18, A16, 1 << 18, 0, 0, 0, A16, None) == ERR_SHAPE
+    p = L.bnn_pack_act_i8                    # Xq, M, K, ldXq, Xb, ldXb, xsum
+    assert p(A16, 0, 100, 100, A16, 4, A16, None) == OK
+    assert p(A16, 1, 100, 100, 0, 4, A16, None) == ERR_NULL
+    assert p(A16, 1, 100, 100, A16, 4, 0, None) == ERR_NULL
+    assert p(A16, 1, 100, 99, A16, 4, A16, None) == ERR_LD
+    assert p(A16, 1, 100, 100, A16 + 4, 4, A16, None) == ERR_ALIGN
+    s = L.bnn_weight_scale_tensor            # W, N, K, ldW, work, alpha
+    assert s(A16, 0, 100, 100, A16, A16, None) == ERR_SHAPE
+    assert s(A16, 4, 100, 100, 0, A16, None) == ERR_NULL
+    assert s(A16, 4, 100, 99, A16, A16, None) == ERR_LD
+    assert s(A16, 4, 100, 100, A4, A16, None) == ERR_ALIGN
 
 
 def test_empty_calls_launch_nothing(L):

@@ -24,7 +24,8 @@ __all__ = [
     "BnnError", "lib", "packed_words", "padded_ld", "pack_weights", "pack_activations",
     "xnor_gemm", "linear_fused", "fold_bn_thresholds", "dense_f32_sign_pack",
     "dense_binact_f32", "EPI_DOT_I32", "EPI_SCALE_F32", "EPI_RESIDUAL_F32",
-    "EPI_THRESH_PACK", "LIB_PATH",
+    "EPI_THRESH_PACK", "EPI_ALPHA_TENSOR", "EPI_BIAS_F32", "LIB_PATH",
+    "weight_scale_tensor", "quantize_act_i8", "pack_act_i8", "bwn_i8_linear", "MAX_K_I8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbnn.so")
@@ -33,6 +34,9 @@ EPI_DOT_I32 = 1
 EPI_SCALE_F32 = 2
 EPI_RESIDUAL_F32 = 4
 EPI_THRESH_PACK = 8
+EPI_ALPHA_TENSOR = 16
+EPI_BIAS_F32 = 32
+MAX_K_I8 = 1 << 17
 
 _STATUS = {
     0: "BNN_OK", 1: "BNN_ERR_NULL", 2: "BNN_ERR_SHAPE", 3: "BNN_ERR_LD",
@@ -62,6 +66,22 @@ class _FusedArgs(ctypes.Structure):
         ("R", ctypes.c_void_p), ("ldR", ctypes.c_int64),
         ("tau", ctypes.c_void_p), ("dir", ctypes.c_void_p),
         ("Op", ctypes.c_void_p), ("ldOp", ctypes.c_int64),
+        ("bias", ctypes.c_void_p),
+    ]
+
+
+class _I8Args(ctypes.Structure):
+    _fields_ = [
+        ("Xb", ctypes.c_void_p), ("ldXb", ctypes.c_int64),
+        ("xsum", ctypes.c_void_p),
+        ("Xq", ctypes.c_void_p), ("ldXq", ctypes.c_int64),
+        ("xscale", ctypes.c_void_p),
+        ("Wp", ctypes.c_void_p), ("ldWp", ctypes.c_int64),
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("epilogue", ctypes.c_uint32),
+        ("D", ctypes.c_void_p), ("ldD", ctypes.c_int64),
+        ("alpha", ctypes.c_void_p),
+        ("Y", ctypes.c_void_p), ("ldY", ctypes.c_int64),
     ]
 
 
@@ -91,6 +111,10 @@ def lib() -> ctypes.CDLL:
             "bnn_fold_bn_thresholds_host": [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _vp, _vp],
             "bnn_dense_f32_sign_pack": [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp],
             "bnn_dense_binact_f32": [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp],
+            "bnn_weight_scale_tensor": [_vp, _i64, _i64, _i64, _vp, _vp, _vp],
+            "bnn_quantize_act_i8": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp],
+            "bnn_pack_act_i8": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
+            "bnn_bwn_i8_linear": [ctypes.POINTER(_I8Args), _vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -209,7 +233,7 @@ def xnor_gemm(Xp: torch.Tensor, Wp: torch.Tensor, K: int, *, alpha: torch.Tensor
 
 def linear_fused(Xp: torch.Tensor, Wp: torch.Tensor, K: int, epilogue: int, *,
                  alpha=None, R=None, tau=None, dir=None, D=None, Y=None, Op=None,
-                 M: int | None = None):
+                 bias=None, M: int | None = None):
     """XNOR-popcount GEMM with a fused epilogue (OR of EPI_* flags).
 
     Returns a dict with the outputs the flags ask for: ``D`` (int32 [M, N]),
@@ -245,6 +269,8 @@ def linear_fused(Xp: torch.Tensor, Wp: torch.Tensor, K: int, epilogue: int, *,
         a.dir = dir.data_ptr()
     if Op is not None:
         a.Op, a.ldOp = Op.data_ptr(), _ld(Op)
+    if bias is not None:
+        a.bias = bias.data_ptr()
     _check(lib().bnn_linear_fused(ctypes.byref(a), _stream(dev)), "bnn_linear_fused")
     return {"D": D, "Y": Y, "Op": Op}
 
@@ -284,3 +310,94 @@ def dense_binact_f32(Xp: torch.Tensor, W: torch.Tensor, K: int, *, out: torch.Te
     _check(lib().bnn_dense_binact_f32(_ptr(Xp), _ld(Xp), _ptr(W), _ld(W), M, N, int(K),
                                       _ptr(Y), _ld(Y), _stream(Xp.device)), "bnn_dense_binact_f32")
     return Y
+
+
+def weight_scale_tensor(W: torch.Tensor, *, out: torch.Tensor | None = None) -> torch.Tensor:
+    """One scale for the whole matrix, ||W||_1 / (N K) (fp32 [1])."""
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    work = torch.empty(N, dtype=torch.float64, device=W.device)
+    a = torch.empty(1, dtype=torch.float32, device=W.device) if out is None else out
+    _check(lib().bnn_weight_scale_tensor(_ptr(W), N, K, _ld(W), _ptr(work), _ptr(a),
+                                         _stream(W.device)), "bnn_weight_scale_tensor")
+    return a
+
+
+def i8_ld(K: int) -> int:
+    """Row stride of an int8 activation matrix: K rounded up to 16 bytes."""
+    return (int(K) + 15) // 16 * 16
+
+
+def _planes_ld(Xb: torch.Tensor) -> int:
+    if Xb.dim() != 3 or Xb.shape[1] != 8 or Xb.stride(2) != 1 or Xb.stride(0) != 8 * Xb.stride(1):
+        raise ValueError("bit planes must be an int32 tensor [M, 8, ld] with row stride 8*ld")
+    return Xb.stride(1)
+
+
+def quantize_act_i8(X: torch.Tensor, *, want_int8: bool = True, want_planes: bool = True):
+    """Absmax INT8 quantization per row of fp32 X [M, K].
+
+    Returns a dict: ``Xq`` int8 [M, K] (row stride a multiple of 16) or None,
+    ``Xb`` int32 bit planes [M, 8, ld] and ``xsum`` int32 [M] (or None), and
+    ``xscale`` fp32 [M] (X ~= xscale * Xq)."""
+    _dev(X, torch.float32, "X")
+    M, K = X.shape
+    dev = X.device
+    Xq = torch.empty((M, i8_ld(K)), dtype=torch.int8, device=dev)[:, :K] if want_int8 else None
+    Xb = torch.empty((M, 8, padded_ld(K)), dtype=torch.int32, device=dev) if want_planes else None
+    xsum = torch.empty(M, dtype=torch.int32, device=dev) if want_planes else None
+    xscale = torch.empty(M, dtype=torch.float32, device=dev)
+    _check(lib().bnn_quantize_act_i8(_ptr(X), M, K, _ld(X),
+                                     _ptr(Xq), Xq.stride(0) if Xq is not None else 0,
+                                     _ptr(Xb), _planes_ld(Xb) if Xb is not None else 0, _ptr(xsum),
+                                     _ptr(xscale), _stream(dev)), "bnn_quantize_act_i8")
+    return {"Xq": Xq, "Xb": Xb, "xsum": xsum, "xscale": xscale}
+
+
+def pack_act_i8(Xq: torch.Tensor):
+    """Bit planes [M, 8, ld] and row sums [M] of int8 activations [M, K]."""
+    _dev(Xq, torch.int8, "Xq")
+    M, K = Xq.shape
+    Xb = torch.empty((M, 8, padded_ld(K)), dtype=torch.int32, device=Xq.device)
+    xsum = torch.empty(M, dtype=torch.int32, device=Xq.device)
+    _check(lib().bnn_pack_act_i8(_ptr(Xq), M, K, _ld(Xq), _ptr(Xb), _planes_ld(Xb), _ptr(xsum),
+                                 _stream(Xq.device)), "bnn_pack_act_i8")
+    return Xb, xsum
+
+
+def bwn_i8_linear(Wp: torch.Tensor, K: int, epilogue: int, *, Xb=None, xsum=None, Xq=None,
+                  xscale=None, alpha=None, D=None, Y=None, M: int | None = None):
+    """Binary weights x INT8 activations: D = sum q * s (int32) and/or
+    Y = alpha * D (* xscale) (fp32), from bit planes (GEMV, M <= 2) or int8
+    rows (MFMA GEMM).  Returns a dict with ``D`` and ``Y``."""
+    _dev(Wp, torch.int32, "Wp")
+    if M is None:
+        M = (Xb if Xb is not None else Xq).shape[0]
+    N = Wp.shape[0]
+    dev = Wp.device
+    if epilogue & EPI_DOT_I32 and D is None:
+        D = torch.empty((M, N), dtype=torch.int32, device=dev)
+    if epilogue & EPI_SCALE_F32 and Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    a = _I8Args()
+    if Xb is not None:
+        _dev(Xb, torch.int32, "Xb")
+        a.Xb, a.ldXb = Xb.data_ptr(), _planes_ld(Xb)
+    if xsum is not None:
+        a.xsum = xsum.data_ptr()
+    if Xq is not None:
+        _dev(Xq, torch.int8, "Xq")
+        a.Xq, a.ldXq = Xq.data_ptr(), _ld(Xq)
+    if xscale is not None:
+        a.xscale = xscale.data_ptr()
+    a.Wp, a.ldWp = Wp.data_ptr(), _ld(Wp)
+    a.M, a.N, a.K = M, N, int(K)
+    a.epilogue = int(epilogue)
+    if D is not None:
+        a.D, a.ldD = D.data_ptr(), _ld(D)
+    if alpha is not None:
+        a.alpha = alpha.data_ptr()
+    if Y is not None:
+        a.Y, a.ldY = Y.data_ptr(), _ld(Y)
+    _check(lib().bnn_bwn_i8_linear(ctypes.byref(a), _stream(dev)), "bnn_bwn_i8_linear")
+    return {"D": D, "Y": Y}

@@ -46,9 +46,16 @@ bnn_status validate_fused(const bnn_fused_args* a) {
     // the GEMM grid (256-row x 16-column tiles) must fit one launch dimension
     if (((a->M + 255) / 256) * ((a->N + 15) / 16) > ((int64_t)1 << 31) - 1) return BNN_ERR_SHAPE;
     const uint32_t f = a->epilogue;
-    const uint32_t known = BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32 | BNN_EPI_RESIDUAL_F32 | BNN_EPI_THRESH_PACK;
-    if (f == 0 || (f & ~known) != 0) return BNN_ERR_UNSUPPORTED;
-    if ((f & BNN_EPI_RESIDUAL_F32) && !(f & BNN_EPI_SCALE_F32)) return BNN_ERR_UNSUPPORTED;
+    const uint32_t known = BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32 | BNN_EPI_RESIDUAL_F32 | BNN_EPI_THRESH_PACK |
+                           BNN_EPI_ALPHA_TENSOR | BNN_EPI_BIAS_F32;
+    if ((f & ~known) != 0) return BNN_ERR_UNSUPPORTED;
+    if (!(f & (BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32 | BNN_EPI_THRESH_PACK))) return BNN_ERR_UNSUPPORTED;
+    if ((f & (BNN_EPI_RESIDUAL_F32 | BNN_EPI_ALPHA_TENSOR | BNN_EPI_BIAS_F32)) && !(f & BNN_EPI_SCALE_F32))
+        return BNN_ERR_UNSUPPORTED;
+    if (f & BNN_EPI_BIAS_F32) {
+        if (!a->bias) return BNN_ERR_NULL;
+        if (misaligned4(a->bias)) return BNN_ERR_ALIGN;
+    }
     if ((st = check_packed(a->Xp, a->K, a->ldXp)) != BNN_OK) return st;
     if ((st = check_packed(a->Wp, a->K, a->ldWp)) != BNN_OK) return st;
     if (f & BNN_EPI_DOT_I32) {
@@ -91,9 +98,74 @@ bnn_status run_fused(const bnn_fused_args* a, hipStream_t s) {
     e.R = a->R; e.ldR = a->ldR;
     e.tau = a->tau; e.dir = a->dir;
     e.Op = a->Op; e.ldOp = a->ldOp;
+    e.bias = a->bias;
     if (bnn::gemv_eligible(a->M, a->K, e.flags))
         return from_hip(bnn::launch_xnor_gemv(a->Xp, a->ldXp, a->Wp, a->ldWp, a->M, a->N, a->K, e, s));
     return from_hip(bnn::launch_xnor_gemm(a->Xp, a->ldXp, a->Wp, a->ldWp, a->M, a->N, a->K, e, s));
+}
+
+bnn_status check_i8_rows(const int8_t* p, int64_t K, int64_t ld) {
+    if (ld < K) return BNN_ERR_LD;
+    if (misaligned16(p) || (ld % 16) != 0) return BNN_ERR_ALIGN;
+    return BNN_OK;
+}
+
+bnn_status check_k_i8(int64_t K) {
+    return (K < 1 || K > BNN_MAX_K_I8) ? BNN_ERR_SHAPE : BNN_OK;
+}
+
+// Which kernel serves a bnn_i8_args call: 1 = bit-plane GEMV, 2 = MFMA GEMM.
+int i8_path(const bnn_i8_args* a) {
+    if (a->Xb && a->xsum && (a->M == 0 || bnn::i8_gemv_eligible(a->M, a->K))) return 1;
+    if (a->Xq) return 2;
+    return 0;
+}
+
+bnn_status validate_i8(const bnn_i8_args* a) {
+    if (!a) return BNN_ERR_NULL;
+    bnn_status st;
+    if ((st = check_rows(a->M)) != BNN_OK) return st;
+    if ((st = check_rows(a->N)) != BNN_OK) return st;
+    if ((st = check_k_i8(a->K)) != BNN_OK) return st;
+    if (((a->M + 127) / 128) * ((a->N + 127) / 128) > ((int64_t)1 << 31) - 1) return BNN_ERR_SHAPE;
+    const uint32_t f = a->epilogue;
+    const uint32_t known = BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32 | BNN_EPI_ALPHA_TENSOR;
+    if ((f & ~known) != 0 || !(f & (BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32))) return BNN_ERR_UNSUPPORTED;
+    if ((f & BNN_EPI_ALPHA_TENSOR) && !(f & BNN_EPI_SCALE_F32)) return BNN_ERR_UNSUPPORTED;
+    if ((st = check_packed(a->Wp, a->K, a->ldWp)) != BNN_OK) return st;
+    const int path = i8_path(a);
+    if (path == 0) return BNN_ERR_NULL;
+    if (path == 1) {
+        if ((st = check_packed(a->Xb, a->K, a->ldXb)) != BNN_OK) return st;
+        if (misaligned4(a->xsum)) return BNN_ERR_ALIGN;
+    } else {
+        if ((st = check_i8_rows(a->Xq, a->K, a->ldXq)) != BNN_OK) return st;
+    }
+    if (a->xscale && misaligned4(a->xscale)) return BNN_ERR_ALIGN;
+    if (f & BNN_EPI_DOT_I32) {
+        if (!a->D) return BNN_ERR_NULL;
+        if (a->ldD < a->N) return BNN_ERR_LD;
+        if (misaligned4(a->D)) return BNN_ERR_ALIGN;
+    }
+    if (f & BNN_EPI_SCALE_F32) {
+        if (!a->Y || !a->alpha) return BNN_ERR_NULL;
+        if (a->ldY < a->N) return BNN_ERR_LD;
+        if (misaligned4(a->Y) || misaligned4(a->alpha)) return BNN_ERR_ALIGN;
+    }
+    return BNN_OK;
+}
+
+// Shared checks of the two INT8 activation writers.
+bnn_status check_act_i8_out(int64_t M, int64_t K, uint32_t* Xb, int64_t ldXb, int32_t* xsum) {
+    bnn_status st;
+    if ((st = check_rows(M)) != BNN_OK) return st;
+    if ((st = check_k_i8(K)) != BNN_OK) return st;
+    if (Xb) {
+        if ((st = check_packed(Xb, K, ldXb)) != BNN_OK) return st;
+        if (!xsum) return BNN_ERR_NULL;
+        if (misaligned4(xsum)) return BNN_ERR_ALIGN;
+    }
+    return BNN_OK;
 }
 
 }  // namespace
@@ -177,6 +249,67 @@ bnn_status bnn_linear_fused(const bnn_fused_args* args, bnn_stream_t stream)
     const bnn_status st = validate_fused(args);
     if (st != BNN_OK) return st;
     return run_fused(args, as_stream(stream));
+}
+
+bnn_status bnn_weight_scale_tensor(const float* W, int64_t N, int64_t K, int64_t ldW,
+                                   double* work, float* alpha, bnn_stream_t stream)
+{
+    bnn_status st;
+    if ((st = check_rows(N)) != BNN_OK) return st;
+    if ((st = check_k(K)) != BNN_OK) return st;
+    if (N < 1) return BNN_ERR_SHAPE;
+    if (!W || !work || !alpha) return BNN_ERR_NULL;
+    if (ldW < K) return BNN_ERR_LD;
+    if (misaligned4(W) || misaligned4(alpha) || (reinterpret_cast<uintptr_t>(work) & 7u) != 0)
+        return BNN_ERR_ALIGN;
+    return from_hip(bnn::launch_alpha_tensor(W, N, K, ldW, work, alpha, as_stream(stream)));
+}
+
+bnn_status bnn_quantize_act_i8(const float* X, int64_t M, int64_t K, int64_t ldX,
+                               int8_t* Xq, int64_t ldXq,
+                               uint32_t* Xb, int64_t ldXb, int32_t* xsum,
+                               float* xscale, bnn_stream_t stream)
+{
+    bnn_status st;
+    if ((st = check_act_i8_out(M, K, Xb, ldXb, xsum)) != BNN_OK) return st;
+    if (!X || !xscale || (!Xq && !Xb)) return BNN_ERR_NULL;
+    if (ldX < K) return BNN_ERR_LD;
+    if (Xq && ldXq < K) return BNN_ERR_LD;
+    if (misaligned4(X) || misaligned4(xscale)) return BNN_ERR_ALIGN;
+    if (M == 0) return BNN_OK;
+    return from_hip(bnn::launch_act_i8(X, ldX, nullptr, 0, M, K, Xq, ldXq, Xb, ldXb, xsum, xscale,
+                                       as_stream(stream)));
+}
+
+bnn_status bnn_pack_act_i8(const int8_t* Xq, int64_t M, int64_t K, int64_t ldXq,
+                           uint32_t* Xb, int64_t ldXb, int32_t* xsum, bnn_stream_t stream)
+{
+    bnn_status st;
+    if (!Xq || !Xb) return BNN_ERR_NULL;
+    if ((st = check_act_i8_out(M, K, Xb, ldXb, xsum)) != BNN_OK) return st;
+    if (ldXq < K) return BNN_ERR_LD;
+    if (M == 0) return BNN_OK;
+    return from_hip(bnn::launch_act_i8(nullptr, 0, Xq, ldXq, M, K, nullptr, 0, Xb, ldXb, xsum, nullptr,
+                                       as_stream(stream)));
+}
+
+bnn_status bnn_bwn_i8_linear(const bnn_i8_args* args, bnn_stream_t stream)
+{
+    const bnn_status st = validate_i8(args);
+    if (st != BNN_OK) return st;
+    if (args->M == 0 || args->N == 0) return BNN_OK;
+    bnn::EpilogueI8 e;
+    e.flags = args->epilogue;
+    e.D = args->D; e.ldD = args->ldD;
+    e.alpha = args->alpha;
+    e.xscale = args->xscale;
+    e.Y = args->Y; e.ldY = args->ldY;
+    hipStream_t s = as_stream(stream);
+    if (i8_path(args) == 1)
+        return from_hip(bnn::launch_bwn_i8_gemv(args->Xb, args->ldXb, args->xsum, args->Wp, args->ldWp,
+                                                args->M, args->N, args->K, e, s));
+    return from_hip(bnn::launch_bwn_i8_gemm(args->Xq, args->ldXq, args->Wp, args->ldWp,
+                                            args->M, args->N, args->K, e, s));
 }
 
 bnn_status bnn_fold_bn_thresholds_host(const float* gamma, const float* beta,

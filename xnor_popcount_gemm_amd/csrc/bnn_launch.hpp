@@ -12,17 +12,32 @@ namespace bnn {
 struct Epilogue {
     uint32_t flags;          // BNN_EPI_* bits
     int32_t* D; int64_t ldD;
-    const float* alpha;
+    const float* alpha;      // [N], or alpha[0] for all n with EPI_ALPHA_TENSOR
     float* Y; int64_t ldY;
     const float* R; int64_t ldR;
     const float* tau; const int8_t* dir;
     uint32_t* Op; int64_t ldOp;
+    const float* bias;       // [N] with EPI_BIAS
 };
 
-enum : uint32_t { EPI_DOT = 1u, EPI_SCALE = 2u, EPI_RESIDUAL = 4u, EPI_THRESH = 8u };
+enum : uint32_t { EPI_DOT = 1u, EPI_SCALE = 2u, EPI_RESIDUAL = 4u, EPI_THRESH = 8u,
+                  EPI_ALPHA_TENSOR = 16u, EPI_BIAS = 32u };
+
+// Epilogue of binary weights x INT8 activations.
+struct EpilogueI8 {
+    uint32_t flags;          // EPI_DOT, EPI_SCALE, EPI_ALPHA_TENSOR
+    int32_t* D; int64_t ldD;
+    const float* alpha;      // [N], or alpha[0] with EPI_ALPHA_TENSOR
+    const float* xscale;     // [M] or nullptr
+    float* Y; int64_t ldY;
+};
 
 hipError_t launch_pack_dense(const float* X, int64_t rows, int64_t K, int64_t ldX,
                              uint32_t* P, int64_t ldP, float* alpha, hipStream_t s);
+
+// alpha[0] = fl32(sum |W| / (N K)), fp64 sums; work holds N doubles.
+hipError_t launch_alpha_tensor(const float* W, int64_t N, int64_t K, int64_t ldW,
+                               double* work, float* alpha, hipStream_t s);
 
 hipError_t launch_pack_im2col3x3(const float* X, int64_t B, int64_t H, int64_t W, int64_t C,
                                  uint32_t* P, int64_t ldP, hipStream_t s);
@@ -36,6 +51,24 @@ bool gemv_eligible(int64_t M, int64_t K, uint32_t flags);
 
 hipError_t launch_xnor_gemv(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
                             int64_t M, int64_t N, int64_t K, const Epilogue& e, hipStream_t s);
+
+// Per-row absmax INT8 quantization (X != nullptr) or plain re-layout of int8
+// rows (Xq_in != nullptr): writes any of Q (int8), bit planes + row sums, and
+// the row scale.
+hipError_t launch_act_i8(const float* X, int64_t ldX, const int8_t* Xq_in, int64_t ldXq_in,
+                         int64_t M, int64_t K,
+                         int8_t* Q, int64_t ldQ, uint32_t* Xb, int64_t ldXb, int32_t* xsum,
+                         float* xscale, hipStream_t s);
+
+// True when the bit-plane GEMV serves binary weights x INT8 activations.
+bool i8_gemv_eligible(int64_t M, int64_t K);
+
+hipError_t launch_bwn_i8_gemv(const uint32_t* Xb, int64_t ldXb, const int32_t* xsum,
+                              const uint32_t* Wp, int64_t ldW,
+                              int64_t M, int64_t N, int64_t K, const EpilogueI8& e, hipStream_t s);
+
+hipError_t launch_bwn_i8_gemm(const int8_t* Xq, int64_t ldXq, const uint32_t* Wp, int64_t ldW,
+                              int64_t M, int64_t N, int64_t K, const EpilogueI8& e, hipStream_t s);
 
 hipError_t launch_dense_f32_sign_pack(const float* X, int64_t ldX, const float* W, int64_t ldW,
                                       int64_t M, int64_t N, int64_t K,

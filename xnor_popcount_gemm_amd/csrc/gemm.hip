@@ -37,7 +37,6 @@
 namespace bnn {
 namespace {
 
-constexpr int kThreads = 256;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -166,14 +165,18 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
         // The residual and alpha pieces of all passes are requested before
         // any is used, so their latencies overlap instead of adding up.
         f32x4 rv[G4];
-        float4 av[G4];
+        float4 av[G4], bv[G4];
 #pragma unroll
         for (int q = 0; q < G4; ++q) {
             const int idx = q * 64 + lane;
             const int r = idx / G4, cg = idx - (idx / G4) * G4;
             const int m = min(wrow0 + r, M - 1);
             const int n = n0 + c0 + 4 * cg;
-            if (e.flags & EPI_SCALE) av[q] = *reinterpret_cast<const float4*>(e.alpha + n);
+            if (e.flags & EPI_SCALE) {
+                if (e.flags & EPI_ALPHA_TENSOR) { const float a = e.alpha[0]; av[q] = make_float4(a, a, a, a); }
+                else av[q] = *reinterpret_cast<const float4*>(e.alpha + n);
+            }
+            if (e.flags & EPI_BIAS) bv[q] = *reinterpret_cast<const float4*>(e.bias + n);
             if (e.flags & EPI_RESIDUAL)
                 rv[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(e.R + (int64_t)m * e.ldR + n));
         }
@@ -193,6 +196,10 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
                 if (e.flags & EPI_SCALE) {
                     const float4 a = av[q];
                     f32x4 y = {a.x * (float)d[0], a.y * (float)d[1], a.z * (float)d[2], a.w * (float)d[3]};
+                    if (e.flags & EPI_BIAS) {
+                        const float4 b = bv[q];
+                        y = y + (f32x4){b.x, b.y, b.z, b.w};
+                    }
                     if (e.flags & EPI_RESIDUAL) y = y + rv[q];
                     __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(e.Y + (int64_t)m * e.ldY + n));
                 }
@@ -232,7 +239,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
     const bool full = (ncols == TN);
     if (EPI_LDS && full && !(e.flags & EPI_THRESH) &&
         (!(e.flags & EPI_DOT) || (aligned16(e.D) && e.ldD % 4 == 0)) &&
-        (!(e.flags & EPI_SCALE) || (aligned16(e.Y) && e.ldY % 4 == 0 && aligned16(e.alpha))) &&
+        (!(e.flags & EPI_SCALE) || (aligned16(e.Y) && e.ldY % 4 == 0 &&
+                                    ((e.flags & EPI_ALPHA_TENSOR) || aligned16(e.alpha)))) &&
+        (!(e.flags & EPI_BIAS) || aligned16(e.bias)) &&
         (!(e.flags & EPI_RESIDUAL) || (aligned16(e.R) && e.ldR % 4 == 0))) {
         epilogue_lds<TN>(acc, lds_epi + wave * kLdsWords, wrow0, M, n0, K, e);
         return;
@@ -246,7 +255,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
     int32_t* drow = e.D + (int64_t)m * e.ldD + n0;
     float* yrow = e.Y + (int64_t)m * e.ldY + n0;
     const float* rrow = e.R + (int64_t)m * e.ldR + n0;
-    cptr_f32 al = (cptr_f32)(e.alpha + n0);
+    // per-tensor alpha: every column reads alpha[0]
+    const int astr = (e.flags & EPI_ALPHA_TENSOR) ? 0 : 1;
+    cptr_f32 al = (cptr_f32)(e.alpha + n0 * astr);
+    cptr_f32 bi = (cptr_f32)(e.bias + n0);
 #pragma unroll
     for (int q = 0; q < TN / 4; ++q) {
         int32_t d[4];
@@ -262,7 +274,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
         if (e.flags & EPI_SCALE) {
             float y[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = al[min(4 * q + i, ncols - 1)] * (float)d[i];
+            for (int i = 0; i < 4; ++i) y[i] = al[min(4 * q + i, ncols - 1) * astr] * (float)d[i];
+            if (e.flags & EPI_BIAS) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = y[i] + bi[min(4 * q + i, ncols - 1)];
+            }
             if (e.flags & EPI_RESIDUAL) {
                 if (vecR) {
                     const float4 rv = *reinterpret_cast<const float4*>(rrow + 4 * q);

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
     const bool last = gl == G - 1;                // the lane that ends with a row's total
     for (int64_t s0 = wave * U; s0 < nsteps; s0 += nwaves * U) {
         u32x4 wv[U][CPL];
-        float av[U], rv[U][MR];
+        float av[U], bv[U], rv[U][MR];
         // all loads of the U row-steps (weights, alpha, residual) go out
         // before the first is consumed
 #pragma unroll
@@ -98,7 +98,9 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
                 if (row < N && c < Kw4) wv[u][i] = load_stream(Wp + row * ldW + 4 * c);
             }
             av[u] = 0.0f;
-            if ((e.flags & EPI_SCALE) && row < N) av[u] = e.alpha[row];
+            bv[u] = 0.0f;
+            if ((e.flags & EPI_SCALE) && row < N) av[u] = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : row];
+            if ((e.flags & EPI_BIAS) && row < N) bv[u] = e.bias[row];
 #pragma unroll
             for (int mr = 0; mr < MR; ++mr) {
                 rv[u][mr] = 0.0f;
@@ -129,6 +131,7 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
                     if (e.flags & EPI_DOT) e.D[(int64_t)mr * e.ldD + row] = d;
                     if (e.flags & EPI_SCALE) {
                         float y = av[u] * (float)d;
+                        if (e.flags & EPI_BIAS) y = y + bv[u];
                         if (e.flags & EPI_RESIDUAL) y = y + rv[u][mr];
                         e.Y[(int64_t)mr * e.ldY + row] = y;
                     }

@@ -246,6 +246,45 @@ int grid_for_rows(int64_t rows) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// One scale for the whole weight matrix, ||W||_1 / (N K) ("Extreme
+// Quantization", eq. (8)).  Pass 1: one wave per row sums |W| in fp64 (the
+// same per-lane order and butterfly as alpha above) into work[n].  Pass 2:
+// one workgroup adds work[0 .. N) in a fixed order (thread-strided partial
+// sums, then a fixed butterfly and a fixed sum over waves), divides by N*K in
+// fp64 and rounds once to fp32.  The same on every run; the fp64 error is
+// far below the final fp32 rounding step.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_row_abs_sum(
+    const float* __restrict__ W, int64_t rows, int K, int64_t ldW, double* __restrict__ work)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+    for (int64_t r = wave; r < rows; r += nwaves) {
+        const float* __restrict__ wr = W + r * ldW;
+        double asum = 0.0;
+        for (int k = 4 * lane; k < K; k += 4 * 64) asum = abs_sum4(load_frag<VEC>(wr, k, K), asum);
+        asum = wave_sum_f64(asum);
+        if (lane == 0) work[r] = asum;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_tensor_alpha(
+    const double* __restrict__ work, int64_t rows, double count, float* __restrict__ alpha)
+{
+    __shared__ double part[kThreads / 64];
+    double s = 0.0;
+    for (int64_t r = threadIdx.x; r < rows; r += kThreads) s += work[r];
+    s = wave_sum_f64(s);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = part[0];
+        for (int w = 1; w < kThreads / 64; ++w) t += part[w];
+        alpha[0] = (float)(t / count);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_pack_dense(const float* X, int64_t rows, int64_t K, int64_t ldX,
@@ -313,6 +352,22 @@ hipError_t launch_pack_im2col3x3(const float* X, int64_t B, int64_t H, int64_t W
         BNN_IM2COL(false, 0);
     }
 #undef BNN_IM2COL
+    return hipGetLastError();
+}
+
+hipError_t launch_alpha_tensor(const float* W, int64_t N, int64_t K, int64_t ldW,
+                               double* work, float* alpha, hipStream_t s)
+{
+    const bool vec = (reinterpret_cast<uintptr_t>(W) & 15u) == 0 && ldW % 4 == 0;
+    int64_t blocks = (N + 3) / 4;
+    if (blocks > 8192) blocks = 8192;
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if (vec) hipLaunchKernelGGL((k_row_abs_sum<true>), grid, block, 0, s, W, N, (int)K, ldW, work);
+    else     hipLaunchKernelGGL((k_row_abs_sum<false>), grid, block, 0, s, W, N, (int)K, ldW, work);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_tensor_alpha, dim3(1), block, 0, s, (const double*)work, N,
+                       (double)N * (double)K, alpha);
     return hipGetLastError();
 }
 
