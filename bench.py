@@ -44,6 +44,7 @@ XOR_LANES, BCNT_LANES = 128, 64
 MIX_LANE_OPS_PER_CLK = 2.0 / (1.0 / XOR_LANES + 1.0 / BCNT_LANES)
 PEAK_INT_OPS = NUM_CU * CLOCK_HZ * MIX_LANE_OPS_PER_CLK   # 52.43e12 lane-ops/s
 PEAK_HBM = 8.0e12                                    # bytes/s
+PEAK_INT8_MFMA = 5.0e15                              # dense int8 matrix-core ops/s (MAC = 2 ops)
 METRIC = "binary GEMM ops/s (TOPS, % int-VALU peak) + batch-1 GEMV HBM GB/s"
 GEMV_COPIES = 191
 
@@ -60,7 +61,7 @@ def parse_args():
     p.add_argument("--size", type=int, default=16384, help="M = N = K of the headline GEMM step")
     p.add_argument("--no-secondary", action="store_true", help="skip the GEMV / MLP / conv / 8192 runs")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv"], default=None,
+    p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv", "i8"], default=None,
                    help="run one workload only (for profiler runs); prints its JSON")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calib", action="store_true",
@@ -254,6 +255,116 @@ def gemv_bench(bnn, torch, N, K, reps=20):
     return res
 
 
+def i8_gemv_bench(bnn, torch, N, K, reps=20):
+    """Binary weights x INT8 activations at the decode shape: the bit-plane
+    GEMV streaming 191 stacked weight copies in one launch, and exact-shape
+    decode calls (quantize the fp32 vector, then the GEMV) from a HIP graph."""
+    import workloads
+    log(f"i8 gemv N={N} K={K}: {GEMV_COPIES} stacked copies")
+    W = torch.from_numpy(workloads.normal_f32(workloads.seed_for(3, 0) + K, (N, K))).cuda()
+    x = torch.from_numpy(workloads.normal_f32(workloads.seed_for(3, 1) + K, (1, K))).cuda()
+    Wp, a = bnn.pack_weights(W)
+    del W
+    q = bnn.quantize_act_i8(x, want_int8=False)
+    G = GEMV_COPIES
+    Wst = Wp.repeat(G, 1)
+    ast = a.repeat(G)
+    Nt = G * N
+    Y = torch.empty((1, Nt), dtype=torch.float32, device="cuda")
+    kw = (K + 31) // 32
+    flags = bnn.EPI_SCALE_F32
+
+    def run(Wm, am, y):
+        bnn.bwn_i8_linear(Wm, K, flags, Xb=q["Xb"], xsum=q["xsum"], xscale=q["xscale"], alpha=am, Y=y)
+
+    for _ in range(3):
+        run(Wst, ast, Y)
+    ts = [Ev() for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in ts:
+        e.start()
+        run(Wst, ast, Y)
+        e.stop()
+    torch.cuda.synchronize()
+    ms = [e.ms() for e in ts]
+    # weights + 8 activation planes + xsum + xscale + alpha + y
+    bytes_stream = 4.0 * Nt * kw + 32.0 * kw + 8.0 + 4.0 * Nt + 4.0 * Nt
+    t_stream = statistics.mean(ms) * 1e-3
+    ys = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    order = [(i * 37) % G for i in range(2 * G)]
+
+    def seq():
+        for g in order:
+            qq = bnn.quantize_act_i8(x, want_int8=False)
+            bnn.bwn_i8_linear(Wst[g * N:(g + 1) * N], K, flags, Xb=qq["Xb"], xsum=qq["xsum"],
+                              xscale=qq["xscale"], alpha=ast[g * N:(g + 1) * N], Y=ys)
+    seq()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        seq()
+    graph.replay()
+    torch.cuda.synchronize()
+    e = Ev()
+    e.start()
+    graph.replay()
+    e.stop()
+    torch.cuda.synchronize()
+    per_call_ms = e.ms() / len(order)
+    res = dict(
+        N=N, K=K, copies=G, stream_ms_mean=statistics.mean(ms), stream_ms_median=median(ms),
+        stream_bytes=bytes_stream, stream_GBps=bytes_stream / t_stream / 1e9,
+        stream_frac_hbm=bytes_stream / t_stream / PEAK_HBM,
+        # 8 (v_and, v_bcnt) pairs per weight word: the VALU share of the same time
+        stream_valu_frac=16.0 * Nt * kw / t_stream / PEAK_INT_OPS,
+        decode_call_us_quantize_plus_gemv=1e3 * per_call_ms,
+    )
+    del Wst, ast, Wp, a, Y, graph
+    torch.cuda.empty_cache()
+    return res
+
+
+def i8_gemm_bench(bnn, torch, M, N, K, reps=10, warmup=2):
+    """Binary weights x INT8 activations with many activation rows: quantize
+    the fp32 activations (int8 rows), then the int8 MFMA GEMM writing int32 D
+    and fp32 Y.  Rated against the dense int8 matrix-core peak."""
+    import workloads
+    log(f"i8 gemm {M}x{N}x{K}")
+    X = torch.from_numpy(workloads.normal_f32(workloads.seed_for(4, 0) + 17, (M, K))).cuda()
+    W = torch.from_numpy(workloads.normal_f32(workloads.seed_for(4, 1) + 17, (N, K))).cuda()
+    Wp, a = bnn.pack_weights(W)
+    del W
+    D = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    flags = bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32
+    pool = [(Ev(), Ev()) for _ in range(reps)]
+
+    def step(e):
+        if e: e[0].start()
+        q = bnn.quantize_act_i8(X, want_planes=False)
+        if e: e[0].stop(); e[1].start()
+        bnn.bwn_i8_linear(Wp, K, flags, Xq=q["Xq"], xscale=q["xscale"], alpha=a, D=D, Y=Y)
+        if e: e[1].stop()
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    for e in pool:
+        step(e)
+    torch.cuda.synchronize()
+    qms = [e[0].ms() for e in pool]
+    gms = [e[1].ms() for e in pool]
+    ops = 2.0 * M * N * K
+    t = statistics.mean(gms) * 1e-3
+    res = dict(M=M, N=N, K=K, gemm_ms_mean=statistics.mean(gms), gemm_ms_median=median(gms),
+               quantize_ms_median=median(qms), int8_tops=ops / t / 1e12,
+               frac_int8_mfma_peak=ops / t / PEAK_INT8_MFMA,
+               quantize_GBps=(4.0 * M * K + 1.0 * M * K + 4.0 * M) / (median(qms) * 1e-3) / 1e9)
+    del X, Wp, a, D, Y
+    torch.cuda.empty_cache()
+    return res
+
+
 def mlp_bench(bnn, torch, reps=20, warmup=3):
     import workloads
     c = workloads.WORKLOADS[2]
@@ -422,6 +533,9 @@ def main():
             r = [gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]]
         elif args.only == "mlp":
             r = mlp_bench(bnn, torch)
+        elif args.only == "i8":
+            r = {"gemv": [i8_gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]],
+                 "gemm": i8_gemm_bench(bnn, torch, 8192, 8192, 8192)}
         else:
             r = [conv_bench(bnn, torch, s) for s in workloads.WORKLOADS[5]["shapes"]]
         if args.copy_calib:
@@ -496,6 +610,25 @@ def main():
             "binary_tops_step": round(g8["binops_per_step"] / (g8["ms_per_step"] * 1e-3) / 1e12, 2),
             "gemm_int_valu_frac": round(g8["gemm_int_ops_per_s"] / PEAK_INT_OPS, 4),
             "gemm_ms": round(g8["gemm_ms_median"], 4), "ms_per_step": round(g8["ms_per_step"], 4),
+        }
+        iv = [i8_gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]]
+        sec["i8act_gemv_batch1"] = {
+            "metric": "binary weights x INT8 activations, batch-1 GEMV HBM GB/s (191 stacked copies)",
+            "value": round(min(r["stream_GBps"] for r in iv), 1),
+            "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(min(r["stream_GBps"] for r in iv), 1),
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": round(min(r["stream_frac_hbm"] for r in iv), 4)},
+            "shapes": iv,
+        }
+        ig = i8_gemm_bench(bnn, torch, 8192, 8192, 8192)
+        sec["i8act_gemm_8192"] = {
+            "metric": "binary weights x INT8 activations, int8 MFMA GEMM ops/s",
+            "value": round(ig["int8_tops"], 1), "unit": "TOPS",
+            "roofline": {"bound": "mfma", "achieved": round(ig["int8_tops"], 1),
+                         "peak": PEAK_INT8_MFMA / 1e12, "unit": "TOPS",
+                         "frac": round(ig["frac_int8_mfma_peak"], 4)},
+            "detail": ig,
         }
         sec["binary_mlp_batch1024"] = mlp_bench(bnn, torch)
         sec["conv_block"] = [conv_bench(bnn, torch, s) for s in workloads.WORKLOADS[5]["shapes"]]

@@ -65,6 +65,19 @@ __device__ __forceinline__ uint32_t sum_reduce_to_last(uint32_t v, int glog2) {
     return v;
 }
 
+// The same group sum with the group size fixed at compile time: each step is
+// one DPP add (the row shift folded into the add), nothing is selected.
+template <int GLOG2>
+__device__ __forceinline__ uint32_t sum_reduce_to_last_t(uint32_t v) {
+    if (GLOG2 >= 1) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);
+    if (GLOG2 >= 2) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);
+    if (GLOG2 >= 3) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);
+    if (GLOG2 >= 4) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);
+    if (GLOG2 >= 5) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+    if (GLOG2 >= 6) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+    return v;
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);

@@ -20,6 +20,7 @@
 // weights instead of 32 multiply-adds, so the GEMV stays bound by the 1-bit
 // weight stream.  Plane pad bits are 0 (value 0), so weight pad bits never
 // contribute.
+#include <stdio.h>
 #include <stdlib.h>
 
 #include "bnn_device.hpp"
@@ -184,30 +185,34 @@ __global__ __launch_bounds__(kThreads) void k_act_i8(
     }
 }
 
-// Bit-plane GEMV: G lanes share one weight row (the smallest power of two
-// covering its 16-byte granules, at most 64), 64/G rows per wave step, U
-// row-steps per iteration with all their loads issued first (as in the XNOR
-// GEMV).  Each lane keeps its granules of all 8 planes of the MR activation
-// rows in registers for the whole kernel.
-template <int MR, int CPL, int U>
+// Bit-plane GEMV: G = 2^GLOG2 lanes share one weight row and read it in
+// consecutive 16-byte granules (coalesced), 64/G rows per wave step, CPL
+// granules per lane, U row-steps per group with all their loads issued
+// first.  Each lane keeps its granules of all 8 planes of the MR activation
+// rows in registers for the whole kernel.  Per row-step a lane does
+// 8 (v_and, v_bcnt) per word, 7 shift-adds to weigh the planes, and the
+// group sum takes GLOG2 DPP adds.
+template <int MR, int CPL, int U, int GLOG2>
 __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
     const uint32_t* __restrict__ Xb, int64_t ldXb, const int32_t* __restrict__ xsum,
-    const uint32_t* __restrict__ Wp, int64_t ldW, int N, int K, int glog2, EpilogueI8 e)
+    const uint32_t* __restrict__ Wp, int64_t ldW, int N, int K, EpilogueI8 e)
 {
+    constexpr int G = 1 << GLOG2;
+    constexpr int RPS = 64 >> GLOG2;
     const int lane = threadIdx.x & 63;
-    const int G = 1 << glog2;
-    const int RPS = 64 >> glog2;
     const int gl = lane & (G - 1);
-    const int go = lane >> glog2;
+    const int go = lane >> GLOG2;
     const int Kw = (K + 31) >> 5;
     const int Kw4 = (Kw + 3) >> 2;
 
     u32x4 xg[MR][8][CPL];
+    bool live[CPL];                               // granule inside the row
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = gl + G * i;
+        live[i] = c < Kw4;
         u32x4 wm = (u32x4){0u, 0u, 0u, 0u};        // words >= Kw read as 0
-        if (c < Kw4) {
+        if (live[i]) {
             wm.x = (4 * c + 0 < Kw) ? ~0u : 0u;
             wm.y = (4 * c + 1 < Kw) ? ~0u : 0u;
             wm.z = (4 * c + 2 < Kw) ? ~0u : 0u;
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
                 u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-                if (c < Kw4) v = *reinterpret_cast<const u32x4*>(Xb + ((int64_t)mr * 8 + b) * ldXb + 4 * c);
+                if (live[i]) v = *reinterpret_cast<const u32x4*>(Xb + ((int64_t)mr * 8 + b) * ldXb + 4 * c);
                 xg[mr][b][i] = v & wm;
             }
     }
@@ -232,27 +237,30 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
 
     const int64_t nsteps = ((int64_t)N + RPS - 1) / RPS;
     const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+    const int64_t stride = (((int64_t)gridDim.x * kThreads) >> 6) * U;
     const bool last = gl == G - 1;
-    for (int64_t s0 = wave * U; s0 < nsteps; s0 += nwaves * U) {
-        u32x4 wv[U][CPL];
+    const int64_t step_words = (int64_t)RPS * ldW;     // one row-step further down
+    for (int64_t s0 = wave * U; s0 < nsteps; s0 += stride) {
+        const int64_t row0 = s0 * RPS + go;
+        const uint32_t* __restrict__ wp0 = Wp + row0 * ldW + 4 * gl;
+        u32x4 w[U][CPL];
         float av[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t row = (s0 + u) * RPS + go;
+            const int64_t row = row0 + (int64_t)u * RPS;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
-                const int c = gl + G * i;
-                wv[u][i] = (u32x4){0u, 0u, 0u, 0u};
-                if (row < N && c < Kw4)
-                    wv[u][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wp + row * ldW + 4 * c));
+                w[u][i] = (u32x4){0u, 0u, 0u, 0u};
+                if (row < N && live[i])
+                    w[u][i] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4*>(wp0 + u * step_words + 4 * G * i));
             }
             av[u] = 0.0f;
             if ((e.flags & EPI_SCALE) && row < N) av[u] = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : row];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t row = (s0 + u) * RPS + go;
+            const int64_t row = row0 + (int64_t)u * RPS;
 #pragma unroll
             for (int mr = 0; mr < MR; ++mr) {
                 uint32_t acc[8];
@@ -260,10 +268,9 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
                 for (int b = 0; b < 8; ++b) acc[b] = 0u;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
-                    const u32x4 w = wv[u][i];
 #pragma unroll
                     for (int b = 0; b < 8; ++b) {
-                        const u32x4 t = xg[mr][b][i] & w;
+                        const u32x4 t = xg[mr][b][i] & w[u][i];
                         acc[b] = popc_acc(t.x, acc[b]);
                         acc[b] = popc_acc(t.y, acc[b]);
                         acc[b] = popc_acc(t.z, acc[b]);
@@ -275,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
 #pragma unroll
                 for (int b = 1; b < 7; ++b) neg += acc[b] << b;
                 neg -= acc[7] << 7;
-                neg = sum_reduce_to_last(neg, glog2);
+                neg = sum_reduce_to_last_t<GLOG2>(neg);
                 if (last && row < N) {
                     const int32_t d = xs[mr] - 2 * (int32_t)neg;
                     if (e.flags & EPI_DOT) e.D[(int64_t)mr * e.ldD + row] = d;
@@ -313,38 +320,54 @@ hipError_t launch_act_i8(const float* X, int64_t ldX, const int8_t* Xq_in, int64
 }
 
 namespace {
-int i8_cpl(int64_t K, int* glog2_out) {
+// Lane-group shape of the G-lanes GEMV for a row of K: G = 2^glog2 lanes and
+// CPL granules per lane, the fewest lane slots G * CPL covering the row's
+// ceil(Kw/4) granules (G in 16..64, CPL * M <= 4 so the planes fit in
+// registers); among equal slot counts the larger CPL (fewer group sums).
+struct I8Shape { int glog2, cpl; };
+
+bool i8_shape(int64_t M, int64_t K, I8Shape* out) {
     const int64_t kw4 = ((K + 31) / 32 + 3) / 4;
-    int glog2 = 0;
-    while ((1 << glog2) < kw4 && glog2 < 6) ++glog2;
-    const int G = 1 << glog2;
-    const int64_t need = (kw4 + G - 1) / G;
-    if (glog2_out) *glog2_out = glog2;
-    return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 1 << 30;
+    I8Shape best = {0, 0};
+    int64_t best_slots = 0;
+    for (int cpl = 4; cpl >= 1; --cpl) {
+        if (cpl * M > 4) continue;
+        for (int g = 4; g <= 6; ++g) {
+            const int64_t slots = (int64_t)cpl << g;
+            if (slots < kw4) continue;
+            if (best.cpl == 0 || slots < best_slots) { best = {g, cpl}; best_slots = slots; }
+        }
+    }
+    if (best.cpl == 0) return false;
+    if (const char* v = getenv("BNN_I8_SHAPE")) {     // tuning override "glog2,cpl"
+        int g = 0, c = 0;
+        if (sscanf(v, "%d,%d", &g, &c) == 2 && g >= 4 && g <= 6 && c >= 1 && c <= 4 && c * M <= 4 &&
+            ((int64_t)c << g) >= kw4) best = {g, c};
+    }
+    *out = best;
+    return true;
 }
 }  // namespace
 
 bool i8_gemv_eligible(int64_t M, int64_t K) {
-    // registers: MR * CPL granule sets of 8 planes (32 VGPRs each), at most 4
-    const int cpl = i8_cpl(K, nullptr);
-    return M >= 1 && M <= 2 && (int64_t)cpl * M <= 4;
+    I8Shape sh;
+    return M >= 1 && M <= 2 && i8_shape(M, K, &sh);
 }
 
 hipError_t launch_bwn_i8_gemv(const uint32_t* Xb, int64_t ldXb, const int32_t* xsum,
                               const uint32_t* Wp, int64_t ldW,
                               int64_t M, int64_t N, int64_t K, const EpilogueI8& e, hipStream_t s)
 {
-    int glog2 = 0;
-    const int cpl = i8_cpl(K, &glog2);
-    const int G = 1 << glog2;
-    int umax = cpl * M <= 2 ? 4 : 2;
-    if (const char* v = getenv("BNN_GEMV_U")) {       // tuning override: 1, 2 or 4
-        const int u = atoi(v);
-        if (u == 1 || u == 2 || u == 4) umax = u < umax ? u : umax;
-    }
-    const int rps = 64 / G;
-    const int64_t steps = (N + rps - 1) / rps;
     const int cus = num_cus();
+    I8Shape sh;
+    i8_shape(M, K, &sh);
+    int umax = 2;
+    if (const char* v = getenv("BNN_GEMV_U")) {       // tuning override: 1 or 2
+        const int u = atoi(v);
+        if (u == 1 || u == 2) umax = u;
+    }
+    const int rps = 64 >> sh.glog2;
+    const int64_t steps = (N + rps - 1) / rps;
     const bool unroll = umax > 1 && steps >= (int64_t)cus * 4 * 8 * umax;
     const int U = unroll ? umax : 1;
     const int64_t waves = (steps + U - 1) / U;
@@ -354,22 +377,21 @@ hipError_t launch_bwn_i8_gemv(const uint32_t* Xb, int64_t ldXb, const int32_t* x
     if (blocks < 1) blocks = 1;
     const dim3 grid((unsigned)blocks), block(kThreads);
     const int n = (int)N, k = (int)K;
-#define BNN_I8GEMV(MR, CPL, UU) \
-    hipLaunchKernelGGL((k_bwn_i8_gemv<MR, CPL, UU>), grid, block, 0, s, Xb, ldXb, xsum, Wp, ldW, n, k, glog2, e)
+#define BNN_I8GEMV(MR, CPL, UU, GL) \
+    hipLaunchKernelGGL((k_bwn_i8_gemv<MR, CPL, UU, GL>), grid, block, 0, s, Xb, ldXb, xsum, Wp, ldW, n, k, e)
+#define BNN_I8GEMV_G(MR, CPL, UU) \
+    switch (sh.glog2) { case 4: BNN_I8GEMV(MR, CPL, UU, 4); break; case 5: BNN_I8GEMV(MR, CPL, UU, 5); break; \
+                        default: BNN_I8GEMV(MR, CPL, UU, 6); break; }
 #define BNN_I8GEMV_U(MR, CPL) \
-    switch (U) { case 4: BNN_I8GEMV(MR, CPL, 4); break; case 2: BNN_I8GEMV(MR, CPL, 2); break; \
-                 default: BNN_I8GEMV(MR, CPL, 1); break; }
-#define BNN_I8GEMV_U2(MR, CPL) \
-    switch (U) { case 2: BNN_I8GEMV(MR, CPL, 2); break; default: BNN_I8GEMV(MR, CPL, 1); break; }
-    // MR * CPL == 4 holds 128 VGPRs of planes: at most 2 row-steps in flight
+    if (U == 2) { BNN_I8GEMV_G(MR, CPL, 2) } else { BNN_I8GEMV_G(MR, CPL, 1) }
     if (M == 1) {
-        switch (cpl) { case 1: BNN_I8GEMV_U(1, 1); break; case 2: BNN_I8GEMV_U(1, 2); break;
-                       default: BNN_I8GEMV_U2(1, 4); break; }
+        switch (sh.cpl) { case 1: BNN_I8GEMV_U(1, 1); break; case 2: BNN_I8GEMV_U(1, 2); break;
+                          case 3: BNN_I8GEMV_U(1, 3); break; default: BNN_I8GEMV_U(1, 4); break; }
     } else {
-        switch (cpl) { case 1: BNN_I8GEMV_U(2, 1); break; default: BNN_I8GEMV_U2(2, 2); break; }
+        switch (sh.cpl) { case 1: BNN_I8GEMV_U(2, 1); break; default: BNN_I8GEMV_U(2, 2); break; }
     }
-#undef BNN_I8GEMV_U2
 #undef BNN_I8GEMV_U
+#undef BNN_I8GEMV_G
 #undef BNN_I8GEMV
     return hipGetLastError();
 }
