@@ -162,7 +162,8 @@ def test_bwn_i8_gemv_matches_oracle(bnn, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 64), (16, 16, 63), (64, 128, 1000), (130, 257, 100),
-                                   (200, 300, 4096), (3, 1000, 11008), (129, 129, 129), (1, 64, 65)])
+                                   (200, 300, 4096), (3, 1000, 11008), (129, 129, 129), (1, 64, 65),
+                                   (600, 200, 1000), (513, 129, 130), (257, 385, 192)])
 def test_bwn_i8_gemm_matches_oracle(bnn, M, N, K):
     W, ws, a = _weights(7600 + K, N, K)
     X = _act_rows(7700 + K, M, K)

@@ -19,10 +19,16 @@
 // A and B use the same k assignment, so each output is the full sum over k.
 // The int32 result of lane l, register r is row 4*(l/16) + r, column l % 16.
 //
-// Tiling: a 256-thread workgroup computes 128 activation rows x 128 weight
-// rows; its 4 waves take 64 x 64 quarters (4 x 4 fragments each).  The next
-// k-step's A fragments and weight words are loaded before the current
-// step's MFMAs (register double buffering).
+// Tiling: a 256-thread workgroup computes 256 activation rows x 128 weight
+// rows; wave w takes rows 128*(w/2) .. +127 and columns 64*(w%2) .. +63,
+// i.e. 8 x 4 fragments (32 MFMAs per 64-wide k-step against 4 weight
+// expansions).  The workgroup's A tile (256 rows x 64 bytes per k-step) is
+// staged through LDS, double-buffered with one barrier per k-step; each
+// lane's 16-byte piece j of row r sits at slot j ^ ((r / 4) % 4) of the
+// row's four 16-byte slots, so the 16 lanes of a fragment read (16 rows,
+// one k-group) hit 16 distinct 4-bank groups.  The next k-step's A pieces
+// and weight words are loaded into registers before the current step's
+// MFMAs and written to LDS after them.
 #include "bnn_device.hpp"
 #include "bnn_launch.hpp"
 
@@ -30,7 +36,7 @@ namespace bnn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 128, kBN = 128, kKS = 64;
+constexpr int kBM = 256, kBN = 128, kKS = 64;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -58,83 +64,113 @@ __device__ __forceinline__ v4i expand_signs(uint32_t bits16) {
     return r;
 }
 
+constexpr int kAPieces = kBM * kKS / 16 / kThreads;   // 16-byte A pieces per thread per k-step
+
 template <bool TAIL>
-__device__ __forceinline__ void load_step(v4i (&a)[4], uint32_t (&b)[4],
-                                          const int8_t* const (&arow)[4], const uint32_t* const (&wrow)[4],
-                                          int k0, int g, int K)
-{
+__device__ __forceinline__ void load_a_step(v4i (&ar)[kAPieces], const int8_t* const (&arow)[kAPieces],
+                                            int k0, int j, int K) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = load_a<TAIL>(arow[i], k0 + 16 * g, K);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = wrow[j][(k0 >> 5) + (g >> 1)];
+    for (int i = 0; i < kAPieces; ++i) ar[i] = load_a<TAIL>(arow[i], k0 + 16 * j, K);
 }
 
-__global__ __launch_bounds__(kThreads) void k_bwn_i8_gemm(
+__global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
     const int8_t* __restrict__ Xq, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
     int M, int N, int K, int tiles_n, EpilogueI8 e)
 {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) int8_t lds_a[2][kBM * kKS];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
-    const int m0 = tm * kBM + (wave >> 1) * 64;
-    const int n0 = tn * kBN + (wave & 1) * 64;
+    const int m_blk = tm * kBM, n_blk = tn * kBN;
+    const int wm = wave >> 1, wn = wave & 1;
     const int r16 = lane & 15, g = lane >> 4;
 
-    const int8_t* arow[4];
+    // global -> LDS staging of A: thread tid moves piece j = tid % 4 of
+    // rows tid/4 + 64 i (i < 4)
+    const int j = tid & 3;
+    const int8_t* arow[kAPieces];
+    int woff[kAPieces];
+#pragma unroll
+    for (int i = 0; i < kAPieces; ++i) {
+        const int r = (tid >> 2) + 64 * i;
+        arow[i] = Xq + (int64_t)min(m_blk + r, M - 1) * ldX;
+        woff[i] = r * kKS + ((j ^ ((r >> 2) & 3)) << 4);
+    }
+    // fragment reads: row 16 f + r16 of the wave's 128, k-group g
+    int roff[8];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        const int r = wm * 128 + 16 * f + r16;
+        roff[f] = r * kKS + ((g ^ ((r >> 2) & 3)) << 4);
+    }
     const uint32_t* wrow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) arow[i] = Xq + (int64_t)min(m0 + 16 * i + r16, M - 1) * ldX;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wrow[j] = Wp + (int64_t)min(n0 + 16 * j + r16, N - 1) * ldW;
+    for (int q = 0; q < 4; ++q) wrow[q] = Wp + (int64_t)min(n_blk + wn * 64 + 16 * q + r16, N - 1) * ldW;
 
-    v4i acc[4][4];
+    v4i acc[8][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int f = 0; f < 8; ++f)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+        for (int q = 0; q < 4; ++q) acc[f][q] = (v4i){0, 0, 0, 0};
 
     const int steps = (K + kKS - 1) / kKS;
-    const int full_steps = K / kKS;                // steps with all 64 k inside the row
-    v4i a[4];
-    uint32_t b[4];
-    if (full_steps > 0) load_step<false>(a, b, arow, wrow, 0, g, K);
-    else                load_step<true>(a, b, arow, wrow, 0, g, K);
+    const int full_steps = K / kKS;
+    v4i ar[kAPieces];
+    uint32_t bw[4];
+    if (full_steps > 0) load_a_step<false>(ar, arow, 0, j, K);
+    else                load_a_step<true>(ar, arow, 0, j, K);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bw[q] = wrow[q][g >> 1];
+#pragma unroll
+    for (int i = 0; i < kAPieces; ++i) *reinterpret_cast<v4i*>(&lds_a[0][woff[i]]) = ar[i];
+    __syncthreads();
+
     for (int s = 0; s < steps; ++s) {
-        v4i an[4];
-        uint32_t bn[4];
+        const int cur = s & 1;
+        const bool more = s + 1 < steps;
         const int kn = (s + 1) * kKS;
-        if (s + 1 < full_steps)   load_step<false>(an, bn, arow, wrow, kn, g, K);
-        else if (s + 1 < steps)   load_step<true>(an, bn, arow, wrow, kn, g, K);
+        uint32_t bn[4];
+        if (more) {
+            if (s + 1 < full_steps) load_a_step<false>(ar, arow, kn, j, K);
+            else                    load_a_step<true>(ar, arow, kn, j, K);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bn[q] = wrow[q][(kn >> 5) + (g >> 1)];
+        }
         v4i bx[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bx[j] = expand_signs(b[j] >> (16 * (g & 1)));
+        for (int q = 0; q < 4; ++q) bx[q] = expand_signs(bw[q] >> (16 * (g & 1)));
+        const int8_t* la = lds_a[cur];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int f = 0; f < 8; ++f) {
+            const v4i a = *reinterpret_cast<const v4i*>(la + roff[f]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bx[j], acc[i][j], 0, 0, 0);
-        if (s + 1 < steps) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = an[i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = bn[j];
+            for (int q = 0; q < 4; ++q)
+                acc[f][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx[q], acc[f][q], 0, 0, 0);
         }
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < kAPieces; ++i) *reinterpret_cast<v4i*>(&lds_a[cur ^ 1][woff[i]]) = ar[i];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bw[q] = bn[q];
+        }
+        __syncthreads();
     }
 
     // epilogue: lane holds rows 4g + r of each 16-row fragment, column r16
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 16 * j + r16;
+    for (int q = 0; q < 4; ++q) {
+        const int n = n_blk + wn * 64 + 16 * q + r16;
         if (n >= N) continue;
         float an = 0.0f;
         if (e.flags & EPI_SCALE) an = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : n];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int f = 0; f < 8; ++f)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 16 * i + 4 * g + r;
+                const int m = m_blk + wm * 128 + 16 * f + 4 * g + r;
                 if (m >= M) continue;
-                const int32_t d = acc[i][j][r];
+                const int32_t d = acc[f][q][r];
                 if (e.flags & EPI_DOT) e.D[(int64_t)m * e.ldD + n] = d;
                 if (e.flags & EPI_SCALE) {
                     float y = an * (float)d;
