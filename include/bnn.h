@@ -119,7 +119,10 @@ typedef struct bnn_i8_args {
                                          ldXb >= ceil(K/32); plane pad bits 0  */
     const int32_t* xsum;              /* [M] row sums of the int8 values        */
     const int8_t* Xq; int64_t ldXq;   /* int8 rows: 16-byte aligned, ldXq % 16
-                                         == 0, ldXq >= K                        */
+                                         == 0, ldXq >= K; the GEMM reads whole
+                                         16-byte pieces of a row below ldXq
+                                         (bytes from K on are ignored);
+                                         M * ldXq < 2^31                      */
     const float* xscale;              /* [M] activation scales, or NULL (1.0)   */
     const uint32_t* Wp; int64_t ldWp; /* packed weights [N, ldWp] (packed layout) */
     int64_t M, N, K;                  /* 1 <= K <= BNN_MAX_K_I8                 */

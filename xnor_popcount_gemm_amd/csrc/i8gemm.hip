@@ -21,14 +21,17 @@
 //
 // Tiling: a 256-thread workgroup computes 256 activation rows x 128 weight
 // rows; wave w takes rows 128*(w/2) .. +127 and columns 64*(w%2) .. +63,
-// i.e. 8 x 4 fragments (32 MFMAs per 64-wide k-step against 4 weight
-// expansions).  The workgroup's A tile (256 rows x 64 bytes per k-step) is
-// staged through LDS, double-buffered with one barrier per k-step; each
-// lane's 16-byte piece j of row r sits at slot j ^ ((r / 4) % 4) of the
-// row's four 16-byte slots, so the 16 lanes of a fragment read (16 rows,
-// one k-group) hit 16 distinct 4-bank groups.  The next k-step's A pieces
-// and weight words are loaded into registers before the current step's
-// MFMAs and written to LDS after them.
+// i.e. 8 x 4 fragments (32 MFMAs per 64-wide k-half against 4 weight
+// expansions, two halves per 128-wide k-step).  The workgroup's A tile
+// (256 rows x 128 bytes per k-step) is staged through LDS, double-buffered
+// with one barrier per k-step; 16-byte piece j of row r sits at slot
+// j ^ ((r / 2) % 8) of the row's eight slots, so the 16 lanes of a fragment
+// read (16 rows, one k-group) hit 16 distinct 4-bank groups.  The next
+// k-step's A pieces go straight from global memory into the other LDS
+// buffer, and its weight words into registers, before the current step's
+// MFMAs.
+#include <type_traits>
+
 #include "bnn_device.hpp"
 #include "bnn_launch.hpp"
 
@@ -36,18 +39,27 @@ namespace bnn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 256, kBN = 128, kKS = 64;
+constexpr int kBM = 256, kBN = 128, kKS = 128;   // kKS: two MFMA k-widths per step
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// 16 bytes of an int8 row starting at k; bytes at k >= K read as 0.
+// 16 bytes of an int8 row starting at k (a multiple of 16); bytes at k >= K
+// read as 0.  A piece that starts below K ends at or below the row stride
+// (both multiples of 16), so the 16-byte load stays inside the row; pieces
+// that start at or past K are not loaded.
 template <bool TAIL>
 __device__ __forceinline__ v4i load_a(const int8_t* __restrict__ row, int k, int K) {
-    if (!TAIL || k + 16 <= K) return *reinterpret_cast<const v4i*>(row + k);
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    for (int i = 0; i < 16; ++i)
-        if (k + i < K) w[i >> 2] |= ((uint32_t)(uint8_t)row[k + i]) << (8 * (i & 3));
-    return (v4i){(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    if (!TAIL) return *reinterpret_cast<const v4i*>(row + k);
+    v4i v = (v4i){0, 0, 0, 0};
+    if (k < K) v = *reinterpret_cast<const v4i*>(row + k);
+    const int valid = K - k;                       // bytes of the piece inside the row
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int vd = valid - 4 * d;
+        const uint32_t m = vd >= 4 ? ~0u : vd <= 0 ? 0u : (1u << (8 * vd)) - 1u;
+        v[d] = (int)((uint32_t)v[d] & m);
+    }
+    return v;
 }
 
 // 16 weight bits (bit i = element i; 1 means -1) to 16 bytes of +1 / -1.
@@ -64,14 +76,10 @@ __device__ __forceinline__ v4i expand_signs(uint32_t bits16) {
     return r;
 }
 
-constexpr int kAPieces = kBM * kKS / 16 / kThreads;   // 16-byte A pieces per thread per k-step
+constexpr int kAPieces = kBM * kKS / 16 / kThreads;   // 16-byte A pieces per lane per k-step
 
-template <bool TAIL>
-__device__ __forceinline__ void load_a_step(v4i (&ar)[kAPieces], const int8_t* const (&arow)[kAPieces],
-                                            int k0, int j, int K) {
-#pragma unroll
-    for (int i = 0; i < kAPieces; ++i) ar[i] = load_a<TAIL>(arow[i], k0 + 16 * j, K);
-}
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
 __global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
     const int8_t* __restrict__ Xq, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
@@ -86,24 +94,43 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
     const int wm = wave >> 1, wn = wave & 1;
     const int r16 = lane & 15, g = lane >> 4;
 
-    // global -> LDS staging of A: thread tid moves piece j = tid % 4 of
-    // rows tid/4 + 64 i (i < 4)
-    const int j = tid & 3;
-    const int8_t* arow[kAPieces];
-    int woff[kAPieces];
+    // A staging.  Instruction i of wave w fills tile rows 8 (8 w + i) ..
+    // +7 (1 KiB of LDS): lane l takes row r = 8 (8 w + i) + l / 8, LDS slot
+    // l % 8, and loads the piece j stored there, j = slot ^ ((r / 2) % 8).
+    // Full k-steps load straight into LDS (global_load_lds_dwordx4 writes
+    // lane l's 16 bytes at the instruction's LDS base + 16 l); the step
+    // holding the end of the row goes through registers, masked past K.
+    int aoff[kAPieces];                            // byte offset of row r (M * ldX < 2^31)
+    int apiece[kAPieces];                          // byte offset of piece j in the row
 #pragma unroll
     for (int i = 0; i < kAPieces; ++i) {
-        const int r = (tid >> 2) + 64 * i;
-        arow[i] = Xq + (int64_t)min(m_blk + r, M - 1) * ldX;
-        woff[i] = r * kKS + ((j ^ ((r >> 2) & 3)) << 4);
+        const int r = 8 * (8 * wave + i) + (lane >> 3);
+        aoff[i] = min(m_blk + r, M - 1) * (int)ldX;
+        apiece[i] = (((lane & 7) ^ ((r >> 1) & 7)) << 4);
     }
-    // fragment reads: row 16 f + r16 of the wave's 128, k-group g
-    int roff[8];
+    auto stage_direct = [&](int buf, int k0) {
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-        const int r = wm * 128 + 16 * f + r16;
-        roff[f] = r * kKS + ((g ^ ((r >> 2) & 3)) << 4);
-    }
+        for (int i = 0; i < kAPieces; ++i)
+            __builtin_amdgcn_global_load_lds((gptr_t)(Xq + aoff[i] + k0 + apiece[i]),
+                                             (lptr_t)(&lds_a[buf][(8 * wave + i) * 1024]), 16, 0, 0);
+    };
+    auto stage_masked = [&](int buf, int k0) {
+#pragma unroll
+        for (int i = 0; i < kAPieces; ++i) {
+            const v4i v = load_a<true>(Xq + aoff[i], k0 + apiece[i], K);
+            *reinterpret_cast<v4i*>(&lds_a[buf][(8 * wave + i) * 1024 + 16 * lane]) = v;
+        }
+    };
+    // fragment reads: row 16 f + r16 of the wave's 128, piece 4 h + g of the
+    // step (h: first or second 64-wide half)
+    int roff[2][8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            const int r = wm * 128 + 16 * f + r16;
+            roff[h][f] = r * kKS + (((4 * h + g) ^ ((r >> 1) & 7)) << 4);
+        }
     const uint32_t* wrow[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) wrow[q] = Wp + (int64_t)min(n_blk + wn * 64 + 16 * q + r16, N - 1) * ldW;
@@ -114,48 +141,73 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[f][q] = (v4i){0, 0, 0, 0};
 
+    // weight words of a step: half h of column q is word (k0 / 32) + 2 h + g / 2
     const int steps = (K + kKS - 1) / kKS;
     const int full_steps = K / kKS;
-    v4i ar[kAPieces];
-    uint32_t bw[4];
-    if (full_steps > 0) load_a_step<false>(ar, arow, 0, j, K);
-    else                load_a_step<true>(ar, arow, 0, j, K);
+    uint32_t bw[2][4];
+    if (full_steps > 0) stage_direct(0, 0);
+    else                stage_masked(0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bw[q] = wrow[q][g >> 1];
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int i = 0; i < kAPieces; ++i) *reinterpret_cast<v4i*>(&lds_a[0][woff[i]]) = ar[i];
+        for (int q = 0; q < 4; ++q) bw[h][q] = wrow[q][2 * h + (g >> 1)];
+    __builtin_amdgcn_s_waitcnt(0);
+    // the first step's words are complete before the loop, so no load is
+    // pending on the loop-carried registers when an iteration begins
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) asm volatile("" : : "v"(bw[h][q]));
     __syncthreads();
 
-    for (int s = 0; s < steps; ++s) {
+    // One k-step: prefetch step s+1 (DIRECT: straight into LDS), run the 64
+    // MFMAs of step s, wait for the prefetch, barrier.
+    auto kstep = [&](int s, auto direct_tag) {
+        constexpr bool DIRECT = decltype(direct_tag)::value;
         const int cur = s & 1;
         const bool more = s + 1 < steps;
         const int kn = (s + 1) * kKS;
-        uint32_t bn[4];
+        uint32_t bn[2][4];
         if (more) {
-            if (s + 1 < full_steps) load_a_step<false>(ar, arow, kn, j, K);
-            else                    load_a_step<true>(ar, arow, kn, j, K);
+            if (DIRECT) stage_direct(cur ^ 1, kn);
+            else        stage_masked(cur ^ 1, kn);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bn[q] = wrow[q][(kn >> 5) + (g >> 1)];
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bn[h][q] = wrow[q][(kn >> 5) + 2 * h + (g >> 1)];
         }
-        v4i bx[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) bx[q] = expand_signs(bw[q] >> (16 * (g & 1)));
         const int8_t* la = lds_a[cur];
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            const v4i a = *reinterpret_cast<const v4i*>(la + roff[f]);
+        for (int h = 0; h < 2; ++h) {
+            v4i bx[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                acc[f][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx[q], acc[f][q], 0, 0, 0);
+            for (int q = 0; q < 4; ++q) bx[q] = expand_signs(bw[h][q] >> (16 * (g & 1)));
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                const v4i a = *reinterpret_cast<const v4i*>(la + roff[h][f]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[f][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx[q], acc[f][q], 0, 0, 0);
+            }
         }
+        __builtin_amdgcn_sched_barrier(0);         // the step's MFMAs stay ahead of the waits below
         if (more) {
+            __builtin_amdgcn_s_waitcnt(0);        // the prefetched A pieces are in LDS
 #pragma unroll
-            for (int i = 0; i < kAPieces; ++i) *reinterpret_cast<v4i*>(&lds_a[cur ^ 1][woff[i]]) = ar[i];
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bw[q] = bn[q];
+                for (int q = 0; q < 4; ++q) {
+                    asm volatile("" : : "v"(bn[h][q]));
+                    bw[h][q] = bn[h][q];
+                }
         }
         __syncthreads();
-    }
+    };
+    // steps whose successor lies wholly inside K prefetch straight into LDS;
+    // the prefetch of the step holding the end of the row is masked
+    int s = 0;
+    for (; s + 1 < full_steps; ++s) kstep(s, std::true_type{});
+    for (; s < steps; ++s) kstep(s, std::false_type{});
 
     // epilogue: lane holds rows 4g + r of each 16-row fragment, column r16
 #pragma unroll
