@@ -42,6 +42,7 @@ constexpr int kThreads = 256;
 constexpr int kBM = 256, kBN = 128, kKS = 128;   // kKS: two MFMA k-widths per step
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 // 16 bytes of an int8 row starting at k (a multiple of 16); bytes at k >= K
 // read as 0.  A piece that starts below K ends at or below the row stride
@@ -209,7 +210,57 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
     for (; s + 1 < full_steps; ++s) kstep(s, std::true_type{});
     for (; s < steps; ++s) kstep(s, std::false_type{});
 
-    // epilogue: lane holds rows 4g + r of each 16-row fragment, column r16
+    // Epilogue.  Full tiles with 16-byte aligned output rows go through LDS
+    // (the A buffers are free now): in two passes of 4 fragment rows, each
+    // wave parks its 64 x 64 int32 block (16 KiB; column c of row r at word
+    // r * 64 + (c ^ 16 ((r / 4) % 4)), so the 4 lane groups of a fragment
+    // write disjoint 16-bank groups) and reads it back as 16-byte row
+    // pieces, so every store instruction writes 4 whole 256-byte row
+    // segments.  Other tiles store element by element.
+    const bool full = m_blk + kBM <= M && n_blk + kBN <= N &&
+                      (!(e.flags & EPI_DOT) || ((reinterpret_cast<uintptr_t>(e.D) & 15u) == 0 && e.ldD % 4 == 0)) &&
+                      (!(e.flags & EPI_SCALE) || ((reinterpret_cast<uintptr_t>(e.Y) & 15u) == 0 && e.ldY % 4 == 0));
+    if (full) {
+        int32_t* park = reinterpret_cast<int32_t*>(&lds_a[0][0]) + wave * (64 * 64);   // 4 x 16 KiB = both A buffers
+        const int pc = 4 * (lane & 15);            // read-back: 4 columns of row lane/16 (+4 per pass)
+        float an[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (e.flags & EPI_SCALE) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                an[c] = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : n_blk + wn * 64 + pc + c];
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        park[(16 * f + 4 * g + r) * 64 + ((16 * q + r16) ^ (16 * g))] = acc[4 * half + f][q][r];
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                const int row = 4 * p + (lane >> 4);
+                const v4i d = *reinterpret_cast<const v4i*>(&park[row * 64 + (pc ^ (16 * ((row >> 2) & 3)))]);
+                const int64_t m = m_blk + wm * 128 + 64 * half + row;
+                const int n = n_blk + wn * 64 + pc;
+                if (e.flags & EPI_DOT)
+                    __builtin_nontemporal_store(d, reinterpret_cast<v4i*>(e.D + m * e.ldD + n));
+                if (e.flags & EPI_SCALE) {
+                    v4f y = {an[0] * (float)d[0], an[1] * (float)d[1], an[2] * (float)d[2], an[3] * (float)d[3]};
+                    if (e.xscale) {
+                        const float xs = e.xscale[m];
+                        y[0] = y[0] * xs; y[1] = y[1] * xs; y[2] = y[2] * xs; y[3] = y[3] * xs;
+                    }
+                    __builtin_nontemporal_store(y, reinterpret_cast<v4f*>(e.Y + m * e.ldY + n));
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        return;
+    }
+    // lane holds rows 4g + r of each 16-row fragment, column r16
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int n = n_blk + wn * 64 + 16 * q + r16;
