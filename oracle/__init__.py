@@ -91,6 +91,9 @@ def _configure(L):
         "oracle_pack_planes_i8": [_p, _i64, _i64, _p, _i64, _p],
         "oracle_scale_i8": [_p, _p, _i64, _p, _i64, _i64, _p],
         "oracle_scale_bias_residual": [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _p],
+        "oracle_ternary_threshold": [_p, _i64, _i64, _i64, ctypes.c_float, _p],
+        "oracle_ternary_roundclip": [_p, _i64, _i64, _i64, ctypes.c_float, _p],
+        "oracle_pack_ternary": [_p, _i64, _i64, _i64, _p, _p, _p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -383,3 +386,41 @@ def conv_block(X: np.ndarray, W_ohwi: np.ndarray):
     D = dot(im2col_signs(X), sign(Wf))
     R = X.reshape(B * H * Wd, C)
     return D, scale_residual(D, a, R), a
+
+
+def ternary_threshold(W: np.ndarray, delta: float) -> np.ndarray:
+    """Eq. (7): +1 for w > Delta, -1 for w < -Delta, else 0 (int8 [N, K])."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    T = np.empty((N, K), dtype=np.int8)
+    lib().oracle_ternary_threshold(_ptr(W), N, K, K, ctypes.c_float(float(delta)), _ptr(T))
+    return T
+
+
+def ternary_roundclip(W: np.ndarray, gamma: float) -> np.ndarray:
+    """Eq. (9): RoundClip(W / gamma, -1, 1) (int8 [N, K])."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    T = np.empty((N, K), dtype=np.int8)
+    lib().oracle_ternary_roundclip(_ptr(W), N, K, K, ctypes.c_float(float(gamma)), _ptr(T))
+    return T
+
+
+def pack_ternary(T: np.ndarray, ld: int | None = None):
+    """Sign plane, nonzero plane (uint32 [N, ld] each) and nonzero counts [N]."""
+    T = _c(T, np.int8)
+    N, K = T.shape
+    kw = (K + 31) // 32
+    ld = kw if ld is None else ld
+    assert ld >= kw
+    S = np.empty((N, ld), dtype=np.uint32)
+    Z = np.empty((N, ld), dtype=np.uint32)
+    nnz = np.empty(N, dtype=np.int32)
+    lib().oracle_pack_ternary(_ptr(T), N, K, ld, _ptr(S), _ptr(Z), _ptr(nnz))
+    return S, Z, nnz
+
+
+def ternary_b158(W: np.ndarray):
+    """BitNet b1.58 weights (eq. (9)): (T int8 [N, K], gamma)."""
+    g = alpha_tensor(W)
+    return ternary_roundclip(W, g), g

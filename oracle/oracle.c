@@ -27,6 +27,8 @@
  *  [P4] "State of the Art Survey", Bi-Real Net row: FP residual shortcut.
  *  [P5] "BitNet: 1-bit Transformer": activations kept at INT8 next to binary
  *       weights; eq. (8) (one mean-|W| scale for the whole matrix).
+ *  [P5] "Ternary Quantization" eq. (7) (threshold Delta) and "BitNet b1.58"
+ *       eq. (9) (RoundClip(W / gamma, -1, 1), gamma = ||W||_1 / (nm)).
  */
 #include <math.h>
 #include <omp.h>
@@ -231,9 +233,10 @@ API void oracle_dense_pm1_f32out(const int8_t* s, const float* W, int64_t ldw,
 /* [P5] "Binary Neural Networks" eq. (1)-(2) (binary weights times real
  * activations: only additions and subtractions) with the activations
  * quantized to 8-bit integers as in the BitNet section of [P5]:
- * D[m, n] = sum_k x[m, k] * s[n, k] for int8 x and +1/-1 signs s, an exact
- * integer multiply-add (|D| <= 128 K fits int32 for K <= 2^24).  xq is
- * [M, K] (dense), ws is [N, K] (+1/-1), D is [M, N]. */
+ * D[m, n] = sum_k x[m, k] * s[n, k], an exact integer multiply-add over int8
+ * values (|D| <= 128 K fits int32 for K <= 2^24).  The weights s are +1/-1
+ * (binary) or -1/0/+1 (ternary, eq. (7) / (9)); the activations are int8
+ * codes or +1/-1 signs.  xq is [M, K] (dense), ws is [N, K], D is [M, N]. */
 API void oracle_dot_i8(const int8_t* xq, const int8_t* ws, int64_t M, int64_t N, int64_t K, int32_t* D)
 {
     #pragma omp parallel for schedule(static)
@@ -344,6 +347,60 @@ API void oracle_scale_bias_residual(const int32_t* D, const float* alpha, int64_
             float zb = z + bias[n];
             Y[m * N + n] = R ? zb + R[m * ldr + n] : zb;
         }
+}
+
+/* [P5] eq. (7): t = +1 for w > Delta, -1 for w < -Delta, 0 for |w| <= Delta.
+ * The comparisons are IEEE single; a NaN satisfies none of the three cases
+ * and is read as 0 (t = (w > Delta) - (w < -Delta)).  T is dense [N, K]. */
+API void oracle_ternary_threshold(const float* W, int64_t N, int64_t K, int64_t ldw, float delta, int8_t* T)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            float w = W[n * ldw + k];
+            T[n * K + k] = (int8_t)((w > delta) - (w < -delta));
+        }
+}
+
+/* [P5] eq. (9): t = RoundClip(w / gamma, -1, 1) = max(-1, min(1, round(w / gamma))),
+ * with w / gamma one IEEE single division and round() to nearest, ties to
+ * even (rintf); a NaN quotient (gamma = 0 with w = 0, or a NaN weight) gives 0. */
+API void oracle_ternary_roundclip(const float* W, int64_t N, int64_t K, int64_t ldw, float gamma, int8_t* T)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            float r = rintf(W[n * ldw + k] / gamma);
+            int8_t t;
+            if (isnan(r)) t = 0;
+            else if (r > 1.0f) t = 1;
+            else if (r < -1.0f) t = -1;
+            else t = (int8_t)r;
+            T[n * K + k] = t;
+        }
+}
+
+/* Two-plane storage of ternary rows (a storage convention): in the sign plane
+ * S a bit is 1 where t = -1; in the nonzero plane Z a bit is 1 where t != 0;
+ * element k sits in word k / 32 at bit k % 32 of row n (row stride ld); pad
+ * bits and pad words are 0 in both planes.  nnz[n] = number of nonzero t. */
+API void oracle_pack_ternary(const int8_t* T, int64_t N, int64_t K, int64_t ld,
+                             uint32_t* S, uint32_t* Z, int32_t* nnz)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        int32_t cnt = 0;
+        for (int64_t w = 0; w < ld; ++w) { S[n * ld + w] = 0u; Z[n * ld + w] = 0u; }
+        for (int64_t k = 0; k < K; ++k) {
+            int8_t t = T[n * K + k];
+            if (t != 0) {
+                Z[n * ld + k / 32] |= (uint32_t)1u << (k % 32);
+                ++cnt;
+            }
+            if (t == -1) S[n * ld + k / 32] |= (uint32_t)1u << (k % 32);
+        }
+        nnz[n] = cnt;
+    }
 }
 
 /* Number of OpenMP threads the routines above use (for reporting). */

@@ -102,6 +102,19 @@ MUTATIONS = [
      "float zb = z + bias[n];", "float zb = alpha[n * alpha_stride] * ((float)D[m * N + n] + bias[n]);"),
     ("bias: indexed by activation row",
      "float zb = z + bias[n];", "float zb = z + bias[m % N];"),
+    ("ternary threshold: ties at Delta kept nonzero",
+     "T[n * K + k] = (int8_t)((w > delta) - (w < -delta));",
+     "T[n * K + k] = (int8_t)((w >= delta) - (w <= -delta));"),
+    ("ternary RoundClip: truncation",
+     "float r = rintf(W[n * ldw + k] / gamma);", "float r = truncf(W[n * ldw + k] / gamma);"),
+    ("ternary RoundClip: ties away from zero",
+     "float r = rintf(W[n * ldw + k] / gamma);", "float r = roundf(W[n * ldw + k] / gamma);"),
+    ("ternary RoundClip: scaled by gamma instead of divided",
+     "float r = rintf(W[n * ldw + k] / gamma);", "float r = rintf(W[n * ldw + k] * gamma);"),
+    ("ternary pack: sign bit set for +1",
+     "if (t == -1) S[n * ld + k / 32]", "if (t == 1) S[n * ld + k / 32]"),
+    ("ternary pack: zeros counted as nonzero",
+     "if (t != 0) {\n                Z[n * ld + k / 32]", "if (t != 2) {\n                Z[n * ld + k / 32]"),
 ]
 
 

@@ -598,3 +598,96 @@ def test_scale_bias_residual_roundings():
                     if RR is not None:
                         z = round_to_f32(Fraction(float(z)) + Fraction(float(RR[m, n])))
                     assert f32_bits(Y[m, n]) == f32_bits(z)
+
+
+# ---------------------------------------------------------------- ternary weights
+# Page "Extreme Quantization": "Ternary Quantization" eq. (7) and "BitNet
+# b1.58" eq. (9).
+def test_ternary_threshold_cases():
+    d = np.float32(0.25)
+    up = np.nextafter(d, np.float32(1))
+    W = np.array([[0.25, -0.25, up, -up, 0.0, -0.0, 1e-30, np.nan, np.inf, -np.inf, 3.0, -3.0]], np.float32)
+    assert oracle.ternary_threshold(W, d)[0].tolist() == [0, 0, 1, -1, 0, 0, 0, 0, 1, -1, 1, -1]
+    # Delta = 0 reduces to the sign with 0 kept as 0
+    rng = np.random.default_rng(80)
+    W = workloads.normal_f32(80001, (5, 300))
+    np.testing.assert_array_equal(oracle.ternary_threshold(W, 0.0), np.sign(W).astype(np.int8))
+    # huge Delta: everything is 0
+    assert not oracle.ternary_threshold(W, 1e30).any()
+    del rng
+
+
+def test_ternary_roundclip_exact_rounding():
+    # gamma a power of two makes w / gamma exact: ties at .5 go to even
+    g = np.float32(0.5)
+    W = np.array([[0.25, -0.25, 0.75, -0.75, 0.2499999, 0.2500001, 0.0, 100.0, -100.0, np.nan]], np.float32)
+    assert oracle.ternary_roundclip(W, g)[0].tolist() == [0, 0, 1, -1, 0, 1, 0, 1, -1, 0]
+    # random weights: equal to the exactly rounded quotient wherever it is
+    # not within a few ulps of a .5 tie
+    W = workloads.normal_f32(81001, (6, 400))
+    gam = oracle.alpha_tensor(W)
+    T = oracle.ternary_roundclip(W, gam)
+    G = Fraction(float(gam))
+    for n in range(W.shape[0]):
+        for k in range(W.shape[1]):
+            q = Fraction(float(W[n, k])) / G
+            fl = math.floor(q)
+            fr = q - fl
+            if abs(fr - Fraction(1, 2)) < Fraction(1, 10**6):
+                continue
+            r = fl + 1 if fr > Fraction(1, 2) else fl
+            assert int(T[n, k]) == max(-1, min(1, r)), (n, k)
+
+
+def test_ternary_b158_gamma_is_tensor_mean_and_delta_relation():
+    W = workloads.normal_f32(82001, (4, 1000))
+    T, g = oracle.ternary_b158(W)
+    exact = sum((Fraction(float(abs(v))) for v in W.ravel()), Fraction(0)) / W.size
+    assert f32_bits(g) == f32_bits(round_to_f32(exact))
+    # away from the rounding boundary, RoundClip(w / gamma) is eq. (7) with Delta = gamma / 2
+    T7 = oracle.ternary_threshold(W, np.float32(g) / np.float32(2))
+    far = np.abs(np.abs(W.astype(np.float64)) / float(g) - 0.5) > 1e-5
+    np.testing.assert_array_equal(T[far], T7[far])
+    # roughly the familiar share of zeros for a Gaussian at Delta = 0.4 sigma (~31%)
+    assert 0.2 < (T == 0).mean() < 0.45
+
+
+def test_pack_ternary_layout_and_roundtrip():
+    T = np.array([[1, -1, 0, 0, 0, 0, 1, -1]], np.int8)
+    S, Z, nnz = oracle.pack_ternary(T, ld=2)
+    assert S.tolist() == [[0b10000010, 0]] and Z.tolist() == [[0b11000011, 0]] and nnz.tolist() == [4]
+    rng = np.random.default_rng(83)
+    for K in (1, 31, 32, 33, 100, 1000):
+        T = rng.integers(-1, 2, size=(4, K)).astype(np.int8)
+        S, Z, nnz = oracle.pack_ternary(T, ld=(K + 31) // 32 + 1)
+        sb = ((S[..., None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(4, -1).astype(np.int64)
+        zb = ((Z[..., None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(4, -1).astype(np.int64)
+        back = zb * (1 - 2 * sb)
+        np.testing.assert_array_equal(back[:, :K], T.astype(np.int64))
+        assert not sb[:, K:].any() and not zb[:, K:].any()
+        assert (sb <= zb).all()                      # a sign bit only where nonzero
+        np.testing.assert_array_equal(nnz, (T != 0).sum(axis=1))
+
+
+def test_ternary_dot_identities():
+    # integer multiply-add vs numpy, and the two packed identities the GPU uses:
+    #  binary x: sum t x = nnz - 2 popcount((xbits ^ S) & Z)
+    #  int8 x:   sum t q = sum_b c_b (popc(P_b & Z) - 2 popc(P_b & Z & S))
+    rng = np.random.default_rng(84)
+    c = np.array([1, 2, 4, 8, 16, 32, 64, -128], np.int64)
+    for K in (7, 64, 1000):
+        T = rng.integers(-1, 2, size=(6, K)).astype(np.int8)
+        xs = _rand_signs(rng, (5, K))
+        Q = rng.integers(-128, 128, size=(5, K)).astype(np.int8)
+        D1 = oracle.dot_i8(xs, T)
+        D2 = oracle.dot_i8(Q, T)
+        np.testing.assert_array_equal(D1.astype(np.int64), xs.astype(np.int64) @ T.astype(np.int64).T)
+        np.testing.assert_array_equal(D2.astype(np.int64), Q.astype(np.int64) @ T.astype(np.int64).T)
+        S, Z, nnz = oracle.pack_ternary(T)
+        xp = oracle.pack_signs(xs)
+        pc = np.bitwise_count((xp[:, None, :] ^ S[None]) & Z[None]).sum(axis=-1, dtype=np.int64)
+        np.testing.assert_array_equal(nnz[None, :].astype(np.int64) - 2 * pc, D1.astype(np.int64))
+        P, _ = oracle.pack_planes_i8(Q)
+        a = np.bitwise_count(P[:, None, :, :] & Z[None, :, None, :]).sum(axis=-1, dtype=np.int64)
+        b = np.bitwise_count(P[:, None, :, :] & (Z & S)[None, :, None, :]).sum(axis=-1, dtype=np.int64)
+        np.testing.assert_array_equal(((a - 2 * b) * c).sum(axis=-1), D2.astype(np.int64))
