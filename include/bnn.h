@@ -75,6 +75,10 @@ typedef enum bnn_status {
 #define BNN_EPI_THRESH_PACK  8u /* Op bit (m,n) = ((float)(dir[n]*D) >= tau[n]) ? 0 : 1  */
 #define BNN_EPI_ALPHA_TENSOR 16u /* with SCALE: one scale alpha[0] for every n  [P5] eq. (8) */
 #define BNN_EPI_BIAS_F32     32u /* with SCALE: + bias[n] after the scale, before R  [P2]  */
+/* Weight-format flag (OR it into the same field): ternary weights {-1,0,+1},
+ * [P5] "Ternary Quantization" eq. (7) / "BitNet b1.58" eq. (9), stored as
+ * the sign plane Wp and the nonzero plane Zp of bnn_pack_weights_ternary.  */
+#define BNN_W_TERNARY        64u
 
 /* Longest row of the INT8-activation calls: |D| <= 128 K stays exact in fp32. */
 #define BNN_MAX_K_I8 ((int64_t)1 << 17)
@@ -107,6 +111,8 @@ typedef struct bnn_fused_args {
     uint32_t* Op; int64_t ldOp;       /* THRESH_PACK: packed [M, ldOp],
                                          ldOp >= ceil(N/32); pad bits/words 0   */
     const float* bias;                /* BIAS_F32: fp32 [N]                     */
+    const uint32_t* Zp;               /* W_TERNARY: nonzero plane [N, ldWp]     */
+    const int32_t* nnz;               /* W_TERNARY: nonzero count per row [N]   */
 } bnn_fused_args;
 
 /* Arguments of bnn_bwn_i8_linear (binary weights x INT8 activations).  Host
@@ -130,6 +136,7 @@ typedef struct bnn_i8_args {
     int32_t* D; int64_t ldD;          /* DOT_I32: int32 [M, ldD], ldD >= N      */
     const float* alpha;               /* SCALE: fp32 [N] (or [1], ALPHA_TENSOR) */
     float* Y; int64_t ldY;            /* SCALE: fp32 [M, ldY], ldY >= N         */
+    const uint32_t* Zp;               /* W_TERNARY: nonzero plane [N, ldWp]     */
 } bnn_i8_args;
 
 /* Number of 32-bit words that carry K packed bits: ceil(K/32); -1 if K < 0. */
@@ -191,6 +198,8 @@ bnn_status bnn_xnor_gemm(const uint32_t* Xp, int64_t ldXp,
  *               layer (its K is N).  Bits n >= N and words ceil(N/32)..ldOp-1
  *               are written as 0.  tau/dir come from
  *               bnn_fold_bn_thresholds_host.
+ *  W_TERNARY    the weights are ternary (Wp = sign plane, Zp, nnz): every
+ *               epilogue above uses D = nnz[n] - 2 popcount((x ^ S) & Z)
  *  ALPHA_TENSOR with SCALE_F32: alpha[0] scales every column, the single
  *               scale ||W||_1 / (nm) of [P5] eq. (8) (bnn_weight_scale_tensor)
  *  BIAS_F32     with SCALE_F32: Y = fl32(fl32(alpha * D) + bias[n]), then
@@ -199,6 +208,27 @@ bnn_status bnn_xnor_gemm(const uint32_t* Xp, int64_t ldXp,
  * Errors: RESIDUAL, BIAS or ALPHA_TENSOR without SCALE, no flag, or unknown
  * flag bits -> BNN_ERR_UNSUPPORTED. */
 bnn_status bnn_linear_fused(const bnn_fused_args* args, bnn_stream_t stream);
+
+/* Ternary weights, [P5] "Ternary Quantization" eq. (7) and "BitNet b1.58"
+ * eq. (9), packed as two planes with the packed layout above:
+ *     gamma != NULL:  t = RoundClip(W / gamma[0], -1, 1)   (eq. (9): one IEEE
+ *                     single division, round half to even; NaN -> 0); gamma
+ *                     is device memory, normally ||W||_1 / (nm) from
+ *                     bnn_weight_scale_tensor
+ *     gamma == NULL:  t = +1 if W > delta, -1 if W < -delta, else 0 (eq. (7);
+ *                     NaN -> 0)
+ *  Sp   sign plane    [N, ld]: bit 1 where t = -1
+ *  Zp   nonzero plane [N, ld]: bit 1 where t != 0
+ *  nnz  int32 [N]: number of nonzero t per row
+ *  (pad bits and pad words 0 in both planes; both 16-byte aligned, ld % 4
+ *  == 0, ld >= ceil(K/32)).  The dot products then follow from
+ *     binary x: D = nnz[n] - 2 popcount((x ^ S) & Z)
+ *     int8 q:   D = sum_b c_b (popcount(P_b & Z) - 2 popcount(P_b & Z & S))
+ *  W fp32 [N, ldW], ldW >= K.  Errors as for bnn_pack_weights. */
+bnn_status bnn_pack_weights_ternary(const float* W, int64_t N, int64_t K, int64_t ldW,
+                                    const float* gamma, float delta,
+                                    uint32_t* Sp, uint32_t* Zp, int64_t ld, int32_t* nnz,
+                                    bnn_stream_t stream);
 
 /* One scale for the whole weight matrix, [P5] eq. (8):
  *     alpha[0] = fl32( (sum_{n,k} |W[n,k]|) / (N*K) )
@@ -243,12 +273,14 @@ bnn_status bnn_pack_act_i8(const int8_t* Xq, int64_t M, int64_t K, int64_t ldXq,
  *     Y[m,n] = fl32( fl32(alpha_n * (float)D) * xscale[m] )   (xscale given)
  *            = fl32( alpha_n * (float)D )                      (xscale NULL)
  *  alpha_n = alpha[n], or alpha[0] with BNN_EPI_ALPHA_TENSOR.
- *  Path: M <= 2 with Xb and xsum given, and ceil(ceil(K/32)/4) <= 256/M
- *  (K <= 32768 for one row, 16384 for two): the bit-plane streaming
- *  GEMV (the batch-1 decode case of [P2] "Bandwidth math"); otherwise the
- *  int8 MFMA GEMM, which needs Xq.  Flags other than DOT_I32, SCALE_F32 and
- *  ALPHA_TENSOR -> BNN_ERR_UNSUPPORTED; neither usable activation form ->
- *  BNN_ERR_NULL. */
+ *  With BNN_W_TERNARY the weights are ternary (Wp = sign plane, Zp) and
+ *  s(n,k) is -1, 0 or +1; xsum is then not needed.
+ *  Path: M <= 2 with Xb (and xsum, for binary weights) given, and
+ *  ceil(ceil(K/32)/4) <= 256/M (K <= 32768 for one row, 16384 for two): the
+ *  bit-plane streaming GEMV (the batch-1 decode case of [P2] "Bandwidth
+ *  math"); otherwise the int8 MFMA GEMM, which needs Xq.  Flags other than
+ *  DOT_I32, SCALE_F32, ALPHA_TENSOR and W_TERNARY -> BNN_ERR_UNSUPPORTED;
+ *  neither usable activation form -> BNN_ERR_NULL. */
 bnn_status bnn_bwn_i8_linear(const bnn_i8_args* args, bnn_stream_t stream);
 
 /* Fold inference BatchNorm of z = alpha[n] * D followed by sign into the

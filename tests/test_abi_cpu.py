@@ -135,6 +135,12 @@ def _fused(**kw):
     (dict(epilogue=34, Y=A16, ldY=40, alpha=A16), ERR_NULL),                       # bias pointer missing
     (dict(epilogue=34, Y=A16, ldY=40, alpha=A16, bias=A2), ERR_ALIGN),
     (dict(epilogue=18, Y=A16, ldY=40, alpha=A2), ERR_ALIGN),                       # per-tensor alpha, misaligned
+    (dict(epilogue=65), ERR_NULL),                                                 # ternary without Zp
+    (dict(epilogue=65, Zp=A16), ERR_NULL),                                         # ternary without nnz
+    (dict(epilogue=65, Zp=A4, nnz=A16), ERR_ALIGN),
+    (dict(epilogue=65, Zp=A16, nnz=A2), ERR_ALIGN),
+    (dict(epilogue=64), ERR_UNSUPPORTED),                                          # a format flag is no output
+    (dict(epilogue=128), ERR_UNSUPPORTED),
 ])
 def test_linear_fused_validation(L, kw, want):
     a = _fused(**kw)
@@ -180,6 +186,10 @@ def _i8(**kw):
     (dict(epilogue=18, Y=A16, ldY=40, alpha=A16), OK),
     (dict(epilogue=2, Y=A16, ldY=39, alpha=A16), ERR_LD),
     (dict(xscale=A2), ERR_ALIGN),
+    (dict(epilogue=65), ERR_NULL),                                  # ternary without Zp
+    (dict(epilogue=65, Zp=A4), ERR_ALIGN),
+    (dict(epilogue=65, Zp=A16, xsum=0), OK),                        # ternary planes need no row sums
+    (dict(epilogue=1, xsum=0), ERR_NULL),                           # binary planes do
 ])
 def test_bwn_i8_validation(L, kw, want):
     a = _i8(**kw)
@@ -212,6 +222,20 @@ def test_i8_activation_writers_validation(L):
     assert s(A16, 4, 100, 100, 0, A16, None) == ERR_NULL
     assert s(A16, 4, 100, 99, A16, A16, None) == ERR_LD
     assert s(A16, 4, 100, 100, A4, A16, None) == ERR_ALIGN
+
+
+def test_pack_weights_ternary_validation(L):
+    p = L.bnn_pack_weights_ternary          # W, N, K, ldW, gamma, delta, Sp, Zp, ld, nnz
+    f = ctypes.c_float(0.5)
+    assert p(A16, 0, 64, 64, None, f, A16, A16, 4, A16, None) == OK
+    assert p(0, 4, 64, 64, None, f, A16, A16, 4, A16, None) == ERR_NULL
+    assert p(A16, 4, 64, 64, None, f, A16, 0, 4, A16, None) == ERR_NULL
+    assert p(A16, 4, 64, 64, None, f, A16, A16, 4, 0, None) == ERR_NULL
+    assert p(A16, 4, 64, 63, None, f, A16, A16, 4, A16, None) == ERR_LD
+    assert p(A16, 4, 200, 200, None, f, A16, A16, 4, A16, None) == ERR_LD     # ld < ceil(200/32)
+    assert p(A16, 4, 64, 64, None, f, A4, A16, 4, A16, None) == ERR_ALIGN
+    assert p(A16, 4, 64, 64, A2, f, A16, A16, 4, A16, None) == ERR_ALIGN
+    assert p(A16, 4, 0, 64, None, f, A16, A16, 4, A16, None) == ERR_SHAPE
 
 
 def test_empty_calls_launch_nothing(L):

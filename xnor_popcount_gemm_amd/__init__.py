@@ -26,6 +26,7 @@ __all__ = [
     "dense_binact_f32", "EPI_DOT_I32", "EPI_SCALE_F32", "EPI_RESIDUAL_F32",
     "EPI_THRESH_PACK", "EPI_ALPHA_TENSOR", "EPI_BIAS_F32", "LIB_PATH",
     "weight_scale_tensor", "quantize_act_i8", "pack_act_i8", "bwn_i8_linear", "MAX_K_I8",
+    "W_TERNARY", "pack_weights_ternary",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbnn.so")
@@ -36,6 +37,7 @@ EPI_RESIDUAL_F32 = 4
 EPI_THRESH_PACK = 8
 EPI_ALPHA_TENSOR = 16
 EPI_BIAS_F32 = 32
+W_TERNARY = 64
 MAX_K_I8 = 1 << 17
 
 _STATUS = {
@@ -67,6 +69,7 @@ class _FusedArgs(ctypes.Structure):
         ("tau", ctypes.c_void_p), ("dir", ctypes.c_void_p),
         ("Op", ctypes.c_void_p), ("ldOp", ctypes.c_int64),
         ("bias", ctypes.c_void_p),
+        ("Zp", ctypes.c_void_p), ("nnz", ctypes.c_void_p),
     ]
 
 
@@ -82,6 +85,7 @@ class _I8Args(ctypes.Structure):
         ("D", ctypes.c_void_p), ("ldD", ctypes.c_int64),
         ("alpha", ctypes.c_void_p),
         ("Y", ctypes.c_void_p), ("ldY", ctypes.c_int64),
+        ("Zp", ctypes.c_void_p),
     ]
 
 
@@ -115,6 +119,7 @@ def lib() -> ctypes.CDLL:
             "bnn_quantize_act_i8": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp],
             "bnn_pack_act_i8": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
             "bnn_bwn_i8_linear": [ctypes.POINTER(_I8Args), _vp],
+            "bnn_pack_weights_ternary": [_vp, _i64, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _i64, _vp, _vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -233,7 +238,7 @@ def xnor_gemm(Xp: torch.Tensor, Wp: torch.Tensor, K: int, *, alpha: torch.Tensor
 
 def linear_fused(Xp: torch.Tensor, Wp: torch.Tensor, K: int, epilogue: int, *,
                  alpha=None, R=None, tau=None, dir=None, D=None, Y=None, Op=None,
-                 bias=None, M: int | None = None):
+                 bias=None, Zp=None, nnz=None, M: int | None = None):
     """XNOR-popcount GEMM with a fused epilogue (OR of EPI_* flags).
 
     Returns a dict with the outputs the flags ask for: ``D`` (int32 [M, N]),
@@ -271,6 +276,10 @@ def linear_fused(Xp: torch.Tensor, Wp: torch.Tensor, K: int, epilogue: int, *,
         a.Op, a.ldOp = Op.data_ptr(), _ld(Op)
     if bias is not None:
         a.bias = bias.data_ptr()
+    if Zp is not None:
+        a.Zp = Zp.data_ptr()
+    if nnz is not None:
+        a.nnz = nnz.data_ptr()
     _check(lib().bnn_linear_fused(ctypes.byref(a), _stream(dev)), "bnn_linear_fused")
     return {"D": D, "Y": Y, "Op": Op}
 
@@ -366,7 +375,7 @@ def pack_act_i8(Xq: torch.Tensor):
 
 
 def bwn_i8_linear(Wp: torch.Tensor, K: int, epilogue: int, *, Xb=None, xsum=None, Xq=None,
-                  xscale=None, alpha=None, D=None, Y=None, M: int | None = None):
+                  xscale=None, alpha=None, D=None, Y=None, Zp=None, M: int | None = None):
     """Binary weights x INT8 activations: D = sum q * s (int32) and/or
     Y = alpha * D (* xscale) (fp32), from bit planes (GEMV, M <= 2) or int8
     rows (MFMA GEMM).  Returns a dict with ``D`` and ``Y``."""
@@ -399,5 +408,22 @@ def bwn_i8_linear(Wp: torch.Tensor, K: int, epilogue: int, *, Xb=None, xsum=None
         a.alpha = alpha.data_ptr()
     if Y is not None:
         a.Y, a.ldY = Y.data_ptr(), _ld(Y)
+    if Zp is not None:
+        a.Zp = Zp.data_ptr()
     _check(lib().bnn_bwn_i8_linear(ctypes.byref(a), _stream(dev)), "bnn_bwn_i8_linear")
     return {"D": D, "Y": Y}
+
+
+def pack_weights_ternary(W: torch.Tensor, *, gamma: torch.Tensor | None = None, delta: float = 0.0):
+    """Ternary weights as (sign plane Sp [N, ld], nonzero plane Zp [N, ld],
+    nnz int32 [N]): RoundClip(W / gamma) (eq. (9)) when ``gamma`` (a device
+    fp32 [1]) is given, else the threshold ``delta`` (eq. (7))."""
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    Sp = _packed_empty(N, K, W.device)
+    Zp = _packed_empty(N, K, W.device)
+    nnz = torch.empty(N, dtype=torch.int32, device=W.device)
+    _check(lib().bnn_pack_weights_ternary(_ptr(W), N, K, _ld(W), _ptr(gamma), ctypes.c_float(float(delta)),
+                                          _ptr(Sp), _ptr(Zp), _ld(Sp), _ptr(nnz), _stream(W.device)),
+           "bnn_pack_weights_ternary")
+    return Sp, Zp, nnz

@@ -47,7 +47,7 @@ bnn_status validate_fused(const bnn_fused_args* a) {
     if (((a->M + 255) / 256) * ((a->N + 15) / 16) > ((int64_t)1 << 31) - 1) return BNN_ERR_SHAPE;
     const uint32_t f = a->epilogue;
     const uint32_t known = BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32 | BNN_EPI_RESIDUAL_F32 | BNN_EPI_THRESH_PACK |
-                           BNN_EPI_ALPHA_TENSOR | BNN_EPI_BIAS_F32;
+                           BNN_EPI_ALPHA_TENSOR | BNN_EPI_BIAS_F32 | BNN_W_TERNARY;
     if ((f & ~known) != 0) return BNN_ERR_UNSUPPORTED;
     if (!(f & (BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32 | BNN_EPI_THRESH_PACK))) return BNN_ERR_UNSUPPORTED;
     if ((f & (BNN_EPI_RESIDUAL_F32 | BNN_EPI_ALPHA_TENSOR | BNN_EPI_BIAS_F32)) && !(f & BNN_EPI_SCALE_F32))
@@ -55,6 +55,11 @@ bnn_status validate_fused(const bnn_fused_args* a) {
     if (f & BNN_EPI_BIAS_F32) {
         if (!a->bias) return BNN_ERR_NULL;
         if (misaligned4(a->bias)) return BNN_ERR_ALIGN;
+    }
+    if (f & BNN_W_TERNARY) {
+        if ((st = check_packed(a->Zp, a->K, a->ldWp)) != BNN_OK) return st;
+        if (!a->nnz) return BNN_ERR_NULL;
+        if (misaligned4(a->nnz)) return BNN_ERR_ALIGN;
     }
     if ((st = check_packed(a->Xp, a->K, a->ldXp)) != BNN_OK) return st;
     if ((st = check_packed(a->Wp, a->K, a->ldWp)) != BNN_OK) return st;
@@ -99,6 +104,7 @@ bnn_status run_fused(const bnn_fused_args* a, hipStream_t s) {
     e.tau = a->tau; e.dir = a->dir;
     e.Op = a->Op; e.ldOp = a->ldOp;
     e.bias = a->bias;
+    e.Zp = a->Zp; e.nnz = a->nnz;
     if (bnn::gemv_eligible(a->M, a->K, e.flags))
         return from_hip(bnn::launch_xnor_gemv(a->Xp, a->ldXp, a->Wp, a->ldWp, a->M, a->N, a->K, e, s));
     return from_hip(bnn::launch_xnor_gemm(a->Xp, a->ldXp, a->Wp, a->ldWp, a->M, a->N, a->K, e, s));
@@ -116,7 +122,8 @@ bnn_status check_k_i8(int64_t K) {
 
 // Which kernel serves a bnn_i8_args call: 1 = bit-plane GEMV, 2 = MFMA GEMM.
 int i8_path(const bnn_i8_args* a) {
-    if (a->Xb && a->xsum && (a->M == 0 || bnn::i8_gemv_eligible(a->M, a->K))) return 1;
+    const bool tern = (a->epilogue & BNN_W_TERNARY) != 0;
+    if (a->Xb && (a->xsum || tern) && (a->M == 0 || bnn::i8_gemv_eligible(a->M, a->K))) return 1;
     if (a->Xq) return 2;
     return 0;
 }
@@ -129,15 +136,16 @@ bnn_status validate_i8(const bnn_i8_args* a) {
     if ((st = check_k_i8(a->K)) != BNN_OK) return st;
     if (((a->M + 127) / 128) * ((a->N + 127) / 128) > ((int64_t)1 << 31) - 1) return BNN_ERR_SHAPE;
     const uint32_t f = a->epilogue;
-    const uint32_t known = BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32 | BNN_EPI_ALPHA_TENSOR;
+    const uint32_t known = BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32 | BNN_EPI_ALPHA_TENSOR | BNN_W_TERNARY;
     if ((f & ~known) != 0 || !(f & (BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32))) return BNN_ERR_UNSUPPORTED;
+    if ((f & BNN_W_TERNARY) && (st = check_packed(a->Zp, a->K, a->ldWp)) != BNN_OK) return st;
     if ((f & BNN_EPI_ALPHA_TENSOR) && !(f & BNN_EPI_SCALE_F32)) return BNN_ERR_UNSUPPORTED;
     if ((st = check_packed(a->Wp, a->K, a->ldWp)) != BNN_OK) return st;
     const int path = i8_path(a);
     if (path == 0) return BNN_ERR_NULL;
     if (path == 1) {
         if ((st = check_packed(a->Xb, a->K, a->ldXb)) != BNN_OK) return st;
-        if (misaligned4(a->xsum)) return BNN_ERR_ALIGN;
+        if (a->xsum && misaligned4(a->xsum)) return BNN_ERR_ALIGN;
     } else {
         if ((st = check_i8_rows(a->Xq, a->K, a->ldXq)) != BNN_OK) return st;
         // the GEMM addresses activation rows with 32-bit byte offsets
@@ -253,6 +261,23 @@ bnn_status bnn_linear_fused(const bnn_fused_args* args, bnn_stream_t stream)
     return run_fused(args, as_stream(stream));
 }
 
+bnn_status bnn_pack_weights_ternary(const float* W, int64_t N, int64_t K, int64_t ldW,
+                                    const float* gamma, float delta,
+                                    uint32_t* Sp, uint32_t* Zp, int64_t ld, int32_t* nnz,
+                                    bnn_stream_t stream)
+{
+    bnn_status st;
+    if ((st = check_rows(N)) != BNN_OK) return st;
+    if ((st = check_k(K)) != BNN_OK) return st;
+    if (!W || !nnz) return BNN_ERR_NULL;
+    if ((st = check_packed(Sp, K, ld)) != BNN_OK) return st;
+    if ((st = check_packed(Zp, K, ld)) != BNN_OK) return st;
+    if (ldW < K) return BNN_ERR_LD;
+    if (misaligned4(W) || misaligned4(nnz) || (gamma && misaligned4(gamma))) return BNN_ERR_ALIGN;
+    if (N == 0) return BNN_OK;
+    return from_hip(bnn::launch_pack_ternary(W, N, K, ldW, gamma, delta, Sp, Zp, ld, nnz, as_stream(stream)));
+}
+
 bnn_status bnn_weight_scale_tensor(const float* W, int64_t N, int64_t K, int64_t ldW,
                                    double* work, float* alpha, bnn_stream_t stream)
 {
@@ -306,6 +331,7 @@ bnn_status bnn_bwn_i8_linear(const bnn_i8_args* args, bnn_stream_t stream)
     e.alpha = args->alpha;
     e.xscale = args->xscale;
     e.Y = args->Y; e.ldY = args->ldY;
+    e.Zp = args->Zp;
     hipStream_t s = as_stream(stream);
     if (i8_path(args) == 1)
         return from_hip(bnn::launch_bwn_i8_gemv(args->Xb, args->ldXb, args->xsum, args->Wp, args->ldWp,

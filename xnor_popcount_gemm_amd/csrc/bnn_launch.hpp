@@ -18,10 +18,12 @@ struct Epilogue {
     const float* tau; const int8_t* dir;
     uint32_t* Op; int64_t ldOp;
     const float* bias;       // [N] with EPI_BIAS
+    const uint32_t* Zp;      // ternary weights: nonzero plane (same ld as the sign plane Wp)
+    const int32_t* nnz;      // ternary weights: nonzero count per weight row
 };
 
 enum : uint32_t { EPI_DOT = 1u, EPI_SCALE = 2u, EPI_RESIDUAL = 4u, EPI_THRESH = 8u,
-                  EPI_ALPHA_TENSOR = 16u, EPI_BIAS = 32u };
+                  EPI_ALPHA_TENSOR = 16u, EPI_BIAS = 32u, W_TERNARY = 64u };
 
 // Epilogue of binary weights x INT8 activations.
 struct EpilogueI8 {
@@ -30,6 +32,7 @@ struct EpilogueI8 {
     const float* alpha;      // [N], or alpha[0] with EPI_ALPHA_TENSOR
     const float* xscale;     // [M] or nullptr
     float* Y; int64_t ldY;
+    const uint32_t* Zp;      // ternary weights (W_TERNARY): nonzero plane
 };
 
 hipError_t launch_pack_dense(const float* X, int64_t rows, int64_t K, int64_t ldX,
@@ -38,6 +41,12 @@ hipError_t launch_pack_dense(const float* X, int64_t rows, int64_t K, int64_t ld
 // alpha[0] = fl32(sum |W| / (N K)), fp64 sums; work holds N doubles.
 hipError_t launch_alpha_tensor(const float* W, int64_t N, int64_t K, int64_t ldW,
                                double* work, float* alpha, hipStream_t s);
+
+// Ternary weights as sign + nonzero planes and nonzero counts (gamma != nullptr:
+// RoundClip(w / gamma[0]); else the threshold delta).
+hipError_t launch_pack_ternary(const float* W, int64_t N, int64_t K, int64_t ldW, const float* gamma,
+                               float delta, uint32_t* S, uint32_t* Z, int64_t ld, int32_t* nnz,
+                               hipStream_t s);
 
 hipError_t launch_pack_im2col3x3(const float* X, int64_t B, int64_t H, int64_t W, int64_t C,
                                  uint32_t* P, int64_t ldP, hipStream_t s);

@@ -71,16 +71,20 @@ __device__ __forceinline__ void load_w(uint32_t (&w)[CP][KCC], cptr_u32 p, int64
 // MASK: only the first nvalid words are live (the K tail).  FULLN: every
 // column of the tile exists; otherwise columns past nlast re-read the last
 // weight row (their results are discarded).
-template <int TN, int KCC, int CP, bool FULLN, bool MASK>
+// TERN: ternary weights -- wbase rows are the sign plane, zbase rows (same
+// stride) the nonzero plane, and a word contributes popcount((a ^ s) & z).
+template <int TN, int KCC, int CP, bool FULLN, bool MASK, bool TERN>
 __device__ __forceinline__ void xnor_chunk(uint32_t (&acc)[TN], const uint32_t (&a)[KCC],
-                                           const uint32_t* __restrict__ wbase, int k0, int nvalid,
-                                           int64_t ldW, int nlast)
+                                           const uint32_t* __restrict__ wbase, const uint32_t* __restrict__ zbase,
+                                           int k0, int nvalid, int64_t ldW, int nlast)
 {
     int64_t ldw = ldW;
     asm volatile("" : "+s"(ldw));   // keep the TN row offsets out of the loop preheader
     const cptr_u32 p0 = (cptr_u32)(wbase + k0);
-    uint32_t wc[CP][KCC];
+    const cptr_u32 z0 = (cptr_u32)((TERN ? zbase : wbase) + k0);
+    uint32_t wc[CP][KCC], zc[CP][KCC];
     load_w<CP, KCC, FULLN, MASK>(wc, p0, ldw, 0, nlast, nvalid);
+    if (TERN) load_w<CP, KCC, FULLN, MASK>(zc, z0, ldw, 0, nlast, nvalid);
 #pragma unroll
     for (int j = 0; j < TN; j += CP) {
         // Consume the current set's scalar loads here (the counter wait lands
@@ -88,29 +92,41 @@ __device__ __forceinline__ void xnor_chunk(uint32_t (&acc)[TN], const uint32_t (
 #pragma unroll
         for (int c = 0; c < CP; ++c)
 #pragma unroll
-            for (int kk = 0; kk < KCC; ++kk) asm volatile("" : : "s"(wc[c][kk]));
-        uint32_t wn[CP][KCC];
-        if (j + CP < TN)
+            for (int kk = 0; kk < KCC; ++kk) {
+                asm volatile("" : : "s"(wc[c][kk]));
+                if (TERN) asm volatile("" : : "s"(zc[c][kk]));
+            }
+        uint32_t wn[CP][KCC], zn[CP][KCC];
+        if (j + CP < TN) {
             load_w<CP, KCC, FULLN, MASK>(wn, p0 + (FULLN ? (int64_t)(j + CP) * ldw : 0), ldw, j + CP, nlast, nvalid);
+            if (TERN)
+                load_w<CP, KCC, FULLN, MASK>(zn, z0 + (FULLN ? (int64_t)(j + CP) * ldw : 0), ldw, j + CP, nlast, nvalid);
+        }
         __builtin_amdgcn_sched_barrier(0);
         // word-outer, column-inner: CP independent accumulator chains interleave
 #pragma unroll
         for (int kk = 0; kk < KCC; ++kk)
 #pragma unroll
-            for (int c = 0; c < CP; ++c) acc[j + c] = popc_acc(a[kk] ^ wc[c][kk], acc[j + c]);
+            for (int c = 0; c < CP; ++c) {
+                const uint32_t t = TERN ? ((a[kk] ^ wc[c][kk]) & zc[c][kk]) : (a[kk] ^ wc[c][kk]);
+                acc[j + c] = popc_acc(t, acc[j + c]);
+            }
         if (j + CP < TN) {
 #pragma unroll
             for (int c = 0; c < CP; ++c)
 #pragma unroll
-                for (int kk = 0; kk < KCC; ++kk) wc[c][kk] = wn[c][kk];
+                for (int kk = 0; kk < KCC; ++kk) {
+                    wc[c][kk] = wn[c][kk];
+                    if (TERN) zc[c][kk] = zn[c][kk];
+                }
         }
     }
 }
 
-template <int TN, int KC, bool FULLN>
+template <int TN, int KC, bool FULLN, bool TERN>
 __device__ __forceinline__ void xnor_mainloop(uint32_t (&acc)[TN], const uint32_t* __restrict__ xrow,
-                                              const uint32_t* __restrict__ wbase, int Kw,
-                                              int64_t ldW, int nlast)
+                                              const uint32_t* __restrict__ wbase, const uint32_t* __restrict__ zbase,
+                                              int Kw, int64_t ldW, int nlast)
 {
     constexpr int CP = (TN >= 2) ? 2 : 1;
     const int kfull = (Kw / KC) * KC;
@@ -126,7 +142,7 @@ __device__ __forceinline__ void xnor_mainloop(uint32_t (&acc)[TN], const uint32_
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) asm volatile("" : : "v"(a[kk]));
         if (k0 + KC < kfull) load_granules(an, xrow + k0 + KC, KC / 4);
-        xnor_chunk<TN, KC, CP, FULLN, false>(acc, a, wbase, k0, KC, ldW, nlast);
+        xnor_chunk<TN, KC, CP, FULLN, false, TERN>(acc, a, wbase, zbase, k0, KC, ldW, nlast);
     }
     for (int k0 = kfull; k0 < Kw; k0 += 4) {     // 16-byte granules; rows hold ld >= roundup(Kw,4) words
         const int nvalid = min(4, Kw - k0);
@@ -134,7 +150,7 @@ __device__ __forceinline__ void xnor_mainloop(uint32_t (&acc)[TN], const uint32_
         load_granules(t, xrow + k0, 1);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) t[kk] = (kk < nvalid) ? t[kk] : 0u;
-        xnor_chunk<TN, 4, CP, FULLN, true>(acc, t, wbase, k0, nvalid, ldW, nlast);
+        xnor_chunk<TN, 4, CP, FULLN, true, TERN>(acc, t, wbase, zbase, k0, nvalid, ldW, nlast);
     }
 }
 
@@ -151,7 +167,15 @@ __device__ __forceinline__ bool aligned16(const void* p) {
 // so every store (and residual load) instruction covers 64*16/(CH*4) whole
 // row segments of CH*4 bytes.  Only full, 16-byte aligned tiles use it; LDS
 // is private to the wave (no workgroup barrier).
-template <int TN>
+// D of column j of a tile: K - 2 acc for binary weights, nnz[n] - 2 acc for
+// ternary ones (nnz is uniform across the wave: a scalar load).
+template <bool TERN>
+__device__ __forceinline__ int32_t dval(uint32_t acc, int K, const Epilogue& e, int n) {
+    const int32_t base = TERN ? (int32_t)((cptr_u32)(const uint32_t*)e.nnz)[n] : K;
+    return base - 2 * (int32_t)acc;
+}
+
+template <int TN, bool TERN>
 __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t* __restrict__ lds,
                                              int wrow0, int M, int n0, int K, const Epilogue& e)
 {
@@ -161,7 +185,7 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
 #pragma unroll
     for (int c0 = 0; c0 < TN; c0 += CH) {
 #pragma unroll
-        for (int j = 0; j < CH; ++j) lds[lane * (CH + 1) + j] = (uint32_t)(K - 2 * (int32_t)acc[c0 + j]);
+        for (int j = 0; j < CH; ++j) lds[lane * (CH + 1) + j] = (uint32_t)dval<TERN>(acc[c0 + j], K, e, n0 + c0 + j);
         // The residual and alpha pieces of all passes are requested before
         // any is used, so their latencies overlap instead of adding up.
         f32x4 rv[G4];
@@ -209,7 +233,7 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
     }
 }
 
-template <int TN, int KC, bool EPI_LDS, int WAVES>
+template <int TN, int KC, bool EPI_LDS, int WAVES, bool TERN>
 __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
     const uint32_t* __restrict__ Xp, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
     int M, int N, int K, int tiles_n, Epilogue e)
@@ -228,12 +252,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
     const int nlast = N - 1 - n0;                 // last live column of this tile
     const uint32_t* __restrict__ xrow = Xp + (int64_t)min(m, M - 1) * ldX;
     const uint32_t* __restrict__ wbase = Wp + (int64_t)n0 * ldW;
+    const uint32_t* __restrict__ zbase = TERN ? e.Zp + (int64_t)n0 * ldW : wbase;
 
     uint32_t acc[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[j] = 0u;
-    if (n0 + TN <= N) xnor_mainloop<TN, KC, true>(acc, xrow, wbase, Kw, ldW, nlast);
-    else              xnor_mainloop<TN, KC, false>(acc, xrow, wbase, Kw, ldW, nlast);
+    if (n0 + TN <= N) xnor_mainloop<TN, KC, true, TERN>(acc, xrow, wbase, zbase, Kw, ldW, nlast);
+    else              xnor_mainloop<TN, KC, false, TERN>(acc, xrow, wbase, zbase, Kw, ldW, nlast);
 
     const int ncols = min(TN, N - n0);
     const bool full = (ncols == TN);
@@ -243,7 +268,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
                                     ((e.flags & EPI_ALPHA_TENSOR) || aligned16(e.alpha)))) &&
         (!(e.flags & EPI_BIAS) || aligned16(e.bias)) &&
         (!(e.flags & EPI_RESIDUAL) || (aligned16(e.R) && e.ldR % 4 == 0))) {
-        epilogue_lds<TN>(acc, lds_epi + wave * kLdsWords, wrow0, M, n0, K, e);
+        epilogue_lds<TN, TERN>(acc, lds_epi + wave * kLdsWords, wrow0, M, n0, K, e);
         return;
     }
     if (m >= M) return;
@@ -263,7 +288,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
     for (int q = 0; q < TN / 4; ++q) {
         int32_t d[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = K - 2 * (int32_t)acc[4 * q + i];
+        for (int i = 0; i < 4; ++i) d[i] = dval<TERN>(acc[4 * q + i], K, e, n0 + min(4 * q + i, ncols - 1));
         if (e.flags & EPI_DOT) {
             if (vecD) *reinterpret_cast<int4*>(drow + 4 * q) = make_int4(d[0], d[1], d[2], d[3]);
             else {
@@ -310,7 +335,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
             for (int b = 0; b < WB; ++b) {
                 const int j = WB * q + b;
                 const int jj = min(j, ncols - 1);
-                const float v = (float)((int32_t)dir[jj] * (K - 2 * (int32_t)acc[j]));
+                const float v = (float)((int32_t)dir[jj] * dval<TERN>(acc[j], K, e, n0 + jj));
                 const uint32_t bit = (j < ncols && !(v >= tau[jj])) ? 1u : 0u;
                 word |= bit << b;
             }
@@ -381,12 +406,17 @@ hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
         const int w = atoi(v);
         if (w == 4 || w == 8 || w == 16) waves = w;
     }
+    if (e.flags & W_TERNARY) waves = 4;
     const int64_t row_tiles = (M + waves * 64 - 1) / (waves * 64);
     const int tiles_n = (int)((N + tn - 1) / tn);
     const dim3 grid((unsigned)(row_tiles * tiles_n)), block(waves * 64);
     const int m = (int)M, n = (int)N, k = (int)K;
-#define BNN_GEMM(T, L, WV) hipLaunchKernelGGL((k_xnor_gemm<T, 16, L, WV>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e)
-#define BNN_GEMM_W(T, L) switch (waves) { case 8: BNN_GEMM(T, L, 8); break; case 16: BNN_GEMM(T, L, 16); break; default: BNN_GEMM(T, L, 4); break; }
+    // ternary weights: two SGPR planes per word, so 8-word chunks (the same
+    // SGPR budget as the binary 16-word chunks) and 4-wave workgroups
+#define BNN_GEMM(T, L, WV) hipLaunchKernelGGL((k_xnor_gemm<T, 16, L, WV, false>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e)
+#define BNN_GEMM_W(T, L) \
+    if (e.flags & W_TERNARY) hipLaunchKernelGGL((k_xnor_gemm<T, 8, L, 4, true>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e); \
+    else switch (waves) { case 8: BNN_GEMM(T, L, 8); break; case 16: BNN_GEMM(T, L, 16); break; default: BNN_GEMM(T, L, 4); break; }
     if (lds) {
         switch (tn) {
             case 64: BNN_GEMM_W(64, true); break;

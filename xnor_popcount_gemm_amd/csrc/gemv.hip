@@ -44,7 +44,11 @@ __device__ __forceinline__ u32x4 load_stream(const uint32_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-template <int MR, int CPL, int U>
+// TERN: ternary weights -- Wp is the sign plane, e.Zp the nonzero plane and
+// e.nnz the nonzero count per row; a word contributes popcount((x ^ s) & z)
+// (one v_bitop3 + one v_bcnt) and D = nnz - 2 * sum ("Extreme
+// Quantization", eq. (7)).
+template <int MR, int CPL, int U, bool TERN>
 __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
     const uint32_t* __restrict__ Xp, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
     int N, int K, int glog2, Epilogue e)
@@ -84,8 +88,9 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
     const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
     const bool last = gl == G - 1;                // the lane that ends with a row's total
     for (int64_t s0 = wave * U; s0 < nsteps; s0 += nwaves * U) {
-        u32x4 wv[U][CPL];
+        u32x4 wv[U][CPL], zv[U][CPL];
         float av[U], bv[U], rv[U][MR];
+        int32_t kb[U];
         // all loads of the U row-steps (weights, alpha, residual) go out
         // before the first is consumed
 #pragma unroll
@@ -95,8 +100,14 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
             for (int i = 0; i < CPL; ++i) {
                 const int c = gl + G * i;
                 wv[u][i] = (u32x4){0u, 0u, 0u, 0u};
-                if (row < N && c < Kw4) wv[u][i] = load_stream(Wp + row * ldW + 4 * c);
+                zv[u][i] = (u32x4){0u, 0u, 0u, 0u};
+                if (row < N && c < Kw4) {
+                    wv[u][i] = load_stream(Wp + row * ldW + 4 * c);
+                    if (TERN) zv[u][i] = load_stream(e.Zp + row * ldW + 4 * c);
+                }
             }
+            kb[u] = K;
+            if (TERN && row < N) kb[u] = e.nnz[row];
             av[u] = 0.0f;
             bv[u] = 0.0f;
             if ((e.flags & EPI_SCALE) && row < N) av[u] = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : row];
@@ -110,16 +121,20 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = (s0 + u) * RPS + go;
-            if (ragged) {
+            if (ragged || TERN) {
 #pragma unroll
-                for (int i = 0; i < CPL; ++i) wv[u][i] &= wm[i];
+                for (int i = 0; i < CPL; ++i) {
+                    if (TERN) zv[u][i] &= wm[i];
+                    else      wv[u][i] &= wm[i];
+                }
             }
 #pragma unroll
             for (int mr = 0; mr < MR; ++mr) {
                 uint32_t pc = 0u;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
-                    const u32x4 t = xg[mr][i] ^ wv[u][i];
+                    u32x4 t = xg[mr][i] ^ wv[u][i];
+                    if (TERN) t &= zv[u][i];
                     pc = popc_acc(t.x, pc);
                     pc = popc_acc(t.y, pc);
                     pc = popc_acc(t.z, pc);
@@ -127,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
                 }
                 pc = sum_reduce_to_last(pc, glog2);
                 if (last && row < N) {
-                    const int32_t d = K - 2 * (int32_t)pc;
+                    const int32_t d = kb[u] - 2 * (int32_t)pc;
                     if (e.flags & EPI_DOT) e.D[(int64_t)mr * e.ldD + row] = d;
                     if (e.flags & EPI_SCALE) {
                         float y = av[u] * (float)d;
@@ -182,7 +197,9 @@ hipError_t launch_xnor_gemv(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
     if (blocks < 1) blocks = 1;
     const dim3 grid((unsigned)blocks), block(kThreads);
     const int n = (int)N, k = (int)K;
-#define BNN_GEMV(MR, CPL, UU) hipLaunchKernelGGL((k_xnor_gemv<MR, CPL, UU>), grid, block, 0, s, Xp, ldX, Wp, ldW, n, k, glog2, e)
+#define BNN_GEMV(MR, CPL, UU) \
+    if (e.flags & W_TERNARY) hipLaunchKernelGGL((k_xnor_gemv<MR, CPL, UU, true>), grid, block, 0, s, Xp, ldX, Wp, ldW, n, k, glog2, e); \
+    else                     hipLaunchKernelGGL((k_xnor_gemv<MR, CPL, UU, false>), grid, block, 0, s, Xp, ldX, Wp, ldW, n, k, glog2, e)
 #define BNN_GEMV_MR(CPL, UU) \
     switch (M) { case 1: BNN_GEMV(1, CPL, UU); break; case 2: BNN_GEMV(2, CPL, UU); break; \
                  case 3: BNN_GEMV(3, CPL, UU); break; default: BNN_GEMV(4, CPL, UU); break; }

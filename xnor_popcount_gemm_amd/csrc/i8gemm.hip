@@ -77,11 +77,29 @@ __device__ __forceinline__ v4i expand_signs(uint32_t bits16) {
     return r;
 }
 
+// Ternary weights ("Extreme Quantization", eq. (7) / (9)): c holds the
+// lane's 16 nonzero bits (Z) in its low half and its 16 bits of -1 weights
+// (S & Z) in its high half; each byte becomes 0x01 (+1), 0xFF (-1) or 0.
+__device__ __forceinline__ v4i expand_ternary(uint32_t c) {
+    v4i r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t zn = (c >> (4 * q)) & 0xFu;
+        const uint32_t mn = (c >> (16 + 4 * q)) & 0xFu;
+        const uint32_t tz = (zn * 0x00204081u) & 0x01010101u;
+        const uint32_t tm = (mn * 0x00204081u) & 0x01010101u;
+        r[q] = (int)(tz ^ (tm * 0xFEu));           // z=1: 0x01, then m=1 turns it into 0xFF
+    }
+    return r;
+}
+
 constexpr int kAPieces = kBM * kKS / 16 / kThreads;   // 16-byte A pieces per lane per k-step
 
 typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
+// TERN: Wp is the sign plane, e.Zp the nonzero plane of ternary weights.
+template <bool TERN>
 __global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
     const int8_t* __restrict__ Xq, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
     int M, int N, int K, int tiles_n, EpilogueI8 e)
@@ -135,6 +153,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
     const uint32_t* wrow[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) wrow[q] = Wp + (int64_t)min(n_blk + wn * 64 + 16 * q + r16, N - 1) * ldW;
+    const int64_t zdelta = TERN ? e.Zp - Wp : 0;   // nonzero plane: same layout, other base
+    // combined ternary word of lane group g: Z bits low, (S & Z) bits high
+    auto tern_word = [](uint32_t sw, uint32_t zw, int gg) {
+        const int sh = 16 * (gg & 1);
+        return ((zw >> sh) & 0xFFFFu) | (((sw & zw) >> sh) << 16);
+    };
 
     v4i acc[8][4];
 #pragma unroll
@@ -151,7 +175,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bw[h][q] = wrow[q][2 * h + (g >> 1)];
+        for (int q = 0; q < 4; ++q) {
+            bw[h][q] = wrow[q][2 * h + (g >> 1)];
+            if (TERN) bw[h][q] = tern_word(bw[h][q], (wrow[q] + zdelta)[2 * h + (g >> 1)], g);
+        }
     __builtin_amdgcn_s_waitcnt(0);
     // the first step's words are complete before the loop, so no load is
     // pending on the loop-carried registers when an iteration begins
@@ -168,21 +195,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
         const int cur = s & 1;
         const bool more = s + 1 < steps;
         const int kn = (s + 1) * kKS;
-        uint32_t bn[2][4];
+        uint32_t bn[2][4], zn[2][4];
         if (more) {
             if (DIRECT) stage_direct(cur ^ 1, kn);
             else        stage_masked(cur ^ 1, kn);
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) bn[h][q] = wrow[q][(kn >> 5) + 2 * h + (g >> 1)];
+                for (int q = 0; q < 4; ++q) {
+                    bn[h][q] = wrow[q][(kn >> 5) + 2 * h + (g >> 1)];
+                    if (TERN) zn[h][q] = (wrow[q] + zdelta)[(kn >> 5) + 2 * h + (g >> 1)];
+                }
         }
         const int8_t* la = lds_a[cur];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             v4i bx[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bx[q] = expand_signs(bw[h][q] >> (16 * (g & 1)));
+            for (int q = 0; q < 4; ++q)
+                bx[q] = TERN ? expand_ternary(bw[h][q]) : expand_signs(bw[h][q] >> (16 * (g & 1)));
 #pragma unroll
             for (int f = 0; f < 8; ++f) {
                 const v4i a = *reinterpret_cast<const v4i*>(la + roff[h][f]);
@@ -199,7 +230,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     asm volatile("" : : "v"(bn[h][q]));
-                    bw[h][q] = bn[h][q];
+                    if (TERN) asm volatile("" : : "v"(zn[h][q]));
+                    bw[h][q] = TERN ? tern_word(bn[h][q], zn[h][q], g) : bn[h][q];
                 }
         }
         __syncthreads();
@@ -292,8 +324,10 @@ hipError_t launch_bwn_i8_gemm(const int8_t* Xq, int64_t ldXq, const uint32_t* Wp
     const int tiles_n = (int)((N + kBN - 1) / kBN);
     const int64_t tiles_m = (M + kBM - 1) / kBM;
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
-    hipLaunchKernelGGL(k_bwn_i8_gemm, grid, block, 0, s, Xq, ldXq, Wp, ldW,
-                       (int)M, (int)N, (int)K, tiles_n, e);
+    if (e.flags & W_TERNARY)
+        hipLaunchKernelGGL((k_bwn_i8_gemm<true>), grid, block, 0, s, Xq, ldXq, Wp, ldW, (int)M, (int)N, (int)K, tiles_n, e);
+    else
+        hipLaunchKernelGGL((k_bwn_i8_gemm<false>), grid, block, 0, s, Xq, ldXq, Wp, ldW, (int)M, (int)N, (int)K, tiles_n, e);
     return hipGetLastError();
 }
 

@@ -192,7 +192,10 @@ __global__ __launch_bounds__(kThreads) void k_act_i8(
 // rows in registers for the whole kernel.  Per row-step a lane does
 // 8 (v_and, v_bcnt) per word, 7 shift-adds to weigh the planes, and the
 // group sum takes GLOG2 DPP adds.
-template <int MR, int CPL, int U, int GLOG2>
+// TERN: ternary weights -- Wp is the sign plane S and e.Zp the nonzero plane
+// Z; sum_k t_k q_k = sum_b c_b (popcount(P_b & Z) - 2 popcount(P_b & Z & S))
+// (no row sum needed), two (v_and, v_bcnt) pairs per plane and word.
+template <int MR, int CPL, int U, int GLOG2, bool TERN>
 __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
     const uint32_t* __restrict__ Xb, int64_t ldXb, const int32_t* __restrict__ xsum,
     const uint32_t* __restrict__ Wp, int64_t ldW, int N, int K, EpilogueI8 e)
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
     float xsc[MR];
 #pragma unroll
     for (int mr = 0; mr < MR; ++mr) {
-        xs[mr] = xsum[mr];
+        xs[mr] = TERN ? 0 : xsum[mr];
         xsc[mr] = e.xscale ? e.xscale[mr] : 1.0f;
     }
 
@@ -243,17 +246,23 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
     for (int64_t s0 = wave * U; s0 < nsteps; s0 += stride) {
         const int64_t row0 = s0 * RPS + go;
         const uint32_t* __restrict__ wp0 = Wp + row0 * ldW + 4 * gl;
-        u32x4 w[U][CPL];
+        u32x4 w[U][CPL], z[U][CPL];
         float av[U];
+        const uint32_t* __restrict__ zp0 = TERN ? e.Zp + (wp0 - Wp) : wp0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = row0 + (int64_t)u * RPS;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 w[u][i] = (u32x4){0u, 0u, 0u, 0u};
-                if (row < N && live[i])
+                z[u][i] = (u32x4){0u, 0u, 0u, 0u};
+                if (row < N && live[i]) {
                     w[u][i] = __builtin_nontemporal_load(
                         reinterpret_cast<const u32x4*>(wp0 + u * step_words + 4 * G * i));
+                    if (TERN)
+                        z[u][i] = __builtin_nontemporal_load(
+                            reinterpret_cast<const u32x4*>(zp0 + u * step_words + 4 * G * i));
+                }
             }
             av[u] = 0.0f;
             if ((e.flags & EPI_SCALE) && row < N) av[u] = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : row];
@@ -263,28 +272,41 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
             const int64_t row = row0 + (int64_t)u * RPS;
 #pragma unroll
             for (int mr = 0; mr < MR; ++mr) {
-                uint32_t acc[8];
+                uint32_t acc[8], acz[8];
 #pragma unroll
-                for (int b = 0; b < 8; ++b) acc[b] = 0u;
+                for (int b = 0; b < 8; ++b) { acc[b] = 0u; acz[b] = 0u; }
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
+                    // binary: count the -1 weights (bit 1); ternary: the
+                    // -1 weights are S & Z, the nonzero ones Z
+                    const u32x4 wn = TERN ? (w[u][i] & z[u][i]) : w[u][i];
 #pragma unroll
                     for (int b = 0; b < 8; ++b) {
-                        const u32x4 t = xg[mr][b][i] & w[u][i];
+                        const u32x4 t = xg[mr][b][i] & wn;
                         acc[b] = popc_acc(t.x, acc[b]);
                         acc[b] = popc_acc(t.y, acc[b]);
                         acc[b] = popc_acc(t.z, acc[b]);
                         acc[b] = popc_acc(t.w, acc[b]);
+                        if (TERN) {
+                            const u32x4 tz = xg[mr][b][i] & z[u][i];
+                            acz[b] = popc_acc(tz.x, acz[b]);
+                            acz[b] = popc_acc(tz.y, acz[b]);
+                            acz[b] = popc_acc(tz.z, acz[b]);
+                            acz[b] = popc_acc(tz.w, acz[b]);
+                        }
                     }
                 }
-                // sum over the planes with their two's-complement weights
-                uint32_t neg = acc[0];
+                // sum over the planes with their two's-complement weights:
+                // neg = sum of q over the -1 weights, nzs = over the nonzero ones
+                uint32_t neg = acc[0], nzs = acz[0];
 #pragma unroll
-                for (int b = 1; b < 7; ++b) neg += acc[b] << b;
+                for (int b = 1; b < 7; ++b) { neg += acc[b] << b; if (TERN) nzs += acz[b] << b; }
                 neg -= acc[7] << 7;
+                if (TERN) nzs -= acz[7] << 7;
                 neg = sum_reduce_to_last_t<GLOG2>(neg);
+                if (TERN) nzs = sum_reduce_to_last_t<GLOG2>(nzs);
                 if (last && row < N) {
-                    const int32_t d = xs[mr] - 2 * (int32_t)neg;
+                    const int32_t d = (TERN ? (int32_t)nzs : xs[mr]) - 2 * (int32_t)neg;
                     if (e.flags & EPI_DOT) e.D[(int64_t)mr * e.ldD + row] = d;
                     if (e.flags & EPI_SCALE) {
                         float y = av[u] * (float)d;
@@ -378,7 +400,8 @@ hipError_t launch_bwn_i8_gemv(const uint32_t* Xb, int64_t ldXb, const int32_t* x
     const dim3 grid((unsigned)blocks), block(kThreads);
     const int n = (int)N, k = (int)K;
 #define BNN_I8GEMV(MR, CPL, UU, GL) \
-    hipLaunchKernelGGL((k_bwn_i8_gemv<MR, CPL, UU, GL>), grid, block, 0, s, Xb, ldXb, xsum, Wp, ldW, n, k, e)
+    if (e.flags & W_TERNARY) hipLaunchKernelGGL((k_bwn_i8_gemv<MR, CPL, UU, GL, true>), grid, block, 0, s, Xb, ldXb, xsum, Wp, ldW, n, k, e); \
+    else                     hipLaunchKernelGGL((k_bwn_i8_gemv<MR, CPL, UU, GL, false>), grid, block, 0, s, Xb, ldXb, xsum, Wp, ldW, n, k, e)
 #define BNN_I8GEMV_G(MR, CPL, UU) \
     switch (sh.glog2) { case 4: BNN_I8GEMV(MR, CPL, UU, 4); break; case 5: BNN_I8GEMV(MR, CPL, UU, 5); break; \
                         default: BNN_I8GEMV(MR, CPL, UU, 6); break; }

@@ -235,6 +235,66 @@ __global__ __launch_bounds__(kThreads) void k_im2col_band(
     }
 }
 
+// Ternary weights ("Extreme Quantization", eq. (7) and eq. (9)), packed as a
+// sign plane S (bit 1 where t = -1) and a nonzero plane Z (bit 1 where
+// t != 0), with nnz[n] = number of nonzero t of row n.  ROUNDCLIP: t =
+// RoundClip(w / gamma, -1, 1) with gamma read from device memory (one IEEE
+// division, round half to even, NaN -> 0); otherwise t = (w > delta) -
+// (w < -delta).  Elements past K and the pad words are 0 in both planes.
+// Same mapping as k_pack_dense: a wave per row, 8 lanes per word.
+template <bool VEC, bool ROUNDCLIP>
+__global__ __launch_bounds__(kThreads) void k_pack_ternary(
+    const float* __restrict__ W, int64_t rows, int K, int64_t ldW, const float* __restrict__ gamma,
+    float delta, uint32_t* __restrict__ S, uint32_t* __restrict__ Z, int64_t ld, int32_t* __restrict__ nnz)
+{
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & 7;
+    const int grp = lane >> 3;
+    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+    const int ldi = (int)ld;
+    const float gm = ROUNDCLIP ? gamma[0] : 0.0f;
+    for (int64_t r = wave; r < rows; r += nwaves) {
+        const float* __restrict__ wr = W + r * ldW;
+        int32_t cnt = 0;
+        for (int w0 = 0; w0 < ldi; w0 += 8 * kSteps) {
+            Frag f[kSteps];
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u)
+                f[u] = load_frag<VEC>(wr, 32 * (w0 + 8 * u + grp) + 4 * sub, K);
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const int w = w0 + 8 * u + grp;
+                uint32_t sn = 0u, zn = 0u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = __uint_as_float(f[u].u[i]);
+                    int t;
+                    if (ROUNDCLIP) {
+                        const float q = rintf(v / gm);
+                        t = (q != q) ? 0 : (q > 1.0f ? 1 : (q < -1.0f ? -1 : (int)q));
+                    } else {
+                        t = (v > delta ? 1 : 0) - (v < -delta ? 1 : 0);
+                    }
+                    if (32 * w + 4 * sub + i >= K) t = 0;
+                    sn |= (t < 0 ? 1u : 0u) << i;
+                    zn |= (t != 0 ? 1u : 0u) << i;
+                }
+                const uint32_t sw = or_reduce8_to_last(sn << (4 * sub));
+                const uint32_t zw = or_reduce8_to_last(zn << (4 * sub));
+                if (sub == 7 && w < ldi) {
+                    S[r * ld + w] = sw;
+                    Z[r * ld + w] = zw;
+                    cnt += __popc(zw);
+                }
+            }
+        }
+#pragma unroll
+        for (int s2 = 32; s2 >= 1; s2 >>= 1) cnt += __shfl_xor(cnt, s2, 64);
+        if (lane == 0) nnz[r] = cnt;
+    }
+}
+
 int grid_for_rows(int64_t rows) {
     const int64_t waves_per_block = kThreads / 64;
     int64_t blocks = (rows + waves_per_block - 1) / waves_per_block;
@@ -368,6 +428,20 @@ hipError_t launch_alpha_tensor(const float* W, int64_t N, int64_t K, int64_t ldW
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k_tensor_alpha, dim3(1), block, 0, s, (const double*)work, N,
                        (double)N * (double)K, alpha);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_ternary(const float* W, int64_t N, int64_t K, int64_t ldW, const float* gamma,
+                               float delta, uint32_t* S, uint32_t* Z, int64_t ld, int32_t* nnz,
+                               hipStream_t s)
+{
+    const bool vec = aligned16(W) && (ldW % 4 == 0);
+    const dim3 grid(grid_for_rows(N)), block(kThreads);
+    const int k = (int)K;
+#define BNN_TPACK(V, R) hipLaunchKernelGGL((k_pack_ternary<V, R>), grid, block, 0, s, W, N, k, ldW, gamma, delta, S, Z, ld, nnz)
+    if (gamma) { if (vec) BNN_TPACK(true, true); else BNN_TPACK(false, true); }
+    else       { if (vec) BNN_TPACK(true, false); else BNN_TPACK(false, false); }
+#undef BNN_TPACK
     return hipGetLastError();
 }
 
