@@ -61,7 +61,7 @@ def parse_args():
     p.add_argument("--size", type=int, default=16384, help="M = N = K of the headline GEMM step")
     p.add_argument("--no-secondary", action="store_true", help="skip the GEMV / MLP / conv / 8192 runs")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv", "i8"], default=None,
+    p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv", "i8", "tern"], default=None,
                    help="run one workload only (for profiler runs); prints its JSON")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calib", action="store_true",
@@ -365,6 +365,85 @@ def i8_gemm_bench(bnn, torch, M, N, K, reps=10, warmup=2):
     return res
 
 
+def _time_launches(torch, fn, reps, warmup=3):
+    """Mean and median HIP-event time (ms) of back-to-back launches of fn."""
+    for _ in range(warmup):
+        fn()
+    evs = [Ev() for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        e.start()
+        fn()
+        e.stop()
+    torch.cuda.synchronize()
+    ms = [e.ms() for e in evs]
+    return statistics.mean(ms), median(ms)
+
+
+def ternary_bench(bnn, torch, reps=10):
+    """Ternary weights (eq. (9) RoundClip planes): the b1.58 decode GEMV
+    (INT8 activations) and the ternary x binary GEMV over 191 stacked weight
+    copies (HBM GB/s, both planes counted), and 8192^3 GEMMs (ternary x
+    binary XNOR-style, ternary x INT8 on the matrix cores)."""
+    import workloads
+    res = {"gemv": []}
+    G = GEMV_COPIES
+    for sh in workloads.WORKLOADS[3]["shapes"]:
+        N, K = sh["N"], sh["K"]
+        log(f"ternary gemv N={N} K={K}: {G} stacked copies")
+        W = torch.from_numpy(workloads.normal_f32(workloads.seed_for(3, 0) + K, (N, K))).cuda()
+        x = torch.from_numpy(workloads.normal_f32(workloads.seed_for(3, 1) + K, (1, K))).cuda()
+        g = bnn.weight_scale_tensor(W)
+        Sp, Zp, nnz = bnn.pack_weights_ternary(W, gamma=g)
+        del W
+        Sst, Zst, nst = Sp.repeat(G, 1), Zp.repeat(G, 1), nnz.repeat(G)
+        Nt = G * N
+        kw = (K + 31) // 32
+        q = bnn.quantize_act_i8(x, want_int8=False)
+        xp = bnn.pack_activations(x)
+        Y = torch.empty((1, Nt), dtype=torch.float32, device="cuda")
+        fl = bnn.EPI_SCALE_F32 | bnn.EPI_ALPHA_TENSOR | bnn.W_TERNARY
+        i8 = lambda: bnn.bwn_i8_linear(Sst, K, fl, Xb=q["Xb"], xscale=q["xscale"], alpha=g, Zp=Zst, Y=Y)
+        b1 = lambda: bnn.linear_fused(xp, Sst, K, fl, alpha=g, Zp=Zst, nnz=nst, Y=Y)
+        t_i8, _ = _time_launches(torch, i8, reps)
+        t_b1, _ = _time_launches(torch, b1, reps)
+        by_i8 = 8.0 * Nt * kw + 32.0 * kw + 4.0 + 4.0 * Nt
+        by_b1 = 8.0 * Nt * kw + 4.0 * kw + 4.0 * Nt + 4.0 * Nt
+        res["gemv"].append(dict(N=N, K=K, copies=G,
+                                i8act_ms=t_i8, i8act_GBps=by_i8 / (t_i8 * 1e-3) / 1e9,
+                                i8act_frac_hbm=by_i8 / (t_i8 * 1e-3) / PEAK_HBM,
+                                binact_ms=t_b1, binact_GBps=by_b1 / (t_b1 * 1e-3) / 1e9,
+                                binact_frac_hbm=by_b1 / (t_b1 * 1e-3) / PEAK_HBM))
+        del Sst, Zst, nst, Sp, Zp, nnz, Y
+        torch.cuda.empty_cache()
+    S = 8192
+    log(f"ternary gemm {S}^3")
+    X = torch.from_numpy(workloads.normal_f32(workloads.seed_for(4, 0) + 23, (S, S))).cuda()
+    W = torch.from_numpy(workloads.normal_f32(workloads.seed_for(4, 1) + 23, (S, S))).cuda()
+    g = bnn.weight_scale_tensor(W)
+    Sp, Zp, nnz = bnn.pack_weights_ternary(W, gamma=g)
+    del W
+    Xp = bnn.pack_activations(X)
+    q = bnn.quantize_act_i8(X, want_planes=False)
+    del X
+    D = torch.empty((S, S), dtype=torch.int32, device="cuda")
+    Yf = torch.empty((S, S), dtype=torch.float32, device="cuda")
+    fl = bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32 | bnn.EPI_ALPHA_TENSOR | bnn.W_TERNARY
+    tb, _ = _time_launches(torch, lambda: bnn.linear_fused(Xp, Sp, S, fl, alpha=g, Zp=Zp, nnz=nnz, D=D, Y=Yf), 5, 2)
+    ti, _ = _time_launches(torch, lambda: bnn.bwn_i8_linear(Sp, S, fl, Xq=q["Xq"], xscale=q["xscale"], alpha=g,
+                                                         Zp=Zp, D=D, Y=Yf), 5, 2)
+    ops = 2.0 * S * S * S
+    words = float(S) * S * ((S + 31) // 32)
+    res["gemm_8192"] = dict(
+        binact_ms=tb, binact_tops=ops / (tb * 1e-3) / 1e12,
+        # one word-output costs v_xor + v_and (VOP2) + v_bcnt (VOP3): 1/128 + 1/128 + 1/64 CU-clocks
+        binact_frac_word_peak=words / (tb * 1e-3) / (NUM_CU * CLOCK_HZ * 32.0),
+        i8act_ms=ti, i8act_tops=ops / (ti * 1e-3) / 1e12, i8act_frac_int8_mfma=ops / (ti * 1e-3) / PEAK_INT8_MFMA)
+    del Sp, Zp, nnz, Xp, q, D, Yf
+    torch.cuda.empty_cache()
+    return res
+
+
 def mlp_bench(bnn, torch, reps=20, warmup=3):
     import workloads
     c = workloads.WORKLOADS[2]
@@ -533,6 +612,8 @@ def main():
             r = [gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]]
         elif args.only == "mlp":
             r = mlp_bench(bnn, torch)
+        elif args.only == "tern":
+            r = ternary_bench(bnn, torch)
         elif args.only == "i8":
             r = {"gemv": [i8_gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]],
                  "gemm": i8_gemm_bench(bnn, torch, 8192, 8192, 8192)}
@@ -630,6 +711,7 @@ def main():
                          "frac": round(ig["frac_int8_mfma_peak"], 4)},
             "detail": ig,
         }
+        sec["ternary"] = ternary_bench(bnn, torch)
         sec["binary_mlp_batch1024"] = mlp_bench(bnn, torch)
         sec["conv_block"] = [conv_bench(bnn, torch, s) for s in workloads.WORKLOADS[5]["shapes"]]
         line["secondary"] = sec
