@@ -94,6 +94,8 @@ def _configure(L):
         "oracle_ternary_threshold": [_p, _i64, _i64, _i64, ctypes.c_float, _p],
         "oracle_ternary_roundclip": [_p, _i64, _i64, _i64, ctypes.c_float, _p],
         "oracle_pack_ternary": [_p, _i64, _i64, _i64, _p, _p, _p],
+        "oracle_rsign": [_p, _i64, _i64, _i64, _p, _p],
+        "oracle_im2col_pm1": [_p, _i64, _i64, _i64, _i64, _p],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -424,3 +426,49 @@ def ternary_b158(W: np.ndarray):
     """BitNet b1.58 weights (eq. (9)): (T int8 [N, K], gamma)."""
     g = alpha_tensor(W)
     return ternary_roundclip(W, g), g
+
+
+def rsign(X: np.ndarray, beta: np.ndarray) -> np.ndarray:
+    """RSign (ReActNet row): +1 where x >= beta_c (per column c), else -1."""
+    X = _c(X, np.float32)
+    beta = _c(beta, np.float32)
+    rows, cols = X.shape
+    assert beta.shape == (cols,)
+    s = np.empty((rows, cols), dtype=np.int8)
+    lib().oracle_rsign(_ptr(X), rows, cols, cols, _ptr(beta), _ptr(s))
+    return s
+
+
+def im2col_pm1(S: np.ndarray) -> np.ndarray:
+    """[B*H*W, 9*C] im2col of NHWC signs S, taps outside the image +1."""
+    S = _c(S, np.int8)
+    B, H, W, C = S.shape
+    cols = np.empty((B * H * W, 9 * C), dtype=np.int8)
+    lib().oracle_im2col_pm1(_ptr(S), B, H, W, C, _ptr(cols))
+    return cols
+
+
+def conv_block_rsign(X: np.ndarray, W_ohwi: np.ndarray, beta: np.ndarray | None = None):
+    """One binary 3x3 conv block with RSign input: D = conv(RSign(X, beta), sign W),
+    Y = fl(fl(alpha * D) + X) (Bi-Real FP shortcut).  beta None means 0 (the
+    plain sign).  Returns (D [B*H*W, Cout], Y [B, H, W, Cout], alpha)."""
+    B, H, Wd, C = X.shape
+    Cout = W_ohwi.shape[0]
+    assert Cout == C
+    b = np.zeros(C, np.float32) if beta is None else beta
+    S = rsign(X.reshape(B * H * Wd, C), b).reshape(B, H, Wd, C)
+    Wf = np.ascontiguousarray(W_ohwi.reshape(Cout, 9 * C))
+    a = alpha(Wf)
+    D = dot(im2col_pm1(S), sign(Wf))
+    Y = scale_residual(D, a, X.reshape(B * H * Wd, C))
+    return D, Y.reshape(B, H, Wd, Cout), a
+
+
+def conv_chain(X: np.ndarray, weights, betas):
+    """A chain of conv blocks: X_{l+1} = Y_l.  Returns the list of (D, Y)."""
+    out = []
+    for Wl, bl in zip(weights, betas):
+        D, Y, _ = conv_block_rsign(X, Wl, bl)
+        out.append((D, Y))
+        X = Y
+    return out

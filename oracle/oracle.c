@@ -29,6 +29,8 @@
  *       weights; eq. (8) (one mean-|W| scale for the whole matrix).
  *  [P5] "Ternary Quantization" eq. (7) (threshold Delta) and "BitNet b1.58"
  *       eq. (9) (RoundClip(W / gamma, -1, 1), gamma = ||W||_1 / (nm)).
+ *  [P4] "State of the Art Survey", ReActNet row: RSign (a learnable shift of
+ *       the activation distribution before the sign).
  */
 #include <math.h>
 #include <omp.h>
@@ -400,6 +402,40 @@ API void oracle_pack_ternary(const int8_t* T, int64_t N, int64_t K, int64_t ld,
             if (t == -1) S[n * ld + k / 32] |= (uint32_t)1u << (k % 32);
         }
         nnz[n] = cnt;
+    }
+}
+
+/* [P4] ReActNet row, RSign: the sign of an activation after a per-channel
+ * shift.  The page gives no formula; the reading taken is
+ * s = sign(x - beta_c) with sign as in [P5] Notation (+1 for >= 0), decided
+ * as the IEEE single comparison x >= beta_c (for finite values the same as
+ * the sign of the rounded difference; NaN gives -1).  X is [rows, cols] with
+ * row stride ldx, beta has cols entries, s is dense [rows, cols]. */
+API void oracle_rsign(const float* x, int64_t rows, int64_t cols, int64_t ldx, const float* beta, int8_t* s)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            s[r * cols + c] = (x[r * ldx + c] >= beta[c]) ? (int8_t)1 : (int8_t)-1;
+}
+
+/* im2col of a 3x3 / stride 1 / pad 1 convolution over an NHWC tensor of
+ * signs S [B, H, W, C] (+1 / -1): the same gather as oracle_im2col_signs,
+ * with taps outside the image read as +1. */
+API void oracle_im2col_pm1(const int8_t* S, int64_t B, int64_t H, int64_t W, int64_t C, int8_t* cols)
+{
+    const int64_t K = 9 * C;
+    #pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < B * H * W; ++p) {
+        int64_t b = p / (H * W), oh = (p / W) % H, ow = p % W;
+        for (int64_t kh = 0; kh < 3; ++kh)
+            for (int64_t kw = 0; kw < 3; ++kw) {
+                int64_t ih = oh - 1 + kh, iw = ow - 1 + kw;
+                int inside = ih >= 0 && ih < H && iw >= 0 && iw < W;
+                for (int64_t c = 0; c < C; ++c)
+                    cols[p * K + (kh * 3 + kw) * C + c] =
+                        inside ? S[((b * H + ih) * W + iw) * C + c] : (int8_t)1;
+            }
     }
 }
 

@@ -113,6 +113,13 @@ MUTATIONS = [
      "float r = rintf(W[n * ldw + k] / gamma);", "float r = rintf(W[n * ldw + k] * gamma);"),
     ("ternary pack: sign bit set for +1",
      "if (t == -1) S[n * ld + k / 32]", "if (t == 1) S[n * ld + k / 32]"),
+    ("RSign: strict comparison at the tie",
+     "s[r * cols + c] = (x[r * ldx + c] >= beta[c])", "s[r * cols + c] = (x[r * ldx + c] > beta[c])"),
+    ("RSign: shift ignored",
+     "s[r * cols + c] = (x[r * ldx + c] >= beta[c])", "s[r * cols + c] = (x[r * ldx + c] >= 0.0f)"),
+    ("RSign im2col: pad taps -1",
+     "inside ? S[((b * H + ih) * W + iw) * C + c] : (int8_t)1;",
+     "inside ? S[((b * H + ih) * W + iw) * C + c] : (int8_t)-1;"),
     ("ternary pack: zeros counted as nonzero",
      "if (t != 0) {\n                Z[n * ld + k / 32]", "if (t != 2) {\n                Z[n * ld + k / 32]"),
 ]

@@ -691,3 +691,64 @@ def test_ternary_dot_identities():
         a = np.bitwise_count(P[:, None, :, :] & Z[None, :, None, :]).sum(axis=-1, dtype=np.int64)
         b = np.bitwise_count(P[:, None, :, :] & (Z & S)[None, :, None, :]).sum(axis=-1, dtype=np.int64)
         np.testing.assert_array_equal(((a - 2 * b) * c).sum(axis=-1), D2.astype(np.int64))
+
+
+# ---------------------------------------------------------------- RSign and chained conv blocks
+# Page "State of the Art Survey", ReActNet row (RSign) and Bi-Real Net row
+# (FP shortcut per block).
+def test_rsign_is_sign_of_exact_difference():
+    rng = np.random.default_rng(85)
+    X = workloads.normal_f32(85001, (40, 24))
+    beta = (rng.standard_normal(24) * 0.5).astype(np.float32)
+    X[0, :] = beta                                   # ties: x == beta -> +1
+    X[1, :3] = [np.nan, np.inf, -np.inf]
+    s = oracle.rsign(X, beta)
+    for r in range(X.shape[0]):
+        for c in range(X.shape[1]):
+            x, b = float(X[r, c]), float(beta[c])
+            if math.isnan(x):
+                want = -1
+            elif math.isinf(x):
+                want = 1 if x > 0 else -1
+            else:
+                want = 1 if Fraction(x) - Fraction(b) >= 0 else -1
+            assert int(s[r, c]) == want, (r, c)
+    # beta = 0 is the plain sign (Notation of "Extreme Quantization")
+    np.testing.assert_array_equal(oracle.rsign(X, np.zeros(24, np.float32)), oracle.sign(X))
+
+
+def test_im2col_pm1_matches_sign_im2col():
+    X = workloads.normal_f32(86001, (2, 5, 4, 8))
+    S = oracle.sign(X.reshape(-1, 8)).reshape(X.shape)
+    np.testing.assert_array_equal(oracle.im2col_pm1(S), oracle.im2col_signs(X))
+
+
+def test_conv_block_rsign_matches_torch_conv():
+    import torch
+    B, H, W, C = 2, 5, 6, 8
+    X = workloads.normal_f32(87001, (B, H, W, C))
+    Wt = workloads.normal_f32(87002, (C, 3, 3, C))
+    beta = workloads.normal_f32(87003, (C,)) * np.float32(0.3)
+    D, Y, a = oracle.conv_block_rsign(X, Wt, beta)
+    # signs of (x - beta) decided exactly, then a float64 conv with +1 padding
+    xs = np.where(X.astype(np.float64) - beta.astype(np.float64) >= 0, 1.0, -1.0)
+    t = torch.from_numpy(xs).permute(0, 3, 1, 2)
+    t = torch.nn.functional.pad(t, (1, 1, 1, 1), value=1.0)
+    w = torch.from_numpy(np.where(Wt >= 0, 1.0, -1.0)).permute(0, 3, 1, 2)
+    ref = torch.nn.functional.conv2d(t, w).permute(0, 2, 3, 1).reshape(B * H * W, C).numpy()
+    np.testing.assert_array_equal(D.astype(np.float64), ref)
+    np.testing.assert_array_equal(Y.reshape(-1, C), oracle.scale_residual(D, a, X.reshape(-1, C)))
+
+
+def test_conv_chain_composes_blocks():
+    B, H, W, C = 1, 4, 4, 8
+    X = workloads.normal_f32(88001, (B, H, W, C))
+    Ws = [workloads.normal_f32(88002 + i, (C, 3, 3, C)) for i in range(3)]
+    bs = [workloads.normal_f32(88010 + i, (C,)) * np.float32(0.2) for i in range(3)]
+    out = oracle.conv_chain(X, Ws, bs)
+    x = X
+    for (D, Y), Wl, bl in zip(out, Ws, bs):
+        D2, Y2, _ = oracle.conv_block_rsign(x, Wl, bl)
+        np.testing.assert_array_equal(D, D2)
+        np.testing.assert_array_equal(Y, Y2)
+        x = Y2
