@@ -64,7 +64,11 @@ MUTATIONS = [
     ("im2col: tap order transposed",
      "cols[p * K + (kh * 3 + kw) * C + c] = v;", "cols[p * K + (kw * 3 + kh) * C + c] = v;"),
     ("im2col: window not centred",
-     "int64_t ih = oh - 1 + kh, iw = ow - 1 + kw;", "int64_t ih = oh + kh, iw = ow - 1 + kw;"),
+     "int64_t ih = oh - 1 + kh, iw = ow - 1 + kw;\n                int inside = (ih",
+     "int64_t ih = oh + kh, iw = ow - 1 + kw;\n                int inside = (ih"),
+    ("RSign im2col: window not centred",
+     "int64_t ih = oh - 1 + kh, iw = ow - 1 + kw;\n                int inside = ih",
+     "int64_t ih = oh - 1 + kh, iw = ow + kw;\n                int inside = ih"),
     ("first FP layer: single-precision accumulation",
      "acc += (double)X[m * ldx + k] * (double)W[n * ldw + k];", "acc += (double)(X[m * ldx + k] * W[n * ldw + k]);"),
     ("last FP layer: activation signs ignored",
