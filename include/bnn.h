@@ -79,6 +79,12 @@ typedef enum bnn_status {
  * [P5] "Ternary Quantization" eq. (7) / "BitNet b1.58" eq. (9), stored as
  * the sign plane Wp and the nonzero plane Zp of bnn_pack_weights_ternary.  */
 #define BNN_W_TERNARY        64u
+/* With SCALE_F32: after the final Y (scale, bias, residual), also write the
+ * next layer's packed input, Op bit (m,n) = (Y[m,n] >= beta[n]) ? 0 : 1
+ * (RSign of [P4] "State of the Art Survey", ReActNet row, as a per-channel
+ * shift before the sign of [P5] Notation; beta NULL means 0, the plain sign),
+ * packed along n like THRESH_PACK.  Not together with THRESH_PACK.          */
+#define BNN_EPI_SIGN_PACK   128u
 
 /* Longest row of the INT8-activation calls: |D| <= 128 K stays exact in fp32. */
 #define BNN_MAX_K_I8 ((int64_t)1 << 17)
@@ -113,6 +119,8 @@ typedef struct bnn_fused_args {
     const float* bias;                /* BIAS_F32: fp32 [N]                     */
     const uint32_t* Zp;               /* W_TERNARY: nonzero plane [N, ldWp]     */
     const int32_t* nnz;               /* W_TERNARY: nonzero count per row [N]   */
+    const float* beta;                /* SIGN_PACK: RSign shift per column [N],
+                                         or NULL                                */
 } bnn_fused_args;
 
 /* Arguments of bnn_bwn_i8_linear (binary weights x INT8 activations).  Host
@@ -208,6 +216,32 @@ bnn_status bnn_xnor_gemm(const uint32_t* Xp, int64_t ldXp,
  * Errors: RESIDUAL, BIAS or ALPHA_TENSOR without SCALE, no flag, or unknown
  * flag bits -> BNN_ERR_UNSUPPORTED. */
 bnn_status bnn_linear_fused(const bnn_fused_args* args, bnn_stream_t stream);
+
+/* Sign + pack of activations with a per-column shift, RSign of [P4] "State
+ * of the Art Survey" (ReActNet row): bit (m,k) = (X[m,k] >= beta[k]) ? 0 : 1,
+ * an IEEE single comparison (for finite values the sign of X - beta; NaN
+ * gives 1, i.e. -1).  An NHWC image viewed as [B*H*W, C] with beta per
+ * channel gives the packed image that bnn_conv3x3_fused reads.
+ *  X fp32 [M, ldX] (ldX >= K); beta fp32 [K]; Xp packed [M, ldXp] (pad bits
+ *  and pad words written 0). */
+bnn_status bnn_pack_activations_rsign(const float* X, int64_t M, int64_t K, int64_t ldX, const float* beta,
+                                     uint32_t* Xp, int64_t ldXp, bnn_stream_t stream);
+
+/* Binary 3x3 convolution (stride 1, pad 1, pad pixels +1) with implicit
+ * im2col: the XNOR-popcount GEMM of bnn_linear_fused whose activation rows
+ * are gathered on the fly from the packed image instead of read from a
+ * packed im2col matrix ([P2] section "1. Arithmetic": pad bits +1; [P4]
+ * Bi-Real Net row: FP shortcut; the config's ResNet-style block).
+ *  geom   B, H, W, C with R = S = 3, stride = pad = 1; C in {64, 128, 256, 512}
+ *  args   Xp/ldXp = packed NHWC image [B*H*W, ldXp] (C bits per pixel, from
+ *         bnn_pack_activations / bnn_pack_activations_rsign on the image
+ *         viewed as [B*H*W, C], or from a previous call's SIGN_PACK output);
+ *         M = B*H*W; K = 9*C; Wp = packed OHWI weights [N, ldWp >= 9C/32]
+ *         (k = (kh*3 + kw)*C + c, as bnn_pack_weights gives for the
+ *         flattened OHWI tensor); every epilogue flag of bnn_linear_fused
+ *         except W_TERNARY.  M * ldXp < 2^31.
+ * Results are those of bnn_linear_fused on the explicit packed im2col. */
+bnn_status bnn_conv3x3_fused(const bnn_fused_args* args, const bnn_conv_geom* geom, bnn_stream_t stream);
 
 /* Ternary weights, [P5] "Ternary Quantization" eq. (7) and "BitNet b1.58"
  * eq. (9), packed as two planes with the packed layout above:

@@ -26,7 +26,7 @@ __all__ = [
     "dense_binact_f32", "EPI_DOT_I32", "EPI_SCALE_F32", "EPI_RESIDUAL_F32",
     "EPI_THRESH_PACK", "EPI_ALPHA_TENSOR", "EPI_BIAS_F32", "LIB_PATH",
     "weight_scale_tensor", "quantize_act_i8", "pack_act_i8", "bwn_i8_linear", "MAX_K_I8",
-    "W_TERNARY", "pack_weights_ternary",
+    "W_TERNARY", "pack_weights_ternary", "EPI_SIGN_PACK", "pack_activations_rsign", "conv3x3_fused",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbnn.so")
@@ -38,6 +38,7 @@ EPI_THRESH_PACK = 8
 EPI_ALPHA_TENSOR = 16
 EPI_BIAS_F32 = 32
 W_TERNARY = 64
+EPI_SIGN_PACK = 128
 MAX_K_I8 = 1 << 17
 
 _STATUS = {
@@ -70,6 +71,7 @@ class _FusedArgs(ctypes.Structure):
         ("Op", ctypes.c_void_p), ("ldOp", ctypes.c_int64),
         ("bias", ctypes.c_void_p),
         ("Zp", ctypes.c_void_p), ("nnz", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
     ]
 
 
@@ -120,6 +122,8 @@ def lib() -> ctypes.CDLL:
             "bnn_pack_act_i8": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
             "bnn_bwn_i8_linear": [ctypes.POINTER(_I8Args), _vp],
             "bnn_pack_weights_ternary": [_vp, _i64, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _i64, _vp, _vp],
+            "bnn_pack_activations_rsign": [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp],
+            "bnn_conv3x3_fused": [ctypes.POINTER(_FusedArgs), ctypes.POINTER(_ConvGeom), _vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -236,24 +240,15 @@ def xnor_gemm(Xp: torch.Tensor, Wp: torch.Tensor, K: int, *, alpha: torch.Tensor
     return D, Y
 
 
-def linear_fused(Xp: torch.Tensor, Wp: torch.Tensor, K: int, epilogue: int, *,
-                 alpha=None, R=None, tau=None, dir=None, D=None, Y=None, Op=None,
-                 bias=None, Zp=None, nnz=None, M: int | None = None):
-    """XNOR-popcount GEMM with a fused epilogue (OR of EPI_* flags).
-
-    Returns a dict with the outputs the flags ask for: ``D`` (int32 [M, N]),
-    ``Y`` (fp32 [M, N]), ``Op`` (packed [M, ld] of the output signs).
-    """
-    _dev(Xp, torch.int32, "Xp")
-    _dev(Wp, torch.int32, "Wp")
-    M = Xp.shape[0] if M is None else M
+def _fused_struct(Xp, Wp, K, epilogue, M, *, alpha=None, R=None, tau=None, dir=None, D=None, Y=None,
+                  Op=None, bias=None, Zp=None, nnz=None, beta=None):
     N = Wp.shape[0]
     dev = Xp.device
     if epilogue & EPI_DOT_I32 and D is None:
         D = torch.empty((M, N), dtype=torch.int32, device=dev)
     if epilogue & (EPI_SCALE_F32 | EPI_RESIDUAL_F32) and Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    if epilogue & EPI_THRESH_PACK and Op is None:
+    if epilogue & (EPI_THRESH_PACK | EPI_SIGN_PACK) and Op is None:
         Op = _packed_empty(M, N, dev)
     a = _FusedArgs()
     a.Xp, a.ldXp = Xp.data_ptr(), _ld(Xp)
@@ -280,8 +275,51 @@ def linear_fused(Xp: torch.Tensor, Wp: torch.Tensor, K: int, epilogue: int, *,
         a.Zp = Zp.data_ptr()
     if nnz is not None:
         a.nnz = nnz.data_ptr()
-    _check(lib().bnn_linear_fused(ctypes.byref(a), _stream(dev)), "bnn_linear_fused")
-    return {"D": D, "Y": Y, "Op": Op}
+    if beta is not None:
+        a.beta = beta.data_ptr()
+    return a, {"D": D, "Y": Y, "Op": Op}
+
+
+def linear_fused(Xp: torch.Tensor, Wp: torch.Tensor, K: int, epilogue: int, *,
+                 alpha=None, R=None, tau=None, dir=None, D=None, Y=None, Op=None,
+                 bias=None, Zp=None, nnz=None, beta=None, M: int | None = None):
+    """XNOR-popcount GEMM with a fused epilogue (OR of EPI_* flags).
+
+    Returns a dict with the outputs the flags ask for: ``D`` (int32 [M, N]),
+    ``Y`` (fp32 [M, N]), ``Op`` (packed [M, ld] of the output signs).
+    """
+    _dev(Xp, torch.int32, "Xp")
+    _dev(Wp, torch.int32, "Wp")
+    M = Xp.shape[0] if M is None else M
+    a, out = _fused_struct(Xp, Wp, K, epilogue, M, alpha=alpha, R=R, tau=tau, dir=dir, D=D, Y=Y, Op=Op,
+                           bias=bias, Zp=Zp, nnz=nnz, beta=beta)
+    _check(lib().bnn_linear_fused(ctypes.byref(a), _stream(Xp.device)), "bnn_linear_fused")
+    return out
+
+
+def conv3x3_fused(Ximg: torch.Tensor, Wp: torch.Tensor, geom, epilogue: int, **kw):
+    """Binary 3x3 conv with implicit im2col: Ximg is the packed NHWC image
+    [B*H*W, ld] (C bits per pixel), Wp the packed OHWI weights; geom =
+    (B, H, W, C).  Epilogue keywords as for linear_fused."""
+    _dev(Ximg, torch.int32, "Ximg")
+    _dev(Wp, torch.int32, "Wp")
+    B, H, W, C = geom
+    M = B * H * W
+    a, out = _fused_struct(Ximg, Wp, 9 * C, epilogue, M, **kw)
+    g = _ConvGeom(B, H, W, C, 3, 3, 1, 1)
+    _check(lib().bnn_conv3x3_fused(ctypes.byref(a), ctypes.byref(g), _stream(Ximg.device)), "bnn_conv3x3_fused")
+    return out
+
+
+def pack_activations_rsign(X: torch.Tensor, beta: torch.Tensor, *, out: torch.Tensor | None = None):
+    """Packed RSign of fp32 rows [M, K]: bit = (x >= beta_k) ? 0 : 1."""
+    _dev(X, torch.float32, "X")
+    _dev(beta, torch.float32, "beta")
+    M, K = X.shape
+    Xp = _packed_empty(M, K, X.device) if out is None else out
+    _check(lib().bnn_pack_activations_rsign(_ptr(X), M, K, _ld(X), _ptr(beta), _ptr(Xp), _ld(Xp),
+                                            _stream(X.device)), "bnn_pack_activations_rsign")
+    return Xp
 
 
 def fold_bn_thresholds(gamma, beta, mean, var, eps, alpha):

@@ -37,7 +37,9 @@ bnn_status check_rows(int64_t rows) {
     return (rows < 0 || rows > ((int64_t)1 << 31) - 1) ? BNN_ERR_SHAPE : BNN_OK;
 }
 
-bnn_status validate_fused(const bnn_fused_args* a) {
+// conv_cw > 0: the activation operand is a packed NHWC image of conv_cw
+// words per pixel (implicit im2col), not an im2col matrix of K bits per row.
+bnn_status validate_fused(const bnn_fused_args* a, int64_t conv_cw = 0) {
     if (!a) return BNN_ERR_NULL;
     bnn_status st;
     if ((st = check_rows(a->M)) != BNN_OK) return st;
@@ -47,11 +49,14 @@ bnn_status validate_fused(const bnn_fused_args* a) {
     if (((a->M + 255) / 256) * ((a->N + 15) / 16) > ((int64_t)1 << 31) - 1) return BNN_ERR_SHAPE;
     const uint32_t f = a->epilogue;
     const uint32_t known = BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32 | BNN_EPI_RESIDUAL_F32 | BNN_EPI_THRESH_PACK |
-                           BNN_EPI_ALPHA_TENSOR | BNN_EPI_BIAS_F32 | BNN_W_TERNARY;
+                           BNN_EPI_ALPHA_TENSOR | BNN_EPI_BIAS_F32 | BNN_W_TERNARY | BNN_EPI_SIGN_PACK;
     if ((f & ~known) != 0) return BNN_ERR_UNSUPPORTED;
     if (!(f & (BNN_EPI_DOT_I32 | BNN_EPI_SCALE_F32 | BNN_EPI_THRESH_PACK))) return BNN_ERR_UNSUPPORTED;
-    if ((f & (BNN_EPI_RESIDUAL_F32 | BNN_EPI_ALPHA_TENSOR | BNN_EPI_BIAS_F32)) && !(f & BNN_EPI_SCALE_F32))
+    if ((f & (BNN_EPI_RESIDUAL_F32 | BNN_EPI_ALPHA_TENSOR | BNN_EPI_BIAS_F32 | BNN_EPI_SIGN_PACK)) &&
+        !(f & BNN_EPI_SCALE_F32))
         return BNN_ERR_UNSUPPORTED;
+    if ((f & BNN_EPI_SIGN_PACK) && (f & BNN_EPI_THRESH_PACK)) return BNN_ERR_UNSUPPORTED;   // one Op
+    if (conv_cw > 0 && (f & BNN_W_TERNARY)) return BNN_ERR_UNSUPPORTED;
     if (f & BNN_EPI_BIAS_F32) {
         if (!a->bias) return BNN_ERR_NULL;
         if (misaligned4(a->bias)) return BNN_ERR_ALIGN;
@@ -61,8 +66,18 @@ bnn_status validate_fused(const bnn_fused_args* a) {
         if (!a->nnz) return BNN_ERR_NULL;
         if (misaligned4(a->nnz)) return BNN_ERR_ALIGN;
     }
-    if ((st = check_packed(a->Xp, a->K, a->ldXp)) != BNN_OK) return st;
+    if (conv_cw > 0) {
+        if ((st = check_packed(a->Xp, 32 * conv_cw, a->ldXp)) != BNN_OK) return st;
+        if (a->M * a->ldXp > ((int64_t)1 << 31) - 1) return BNN_ERR_SHAPE;   // 32-bit pixel offsets
+    } else {
+        if ((st = check_packed(a->Xp, a->K, a->ldXp)) != BNN_OK) return st;
+    }
     if ((st = check_packed(a->Wp, a->K, a->ldWp)) != BNN_OK) return st;
+    if (f & BNN_EPI_SIGN_PACK) {
+        if (!a->Op) return BNN_ERR_NULL;
+        if (a->ldOp < words_of(a->N)) return BNN_ERR_LD;
+        if (misaligned4(a->Op) || (a->beta && misaligned4(a->beta))) return BNN_ERR_ALIGN;
+    }
     if (f & BNN_EPI_DOT_I32) {
         if (!a->D) return BNN_ERR_NULL;
         if (a->ldD < a->N) return BNN_ERR_LD;
@@ -105,6 +120,7 @@ bnn_status run_fused(const bnn_fused_args* a, hipStream_t s) {
     e.Op = a->Op; e.ldOp = a->ldOp;
     e.bias = a->bias;
     e.Zp = a->Zp; e.nnz = a->nnz;
+    e.beta = a->beta;
     if (bnn::gemv_eligible(a->M, a->K, e.flags))
         return from_hip(bnn::launch_xnor_gemv(a->Xp, a->ldXp, a->Wp, a->ldWp, a->M, a->N, a->K, e, s));
     return from_hip(bnn::launch_xnor_gemm(a->Xp, a->ldXp, a->Wp, a->ldWp, a->M, a->N, a->K, e, s));
@@ -259,6 +275,46 @@ bnn_status bnn_linear_fused(const bnn_fused_args* args, bnn_stream_t stream)
     const bnn_status st = validate_fused(args);
     if (st != BNN_OK) return st;
     return run_fused(args, as_stream(stream));
+}
+
+bnn_status bnn_pack_activations_rsign(const float* X, int64_t M, int64_t K, int64_t ldX, const float* beta,
+                                     uint32_t* Xp, int64_t ldXp, bnn_stream_t stream)
+{
+    bnn_status st;
+    if ((st = check_rows(M)) != BNN_OK) return st;
+    if ((st = check_k(K)) != BNN_OK) return st;
+    if (!X || !beta) return BNN_ERR_NULL;
+    if ((st = check_packed(Xp, K, ldXp)) != BNN_OK) return st;
+    if (ldX < K) return BNN_ERR_LD;
+    if (misaligned4(X) || misaligned4(beta)) return BNN_ERR_ALIGN;
+    if (M == 0) return BNN_OK;
+    return from_hip(bnn::launch_pack_dense_rsign(X, M, K, ldX, beta, Xp, ldXp, as_stream(stream)));
+}
+
+bnn_status bnn_conv3x3_fused(const bnn_fused_args* args, const bnn_conv_geom* geom, bnn_stream_t stream)
+{
+    if (!args || !geom) return BNN_ERR_NULL;
+    if (geom->R != 3 || geom->S != 3 || geom->stride != 1 || geom->pad != 1) return BNN_ERR_UNSUPPORTED;
+    if (geom->B < 0 || geom->H < 1 || geom->W < 1 || geom->C < 1) return BNN_ERR_SHAPE;
+    const int64_t C = geom->C;
+    if (C != 64 && C != 128 && C != 256 && C != 512) return BNN_ERR_UNSUPPORTED;
+    if (args->M != geom->B * geom->H * geom->W || args->K != 9 * C) return BNN_ERR_SHAPE;
+    const bnn_status st = validate_fused(args, C / 32);
+    if (st != BNN_OK) return st;
+    if (args->M == 0 || args->N == 0) return BNN_OK;
+    Epilogue e;
+    e.flags = args->epilogue;
+    e.D = args->D; e.ldD = args->ldD;
+    e.alpha = args->alpha;
+    e.Y = args->Y; e.ldY = args->ldY;
+    e.R = args->R; e.ldR = args->ldR;
+    e.tau = args->tau; e.dir = args->dir;
+    e.Op = args->Op; e.ldOp = args->ldOp;
+    e.bias = args->bias;
+    e.Zp = nullptr; e.nnz = nullptr;
+    e.beta = args->beta;
+    return from_hip(bnn::launch_xnor_conv3x3(args->Xp, args->ldXp, args->Wp, args->ldWp, args->M, args->N,
+                                             geom->H, geom->W, (int)(C / 32), e, as_stream(stream)));
 }
 
 bnn_status bnn_pack_weights_ternary(const float* W, int64_t N, int64_t K, int64_t ldW,

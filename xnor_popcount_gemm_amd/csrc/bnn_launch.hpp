@@ -20,10 +20,11 @@ struct Epilogue {
     const float* bias;       // [N] with EPI_BIAS
     const uint32_t* Zp;      // ternary weights: nonzero plane (same ld as the sign plane Wp)
     const int32_t* nnz;      // ternary weights: nonzero count per weight row
+    const float* beta;       // EPI_SIGN_PACK: per-column RSign shift (nullptr: 0)
 };
 
 enum : uint32_t { EPI_DOT = 1u, EPI_SCALE = 2u, EPI_RESIDUAL = 4u, EPI_THRESH = 8u,
-                  EPI_ALPHA_TENSOR = 16u, EPI_BIAS = 32u, W_TERNARY = 64u };
+                  EPI_ALPHA_TENSOR = 16u, EPI_BIAS = 32u, W_TERNARY = 64u, EPI_SIGN_PACK = 128u };
 
 // Epilogue of binary weights x INT8 activations.
 struct EpilogueI8 {
@@ -48,11 +49,22 @@ hipError_t launch_pack_ternary(const float* W, int64_t N, int64_t K, int64_t ldW
                                float delta, uint32_t* S, uint32_t* Z, int64_t ld, int32_t* nnz,
                                hipStream_t s);
 
+// Sign + pack with a per-column RSign shift: bit = !(x >= beta[k]).
+hipError_t launch_pack_dense_rsign(const float* X, int64_t rows, int64_t K, int64_t ldX, const float* beta,
+                                   uint32_t* P, int64_t ldP, hipStream_t s);
+
 hipError_t launch_pack_im2col3x3(const float* X, int64_t B, int64_t H, int64_t W, int64_t C,
                                  uint32_t* P, int64_t ldP, hipStream_t s);
 
 hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
                             int64_t M, int64_t N, int64_t K, const Epilogue& e, hipStream_t s);
+
+// Implicit-im2col 3x3 binary convolution: Xp is the packed NHWC image
+// [B*H*W, ldX] with C = 32 cw channel bits per pixel (cw in {2, 4, 8, 16}),
+// Wp the packed OHWI weights [N, ldW], K = 9 C, M = B*H*W.
+hipError_t launch_xnor_conv3x3(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
+                               int64_t M, int64_t N, int64_t H, int64_t W, int cw,
+                               const Epilogue& e, hipStream_t s);
 
 // True when the streaming GEMV kernel serves this call (small M, no
 // THRESH_PACK, row length within its register budget).

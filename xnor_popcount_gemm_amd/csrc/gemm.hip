@@ -154,6 +154,96 @@ __device__ __forceinline__ void xnor_mainloop(uint32_t (&acc)[TN], const uint32_
     }
 }
 
+// Implicit im2col of a 3x3 / stride 1 / pad 1 binary convolution: the
+// activation operand is the packed NHWC image (one row of CW = C/32 words
+// per pixel, row stride ldc) and the virtual im2col row of output pixel p is
+// the CW words of each of its 9 neighbours (tap t = 3 kh + kw; k = t C + c,
+// the layout of the explicit im2col and of OHWI weights).  Taps outside the
+// image are +1, i.e. zero words ("First Principles", section "1.
+// Arithmetic": pad bits encode +1).  toff[t] is the neighbour's word offset
+// or -1 outside.  The 9 CW words run through the same 16-word chunks as the
+// dense loop (TPC = 16/CW taps per chunk; the last 9 CW % 16 words form a
+// short tail chunk); the next chunk's neighbour loads are in flight during
+// the current chunk's VALU work.
+template <int CW>
+__device__ __forceinline__ void conv_chunk_load(uint32_t* a, const uint32_t* __restrict__ Xp,
+                                                const int (&toff)[9], int t0, int ntaps)
+{
+#pragma unroll
+    for (int t = 0; t < ntaps; ++t) {
+        const int o = toff[t0 + t];
+        if (CW >= 4) {
+#pragma unroll
+            for (int q = 0; q < CW / 4; ++q) {
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (o >= 0) v = *reinterpret_cast<const uint4*>(Xp + o + 4 * q);
+                a[t * CW + 4 * q] = v.x; a[t * CW + 4 * q + 1] = v.y;
+                a[t * CW + 4 * q + 2] = v.z; a[t * CW + 4 * q + 3] = v.w;
+            }
+        } else {
+            uint2 v = make_uint2(0u, 0u);
+            if (o >= 0) v = *reinterpret_cast<const uint2*>(Xp + o);
+            a[t * CW] = v.x; a[t * CW + 1] = v.y;
+        }
+    }
+}
+
+template <int TN, int CW, bool FULLN>
+__device__ __forceinline__ void conv_mainloop(uint32_t (&acc)[TN], const uint32_t* __restrict__ Xp,
+                                              const int (&toff)[9], const uint32_t* __restrict__ wbase,
+                                              int64_t ldW, int nlast)
+{
+    constexpr int CP = (TN >= 2) ? 2 : 1;
+    constexpr int KC = 16;
+    constexpr int TPC = KC / CW;                  // taps per chunk
+    constexpr int NCH = 9 / TPC;                  // full chunks
+    constexpr int TT = 9 - NCH * TPC;             // taps in the tail chunk
+    uint32_t a[KC], an[KC];
+    if (NCH > 0) conv_chunk_load<CW>(an, Xp, toff, 0, TPC);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) a[kk] = an[kk];
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) asm volatile("" : : "v"(a[kk]));
+        if (c + 1 < NCH) conv_chunk_load<CW>(an, Xp, toff, (c + 1) * TPC, TPC);
+        xnor_chunk<TN, KC, CP, FULLN, false, false>(acc, a, wbase, wbase, c * KC, KC, ldW, nlast);
+    }
+    if (TT > 0) {
+        constexpr int TW = TT > 0 ? TT * CW : 1;
+        uint32_t t[TW];
+        conv_chunk_load<CW>(t, Xp, toff, NCH * TPC, TT);
+        xnor_chunk<TN, TW, CP, FULLN, false, false>(acc, t, wbase, wbase, NCH * KC, TW, ldW, nlast);
+    }
+}
+
+// Packed sign bits of a lane's TN outputs (bit j = column n0 + j), stored
+// like the THRESH_PACK bits: WB = min(TN, 32) bits per store; the last
+// column tile zeroes the rest of the row (pad bits and pad words).
+template <int TN>
+__device__ __forceinline__ void store_row_bits(const uint32_t (&wbits)[(TN + 31) / 32], uint32_t* __restrict__ orow,
+                                               int n0, int ncols, int N, int64_t ldOp, bool last_tile)
+{
+    constexpr int WB = TN < 32 ? TN : 32;
+#pragma unroll
+    for (int q = 0; q < TN / WB; ++q) {
+        const uint32_t word = WB == 32 ? wbits[q] : (wbits[0] >> (WB * q)) & ((1u << (WB & 31)) - 1u);
+        const int nb = n0 + WB * q;
+        if (nb < N) {
+            if (WB == 32) orow[nb >> 5] = word;
+            else if (WB == 16) reinterpret_cast<uint16_t*>(orow)[nb >> 4] = (uint16_t)word;
+            else reinterpret_cast<uint8_t*>(orow)[nb >> 3] = (uint8_t)word;
+        }
+    }
+    if (last_tile) {
+        uint8_t* ob = reinterpret_cast<uint8_t*>(orow);
+        const int64_t first = (int64_t)(n0 + WB * ((ncols + WB - 1) / WB)) / 8;   // after the last store
+        const int64_t wfirst = (first + 3) / 4;
+        for (int64_t b = first; b < wfirst * 4 && b < ldOp * 4; ++b) ob[b] = 0u;
+        for (int64_t w = wfirst; w < ldOp; ++w) orow[w] = 0u;
+    }
+}
+
 __device__ __forceinline__ bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
@@ -181,6 +271,7 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
 {
     constexpr int CH = TN < 32 ? TN : 32;
     constexpr int G4 = CH / 4;
+    constexpr int GLOG = G4 == 8 ? 3 : G4 == 4 ? 2 : G4 == 2 ? 1 : 0;
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int c0 = 0; c0 < TN; c0 += CH) {
@@ -226,6 +317,27 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
                     }
                     if (e.flags & EPI_RESIDUAL) y = y + rv[q];
                     __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(e.Y + (int64_t)m * e.ldY + n));
+                    if (e.flags & EPI_SIGN_PACK) {
+                        // sign(y - beta_n) as bits (0 = +1), OR-ed over the G4 lanes of the
+                        // row segment; the last lane stores the CH bits
+                        uint32_t nib = 0u;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float bt = e.beta ? e.beta[n + i] : 0.0f;
+                            nib |= (y[i] >= bt ? 0u : 1u) << i;
+                        }
+                        uint32_t bits = nib << (4 * cg);
+                        if (GLOG >= 1) bits |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits, 0x111, 0xF, 0xF, true);
+                        if (GLOG >= 2) bits |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits, 0x112, 0xF, 0xF, true);
+                        if (GLOG >= 3) bits |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits, 0x114, 0xF, 0xF, true);
+                        if (cg == G4 - 1) {
+                            const int nb = n0 + c0;
+                            uint32_t* orow = e.Op + (int64_t)m * e.ldOp;
+                            if (CH == 32) orow[nb >> 5] = bits;
+                            else if (CH == 16) reinterpret_cast<uint16_t*>(orow)[nb >> 4] = (uint16_t)bits;
+                            else reinterpret_cast<uint8_t*>(orow)[nb >> 3] = (uint8_t)bits;
+                        }
+                    }
                 }
             }
         }
@@ -233,10 +345,12 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
     }
 }
 
-template <int TN, int KC, bool EPI_LDS, int WAVES, bool TERN>
+// CW > 0: implicit-im2col 3x3 convolution over the packed NHWC image Xp
+// (CW words per pixel, row stride ldX, image convH x convW); K = 9 * 32 CW.
+template <int TN, int KC, bool EPI_LDS, int WAVES, bool TERN, int CW>
 __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
     const uint32_t* __restrict__ Xp, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
-    int M, int N, int K, int tiles_n, Epilogue e)
+    int M, int N, int K, int tiles_n, Epilogue e, int convH, int convW)
 {
     constexpr int kLdsWords = 64 * ((TN < 32 ? TN : 32) + 1);
     __shared__ uint32_t lds_epi[EPI_LDS ? WAVES * kLdsWords : 1];
@@ -257,8 +371,23 @@ __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
     uint32_t acc[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[j] = 0u;
-    if (n0 + TN <= N) xnor_mainloop<TN, KC, true, TERN>(acc, xrow, wbase, zbase, Kw, ldW, nlast);
-    else              xnor_mainloop<TN, KC, false, TERN>(acc, xrow, wbase, zbase, Kw, ldW, nlast);
+    if (CW > 0) {
+        // neighbour word offsets of this lane's output pixel (m = (b H + oh) W + ow)
+        const int mc = min(m, M - 1);
+        const int ow = mc % convW, oh = (mc / convW) % convH;
+        int toff[9];
+#pragma unroll
+        for (int t = 0; t < 9; ++t) {
+            const int dh = t / 3 - 1, dw = t % 3 - 1;
+            const bool inside = oh + dh >= 0 && oh + dh < convH && ow + dw >= 0 && ow + dw < convW;
+            toff[t] = inside ? (mc + dh * convW + dw) * (int)ldX : -1;
+        }
+        if (n0 + TN <= N) conv_mainloop<TN, (CW > 0 ? CW : 2), true>(acc, Xp, toff, wbase, ldW, nlast);
+        else              conv_mainloop<TN, (CW > 0 ? CW : 2), false>(acc, Xp, toff, wbase, ldW, nlast);
+    } else {
+        if (n0 + TN <= N) xnor_mainloop<TN, KC, true, TERN>(acc, xrow, wbase, zbase, Kw, ldW, nlast);
+        else              xnor_mainloop<TN, KC, false, TERN>(acc, xrow, wbase, zbase, Kw, ldW, nlast);
+    }
 
     const int ncols = min(TN, N - n0);
     const bool full = (ncols == TN);
@@ -269,6 +398,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
         (!(e.flags & EPI_BIAS) || aligned16(e.bias)) &&
         (!(e.flags & EPI_RESIDUAL) || (aligned16(e.R) && e.ldR % 4 == 0))) {
         epilogue_lds<TN, TERN>(acc, lds_epi + wave * kLdsWords, wrow0, M, n0, K, e);
+        if ((e.flags & EPI_SIGN_PACK) && tn == tiles_n - 1 && m < M) {
+            // the stores above covered the row's bits up to n0 + TN (a whole
+            // number of bytes); zero what follows up to ldOp words
+            uint32_t* orow = e.Op + (int64_t)m * e.ldOp;
+            uint8_t* ob = reinterpret_cast<uint8_t*>(orow);
+            const int64_t first = (int64_t)(n0 + TN) / 8;
+            const int64_t wfirst = (first + 3) / 4;
+            for (int64_t b = first; b < wfirst * 4 && b < e.ldOp * 4; ++b) ob[b] = 0u;
+            for (int64_t w = wfirst; w < e.ldOp; ++w) orow[w] = 0u;
+        }
         return;
     }
     if (m >= M) return;
@@ -284,6 +423,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
     const int astr = (e.flags & EPI_ALPHA_TENSOR) ? 0 : 1;
     cptr_f32 al = (cptr_f32)(e.alpha + n0 * astr);
     cptr_f32 bi = (cptr_f32)(e.bias + n0);
+    uint32_t sbits[(TN + 31) / 32];               // SIGN_PACK: bit j = sign of column n0 + j
+#pragma unroll
+    for (int w = 0; w < (TN + 31) / 32; ++w) sbits[w] = 0u;
 #pragma unroll
     for (int q = 0; q < TN / 4; ++q) {
         int32_t d[4];
@@ -318,8 +460,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_xnor_gemm(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) if (4 * q + i < ncols) yrow[4 * q + i] = y[i];
             }
+            if (e.flags & EPI_SIGN_PACK) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = 4 * q + i;
+                    const float bt = e.beta ? e.beta[n0 + min(j, ncols - 1)] : 0.0f;
+                    if (j < ncols && !(y[i] >= bt)) sbits[j >> 5] |= 1u << (j & 31);
+                }
+            }
         }
     }
+    if (e.flags & EPI_SIGN_PACK)
+        store_row_bits<TN>(sbits, e.Op + (int64_t)m * e.ldOp, n0, ncols, N, e.ldOp, tn == tiles_n - 1);
     if (e.flags & EPI_THRESH) {
         // Output bits of this lane's row, packed along n: bit (n % 32) of word
         // n / 32.  A tile owns TN/8 whole bytes of the row (n0 is a multiple
@@ -413,9 +565,9 @@ hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
     const int m = (int)M, n = (int)N, k = (int)K;
     // ternary weights: two SGPR planes per word, so 8-word chunks (the same
     // SGPR budget as the binary 16-word chunks) and 4-wave workgroups
-#define BNN_GEMM(T, L, WV) hipLaunchKernelGGL((k_xnor_gemm<T, 16, L, WV, false>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e)
+#define BNN_GEMM(T, L, WV) hipLaunchKernelGGL((k_xnor_gemm<T, 16, L, WV, false, 0>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e, 0, 0)
 #define BNN_GEMM_W(T, L) \
-    if (e.flags & W_TERNARY) hipLaunchKernelGGL((k_xnor_gemm<T, 8, L, 4, true>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e); \
+    if (e.flags & W_TERNARY) hipLaunchKernelGGL((k_xnor_gemm<T, 8, L, 4, true, 0>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e, 0, 0); \
     else switch (waves) { case 8: BNN_GEMM(T, L, 8); break; case 16: BNN_GEMM(T, L, 16); break; default: BNN_GEMM(T, L, 4); break; }
     if (lds) {
         switch (tn) {
@@ -434,6 +586,37 @@ hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
     }
 #undef BNN_GEMM_W
 #undef BNN_GEMM
+    return hipGetLastError();
+}
+
+hipError_t launch_xnor_conv3x3(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
+                               int64_t M, int64_t N, int64_t H, int64_t W, int cw,
+                               const Epilogue& e, hipStream_t s)
+{
+    // the same column-tile choice and LDS epilogue rule as the dense GEMM
+    const int64_t row_waves = (M + 63) / 64;
+    int tn = tile_cols_from_env();
+    if (tn == 0) {
+        const int64_t rounds_wave = (int64_t)num_cus() * 4 * 8;
+        if (row_waves * ((N + 63) / 64) >= 6 * rounds_wave) tn = 64;
+        else if (row_waves * ((N + 31) / 32) >= 3 * rounds_wave) tn = 32;
+        else tn = N <= 8 ? 8 : 16;
+    }
+    const int64_t kw = 9 * (int64_t)cw;
+    const bool lds = kw <= 128 && (e.flags & (EPI_DOT | EPI_SCALE)) && !(e.flags & EPI_THRESH);
+    const int64_t row_tiles = (M + 255) / 256;
+    const int tiles_n = (int)((N + tn - 1) / tn);
+    const dim3 grid((unsigned)(row_tiles * tiles_n)), block(256);
+    const int m = (int)M, n = (int)N, k = (int)(32 * kw), h = (int)H, w = (int)W;
+#define BNN_CONV(T, L, C) hipLaunchKernelGGL((k_xnor_gemm<T, 16, L, 4, false, C>), grid, block, 0, s, Xp, ldX, Wp, ldW, m, n, k, tiles_n, e, h, w)
+#define BNN_CONV_C(T, L) switch (cw) { case 2: BNN_CONV(T, L, 2); break; case 4: BNN_CONV(T, L, 4); break; \
+                                       case 8: BNN_CONV(T, L, 8); break; default: BNN_CONV(T, L, 16); break; }
+#define BNN_CONV_T(L) switch (tn) { case 64: BNN_CONV_C(64, L); break; case 32: BNN_CONV_C(32, L); break; \
+                                    case 16: BNN_CONV_C(16, L); break; default: BNN_CONV_C(8, L); break; }
+    if (lds) { BNN_CONV_T(true) } else { BNN_CONV_T(false) }
+#undef BNN_CONV_T
+#undef BNN_CONV_C
+#undef BNN_CONV
     return hipGetLastError();
 }
 

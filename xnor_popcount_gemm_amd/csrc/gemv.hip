@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
 
 bool gemv_eligible(int64_t M, int64_t K, uint32_t flags) {
     const int64_t kw4 = ((K + 31) / 32 + 3) / 4;
-    return M >= 1 && M <= 4 && !(flags & EPI_THRESH) && kw4 <= 64 * 8;
+    return M >= 1 && M <= 4 && !(flags & (EPI_THRESH | EPI_SIGN_PACK)) && kw4 <= 64 * 8;
 }
 
 hipError_t launch_xnor_gemv(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,

@@ -295,6 +295,47 @@ __global__ __launch_bounds__(kThreads) void k_pack_ternary(
     }
 }
 
+// RSign ("State of the Art Survey", ReActNet row): the sign of x - beta_k,
+// decided as the IEEE single comparison x >= beta_k (bit 0 for +1; NaN -> 1),
+// with one shift per column k (per channel of an NHWC image viewed as
+// [pixels, C]).  Same mapping as k_pack_dense; positions >= K are +1 (0).
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_pack_dense_rsign(
+    const float* __restrict__ X, int64_t rows, int K, int64_t ldX, const float* __restrict__ beta,
+    uint32_t* __restrict__ P, int64_t ldP)
+{
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & 7;
+    const int grp = lane >> 3;
+    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+    const int ldp = (int)ldP;
+    for (int64_t r = wave; r < rows; r += nwaves) {
+        const float* __restrict__ xr = X + r * ldX;
+        uint32_t* __restrict__ pr = P + r * ldP;
+        for (int w0 = 0; w0 < ldp; w0 += 8 * kSteps) {
+            Frag f[kSteps];
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u)
+                f[u] = load_frag<VEC>(xr, 32 * (w0 + 8 * u + grp) + 4 * sub, K);
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const int w = w0 + 8 * u + grp;
+                const int k0 = 32 * w + 4 * sub;
+                uint32_t nib = 0u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int k = k0 + i;
+                    const bool neg = k < K && !(__uint_as_float(f[u].u[i]) >= beta[k]);
+                    nib |= (neg ? 1u : 0u) << i;
+                }
+                const uint32_t word = or_reduce8_to_last(nib << (4 * sub));
+                if (sub == 7 && w < ldp) pr[w] = word;
+            }
+        }
+    }
+}
+
 int grid_for_rows(int64_t rows) {
     const int64_t waves_per_block = kThreads / 64;
     int64_t blocks = (rows + waves_per_block - 1) / waves_per_block;
@@ -442,6 +483,16 @@ hipError_t launch_pack_ternary(const float* W, int64_t N, int64_t K, int64_t ldW
     if (gamma) { if (vec) BNN_TPACK(true, true); else BNN_TPACK(false, true); }
     else       { if (vec) BNN_TPACK(true, false); else BNN_TPACK(false, false); }
 #undef BNN_TPACK
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_dense_rsign(const float* X, int64_t rows, int64_t K, int64_t ldX, const float* beta,
+                                   uint32_t* P, int64_t ldP, hipStream_t s)
+{
+    const bool vec = aligned16(X) && (ldX % 4 == 0);
+    const dim3 grid(grid_for_rows(rows)), block(kThreads);
+    if (vec) hipLaunchKernelGGL((k_pack_dense_rsign<true>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
+    else     hipLaunchKernelGGL((k_pack_dense_rsign<false>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
     return hipGetLastError();
 }
 
