@@ -549,6 +549,62 @@ def conv_bench(bnn, torch, shape, reps=10, warmup=2):
     )
 
 
+def conv_chain_bench(bnn, torch, shape, blocks=4, reps=5, warmup=1):
+    """Chained binary conv blocks (Bi-Real shortcut, RSign inputs): the first
+    packed image from RSign of the fp32 input, then per block the
+    implicit-im2col conv with the fp32 residual and, fused, the packed RSign
+    input of the next block.  Per-block HBM bytes: packed image read, residual
+    read, Y written, next packed image written."""
+    import workloads
+    B, H, Wd, C = shape["B"], shape["H"], shape["W"], shape["C"]
+    M = B * H * Wd
+    log(f"conv chain {H}x{Wd}x{C} x{blocks}: preparing")
+    X = torch.from_numpy(workloads.normal_f32(workloads.seed_for(5, 0) + C, (M, C))).cuda()
+    Wps, als, bts = [], [], []
+    for l in range(blocks):
+        Wt = torch.from_numpy(workloads.normal_f32(workloads.seed_for(5, 1) + C + 10 * l, (C, 9 * C))).cuda()
+        wp, a = bnn.pack_weights(Wt)
+        Wps.append(wp); als.append(a)
+        bts.append(torch.from_numpy(workloads.normal_f32(workloads.seed_for(5, 2) + C + l, (C,)) * 0.3).cuda())
+    ld = bnn.padded_ld(C)
+    imgs = [torch.empty((M, ld), dtype=torch.int32, device="cuda") for _ in range(2)]
+    Ys = [torch.empty((M, C), dtype=torch.float32, device="cuda") for _ in range(2)]
+    fl = bnn.EPI_SCALE_F32 | bnn.EPI_RESIDUAL_F32 | bnn.EPI_SIGN_PACK
+
+    def chain(ev):
+        if ev: ev[0].start()
+        bnn.pack_activations_rsign(X, bts[0], out=imgs[0])
+        if ev: ev[0].stop()
+        R = X
+        for l in range(blocks):
+            if ev: ev[1 + l].start()
+            bnn.conv3x3_fused(imgs[l % 2], Wps[l], (B, H, Wd, C), fl, alpha=als[l], R=R,
+                              beta=bts[(l + 1) % blocks], Y=Ys[l % 2], Op=imgs[(l + 1) % 2])
+            if ev: ev[1 + l].stop()
+            R = Ys[l % 2]
+
+    for _ in range(warmup):
+        chain(None)
+    pool = [[Ev() for _ in range(blocks + 1)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for ev in pool:
+        chain(ev)
+    torch.cuda.synchronize()
+    first_ms = median([ev[0].ms() for ev in pool])
+    block_ms = statistics.mean([ev[1 + l].ms() for ev in pool for l in range(blocks)])
+    kw = 9 * C // 32
+    lane_ops = 2.0 * M * C * kw
+    block_bytes = 4.0 * M * ld + 4.0 * M * C + 4.0 * M * C + 4.0 * M * ld
+    ideal_ms = 1e3 * max(block_bytes / PEAK_HBM, lane_ops / PEAK_INT_OPS)
+    res = dict(B=B, H=H, W=Wd, C=C, M=M, blocks=blocks, first_pack_ms=first_ms, block_ms=block_ms,
+               block_bytes=block_bytes, block_GBps=block_bytes / (block_ms * 1e-3) / 1e9,
+               block_ideal_ms=ideal_ms, block_frac_of_bound=ideal_ms / block_ms,
+               block_int_valu_frac=lane_ops / (block_ms * 1e-3) / PEAK_INT_OPS)
+    del X, Wps, imgs, Ys
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(M, N, K, target_s):
     """The oracle (unchanged) on a row sample of the same GEMM step: the
     weight-side work (sign and alpha of all N rows) once, the per-row chain
@@ -618,7 +674,8 @@ def main():
             r = {"gemv": [i8_gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]],
                  "gemm": i8_gemm_bench(bnn, torch, 8192, 8192, 8192)}
         else:
-            r = [conv_bench(bnn, torch, s) for s in workloads.WORKLOADS[5]["shapes"]]
+            r = {"block": [conv_bench(bnn, torch, s) for s in workloads.WORKLOADS[5]["shapes"]],
+                 "chain": [conv_chain_bench(bnn, torch, s) for s in workloads.WORKLOADS[5]["shapes"]]}
         if args.copy_calib:
             copy_calibration(torch)
         print(json.dumps({"only": args.only, "result": r}))
@@ -714,6 +771,7 @@ def main():
         sec["ternary"] = ternary_bench(bnn, torch)
         sec["binary_mlp_batch1024"] = mlp_bench(bnn, torch)
         sec["conv_block"] = [conv_bench(bnn, torch, s) for s in workloads.WORKLOADS[5]["shapes"]]
+        sec["conv_chain"] = [conv_chain_bench(bnn, torch, s) for s in workloads.WORKLOADS[5]["shapes"]]
         line["secondary"] = sec
     print(json.dumps(line), flush=True)
 
