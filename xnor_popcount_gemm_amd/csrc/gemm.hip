@@ -199,6 +199,10 @@ __device__ __forceinline__ void conv_mainloop(uint32_t (&acc)[TN], const uint32_
     constexpr int NCH = 9 / TPC;                  // full chunks
     constexpr int TT = 9 - NCH * TPC;             // taps in the tail chunk
     uint32_t a[KC], an[KC];
+    constexpr int TW = TT > 0 ? TT * CW : 1;
+    uint32_t t[TW];
+    // the tail taps are requested with the first chunk: no exposed load at the end
+    if (TT > 0) conv_chunk_load<CW>(t, Xp, toff, NCH * TPC, TT);
     if (NCH > 0) conv_chunk_load<CW>(an, Xp, toff, 0, TPC);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -209,12 +213,7 @@ __device__ __forceinline__ void conv_mainloop(uint32_t (&acc)[TN], const uint32_
         if (c + 1 < NCH) conv_chunk_load<CW>(an, Xp, toff, (c + 1) * TPC, TPC);
         xnor_chunk<TN, KC, CP, FULLN, false, false>(acc, a, wbase, wbase, c * KC, KC, ldW, nlast);
     }
-    if (TT > 0) {
-        constexpr int TW = TT > 0 ? TT * CW : 1;
-        uint32_t t[TW];
-        conv_chunk_load<CW>(t, Xp, toff, NCH * TPC, TT);
-        xnor_chunk<TN, TW, CP, FULLN, false, false>(acc, t, wbase, wbase, NCH * KC, TW, ldW, nlast);
-    }
+    if (TT > 0) xnor_chunk<TN, TW, CP, FULLN, false, false>(acc, t, wbase, wbase, NCH * KC, TW, ldW, nlast);
 }
 
 // Packed sign bits of a lane's TN outputs (bit j = column n0 + j), stored
@@ -280,7 +279,7 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
         // The residual and alpha pieces of all passes are requested before
         // any is used, so their latencies overlap instead of adding up.
         f32x4 rv[G4];
-        float4 av[G4], bv[G4];
+        float4 av[G4], bv[G4], tv[G4];
 #pragma unroll
         for (int q = 0; q < G4; ++q) {
             const int idx = q * 64 + lane;
@@ -292,6 +291,10 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
                 else av[q] = *reinterpret_cast<const float4*>(e.alpha + n);
             }
             if (e.flags & EPI_BIAS) bv[q] = *reinterpret_cast<const float4*>(e.bias + n);
+            if (e.flags & EPI_SIGN_PACK) {
+                tv[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (e.beta) tv[q] = make_float4(e.beta[n], e.beta[n + 1], e.beta[n + 2], e.beta[n + 3]);
+            }
             if (e.flags & EPI_RESIDUAL)
                 rv[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(e.R + (int64_t)m * e.ldR + n));
         }
@@ -320,12 +323,9 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
                     if (e.flags & EPI_SIGN_PACK) {
                         // sign(y - beta_n) as bits (0 = +1), OR-ed over the G4 lanes of the
                         // row segment; the last lane stores the CH bits
-                        uint32_t nib = 0u;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float bt = e.beta ? e.beta[n + i] : 0.0f;
-                            nib |= (y[i] >= bt ? 0u : 1u) << i;
-                        }
+                        const float4 bt = tv[q];
+                        const uint32_t nib = (y[0] >= bt.x ? 0u : 1u) | ((y[1] >= bt.y ? 0u : 1u) << 1) |
+                                             ((y[2] >= bt.z ? 0u : 1u) << 2) | ((y[3] >= bt.w ? 0u : 1u) << 3);
                         uint32_t bits = nib << (4 * cg);
                         if (GLOG >= 1) bits |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits, 0x111, 0xF, 0xF, true);
                         if (GLOG >= 2) bits |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits, 0x112, 0xF, 0xF, true);
