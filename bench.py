@@ -339,27 +339,34 @@ def i8_gemm_bench(bnn, torch, M, N, K, reps=10, warmup=2):
     flags = bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32
     pool = [(Ev(), Ev()) for _ in range(reps)]
 
-    def step(e):
+    def step(e, rowsums=True):
+        # the quantizer also writes the row sums, which let the GEMM expand
+        # the weight bits to 0/1 bytes (cheaper than +1/-1)
         if e: e[0].start()
-        q = bnn.quantize_act_i8(X, want_planes=False)
+        q = bnn.quantize_act_i8(X, want_planes=False, want_xsum=rowsums)
         if e: e[0].stop(); e[1].start()
-        bnn.bwn_i8_linear(Wp, K, flags, Xq=q["Xq"], xscale=q["xscale"], alpha=a, D=D, Y=Y)
+        bnn.bwn_i8_linear(Wp, K, flags, Xq=q["Xq"], xsum=q["xsum"], xscale=q["xscale"], alpha=a, D=D, Y=Y)
         if e: e[1].stop()
 
-    for _ in range(warmup):
-        step(None)
-    torch.cuda.synchronize()
-    for e in pool:
-        step(e)
-    torch.cuda.synchronize()
-    qms = [e[0].ms() for e in pool]
-    gms = [e[1].ms() for e in pool]
+    res = dict(M=M, N=N, K=K)
     ops = 2.0 * M * N * K
-    t = statistics.mean(gms) * 1e-3
-    res = dict(M=M, N=N, K=K, gemm_ms_mean=statistics.mean(gms), gemm_ms_median=median(gms),
-               quantize_ms_median=median(qms), int8_tops=ops / t / 1e12,
-               frac_int8_mfma_peak=ops / t / PEAK_INT8_MFMA,
-               quantize_GBps=(4.0 * M * K + 1.0 * M * K + 4.0 * M) / (median(qms) * 1e-3) / 1e9)
+    for rowsums in (False, True):
+        for _ in range(warmup):
+            step(None, rowsums)
+        torch.cuda.synchronize()
+        for e in pool:
+            step(e, rowsums)
+        torch.cuda.synchronize()
+        qms = [e[0].ms() for e in pool]
+        gms = [e[1].ms() for e in pool]
+        t = statistics.mean(gms) * 1e-3
+        if not rowsums:
+            res.update(gemm_ms_mean_signs=statistics.mean(gms), int8_tops_signs=ops / t / 1e12)
+            continue
+        res.update(gemm_ms_mean=statistics.mean(gms), gemm_ms_median=median(gms),
+                   quantize_ms_median=median(qms), int8_tops=ops / t / 1e12,
+                   frac_int8_mfma_peak=ops / t / PEAK_INT8_MFMA,
+                   quantize_GBps=(4.0 * M * K + 1.0 * M * K + 8.0 * M) / (median(qms) * 1e-3) / 1e9)
     del X, Wp, a, D, Y
     torch.cuda.empty_cache()
     return res

@@ -127,11 +127,17 @@ typedef struct bnn_fused_args {
  * struct; every pointer is device memory.  The activations come in either
  * (or both) of two forms written by bnn_quantize_act_i8 / bnn_pack_act_i8:
  *   bit planes  Xb [M, 8, ldXb] + xsum [M]  (read by the bit-plane GEMV);
- *   int8 rows   Xq [M, ldXq]                (read by the MFMA GEMM). */
+ *   int8 rows   Xq [M, ldXq]                (read by the MFMA GEMM, with
+ *                                            xsum too when given). */
 typedef struct bnn_i8_args {
     const uint32_t* Xb; int64_t ldXb; /* planes: 16-byte aligned, ldXb % 4 == 0,
                                          ldXb >= ceil(K/32); plane pad bits 0  */
-    const int32_t* xsum;              /* [M] row sums of the int8 values        */
+    const int32_t* xsum;              /* [M] row sums of the int8 values: sum
+                                         over k < K of q[m,k] (4-byte aligned);
+                                         required by the GEMV with binary
+                                         weights; optional for the GEMM, which
+                                         with binary weights then trusts it
+                                         (a cheaper weight expansion)         */
     const int8_t* Xq; int64_t ldXq;   /* int8 rows: 16-byte aligned, ldXq % 16
                                          == 0, ldXq >= K; the GEMM reads whole
                                          16-byte pieces of a row below ldXq
@@ -286,7 +292,8 @@ bnn_status bnn_weight_scale_tensor(const float* W, int64_t N, int64_t K, int64_t
  *        (m*8 + b)*ldXb and holds bit b of each two's-complement byte q[m,k]
  *        at word k/32, bit k%32; pad bits and pad words are written 0;
  *        16-byte aligned, ldXb % 4 == 0, ldXb >= ceil(K/32);
- *  xsum  int32 [M] = sum_k q[m,k] (required with Xb, else ignored);
+ *  xsum  int32 [M] = sum_k q[m,k] (required with Xb; else written when
+ *        non-NULL);
  *  xscale fp32 [M] (required).
  *  X fp32 [M, ldX], ldX >= K.  1 <= K <= BNN_MAX_K_I8. */
 bnn_status bnn_quantize_act_i8(const float* X, int64_t M, int64_t K, int64_t ldX,

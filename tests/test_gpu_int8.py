@@ -98,6 +98,12 @@ def test_quantize_unaligned_source_and_single_outputs(bnn):
     np.testing.assert_array_equal(host_u32(b["Xb"]), P_ref)
     np.testing.assert_array_equal(host(b["xsum"]), xs_ref)
     _bits_equal(host(b["xscale"]), s_ref, "xscale")
+    banner("quantize_act_i8 int8 + row sums, no planes")
+    c = bnn.quantize_act_i8(Xt, want_planes=False, want_xsum=True)
+    torch.cuda.synchronize()
+    assert c["Xb"] is None
+    np.testing.assert_array_equal(host(c["Xq"]), Q_ref)
+    np.testing.assert_array_equal(host(c["xsum"]), xs_ref)
 
 
 @pytest.mark.parametrize("M,K,pad", [(1, 1, 0), (2, 33, 4), (3, 4096, 0), (5, 1000, 8), (1, 11008, 0),
@@ -135,6 +141,8 @@ def _check_linear(bnn, Q, xscale, W, ws, a, *, path, per_tensor=False):
         Qd = torch.zeros((M, bnn.i8_ld(K)), dtype=torch.int8, device="cuda")
         Qd[:, :K] = dev(Q)
         kw = dict(Xq=Qd[:, :K])
+        if path == "gemm_xsum":                     # row sums given: the 0/1 weight expansion
+            kw["xsum"] = dev(Q.astype(np.int64).sum(axis=1).astype(np.int32))
     xs_d = dev(xscale) if xscale is not None else None
     out = bnn.bwn_i8_linear(Wp, K, flags, alpha=dev(alpha), xscale=xs_d, **kw)
     torch.cuda.synchronize()
@@ -164,21 +172,23 @@ def test_bwn_i8_gemv_matches_oracle(bnn, M, N, K):
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 64), (16, 16, 63), (64, 128, 1000), (130, 257, 100),
                                    (200, 300, 4096), (3, 1000, 11008), (129, 129, 129), (1, 64, 65),
                                    (600, 200, 1000), (513, 129, 130), (257, 385, 192)])
-def test_bwn_i8_gemm_matches_oracle(bnn, M, N, K):
+@pytest.mark.parametrize("path", ["gemm", "gemm_xsum"])
+def test_bwn_i8_gemm_matches_oracle(bnn, M, N, K, path):
     W, ws, a = _weights(7600 + K, N, K)
     X = _act_rows(7700 + K, M, K)
     Q, xs = oracle.quantize_absmax_i8(X)
-    banner(f"bwn_i8 gemm quantized M={M} N={N} K={K}")
-    _check_linear(bnn, Q, xs, W, ws, a, path="gemm")
+    banner(f"bwn_i8 {path} quantized M={M} N={N} K={K}")
+    _check_linear(bnn, Q, xs, W, ws, a, path=path)
     Qf = _full_range_i8(7800 + K, M, K)
-    banner(f"bwn_i8 gemm full-range int8 M={M} N={N} K={K}")
-    _check_linear(bnn, Qf, None, W, ws, a, path="gemm", per_tensor=True)
+    banner(f"bwn_i8 {path} full-range int8 M={M} N={N} K={K}")
+    _check_linear(bnn, Qf, None, W, ws, a, path=path, per_tensor=True)
 
 
-@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("path", ["gemv", "gemm", "gemm_xsum"])
 def test_bwn_i8_extreme_sums(bnn, path):
     # |D| reaches 128 K at the largest K: every activation -128, every weight -1
     M, N, K = (1 if path == "gemv" else 4), 8, 32768 if path == "gemv" else 131072
+    # (with row sums: xsum = -2^24 and D = xsum - 2 sum q w reaches +2^24)
     Q = np.full((M, K), -128, np.int8)
     W = -np.ones((N, K), np.float32)
     W[1::2] *= -1.0                                  # odd rows +1
@@ -196,7 +206,7 @@ def test_bwn_i8_strided_outputs_and_dot_only(bnn):
     Qd = torch.zeros((M, bnn.i8_ld(K)), dtype=torch.int8, device="cuda")
     Qd[:, :K] = dev(Q)
     D_ref = oracle.dot_i8(Q, ws)
-    for kw in (dict(Xb=Xb, xsum=xsum), dict(Xq=Qd[:, :K])):
+    for kw in (dict(Xb=Xb, xsum=xsum), dict(Xq=Qd[:, :K]), dict(Xq=Qd[:, :K], xsum=xsum, M=M)):
         Dbig = torch.full((M, N + 13), -7, dtype=torch.int32, device="cuda")
         banner(f"bwn_i8 strided D {list(kw)}")
         bnn.bwn_i8_linear(Wp, K, bnn.EPI_DOT_I32, D=Dbig[:, :N], **kw)

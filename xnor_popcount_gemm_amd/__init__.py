@@ -381,18 +381,24 @@ def _planes_ld(Xb: torch.Tensor) -> int:
     return Xb.stride(1)
 
 
-def quantize_act_i8(X: torch.Tensor, *, want_int8: bool = True, want_planes: bool = True):
+def quantize_act_i8(X: torch.Tensor, *, want_int8: bool = True, want_planes: bool = True,
+                    want_xsum: bool | None = None):
     """Absmax INT8 quantization per row of fp32 X [M, K].
 
     Returns a dict: ``Xq`` int8 [M, K] (row stride a multiple of 16) or None,
-    ``Xb`` int32 bit planes [M, 8, ld] and ``xsum`` int32 [M] (or None), and
-    ``xscale`` fp32 [M] (X ~= xscale * Xq)."""
+    ``Xb`` int32 bit planes [M, 8, ld] (or None), ``xsum`` int32 [M] row
+    sums (always with planes; else when ``want_xsum``), and ``xscale`` fp32
+    [M] (X ~= xscale * Xq)."""
     _dev(X, torch.float32, "X")
     M, K = X.shape
     dev = X.device
+    if want_xsum is None:
+        want_xsum = want_planes
+    if want_planes and not want_xsum:
+        raise ValueError("bit planes come with their row sums")
     Xq = torch.empty((M, i8_ld(K)), dtype=torch.int8, device=dev)[:, :K] if want_int8 else None
     Xb = torch.empty((M, 8, padded_ld(K)), dtype=torch.int32, device=dev) if want_planes else None
-    xsum = torch.empty(M, dtype=torch.int32, device=dev) if want_planes else None
+    xsum = torch.empty(M, dtype=torch.int32, device=dev) if want_xsum else None
     xscale = torch.empty(M, dtype=torch.float32, device=dev)
     _check(lib().bnn_quantize_act_i8(_ptr(X), M, K, _ld(X),
                                      _ptr(Xq), Xq.stride(0) if Xq is not None else 0,

@@ -164,6 +164,7 @@ bnn_status validate_i8(const bnn_i8_args* a) {
         if (a->xsum && misaligned4(a->xsum)) return BNN_ERR_ALIGN;
     } else {
         if ((st = check_i8_rows(a->Xq, a->K, a->ldXq)) != BNN_OK) return st;
+        if (a->xsum && misaligned4(a->xsum)) return BNN_ERR_ALIGN;
         // the GEMM addresses activation rows with 32-bit byte offsets
         if (a->M * a->ldXq > ((int64_t)1 << 31) - 1) return BNN_ERR_SHAPE;
     }
@@ -189,8 +190,8 @@ bnn_status check_act_i8_out(int64_t M, int64_t K, uint32_t* Xb, int64_t ldXb, in
     if (Xb) {
         if ((st = check_packed(Xb, K, ldXb)) != BNN_OK) return st;
         if (!xsum) return BNN_ERR_NULL;
-        if (misaligned4(xsum)) return BNN_ERR_ALIGN;
     }
+    if (xsum && misaligned4(xsum)) return BNN_ERR_ALIGN;
     return BNN_OK;
 }
 
@@ -388,6 +389,7 @@ bnn_status bnn_bwn_i8_linear(const bnn_i8_args* args, bnn_stream_t stream)
     e.xscale = args->xscale;
     e.Y = args->Y; e.ldY = args->ldY;
     e.Zp = args->Zp;
+    e.xsum = (args->epilogue & BNN_W_TERNARY) ? nullptr : args->xsum;
     hipStream_t s = as_stream(stream);
     if (i8_path(args) == 1)
         return from_hip(bnn::launch_bwn_i8_gemv(args->Xb, args->ldXb, args->xsum, args->Wp, args->ldWp,

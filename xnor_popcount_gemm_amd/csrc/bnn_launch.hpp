@@ -34,6 +34,7 @@ struct EpilogueI8 {
     const float* xscale;     // [M] or nullptr
     float* Y; int64_t ldY;
     const uint32_t* Zp;      // ternary weights (W_TERNARY): nonzero plane
+    const int32_t* xsum;     // MFMA GEMM, binary weights: [M] row sums of q, or nullptr
 };
 
 hipError_t launch_pack_dense(const float* X, int64_t rows, int64_t K, int64_t ldX,

@@ -10,26 +10,40 @@
 // With many activation rows this is a dense contraction, so it runs on the
 // int8 matrix cores: v_mfma_i32_16x16x64_i8 (16 rows x 16 columns x 64 k per
 // instruction, exact int32 accumulation).  The weights stay 1-bit in memory;
-// each lane expands the 16 weight bits of its B fragment to 16 bytes of
-// +1 / -1 right before the MFMA (a multiply spreads a nibble into bytes; an
-// XOR turns 0/1 bytes into 0x01/0xFF without borrows between bytes).
+// each lane expands the 16 weight bits of its B fragment to 16 bytes right
+// before the MFMA (a multiply spreads a nibble into bytes).  Given the row
+// sums xsum[m] = sum_k q[m,k], the bytes are the bits themselves (0 / 1)
+// and D = xsum - 2 sum_k q w; otherwise an XOR makes them +1 / -1 (0x01 /
+// 0xFF, no borrows between bytes).
+//
+// On this chip a SIMD does not issue VALU work while its matrix core runs an
+// MFMA (measured: the times add), so the expansion cost counts in full.  It
+// is spent per weight column and amortised over the rows that share the
+// expanded fragment; each wave therefore spans all 256 rows of the
+// workgroup tile: 16 x 2 fragments, 32 MFMAs per 64-wide k-step against 2
+// weight-fragment expansions.
 //
 // Fragment layout used for both operands: lane l holds row (A) or column (B)
 // l % 16 and the 16 consecutive k of group l / 16 within the 64-wide step.
 // A and B use the same k assignment, so each output is the full sum over k.
 // The int32 result of lane l, register r is row 4*(l/16) + r, column l % 16.
 //
-// Tiling: a 256-thread workgroup computes 256 activation rows x 128 weight
-// rows; wave w takes rows 128*(w/2) .. +127 and columns 64*(w%2) .. +63,
-// i.e. 8 x 4 fragments (32 MFMAs per 64-wide k-half against 4 weight
-// expansions, two halves per 128-wide k-step).  The workgroup's A tile
-// (256 rows x 128 bytes per k-step) is staged through LDS, double-buffered
-// with one barrier per k-step; 16-byte piece j of row r sits at slot
-// j ^ ((r / 2) % 8) of the row's eight slots, so the 16 lanes of a fragment
-// read (16 rows, one k-group) hit 16 distinct 4-bank groups.  The next
-// k-step's A pieces go straight from global memory into the other LDS
-// buffer, and its weight words into registers, before the current step's
-// MFMAs.
+// Tiling: a 512-thread workgroup (8 waves) computes 256 activation rows x
+// 256 weight rows; wave w takes all rows and columns 32 w .. +31.  The
+// workgroup's A tile (256 rows x 64 bytes per k-step) goes straight from
+// global memory into a ring of 4 LDS buffers (global_load_lds), issued 3
+// steps ahead of its use, with one barrier per step; 16-byte piece j of A
+// row r sits at slot j ^ h(r), h(r) = ((r / 2) ^ (r / 4)) % 4, of the row's
+// four slots.  A fragment read (16 rows of one k-group) then has every 8
+// consecutive lanes on 8 distinct 4-bank groups of a 32-bank window:
+// 16-byte LDS reads are served 8 lanes at a time, and a pattern that is
+// only distinct across 16 lanes (h = (r / 4) % 4) measured half the
+// throughput of this one.  The weight bits move in chunks of 8 k-steps
+// (64 bytes per weight row, whole 64-byte L2 requests; a request per row
+// and step would carry 8 useful bytes) into a double-buffered LDS chunk,
+// one chunk ahead.  With the A tile shared by 256 weight rows, the L2
+// request rate (the limit of a 256 x 128 tile) stays below one per clock
+// and channel.
 #include <type_traits>
 
 #include "bnn_device.hpp"
@@ -38,8 +52,14 @@
 namespace bnn {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBM = 256, kBN = 128, kKS = 128;   // kKS: two MFMA k-widths per step
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kBM = 256, kBN = 256, kKS = 64;  // workgroup tile: activation rows x weight rows x k-step
+constexpr int kWN = kBN / kWaves;               // wave tile: all kBM rows x kWN columns
+constexpr int kFM = kBM / 16, kFN = kWN / 16;   // 16 x 16 fragments per wave tile
+constexpr int kNB = 4;          // A ring depth: a step's loads are issued kNB - 1 steps ahead
+constexpr int kCS = 8;          // k-steps per weight chunk (64 bytes of bits per weight row)
+constexpr int kCW = kCS * kKS / 32;             // words per weight row in a chunk (16)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -77,6 +97,15 @@ __device__ __forceinline__ v4i expand_signs(uint32_t bits16) {
     return r;
 }
 
+// 16 weight bits to 16 bytes holding the bits themselves (0 or 1).
+__device__ __forceinline__ v4i expand_bits01(uint32_t bits16) {
+    v4i r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        r[q] = (int)((((bits16 >> (4 * q)) & 0xFu) * 0x00204081u) & 0x01010101u);
+    return r;
+}
+
 // Ternary weights ("Extreme Quantization", eq. (7) / (9)): c holds the
 // lane's 16 nonzero bits (Z) in its low half and its 16 bits of -1 weights
 // (S & Z) in its high half; each byte becomes 0x01 (+1), 0xFF (-1) or 0.
@@ -93,190 +122,304 @@ __device__ __forceinline__ v4i expand_ternary(uint32_t c) {
     return r;
 }
 
-constexpr int kAPieces = kBM * kKS / 16 / kThreads;   // 16-byte A pieces per lane per k-step
+constexpr int kAPieces = kBM * kKS / 16 / kThreads;      // 16-byte A pieces per lane per k-step
+constexpr int kBPieces = kBN * kCW * 4 / 16 / kThreads;  // 16-byte weight pieces per lane per chunk
+static_assert(kAPieces == 2 && kBPieces == 2 && kFN == 2, "the staging below assumes these");
+
+// s_waitcnt immediate that waits for at most n outstanding vector-memory
+// operations (vmcnt in bits 3:0 and 15:14) and not on the other counters.
+constexpr unsigned waitcnt_vm(int n) {
+    return (unsigned)(n & 0xF) | ((unsigned)((n >> 4) & 3) << 14) | (0x7u << 4) | (0xFu << 8);
+}
+
+// Workgroup barrier without the release/acquire fence of __syncthreads():
+// that fence also waits for every direct-to-LDS load in flight, which would
+// drain the prefetch ring each step.  The caller first waits for the loads
+// the next step reads (its own, by vmcnt; the barrier then covers the
+// other waves'), and the LDS reads of the finished step have all returned
+// (the MFMAs consumed them).  The clobber keeps the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
 
 typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
+template <int I> using Ic = std::integral_constant<int, I>;
+
 // TERN: Wp is the sign plane, e.Zp the nonzero plane of ternary weights.
-template <bool TERN>
-__global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
+// XS: binary weights with the activation row sums e.xsum given.
+template <bool TERN, bool XS>
+__global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
     const int8_t* __restrict__ Xq, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
     int M, int N, int K, int tiles_n, EpilogueI8 e)
 {
-    __shared__ __attribute__((aligned(16))) int8_t lds_a[2][kBM * kKS];
+    static_assert(!(TERN && XS), "row sums serve binary weights only");
+    constexpr int kPL = TERN ? 2 : 1;                // weight planes
+    // Separate LDS objects, each reached through a compile-time index, so
+    // the compiler can tell a load into one buffer from a read of another
+    // and does not wait for the prefetch before the current step's reads.
+    __shared__ __attribute__((aligned(16))) int8_t lds_a0[kBM * kKS], lds_a1[kBM * kKS],
+                                                   lds_a2[kBM * kKS], lds_a3[kBM * kKS];
+    // weight chunks: sign (or binary) plane and, ternary, the nonzero plane
+    __shared__ __attribute__((aligned(16))) uint32_t lds_b0[kBN * kCW], lds_b1[kBN * kCW];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_z0[TERN ? kBN * kCW : 1], lds_z1[TERN ? kBN * kCW : 1];
+    auto abuf = [&](auto I) -> int8_t* {
+        constexpr int i = decltype(I)::value & 3;
+        if constexpr (i == 0) return lds_a0;
+        else if constexpr (i == 1) return lds_a1;
+        else if constexpr (i == 2) return lds_a2;
+        else return lds_a3;
+    };
+    auto bbuf = [&](auto I) -> uint32_t* {
+        if constexpr ((decltype(I)::value & 1) == 0) return lds_b0;
+        else return lds_b1;
+    };
+    auto zbuf = [&](auto I) -> uint32_t* {
+        if constexpr ((decltype(I)::value & 1) == 0) return lds_z0;
+        else return lds_z1;
+    };
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
-    const int m_blk = tm * kBM, n_blk = tn * kBN;
-    const int wm = wave >> 1, wn = wave & 1;
     const int r16 = lane & 15, g = lane >> 4;
 
-    // A staging.  Instruction i of wave w fills tile rows 8 (8 w + i) ..
-    // +7 (1 KiB of LDS): lane l takes row r = 8 (8 w + i) + l / 8, LDS slot
-    // l % 8, and loads the piece j stored there, j = slot ^ ((r / 2) % 8).
-    // Full k-steps load straight into LDS (global_load_lds_dwordx4 writes
-    // lane l's 16 bytes at the instruction's LDS base + 16 l); the step
-    // holding the end of the row goes through registers, masked past K.
+    // Tile order.  Workgroups go to the 8 XCDs round-robin by id; renumber
+    // so that each XCD owns a contiguous range of tiles, and walk that range
+    // in groups of kGroupM activation-row tiles per weight-row tile, so the
+    // workgroups resident on one XCD share their A rows and weight rows in
+    // that XCD's L2.
+    int tile = blockIdx.x;
+    const int ntiles = gridDim.x;
+    if (ntiles % 8 == 0) tile = (tile % 8) * (ntiles / 8) + tile / 8;
+    constexpr int kGroupM = 8;
+    const int tiles_m = ntiles / tiles_n;
+    const int grp = tile / (kGroupM * tiles_n);
+    const int gm0 = grp * kGroupM;
+    const int gsz = min(tiles_m - gm0, kGroupM);
+    const int in_grp = tile - grp * kGroupM * tiles_n;
+    const int tm = gm0 + in_grp % gsz, tn = in_grp / gsz;
+    const int m_blk = tm * kBM, n_blk = tn * kBN;
+
+    // A staging.  Instruction i of wave w fills tile rows 16 (kAPieces w + i)
+    // .. +15 (1 KiB of LDS): lane l takes row r = 16 (kAPieces w + i) + l / 4,
+    // LDS slot l % 4, and loads the piece j stored there, j = slot ^ h(r),
+    // h(r) = ((r / 2) ^ (r / 4)) % 4 = ((l / 8) ^ (l / 16)) % 4.  Steps inside
+    // K load straight into LDS (global_load_lds_dwordx4 writes lane l's 16
+    // bytes at the instruction's LDS base + 16 l); the step holding the end
+    // of the row goes through registers, masked past K.
     int aoff[kAPieces];                            // byte offset of row r (M * ldX < 2^31)
-    int apiece[kAPieces];                          // byte offset of piece j in the row
 #pragma unroll
-    for (int i = 0; i < kAPieces; ++i) {
-        const int r = 8 * (8 * wave + i) + (lane >> 3);
-        aoff[i] = min(m_blk + r, M - 1) * (int)ldX;
-        apiece[i] = (((lane & 7) ^ ((r >> 1) & 7)) << 4);
-    }
-    auto stage_direct = [&](int buf, int k0) {
+    for (int i = 0; i < kAPieces; ++i)
+        aoff[i] = min(m_blk + 16 * (kAPieces * wave + i) + (lane >> 2), M - 1) * (int)ldX;
+    const int apiece = ((lane & 3) ^ (((lane >> 3) ^ (lane >> 4)) & 3)) << 4;   // byte offset of piece j
+    // Weight staging.  A chunk holds words kCW c .. +kCW-1 of each weight
+    // row of the tile; column c's 64 bytes take LDS slots 4 c .. 4 c + 3
+    // (16 bytes each) and its 16-byte piece p sits in slot 4 c + ((p + c / 4)
+    // % 4), so the 16 columns of a fragment read fall on 16 distinct 4-bank
+    // groups.  Instruction j of wave w fills slots 4 (128 j + 16 w) .. +63:
+    // lane l takes column 128 j + 16 w + l / 4 and piece ((l % 4) - l / 16)
+    // % 4.  A piece that starts at or past the row stride (only beyond K)
+    // reads the row's last piece instead: its bits meet zero activations or
+    // steps that are not computed.
+    const uint32_t* __restrict__ brow[kBPieces];
+    const int bpiece = ((lane & 3) - (lane >> 4)) & 3;
 #pragma unroll
-        for (int i = 0; i < kAPieces; ++i)
-            __builtin_amdgcn_global_load_lds((gptr_t)(Xq + aoff[i] + k0 + apiece[i]),
-                                             (lptr_t)(&lds_a[buf][(8 * wave + i) * 1024]), 16, 0, 0);
-    };
-    auto stage_masked = [&](int buf, int k0) {
+    for (int j = 0; j < kBPieces; ++j)
+        brow[j] = Wp + (int64_t)min(n_blk + 128 * j + 16 * wave + (lane >> 2), N - 1) * ldW;
+    const int64_t zdelta = TERN ? e.Zp - Wp : 0;   // the nonzero plane shares Wp's layout
+    const int ldw = (int)ldW;
+    auto issue_a = [&](auto I, int k0, bool direct) {
+        int8_t* la = abuf(I);
+        if (direct) {
 #pragma unroll
-        for (int i = 0; i < kAPieces; ++i) {
-            const v4i v = load_a<true>(Xq + aoff[i], k0 + apiece[i], K);
-            *reinterpret_cast<v4i*>(&lds_a[buf][(8 * wave + i) * 1024 + 16 * lane]) = v;
+            for (int i = 0; i < kAPieces; ++i)
+                __builtin_amdgcn_global_load_lds((gptr_t)(Xq + aoff[i] + k0 + apiece),
+                                                 (lptr_t)(la + (kAPieces * wave + i) * 1024), 16, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kAPieces; ++i) {
+                const v4i v = load_a<true>(Xq + aoff[i], k0 + apiece, K);
+                *reinterpret_cast<v4i*>(la + (kAPieces * wave + i) * 1024 + 16 * lane) = v;
+            }
         }
     };
-    // fragment reads: row 16 f + r16 of the wave's 128, piece 4 h + g of the
-    // step (h: first or second 64-wide half)
-    int roff[2][8];
+    auto issue_b = [&](auto I, int chunk) {
+        uint32_t* lb = bbuf(I);
+        uint32_t* lz = zbuf(I);
+        const int w0 = min(kCW * chunk + 4 * bpiece, ldw - 4);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            const int r = wm * 128 + 16 * f + r16;
-            roff[h][f] = r * kKS + (((4 * h + g) ^ ((r >> 1) & 7)) << 4);
+        for (int j = 0; j < kBPieces; ++j) {
+            __builtin_amdgcn_global_load_lds((gptr_t)(brow[j] + w0), (lptr_t)(lb + 4 * (128 * j + 16 * wave) * 4),
+                                             16, 0, 0);
+            if (TERN)
+                __builtin_amdgcn_global_load_lds((gptr_t)(brow[j] + zdelta + w0),
+                                                 (lptr_t)(lz + 4 * (128 * j + 16 * wave) * 4), 16, 0, 0);
         }
-    const uint32_t* wrow[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) wrow[q] = Wp + (int64_t)min(n_blk + wn * 64 + 16 * q + r16, N - 1) * ldW;
-    const int64_t zdelta = TERN ? e.Zp - Wp : 0;   // nonzero plane: same layout, other base
+    };
+    // fragment reads: A row 16 f + r16, k-group g at byte abase + 1024 f
+    // (h(16 f + r16) = h(r16)); weight word 2 t + g / 2 of chunk step t of
+    // column wave kWN + 16 q + r16: piece t / 2, word 2 (t % 2) + g / 2 of it
+    const int abase = r16 * kKS + ((g ^ (((r16 >> 1) ^ (r16 >> 2)) & 3)) << 4);
+    const int bcol0 = wave * kWN + r16;            // + 16 q
+    const int bcr = (r16 >> 2) & 3;                // (column / 4) % 4, the same for both q
     // combined ternary word of lane group g: Z bits low, (S & Z) bits high
     auto tern_word = [](uint32_t sw, uint32_t zw, int gg) {
         const int sh = 16 * (gg & 1);
         return ((zw >> sh) & 0xFFFFu) | (((sw & zw) >> sh) << 16);
     };
 
-    v4i acc[8][4];
+    v4i acc[kFM][kFN];
 #pragma unroll
-    for (int f = 0; f < 8; ++f)
+    for (int f = 0; f < kFM; ++f)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[f][q] = (v4i){0, 0, 0, 0};
+        for (int q = 0; q < kFN; ++q) acc[f][q] = (v4i){0, 0, 0, 0};
 
-    // weight words of a step: half h of column q is word (k0 / 32) + 2 h + g / 2
     const int steps = (K + kKS - 1) / kKS;
     const int full_steps = K / kKS;
-    uint32_t bw[2][4];
-    if (full_steps > 0) stage_direct(0, 0);
-    else                stage_masked(0, 0);
+    const int chunks = (steps + kCS - 1) / kCS;
+    constexpr int kA = kAPieces;                   // vector-memory instructions per direct A step
+    constexpr int kB = kBPieces * kPL;             // ... per weight chunk
+
+    // step s (chunk step t = s % kCS) reads A buffer s % 4 and weight
+    // buffer (s / kCS) % 2
+    auto compute = [&](auto IA, auto IB, int t) {
+        const uint32_t* lb = bbuf(IB);
+        const uint32_t* lz = zbuf(IB);
+        const int8_t* la = abuf(IA);
+        // LDS reads run ahead of their use: the weight words and the first
+        // kH A fragments are issued before the weight expansion; fragment
+        // f + kH is requested as soon as the MFMAs of fragment f, whose
+        // registers it takes, have been issued.
+        constexpr int kH = TERN ? kFM / 4 : kFM / 2;
+        const int bw = 4 * (((t >> 1) + bcr) & 3) + 2 * (t & 1) + (g >> 1);
+        uint32_t sw[kFN], zw[kFN];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bw[h][q] = wrow[q][2 * h + (g >> 1)];
-            if (TERN) bw[h][q] = tern_word(bw[h][q], (wrow[q] + zdelta)[2 * h + (g >> 1)], g);
+        for (int q = 0; q < kFN; ++q) {
+            sw[q] = lb[(bcol0 + 16 * q) * kCW + bw];
+            if (TERN) zw[q] = lz[(bcol0 + 16 * q) * kCW + bw];
         }
-    __builtin_amdgcn_s_waitcnt(0);
-    // the first step's words are complete before the loop, so no load is
-    // pending on the loop-carried registers when an iteration begins
+        v4i a[kH];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+        for (int f = 0; f < kH; ++f) a[f] = *reinterpret_cast<const v4i*>(la + abase + 1024 * f);
+        v4i bx[kFN];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) asm volatile("" : : "v"(bw[h][q]));
+        for (int q = 0; q < kFN; ++q) {
+            if (TERN) bx[q] = expand_ternary(tern_word(sw[q], zw[q], g));
+            else if (XS) bx[q] = expand_bits01(sw[q] >> (16 * (g & 1)));
+            else bx[q] = expand_signs(sw[q] >> (16 * (g & 1)));
+        }
+#pragma unroll
+        for (int f = 0; f < kFM; ++f) {
+#pragma unroll
+            for (int q = 0; q < kFN; ++q)
+                acc[f][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f % kH], bx[q], acc[f][q], 0, 0, 0);
+            if (f + kH < kFM) a[f % kH] = *reinterpret_cast<const v4i*>(la + abase + 1024 * (f + kH));
+        }
+        // keep that order (DS reads, VALU, then MFMA / DS pairs, then MFMAs)
+        __builtin_amdgcn_sched_group_barrier(0x100, kFN * kPL + kH, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1000, 0);
+#pragma unroll
+        for (int f = 0; f < kFM - kH; ++f) {
+            __builtin_amdgcn_sched_group_barrier(0x008, kFN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kH * kFN, 0);
+        __builtin_amdgcn_sched_barrier(0);           // the step's MFMAs stay ahead of the wait
+    };
+
+    // Prologue: weight chunk 0, then A steps 0 .. 2.
+    issue_b(Ic<0>{}, 0);
+    if (0 < steps) issue_a(Ic<0>{}, 0, 0 < full_steps);
+    if (1 < steps) issue_a(Ic<1>{}, kKS, 1 < full_steps);
+    if (2 < steps) issue_a(Ic<2>{}, 2 * kKS, 2 < full_steps);
+    if (steps >= 3 && full_steps >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kA));
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // One k-step: prefetch step s+1 (DIRECT: straight into LDS), run the 64
-    // MFMAs of step s, wait for the prefetch, barrier.
-    auto kstep = [&](int s, auto direct_tag) {
-        constexpr bool DIRECT = decltype(direct_tag)::value;
-        const int cur = s & 1;
-        const bool more = s + 1 < steps;
-        const int kn = (s + 1) * kKS;
-        uint32_t bn[2][4], zn[2][4];
-        if (more) {
-            if (DIRECT) stage_direct(cur ^ 1, kn);
-            else        stage_masked(cur ^ 1, kn);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    bn[h][q] = wrow[q][(kn >> 5) + 2 * h + (g >> 1)];
-                    if (TERN) zn[h][q] = (wrow[q] + zdelta)[(kn >> 5) + 2 * h + (g >> 1)];
-                }
-        }
-        const int8_t* la = lds_a[cur];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            v4i bx[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                bx[q] = TERN ? expand_ternary(bw[h][q]) : expand_signs(bw[h][q] >> (16 * (g & 1)));
-#pragma unroll
-            for (int f = 0; f < 8; ++f) {
-                const v4i a = *reinterpret_cast<const v4i*>(la + roff[h][f]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[f][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx[q], acc[f][q], 0, 0, 0);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);         // the step's MFMAs stay ahead of the waits below
-        if (more) {
-            __builtin_amdgcn_s_waitcnt(0);        // the prefetched A pieces are in LDS
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    asm volatile("" : : "v"(bn[h][q]));
-                    if (TERN) asm volatile("" : : "v"(zn[h][q]));
-                    bw[h][q] = TERN ? tern_word(bn[h][q], zn[h][q], g) : bn[h][q];
-                }
-        }
-        __syncthreads();
+    // Steady state: step s first issues the next weight chunk (when s starts
+    // a chunk) and A step s + 3, into the buffers read during the previous
+    // chunk / step; all of it inside K, so every load is direct and the
+    // count of loads issued after those of step s + 1 is known: A of steps
+    // s + 2 and s + 3, and the chunks issued in steps s - 1 and s.
+    auto fast_step = [&](int s, auto P) {
+        constexpr int ph = decltype(P)::value;      // s % (2 kCS)
+        constexpr int t = ph % kCS;
+        if constexpr (t == 0) issue_b(Ic<(ph / kCS + 1) & 1>{}, s / kCS + 1);
+        issue_a(Ic<(ph + kNB - 1) & 3>{}, (s + kNB - 1) * kKS, true);
+        __builtin_amdgcn_sched_barrier(0);           // the prefetch goes out before the step's LDS reads
+        compute(Ic<ph & 3>{}, Ic<(ph / kCS) & 1>{}, t);
+        constexpr int after = 2 * kA + ((t == 1) ? kB : 0) + ((t == 0) ? kB : 0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(after));
+        barrier_keep_loads();
     };
-    // steps whose successor lies wholly inside K prefetch straight into LDS;
-    // the prefetch of the step holding the end of the row is masked
+    static_assert(2 * kA + 2 * kB <= 63, "vmcnt holds at most 63");
+    // General step (the tail, where loads may be masked or missing): the
+    // same order with every issue checked, and a full wait.
+    auto step = [&](int s, auto P) {
+        constexpr int ph = decltype(P)::value;
+        constexpr int t = ph % kCS;
+        if (t == 0 && s / kCS + 1 < chunks) issue_b(Ic<(ph / kCS + 1) & 1>{}, s / kCS + 1);
+        const int t_issue = s + kNB - 1;
+        if (t_issue < steps) issue_a(Ic<(ph + kNB - 1) & 3>{}, t_issue * kKS, t_issue < full_steps);
+        compute(Ic<ph & 3>{}, Ic<(ph / kCS) & 1>{}, t);
+        __syncthreads();                             // waits for all loads (its fence)
+    };
+    auto run16 = [&](int s0, auto body) {
+        body(s0 + 0, Ic<0>{});  body(s0 + 1, Ic<1>{});  body(s0 + 2, Ic<2>{});  body(s0 + 3, Ic<3>{});
+        body(s0 + 4, Ic<4>{});  body(s0 + 5, Ic<5>{});  body(s0 + 6, Ic<6>{});  body(s0 + 7, Ic<7>{});
+        body(s0 + 8, Ic<8>{});  body(s0 + 9, Ic<9>{});  body(s0 + 10, Ic<10>{}); body(s0 + 11, Ic<11>{});
+        body(s0 + 12, Ic<12>{}); body(s0 + 13, Ic<13>{}); body(s0 + 14, Ic<14>{}); body(s0 + 15, Ic<15>{});
+    };
     int s = 0;
-    for (; s + 1 < full_steps; ++s) kstep(s, std::true_type{});
-    for (; s < steps; ++s) kstep(s, std::false_type{});
+    // a 16-step block is fast while its A issues (up to step s + 18) lie in K
+    // and its chunk issues (up to chunk s / 8 + 2) exist
+    for (; s + 16 + kNB - 1 <= full_steps && s / kCS + 2 < chunks; s += 16)
+        run16(s, fast_step);
+    for (; s < steps; s += 16)
+        run16(s, [&](int ss, auto P) { if (ss < steps) step(ss, P); });
 
     // Epilogue.  Full tiles with 16-byte aligned output rows go through LDS
-    // (the A buffers are free now): in two passes of 4 fragment rows, each
-    // wave parks its 64 x 64 int32 block (16 KiB; column c of row r at word
-    // r * 64 + (c ^ 16 ((r / 4) % 4)), so the 4 lane groups of a fragment
-    // write disjoint 16-bank groups) and reads it back as 16-byte row
-    // pieces, so every store instruction writes 4 whole 256-byte row
-    // segments.  Other tiles store element by element.
+    // (the A buffers are free now): in 8 passes of 2 fragment rows, each
+    // wave parks its 32 x kWN int32 block in its own 8 KiB half of an A
+    // buffer (column c of row r at word r * 36 + c: the stride of 36 words
+    // puts the 4 lane groups of a fragment, rows 4 apart, on disjoint
+    // 16-bank groups) and reads it back as 16-byte row pieces, so every store
+    // instruction writes 8 whole 128-byte row segments.  Other tiles store
+    // element by element.
     const bool full = m_blk + kBM <= M && n_blk + kBN <= N &&
                       (!(e.flags & EPI_DOT) || ((reinterpret_cast<uintptr_t>(e.D) & 15u) == 0 && e.ldD % 4 == 0)) &&
                       (!(e.flags & EPI_SCALE) || ((reinterpret_cast<uintptr_t>(e.Y) & 15u) == 0 && e.ldY % 4 == 0));
     if (full) {
-        int32_t* park = reinterpret_cast<int32_t*>(&lds_a[0][0]) + wave * (64 * 64);   // 4 x 16 KiB = both A buffers
-        const int pc = 4 * (lane & 15);            // read-back: 4 columns of row lane/16 (+4 per pass)
+        constexpr int kPS = 36;                    // parked row stride in words
+        static_assert(32 * kPS * 4 <= kBM * kKS / 2, "a wave's parked block fits half an A buffer");
+        int8_t* pb = (wave >> 1) == 0 ? lds_a0 : (wave >> 1) == 1 ? lds_a1 : (wave >> 1) == 2 ? lds_a2 : lds_a3;
+        int32_t* park = reinterpret_cast<int32_t*>(pb + (wave & 1) * (kBM * kKS / 2));
+        const int pc = 4 * (lane & 7);             // read-back: 4 columns of row 8 p + lane / 8
+        const int n = n_blk + wave * kWN + pc;
         float an[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (e.flags & EPI_SCALE) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                an[c] = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : n_blk + wn * 64 + pc + c];
+            for (int c = 0; c < 4; ++c) an[c] = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : n + c];
         }
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int pass = 0; pass < kFM / 2; ++pass) {
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
+            for (int f = 0; f < 2; ++f)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < kFN; ++q)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        park[(16 * f + 4 * g + r) * 64 + ((16 * q + r16) ^ (16 * g))] = acc[4 * half + f][q][r];
+                        park[(16 * f + 4 * g + r) * kPS + 16 * q + r16] = acc[2 * pass + f][q][r];
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int p = 0; p < 16; ++p) {
-                const int row = 4 * p + (lane >> 4);
-                const v4i d = *reinterpret_cast<const v4i*>(&park[row * 64 + (pc ^ (16 * ((row >> 2) & 3)))]);
-                const int64_t m = m_blk + wm * 128 + 64 * half + row;
-                const int n = n_blk + wn * 64 + pc;
+            for (int p = 0; p < 4; ++p) {
+                const int row = 8 * p + (lane >> 3);
+                v4i d = *reinterpret_cast<const v4i*>(&park[row * kPS + pc]);
+                const int64_t m = m_blk + 32 * pass + row;
+                if (XS) {
+                    const int32_t xs = e.xsum[m];
+                    d[0] = xs - 2 * d[0]; d[1] = xs - 2 * d[1]; d[2] = xs - 2 * d[2]; d[3] = xs - 2 * d[3];
+                }
                 if (e.flags & EPI_DOT)
                     __builtin_nontemporal_store(d, reinterpret_cast<v4i*>(e.D + m * e.ldD + n));
                 if (e.flags & EPI_SCALE) {
@@ -294,18 +437,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwn_i8_gemm(
     }
     // lane holds rows 4g + r of each 16-row fragment, column r16
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int n = n_blk + wn * 64 + 16 * q + r16;
+    for (int q = 0; q < kFN; ++q) {
+        const int n = n_blk + wave * kWN + 16 * q + r16;
         if (n >= N) continue;
         float an = 0.0f;
         if (e.flags & EPI_SCALE) an = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : n];
 #pragma unroll
-        for (int f = 0; f < 8; ++f)
+        for (int f = 0; f < kFM; ++f)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = m_blk + wm * 128 + 16 * f + 4 * g + r;
+                const int m = m_blk + 16 * f + 4 * g + r;
                 if (m >= M) continue;
-                const int32_t d = acc[f][q][r];
+                int32_t d = acc[f][q][r];
+                if (XS) d = e.xsum[m] - 2 * d;     // D = xsum - 2 sum q w
                 if (e.flags & EPI_DOT) e.D[(int64_t)m * e.ldD + n] = d;
                 if (e.flags & EPI_SCALE) {
                     float y = an * (float)d;
@@ -325,9 +469,11 @@ hipError_t launch_bwn_i8_gemm(const int8_t* Xq, int64_t ldXq, const uint32_t* Wp
     const int64_t tiles_m = (M + kBM - 1) / kBM;
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
     if (e.flags & W_TERNARY)
-        hipLaunchKernelGGL((k_bwn_i8_gemm<true>), grid, block, 0, s, Xq, ldXq, Wp, ldW, (int)M, (int)N, (int)K, tiles_n, e);
+        hipLaunchKernelGGL((k_bwn_i8_gemm<true, false>), grid, block, 0, s, Xq, ldXq, Wp, ldW, (int)M, (int)N, (int)K, tiles_n, e);
+    else if (e.xsum)
+        hipLaunchKernelGGL((k_bwn_i8_gemm<false, true>), grid, block, 0, s, Xq, ldXq, Wp, ldW, (int)M, (int)N, (int)K, tiles_n, e);
     else
-        hipLaunchKernelGGL((k_bwn_i8_gemm<false>), grid, block, 0, s, Xq, ldXq, Wp, ldW, (int)M, (int)N, (int)K, tiles_n, e);
+        hipLaunchKernelGGL((k_bwn_i8_gemm<false, false>), grid, block, 0, s, Xq, ldXq, Wp, ldW, (int)M, (int)N, (int)K, tiles_n, e);
     return hipGetLastError();
 }
 

@@ -61,8 +61,8 @@ __device__ __forceinline__ uint32_t gather_bit_of_bytes(uint32_t v, int b) {
 }
 
 // One workgroup per activation row.  FROM_F32: quantize X (absmax per row);
-// otherwise re-lay int8 input rows.  Writes any of: int8 Q, bit planes +
-// row sum, row scale.  Each thread owns 16 consecutive elements per 4096-wide
+// otherwise re-lay int8 input rows.  Writes any of: int8 Q, bit planes, row
+// sum, row scale.  Each thread owns 16 consecutive elements per 4096-wide
 // block of the row; a pair of lanes forms one 32-bit plane word (DPP).
 template <bool FROM_F32>
 __global__ __launch_bounds__(kThreads) void k_act_i8(
@@ -172,6 +172,8 @@ __global__ __launch_bounds__(kThreads) void k_act_i8(
         const int64_t pad = ldXb - Kw;             // pad words hold 0
         for (int64_t i = tid; i < 8 * pad; i += kThreads)
             Xb[(m * 8 + i / pad) * ldXb + Kw + i % pad] = 0u;
+    }
+    if (xsum) {
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1) tsum += __shfl_xor(tsum, s, 64);
         if (lane == 0) red_i[wave] = tsum;
