@@ -144,7 +144,8 @@ typedef struct bnn_i8_args {
                                          (bytes from K on are ignored);
                                          M * ldXq < 2^31                      */
     const float* xscale;              /* [M] activation scales, or NULL (1.0)   */
-    const uint32_t* Wp; int64_t ldWp; /* packed weights [N, ldWp] (packed layout) */
+    const uint32_t* Wp; int64_t ldWp; /* packed weights [N, ldWp] (packed layout);
+                                         the GEMM needs N * ldWp < 2^29      */
     int64_t M, N, K;                  /* 1 <= K <= BNN_MAX_K_I8                 */
     uint32_t epilogue;                /* DOT_I32 | SCALE_F32 [| ALPHA_TENSOR]   */
     int32_t* D; int64_t ldD;          /* DOT_I32: int32 [M, ldD], ldD >= N      */

@@ -174,6 +174,9 @@ def _i8(**kw):
     (dict(Xb=0, Xq=A16, ldXq=100), ERR_ALIGN),                      # ldXq % 16
     (dict(Xb=0, Xq=A16 + 4, ldXq=112), ERR_ALIGN),
     (dict(Xb=0, Xq=A16, ldXq=96), ERR_LD),
+    (dict(Xb=0, Xq=A16, ldXq=112, xsum=A2), ERR_ALIGN),             # GEMM row sums are read too
+    (dict(Xb=0, Xq=A16, ldXq=112, N=1 << 25, ldWp=16, ldD=1 << 25), ERR_SHAPE),   # past 32-bit offsets
+    (dict(Xb=0, Xq=A16, ldXq=112, N=(1 << 25) - 1, ldWp=16, ldD=1 << 25), OK),
     (dict(M=3), ERR_NULL),                                          # planes serve M <= 2 only
     (dict(K=(1 << 17) + 1), ERR_SHAPE),
     (dict(K=0), ERR_SHAPE),
@@ -207,6 +210,8 @@ def test_i8_activation_writers_validation(L):
     assert q(A16, 1, 100, 100, 0, 0, 0, 0, 0, A16, None) == ERR_NULL       # no output form
     assert q(A16, 1, 100, 100, A16, 112, A16, 4, A16, 0, None) == ERR_NULL  # xscale required
     assert q(A16, 1, 100, 100, 0, 0, A16, 4, 0, A16, None) == ERR_NULL      # planes need xsum
+    assert q(A16, 0, 100, 100, A16, 112, 0, 0, A16, A16, None) == OK        # row sums without planes
+    assert q(A16, 1, 100, 100, A16, 112, 0, 0, A2, A16, None) == ERR_ALIGN
     assert q(A16, 1, 100, 99, A16, 112, 0, 0, 0, A16, None) == ERR_LD
     assert q(A16, 1, 100, 100, A16, 99, 0, 0, 0, A16, None) == ERR_LD
     assert q(A16, 1, 100, 100, 0, 0, A16, 6, A16, A16, None) == ERR_ALIGN

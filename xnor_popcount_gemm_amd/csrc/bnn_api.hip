@@ -165,8 +165,10 @@ bnn_status validate_i8(const bnn_i8_args* a) {
     } else {
         if ((st = check_i8_rows(a->Xq, a->K, a->ldXq)) != BNN_OK) return st;
         if (a->xsum && misaligned4(a->xsum)) return BNN_ERR_ALIGN;
-        // the GEMM addresses activation rows with 32-bit byte offsets
+        // the GEMM addresses activation rows and weight rows with 32-bit
+        // byte offsets
         if (a->M * a->ldXq > ((int64_t)1 << 31) - 1) return BNN_ERR_SHAPE;
+        if (a->N * a->ldWp >= ((int64_t)1 << 29)) return BNN_ERR_SHAPE;
     }
     if (a->xscale && misaligned4(a->xscale)) return BNN_ERR_ALIGN;
     if (f & BNN_EPI_DOT_I32) {

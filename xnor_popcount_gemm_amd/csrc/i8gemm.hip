@@ -31,7 +31,7 @@
 // Tiling: a 512-thread workgroup (8 waves) computes 256 activation rows x
 // 256 weight rows; wave w takes all rows and columns 32 w .. +31.  The
 // workgroup's A tile (256 rows x 64 bytes per k-step) goes straight from
-// global memory into a ring of 4 LDS buffers (global_load_lds), issued 3
+// global memory into a ring of 4 LDS buffers (buffer loads to LDS), issued 3
 // steps ahead of its use, with one barrier per step; 16-byte piece j of A
 // row r sits at slot j ^ h(r), h(r) = ((r / 2) ^ (r / 4)) % 4, of the row's
 // four slots.  A fragment read (16 rows of one k-group) then has every 8
@@ -141,8 +141,16 @@ constexpr unsigned waitcnt_vm(int n) {
 // memory accesses across the barrier.
 __device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
 
-typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Buffer resource over [base, base + bytes) for raw (stride 0) dword loads.
+// The tiles move with buffer loads to LDS rather than global_load_lds: the
+// latter is a FLAT instruction, and with one in flight the compiler no
+// longer counts LDS reads in order, so it waits for all of them at the
+// first use.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
 
 template <int I> using Ic = std::integral_constant<int, I>;
 
@@ -204,10 +212,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
     // .. +15 (1 KiB of LDS): lane l takes row r = 16 (kAPieces w + i) + l / 4,
     // LDS slot l % 4, and loads the piece j stored there, j = slot ^ h(r),
     // h(r) = ((r / 2) ^ (r / 4)) % 4 = ((l / 8) ^ (l / 16)) % 4.  Steps inside
-    // K load straight into LDS (global_load_lds_dwordx4 writes lane l's 16
-    // bytes at the instruction's LDS base + 16 l); the step holding the end
-    // of the row goes through registers, masked past K.
-    int aoff[kAPieces];                            // byte offset of row r (M * ldX < 2^31)
+    // K load straight into LDS (a 16-byte buffer load to LDS writes lane l's
+    // 16 bytes at the instruction's LDS base + 16 l); the step holding the
+    // end of the row goes through registers, masked past K.
+    const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(Xq, M * (int)ldX);          // M * ldX < 2^31
+    int aoff[kAPieces];                            // byte offset of row r
 #pragma unroll
     for (int i = 0; i < kAPieces; ++i)
         aoff[i] = min(m_blk + 16 * (kAPieces * wave + i) + (lane >> 2), M - 1) * (int)ldX;
@@ -221,20 +230,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
     // % 4.  A piece that starts at or past the row stride (only beyond K)
     // reads the row's last piece instead: its bits meet zero activations or
     // steps that are not computed.
-    const uint32_t* __restrict__ brow[kBPieces];
+    const int ldw = (int)ldW;
+    const __amdgpu_buffer_rsrc_t brsrc = buffer_rsrc(Wp, N * ldw * 4);           // N * ldW < 2^29
+    const __amdgpu_buffer_rsrc_t zrsrc = buffer_rsrc(TERN ? e.Zp : Wp, N * ldw * 4);
+    int boff[kBPieces];                            // word offset of the lane's weight row
     const int bpiece = ((lane & 3) - (lane >> 4)) & 3;
 #pragma unroll
-    for (int j = 0; j < kBPieces; ++j)
-        brow[j] = Wp + (int64_t)min(n_blk + 128 * j + 16 * wave + (lane >> 2), N - 1) * ldW;
-    const int64_t zdelta = TERN ? e.Zp - Wp : 0;   // the nonzero plane shares Wp's layout
-    const int ldw = (int)ldW;
+    for (int j = 0; j < kBPieces; ++j) boff[j] = min(n_blk + 128 * j + 16 * wave + (lane >> 2), N - 1) * ldw;
     auto issue_a = [&](auto I, int k0, bool direct) {
         int8_t* la = abuf(I);
         if (direct) {
 #pragma unroll
             for (int i = 0; i < kAPieces; ++i)
-                __builtin_amdgcn_global_load_lds((gptr_t)(Xq + aoff[i] + k0 + apiece),
-                                                 (lptr_t)(la + (kAPieces * wave + i) * 1024), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lptr_t)(la + (kAPieces * wave + i) * 1024), 16,
+                                                         aoff[i] + k0 + apiece, 0, 0, 0);
         } else {
 #pragma unroll
             for (int i = 0; i < kAPieces; ++i) {
@@ -249,11 +258,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
         const int w0 = min(kCW * chunk + 4 * bpiece, ldw - 4);
 #pragma unroll
         for (int j = 0; j < kBPieces; ++j) {
-            __builtin_amdgcn_global_load_lds((gptr_t)(brow[j] + w0), (lptr_t)(lb + 4 * (128 * j + 16 * wave) * 4),
-                                             16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, (lptr_t)(lb + 4 * (128 * j + 16 * wave) * 4), 16,
+                                                     (boff[j] + w0) * 4, 0, 0, 0);
             if (TERN)
-                __builtin_amdgcn_global_load_lds((gptr_t)(brow[j] + zdelta + w0),
-                                                 (lptr_t)(lz + 4 * (128 * j + 16 * wave) * 4), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(zrsrc, (lptr_t)(lz + 4 * (128 * j + 16 * wave) * 4), 16,
+                                                         (boff[j] + w0) * 4, 0, 0, 0);
         }
     };
     // fragment reads: A row 16 f + r16, k-group g at byte abase + 1024 f
@@ -280,34 +289,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
     constexpr int kA = kAPieces;                   // vector-memory instructions per direct A step
     constexpr int kB = kBPieces * kPL;             // ... per weight chunk
 
-    // step s (chunk step t = s % kCS) reads A buffer s % 4 and weight
-    // buffer (s / kCS) % 2
-    auto compute = [&](auto IA, auto IB, int t) {
+    // The expanded weight fragments of the next step are prepared at the end
+    // of the current one (its chunk is in LDS by then), so a step starts
+    // with its MFMAs as soon as the first A fragment arrives.
+    v4i bx[kFN];
+    auto load_bx = [&](auto IB, int t) {
         const uint32_t* lb = bbuf(IB);
         const uint32_t* lz = zbuf(IB);
-        const int8_t* la = abuf(IA);
-        // LDS reads run ahead of their use: the weight words and the first
-        // kH A fragments are issued before the weight expansion; fragment
-        // f + kH is requested as soon as the MFMAs of fragment f, whose
-        // registers it takes, have been issued.
-        constexpr int kH = TERN ? kFM / 4 : kFM / 2;
         const int bw = 4 * (((t >> 1) + bcr) & 3) + 2 * (t & 1) + (g >> 1);
-        uint32_t sw[kFN], zw[kFN];
 #pragma unroll
         for (int q = 0; q < kFN; ++q) {
-            sw[q] = lb[(bcol0 + 16 * q) * kCW + bw];
-            if (TERN) zw[q] = lz[(bcol0 + 16 * q) * kCW + bw];
+            const uint32_t sw = lb[(bcol0 + 16 * q) * kCW + bw];
+            if (TERN) bx[q] = expand_ternary(tern_word(sw, lz[(bcol0 + 16 * q) * kCW + bw], g));
+            else if (XS) bx[q] = expand_bits01(sw >> (16 * (g & 1)));
+            else bx[q] = expand_signs(sw >> (16 * (g & 1)));
         }
+    };
+    // step s (chunk step t = s % kCS) reads A buffer s % 4; LDS reads run
+    // ahead of their use: the first kH A fragments are issued first, and
+    // fragment f + kH as soon as the MFMAs of fragment f, whose registers it
+    // takes, have been issued.
+    auto compute = [&](auto IA) {
+        const int8_t* la = abuf(IA);
+        constexpr int kH = TERN ? kFM / 4 : kFM / 2;
         v4i a[kH];
 #pragma unroll
         for (int f = 0; f < kH; ++f) a[f] = *reinterpret_cast<const v4i*>(la + abase + 1024 * f);
-        v4i bx[kFN];
-#pragma unroll
-        for (int q = 0; q < kFN; ++q) {
-            if (TERN) bx[q] = expand_ternary(tern_word(sw[q], zw[q], g));
-            else if (XS) bx[q] = expand_bits01(sw[q] >> (16 * (g & 1)));
-            else bx[q] = expand_signs(sw[q] >> (16 * (g & 1)));
-        }
 #pragma unroll
         for (int f = 0; f < kFM; ++f) {
 #pragma unroll
@@ -315,15 +322,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
                 acc[f][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f % kH], bx[q], acc[f][q], 0, 0, 0);
             if (f + kH < kFM) a[f % kH] = *reinterpret_cast<const v4i*>(la + abase + 1024 * (f + kH));
         }
-        // keep that order (DS reads, VALU, then MFMA / DS pairs, then MFMAs)
-        __builtin_amdgcn_sched_group_barrier(0x100, kFN * kPL + kH, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 1000, 0);
+        // keep that order (DS reads, then MFMA / DS pairs, then MFMAs)
+        __builtin_amdgcn_sched_group_barrier(0x100, kH, 0);
 #pragma unroll
         for (int f = 0; f < kFM - kH; ++f) {
             __builtin_amdgcn_sched_group_barrier(0x008, kFN, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, kH * kFN, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // after step s: the weight fragments of step s + 1
+    auto next_bx = [&](auto P) {
+        constexpr int ph = (decltype(P)::value + 1) % (2 * kCS);
+        load_bx(Ic<(ph / kCS) & 1>{}, ph % kCS);
         __builtin_amdgcn_sched_barrier(0);           // the step's MFMAs stay ahead of the wait
     };
 
@@ -335,6 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
     if (steps >= 3 && full_steps >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kA));
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    load_bx(Ic<0>{}, 0);
 
     // Steady state: step s first issues the next weight chunk (when s starts
     // a chunk) and A step s + 3, into the buffers read during the previous
@@ -347,7 +360,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
         if constexpr (t == 0) issue_b(Ic<(ph / kCS + 1) & 1>{}, s / kCS + 1);
         issue_a(Ic<(ph + kNB - 1) & 3>{}, (s + kNB - 1) * kKS, true);
         __builtin_amdgcn_sched_barrier(0);           // the prefetch goes out before the step's LDS reads
-        compute(Ic<ph & 3>{}, Ic<(ph / kCS) & 1>{}, t);
+        compute(Ic<ph & 3>{});
+        next_bx(P);
         constexpr int after = 2 * kA + ((t == 1) ? kB : 0) + ((t == 0) ? kB : 0);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(after));
         barrier_keep_loads();
@@ -361,7 +375,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
         if (t == 0 && s / kCS + 1 < chunks) issue_b(Ic<(ph / kCS + 1) & 1>{}, s / kCS + 1);
         const int t_issue = s + kNB - 1;
         if (t_issue < steps) issue_a(Ic<(ph + kNB - 1) & 3>{}, t_issue * kKS, t_issue < full_steps);
-        compute(Ic<ph & 3>{}, Ic<(ph / kCS) & 1>{}, t);
+        compute(Ic<ph & 3>{});
+        if (s + 1 < steps) next_bx(P);
         __syncthreads();                             // waits for all loads (its fence)
     };
     auto run16 = [&](int s0, auto body) {
