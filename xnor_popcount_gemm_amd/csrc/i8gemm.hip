@@ -29,21 +29,22 @@
 // The int32 result of lane l, register r is row 4*(l/16) + r, column l % 16.
 //
 // Tiling: a 512-thread workgroup (8 waves) computes 256 activation rows x
-// 256 weight rows; wave w takes all rows and columns 32 w .. +31.  The
-// workgroup's A tile (256 rows x 64 bytes per k-step) goes straight from
-// global memory into a ring of 4 LDS buffers (buffer loads to LDS), issued 3
-// steps ahead of its use, with one barrier per step; 16-byte piece j of A
-// row r sits at slot j ^ h(r), h(r) = ((r / 2) ^ (r / 4)) % 4, of the row's
-// four slots.  A fragment read (16 rows of one k-group) then has every 8
-// consecutive lanes on 8 distinct 4-bank groups of a 32-bank window:
-// 16-byte LDS reads are served 8 lanes at a time, and a pattern that is
-// only distinct across 16 lanes (h = (r / 4) % 4) measured half the
-// throughput of this one.  The weight bits move in chunks of 8 k-steps
-// (64 bytes per weight row, whole 64-byte L2 requests; a request per row
-// and step would carry 8 useful bytes) into a double-buffered LDS chunk,
-// one chunk ahead.  With the A tile shared by 256 weight rows, the L2
-// request rate (the limit of a 256 x 128 tile) stays below one per clock
-// and channel.
+// 256 weight rows; wave w takes all rows and columns 32 w .. +31.  The k
+// range is walked in stages of 128 (two MFMA k-steps) with one barrier per
+// stage.  The workgroup's A tile (256 rows x 128 bytes per stage) goes
+// straight from global memory into a ring of LDS buffers (buffer loads to
+// LDS): 4 buffers issued 3 stages ahead of their use (binary weights), 2
+// buffers 1 stage ahead (ternary, whose second weight plane takes the LDS of
+// the other two); 16-byte piece j of A row r sits
+// at slot j ^ (r % 8) of the row's eight slots, so every 8 consecutive
+// lanes of a fragment read (8 rows of one k-group) fall on 8 distinct
+// 4-bank groups of a 32-bank window: 16-byte LDS reads are served 8 lanes
+// at a time (a pattern distinct only across 16 lanes measured half the
+// throughput).  The weight bits move in chunks of 4 stages (64 bytes per
+// weight row, whole 64-byte L2 requests; a request per row and k-step
+// would carry 8 useful bytes) into a double-buffered LDS chunk.  With the A
+// tile shared by 256 weight rows, the L2 request rate (the limit of a
+// 256 x 128 tile) stays below one per clock and channel.
 #include <type_traits>
 
 #include "bnn_device.hpp"
@@ -54,12 +55,12 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBM = 256, kBN = 256, kKS = 64;  // workgroup tile: activation rows x weight rows x k-step
+constexpr int kBM = 256, kBN = 256, kKS = 64;  // workgroup tile: activation rows x weight rows x MFMA k-step
+constexpr int kSub = 2, kST = kSub * kKS;       // k-steps per stage, k per stage
 constexpr int kWN = kBN / kWaves;               // wave tile: all kBM rows x kWN columns
 constexpr int kFM = kBM / 16, kFN = kWN / 16;   // 16 x 16 fragments per wave tile
-constexpr int kNB = 4;          // A ring depth: a step's loads are issued kNB - 1 steps ahead
-constexpr int kCS = 8;          // k-steps per weight chunk (64 bytes of bits per weight row)
-constexpr int kCW = kCS * kKS / 32;             // words per weight row in a chunk (16)
+constexpr int kCS = 4;          // stages per weight chunk
+constexpr int kCW = kCS * kST / 32;             // words per weight row in a chunk (16: 64 bytes)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -122,9 +123,9 @@ __device__ __forceinline__ v4i expand_ternary(uint32_t c) {
     return r;
 }
 
-constexpr int kAPieces = kBM * kKS / 16 / kThreads;      // 16-byte A pieces per lane per k-step
+constexpr int kAPieces = kBM * kST / 16 / kThreads;      // 16-byte A pieces per lane per stage
 constexpr int kBPieces = kBN * kCW * 4 / 16 / kThreads;  // 16-byte weight pieces per lane per chunk
-static_assert(kAPieces == 2 && kBPieces == 2 && kFN == 2, "the staging below assumes these");
+static_assert(kAPieces == 4 && kBPieces == 2 && kFN == 2 && kSub == 2, "the staging below assumes these");
 
 // s_waitcnt immediate that waits for at most n outstanding vector-memory
 // operations (vmcnt in bits 3:0 and 15:14) and not on the other counters.
@@ -163,16 +164,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
 {
     static_assert(!(TERN && XS), "row sums serve binary weights only");
     constexpr int kPL = TERN ? 2 : 1;                // weight planes
+    constexpr int kNB = 2;                           // A ring depth
     // Separate LDS objects, each reached through a compile-time index, so
     // the compiler can tell a load into one buffer from a read of another
-    // and does not wait for the prefetch before the current step's reads.
-    __shared__ __attribute__((aligned(16))) int8_t lds_a0[kBM * kKS], lds_a1[kBM * kKS],
-                                                   lds_a2[kBM * kKS], lds_a3[kBM * kKS];
-    // weight chunks: sign (or binary) plane and, ternary, the nonzero plane
+    // and does not wait for the prefetch before the current stage's reads.
+    __shared__ __attribute__((aligned(16))) int8_t lds_a0[kBM * kST], lds_a1[kBM * kST];
+    __shared__ __attribute__((aligned(16))) int8_t lds_a2[kNB > 2 ? kBM * kST : 16], lds_a3[kNB > 3 ? kBM * kST : 16];
+    // weight chunks (two buffers): sign (or binary) plane and, ternary, the
+    // nonzero plane
     __shared__ __attribute__((aligned(16))) uint32_t lds_b0[kBN * kCW], lds_b1[kBN * kCW];
-    __shared__ __attribute__((aligned(16))) uint32_t lds_z0[TERN ? kBN * kCW : 1], lds_z1[TERN ? kBN * kCW : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_z0[TERN ? kBN * kCW : 4], lds_z1[TERN ? kBN * kCW : 4];
     auto abuf = [&](auto I) -> int8_t* {
-        constexpr int i = decltype(I)::value & 3;
+        constexpr int i = decltype(I)::value % kNB;
         if constexpr (i == 0) return lds_a0;
         else if constexpr (i == 1) return lds_a1;
         else if constexpr (i == 2) return lds_a2;
@@ -208,19 +211,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
     const int tm = gm0 + in_grp % gsz, tn = in_grp / gsz;
     const int m_blk = tm * kBM, n_blk = tn * kBN;
 
-    // A staging.  Instruction i of wave w fills tile rows 16 (kAPieces w + i)
-    // .. +15 (1 KiB of LDS): lane l takes row r = 16 (kAPieces w + i) + l / 4,
-    // LDS slot l % 4, and loads the piece j stored there, j = slot ^ h(r),
-    // h(r) = ((r / 2) ^ (r / 4)) % 4 = ((l / 8) ^ (l / 16)) % 4.  Steps inside
-    // K load straight into LDS (a 16-byte buffer load to LDS writes lane l's
-    // 16 bytes at the instruction's LDS base + 16 l); the step holding the
-    // end of the row goes through registers, masked past K.
+    // A staging.  Instruction i of wave w fills tile rows 8 (kAPieces w + i)
+    // .. +7 (1 KiB of LDS): lane l takes row r = 8 (kAPieces w + i) + l / 8,
+    // LDS slot l % 8, and loads the piece j stored there, j = slot ^ (r % 8)
+    // = (l % 8) ^ (l / 8).  Stages inside K load straight into LDS (a 16-byte
+    // buffer load to LDS writes lane l's 16 bytes at the instruction's LDS
+    // base + 16 l); the stage holding the end of the row goes through
+    // registers, masked past K.
     const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(Xq, M * (int)ldX);          // M * ldX < 2^31
     int aoff[kAPieces];                            // byte offset of row r
 #pragma unroll
     for (int i = 0; i < kAPieces; ++i)
-        aoff[i] = min(m_blk + 16 * (kAPieces * wave + i) + (lane >> 2), M - 1) * (int)ldX;
-    const int apiece = ((lane & 3) ^ (((lane >> 3) ^ (lane >> 4)) & 3)) << 4;   // byte offset of piece j
+        aoff[i] = min(m_blk + 8 * (kAPieces * wave + i) + (lane >> 3), M - 1) * (int)ldX;
+    const int apiece = ((lane & 7) ^ (lane >> 3)) << 4;   // byte offset of piece j in the row
     // Weight staging.  A chunk holds words kCW c .. +kCW-1 of each weight
     // row of the tile; column c's 64 bytes take LDS slots 4 c .. 4 c + 3
     // (16 bytes each) and its 16-byte piece p sits in slot 4 c + ((p + c / 4)
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
     // lane l takes column 128 j + 16 w + l / 4 and piece ((l % 4) - l / 16)
     // % 4.  A piece that starts at or past the row stride (only beyond K)
     // reads the row's last piece instead: its bits meet zero activations or
-    // steps that are not computed.
+    // stages that are not computed.
     const int ldw = (int)ldW;
     const __amdgpu_buffer_rsrc_t brsrc = buffer_rsrc(Wp, N * ldw * 4);           // N * ldW < 2^29
     const __amdgpu_buffer_rsrc_t zrsrc = buffer_rsrc(TERN ? e.Zp : Wp, N * ldw * 4);
@@ -258,17 +261,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
         const int w0 = min(kCW * chunk + 4 * bpiece, ldw - 4);
 #pragma unroll
         for (int j = 0; j < kBPieces; ++j) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, (lptr_t)(lb + 4 * (128 * j + 16 * wave) * 4), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, (lptr_t)(lb + 16 * (128 * j + 16 * wave)), 16,
                                                      (boff[j] + w0) * 4, 0, 0, 0);
             if (TERN)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(zrsrc, (lptr_t)(lz + 4 * (128 * j + 16 * wave) * 4), 16,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(zrsrc, (lptr_t)(lz + 16 * (128 * j + 16 * wave)), 16,
                                                          (boff[j] + w0) * 4, 0, 0, 0);
         }
     };
-    // fragment reads: A row 16 f + r16, k-group g at byte abase + 1024 f
-    // (h(16 f + r16) = h(r16)); weight word 2 t + g / 2 of chunk step t of
-    // column wave kWN + 16 q + r16: piece t / 2, word 2 (t % 2) + g / 2 of it
-    const int abase = r16 * kKS + ((g ^ (((r16 >> 1) ^ (r16 >> 2)) & 3)) << 4);
+    // fragment reads: A row 16 f + r16, k-group g of sub-step u at byte
+    // abase[u] + 2048 f ((16 f + r16) % 8 = r16 % 8); weight word 2 t + g / 2
+    // of chunk k-step t = 2 (stage % 4) + u of column wave kWN + 16 q + r16:
+    // piece stage % 4, word 2 u + g / 2 of it
+    int abase[kSub];
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) abase[u] = r16 * kST + (((4 * u + g) ^ (r16 & 7)) << 4);
     const int bcol0 = wave * kWN + r16;            // + 16 q
     const int bcr = (r16 >> 2) & 3;                // (column / 4) % 4, the same for both q
     // combined ternary word of lane group g: Z bits low, (S & Z) bits high
@@ -283,119 +289,142 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
 #pragma unroll
         for (int q = 0; q < kFN; ++q) acc[f][q] = (v4i){0, 0, 0, 0};
 
-    const int steps = (K + kKS - 1) / kKS;
-    const int full_steps = K / kKS;
-    const int chunks = (steps + kCS - 1) / kCS;
-    constexpr int kA = kAPieces;                   // vector-memory instructions per direct A step
+    const int stages = (K + kST - 1) / kST;
+    const int full_stages = K / kST;
+    const int chunks = (stages + kCS - 1) / kCS;
+    constexpr int kA = kAPieces;                   // vector-memory instructions per direct A stage
     constexpr int kB = kBPieces * kPL;             // ... per weight chunk
 
-    // The expanded weight fragments of the next step are prepared at the end
-    // of the current one (its chunk is in LDS by then), so a step starts
-    // with its MFMAs as soon as the first A fragment arrives.
+    // The weight words of the next stage are read at the end of the current
+    // one (its chunk is in LDS by then) and those of its first k-step
+    // expanded, so a stage starts with its MFMAs as soon as the first A
+    // fragment arrives; the second k-step's words are expanded between the
+    // MFMAs of the two k-steps (into the same registers).
     v4i bx[kFN];
-    auto load_bx = [&](auto IB, int t) {
-        const uint32_t* lb = bbuf(IB);
-        const uint32_t* lz = zbuf(IB);
-        const int bw = 4 * (((t >> 1) + bcr) & 3) + 2 * (t & 1) + (g >> 1);
+    uint32_t sw1[kFN], zw1[kFN];
+    auto expand = [&](int q, uint32_t sw, uint32_t zw) {
+        if (TERN) bx[q] = expand_ternary(tern_word(sw, zw, g));
+        else if (XS) bx[q] = expand_bits01(sw >> (16 * (g & 1)));
+        else bx[q] = expand_signs(sw >> (16 * (g & 1)));
+    };
+    auto load_bx = [&](auto P) {                  // P: stage % 8
+        constexpr int st = decltype(P)::value;
+        const uint32_t* lb = bbuf(Ic<st / kCS>{});
+        const uint32_t* lz = zbuf(Ic<st / kCS>{});
+        const int bw = 4 * (((st % kCS) + bcr) & 3) + (g >> 1);
 #pragma unroll
         for (int q = 0; q < kFN; ++q) {
-            const uint32_t sw = lb[(bcol0 + 16 * q) * kCW + bw];
-            if (TERN) bx[q] = expand_ternary(tern_word(sw, lz[(bcol0 + 16 * q) * kCW + bw], g));
-            else if (XS) bx[q] = expand_bits01(sw >> (16 * (g & 1)));
-            else bx[q] = expand_signs(sw >> (16 * (g & 1)));
+            const int wi = (bcol0 + 16 * q) * kCW + bw;
+            const uint32_t sw0 = lb[wi];
+            const uint32_t zw0 = TERN ? lz[wi] : 0u;
+            sw1[q] = lb[wi + 2];
+            zw1[q] = TERN ? lz[wi + 2] : 0u;
+            expand(q, sw0, zw0);
         }
     };
-    // step s (chunk step t = s % kCS) reads A buffer s % 4; LDS reads run
-    // ahead of their use: the first kH A fragments are issued first, and
-    // fragment f + kH as soon as the MFMAs of fragment f, whose registers it
-    // takes, have been issued.
+    // stage s reads A buffer s % 3; LDS reads run ahead of their use: the
+    // first kH A fragments are issued first, and each later one as soon as
+    // the MFMAs of the fragment whose registers it takes have been issued
+    // (across the two k-steps of the stage).
     auto compute = [&](auto IA) {
         const int8_t* la = abuf(IA);
         constexpr int kH = TERN ? kFM / 4 : kFM / 2;
+        constexpr int kF = kSub * kFM;             // fragments per stage
         v4i a[kH];
 #pragma unroll
-        for (int f = 0; f < kH; ++f) a[f] = *reinterpret_cast<const v4i*>(la + abase + 1024 * f);
+        for (int f = 0; f < kH; ++f) a[f] = *reinterpret_cast<const v4i*>(la + abase[0] + 2048 * f);
 #pragma unroll
-        for (int f = 0; f < kFM; ++f) {
+        for (int x = 0; x < kF; ++x) {
+            const int f = x % kFM;
+            if (x == kFM) {
+#pragma unroll
+                for (int q = 0; q < kFN; ++q) expand(q, sw1[q], zw1[q]);
+            }
 #pragma unroll
             for (int q = 0; q < kFN; ++q)
-                acc[f][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f % kH], bx[q], acc[f][q], 0, 0, 0);
-            if (f + kH < kFM) a[f % kH] = *reinterpret_cast<const v4i*>(la + abase + 1024 * (f + kH));
+                acc[f][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[x % kH], bx[q], acc[f][q], 0, 0, 0);
+            if (x + kH < kF) {
+                const int un = (x + kH) / kFM, fn = (x + kH) % kFM;
+                a[x % kH] = *reinterpret_cast<const v4i*>(la + abase[un] + 2048 * fn);
+            }
         }
-        // keep that order (DS reads, then MFMA / DS pairs, then MFMAs)
+        // keep that order (DS reads, then MFMA / DS pairs with the second
+        // k-step's expansion between the k-steps, then MFMAs)
         __builtin_amdgcn_sched_group_barrier(0x100, kH, 0);
 #pragma unroll
-        for (int f = 0; f < kFM - kH; ++f) {
+        for (int x = 0; x < kF - kH; ++x) {
+            if (x == kFM) __builtin_amdgcn_sched_group_barrier(0x002, 1000, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, kFN, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, kH * kFN, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    // after step s: the weight fragments of step s + 1
-    auto next_bx = [&](auto P) {
-        constexpr int ph = (decltype(P)::value + 1) % (2 * kCS);
-        load_bx(Ic<(ph / kCS) & 1>{}, ph % kCS);
-        __builtin_amdgcn_sched_barrier(0);           // the step's MFMAs stay ahead of the wait
-    };
 
-    // Prologue: weight chunk 0, then A steps 0 .. 2.
+    // Prologue: weight chunks 0 and 1, then A stages 0 .. kNB - 2.
     issue_b(Ic<0>{}, 0);
-    if (0 < steps) issue_a(Ic<0>{}, 0, 0 < full_steps);
-    if (1 < steps) issue_a(Ic<1>{}, kKS, 1 < full_steps);
-    if (2 < steps) issue_a(Ic<2>{}, 2 * kKS, 2 < full_steps);
-    if (steps >= 3 && full_steps >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kA));
+    issue_b(Ic<1>{}, 1);
+    if (0 < stages) issue_a(Ic<0>{}, 0, 0 < full_stages);
+    if (kNB > 2 && 1 < stages) issue_a(Ic<1>{}, kST, 1 < full_stages);
+    if (kNB > 3 && 2 < stages) issue_a(Ic<2>{}, 2 * kST, 2 < full_stages);
+    if (stages >= kNB - 1 && full_stages >= kNB - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm((kNB - 2) * kA));
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    load_bx(Ic<0>{}, 0);
+    load_bx(Ic<0>{});
 
-    // Steady state: step s first issues the next weight chunk (when s starts
-    // a chunk) and A step s + 3, into the buffers read during the previous
-    // chunk / step; all of it inside K, so every load is direct and the
-    // count of loads issued after those of step s + 1 is known: A of steps
-    // s + 2 and s + 3, and the chunks issued in steps s - 1 and s.
-    auto fast_step = [&](int s, auto P) {
-        constexpr int ph = decltype(P)::value;      // s % (2 kCS)
-        constexpr int t = ph % kCS;
-        if constexpr (t == 0) issue_b(Ic<(ph / kCS + 1) & 1>{}, s / kCS + 1);
-        issue_a(Ic<(ph + kNB - 1) & 3>{}, (s + kNB - 1) * kKS, true);
-        __builtin_amdgcn_sched_barrier(0);           // the prefetch goes out before the step's LDS reads
-        compute(Ic<ph & 3>{});
-        next_bx(P);
-        constexpr int after = 2 * kA + ((t == 1) ? kB : 0) + ((t == 0) ? kB : 0);
+    // Stage s issues A stage s + kNB - 1 (into the buffer read during stage
+    // s - 1), computes, prepares the next stage's weight fragments and, at
+    // the end of the last stage of chunk c - 1 (s = 4 c - 1), issues chunk
+    // c + 1 (into the buffer of chunk c - 1, last read at the end of stage
+    // s - 1).  In the steady state all of it lies inside K, so every load is
+    // direct and the loads issued after those of stage s + 1 are known: A of
+    // stages s + 2 .. s + kNB - 1 and the chunks issued at the ends of stages
+    // s + 2 - kNB .. s.  A chunk is then complete (and, after the barrier,
+    // visible) at least one stage before its first read.
+    auto chunk_issues = [](int lo, int hi) {     // stages t in [lo, hi] with t % 4 == 3 (lo >= -3)
+        int n = 0;
+        for (int t = lo; t <= hi; ++t) n += ((t + 8) % kCS) == kCS - 1;
+        return n;
+    };
+    auto fast_stage = [&](int s, auto P) {
+        constexpr int ph = decltype(P)::value;      // s % 8
+        issue_a(Ic<(ph + kNB - 1) % kNB>{}, (s + kNB - 1) * kST, true);
+        __builtin_amdgcn_sched_barrier(0);           // the prefetch goes out before the stage's LDS reads
+        compute(Ic<ph % kNB>{});
+        load_bx(Ic<(ph + 1) % 8>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ph % kCS == kCS - 1) issue_b(Ic<(ph / kCS + 2) & 1>{}, s / kCS + 2);
+        constexpr int after = (kNB - 2) * kA + kB * chunk_issues(ph + 2 - kNB, ph);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(after));
         barrier_keep_loads();
     };
-    static_assert(2 * kA + 2 * kB <= 63, "vmcnt holds at most 63");
-    // General step (the tail, where loads may be masked or missing): the
+    static_assert((4 - 2) * kAPieces + kBPieces * 2 <= 63, "vmcnt holds at most 63");
+    // General stage (the tail, where loads may be masked or missing): the
     // same order with every issue checked, and a full wait.
-    auto step = [&](int s, auto P) {
+    auto stage = [&](int s, auto P) {
         constexpr int ph = decltype(P)::value;
-        constexpr int t = ph % kCS;
-        if (t == 0 && s / kCS + 1 < chunks) issue_b(Ic<(ph / kCS + 1) & 1>{}, s / kCS + 1);
         const int t_issue = s + kNB - 1;
-        if (t_issue < steps) issue_a(Ic<(ph + kNB - 1) & 3>{}, t_issue * kKS, t_issue < full_steps);
-        compute(Ic<ph & 3>{});
-        if (s + 1 < steps) next_bx(P);
+        if (t_issue < stages)
+            issue_a(Ic<(ph + kNB - 1) % kNB>{}, t_issue * kST, t_issue < full_stages);
+        compute(Ic<ph % kNB>{});
+        if (s + 1 < stages) load_bx(Ic<(ph + 1) % 8>{});
+        if (ph % kCS == kCS - 1 && s / kCS + 2 < chunks) issue_b(Ic<(ph / kCS + 2) & 1>{}, s / kCS + 2);
         __syncthreads();                             // waits for all loads (its fence)
     };
-    auto run16 = [&](int s0, auto body) {
-        body(s0 + 0, Ic<0>{});  body(s0 + 1, Ic<1>{});  body(s0 + 2, Ic<2>{});  body(s0 + 3, Ic<3>{});
-        body(s0 + 4, Ic<4>{});  body(s0 + 5, Ic<5>{});  body(s0 + 6, Ic<6>{});  body(s0 + 7, Ic<7>{});
-        body(s0 + 8, Ic<8>{});  body(s0 + 9, Ic<9>{});  body(s0 + 10, Ic<10>{}); body(s0 + 11, Ic<11>{});
-        body(s0 + 12, Ic<12>{}); body(s0 + 13, Ic<13>{}); body(s0 + 14, Ic<14>{}); body(s0 + 15, Ic<15>{});
+    auto run8 = [&](int s0, auto body) {
+        body(s0 + 0, Ic<0>{}); body(s0 + 1, Ic<1>{}); body(s0 + 2, Ic<2>{}); body(s0 + 3, Ic<3>{});
+        body(s0 + 4, Ic<4>{}); body(s0 + 5, Ic<5>{}); body(s0 + 6, Ic<6>{}); body(s0 + 7, Ic<7>{});
     };
     int s = 0;
-    // a 16-step block is fast while its A issues (up to step s + 18) lie in K
-    // and its chunk issues (up to chunk s / 8 + 2) exist
-    for (; s + 16 + kNB - 1 <= full_steps && s / kCS + 2 < chunks; s += 16)
-        run16(s, fast_step);
-    for (; s < steps; s += 16)
-        run16(s, [&](int ss, auto P) { if (ss < steps) step(ss, P); });
+    // eight stages are fast while their A issues (up to stage s + 6 + kNB)
+    // lie in K
+    for (; s + 8 + kNB - 1 <= full_stages; s += 8) run8(s, fast_stage);
+    for (; s < stages; s += 8)
+        run8(s, [&](int ss, auto P) { if (ss < stages) stage(ss, P); });
 
     // Epilogue.  Full tiles with 16-byte aligned output rows go through LDS
     // (the A buffers are free now): in 8 passes of 2 fragment rows, each
-    // wave parks its 32 x kWN int32 block in its own 8 KiB half of an A
+    // wave parks its 32 x kWN int32 block in its own 8 KiB quarter of an A
     // buffer (column c of row r at word r * 36 + c: the stride of 36 words
     // puts the 4 lane groups of a fragment, rows 4 apart, on disjoint
     // 16-bank groups) and reads it back as 16-byte row pieces, so every store
@@ -406,9 +435,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
                       (!(e.flags & EPI_SCALE) || ((reinterpret_cast<uintptr_t>(e.Y) & 15u) == 0 && e.ldY % 4 == 0));
     if (full) {
         constexpr int kPS = 36;                    // parked row stride in words
-        static_assert(32 * kPS * 4 <= kBM * kKS / 2, "a wave's parked block fits half an A buffer");
-        int8_t* pb = (wave >> 1) == 0 ? lds_a0 : (wave >> 1) == 1 ? lds_a1 : (wave >> 1) == 2 ? lds_a2 : lds_a3;
-        int32_t* park = reinterpret_cast<int32_t*>(pb + (wave & 1) * (kBM * kKS / 2));
+        static_assert(32 * kPS * 4 <= kBM * kST / 4, "a wave's parked block fits a quarter of an A buffer");
+        int8_t* pb = (wave >> 2) == 0 ? lds_a0 : lds_a1;
+        int32_t* park = reinterpret_cast<int32_t*>(pb + (wave & 3) * (kBM * kST / 4));
         const int pc = 4 * (lane & 7);             // read-back: 4 columns of row 8 p + lane / 8
         const int n = n_blk + wave * kWN + pc;
         float an[4] = {0.0f, 0.0f, 0.0f, 0.0f};
