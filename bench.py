@@ -767,12 +767,14 @@ def main():
             "shapes": iv,
         }
         ig = i8_gemm_bench(bnn, torch, 8192, 8192, 8192)
+        idig = source_digest("xnor_popcount_gemm_amd/csrc/i8gemm.hip", "xnor_popcount_gemm_amd/csrc/bnn_device.hpp")
         sec["i8act_gemm_8192"] = {
-            "metric": "binary weights x INT8 activations, int8 MFMA GEMM ops/s",
+            "metric": "binary weights x INT8 activations, int8 MFMA GEMM ops/s (activation row sums given)",
             "value": round(ig["int8_tops"], 1), "unit": "TOPS",
             "roofline": {"bound": "mfma", "achieved": round(ig["int8_tops"], 1),
                          "peak": PEAK_INT8_MFMA / 1e12, "unit": "TOPS",
-                         "frac": round(ig["frac_int8_mfma_peak"], 4)},
+                         "frac": round(ig["frac_int8_mfma_peak"], 4),
+                         "traffic": read_traffic("bwn_i8_gemm_8192_rowsums", idig)},
             "detail": ig,
         }
         sec["ternary"] = ternary_bench(bnn, torch)
