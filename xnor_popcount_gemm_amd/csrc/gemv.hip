@@ -48,7 +48,10 @@ __device__ __forceinline__ u32x4 load_stream(const uint32_t* p) {
 // e.nnz the nonzero count per row; a word contributes popcount((x ^ s) & z)
 // (one v_bitop3 + one v_bcnt) and D = nnz - 2 * sum ("Extreme
 // Quantization", eq. (7)).
-template <int MR, int CPL, int U, bool TERN>
+// XEPI: the epilogue may take the per-tensor alpha or a bias (checked at run
+// time); without it those branches are compiled out, which keeps the
+// binary streaming loop as short as it can be.
+template <int MR, int CPL, int U, bool TERN, bool XEPI>
 __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
     const uint32_t* __restrict__ Xp, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
     int N, int K, int glog2, Epilogue e)
@@ -110,8 +113,8 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
             if (TERN && row < N) kb[u] = e.nnz[row];
             av[u] = 0.0f;
             bv[u] = 0.0f;
-            if ((e.flags & EPI_SCALE) && row < N) av[u] = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : row];
-            if ((e.flags & EPI_BIAS) && row < N) bv[u] = e.bias[row];
+            if ((e.flags & EPI_SCALE) && row < N) av[u] = e.alpha[(XEPI && (e.flags & EPI_ALPHA_TENSOR)) ? 0 : row];
+            if (XEPI && (e.flags & EPI_BIAS) && row < N) bv[u] = e.bias[row];
 #pragma unroll
             for (int mr = 0; mr < MR; ++mr) {
                 rv[u][mr] = 0.0f;
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void k_xnor_gemv(
                     if (e.flags & EPI_DOT) e.D[(int64_t)mr * e.ldD + row] = d;
                     if (e.flags & EPI_SCALE) {
                         float y = av[u] * (float)d;
-                        if (e.flags & EPI_BIAS) y = y + bv[u];
+                        if (XEPI && (e.flags & EPI_BIAS)) y = y + bv[u];
                         if (e.flags & EPI_RESIDUAL) y = y + rv[u][mr];
                         e.Y[(int64_t)mr * e.ldY + row] = y;
                     }
@@ -197,9 +200,11 @@ hipError_t launch_xnor_gemv(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
     if (blocks < 1) blocks = 1;
     const dim3 grid((unsigned)blocks), block(kThreads);
     const int n = (int)N, k = (int)K;
+    const bool xepi = (e.flags & (EPI_BIAS | EPI_ALPHA_TENSOR)) != 0;
 #define BNN_GEMV(MR, CPL, UU) \
-    if (e.flags & W_TERNARY) hipLaunchKernelGGL((k_xnor_gemv<MR, CPL, UU, true>), grid, block, 0, s, Xp, ldX, Wp, ldW, n, k, glog2, e); \
-    else                     hipLaunchKernelGGL((k_xnor_gemv<MR, CPL, UU, false>), grid, block, 0, s, Xp, ldX, Wp, ldW, n, k, glog2, e)
+    if (e.flags & W_TERNARY) hipLaunchKernelGGL((k_xnor_gemv<MR, CPL, UU, true, true>), grid, block, 0, s, Xp, ldX, Wp, ldW, n, k, glog2, e); \
+    else if (xepi)           hipLaunchKernelGGL((k_xnor_gemv<MR, CPL, UU, false, true>), grid, block, 0, s, Xp, ldX, Wp, ldW, n, k, glog2, e); \
+    else                     hipLaunchKernelGGL((k_xnor_gemv<MR, CPL, UU, false, false>), grid, block, 0, s, Xp, ldX, Wp, ldW, n, k, glog2, e)
 #define BNN_GEMV_MR(CPL, UU) \
     switch (M) { case 1: BNN_GEMV(1, CPL, UU); break; case 2: BNN_GEMV(2, CPL, UU); break; \
                  case 3: BNN_GEMV(3, CPL, UU); break; default: BNN_GEMV(4, CPL, UU); break; }
