@@ -299,7 +299,10 @@ __global__ __launch_bounds__(kThreads) void k_pack_ternary(
 // decided as the IEEE single comparison x >= beta_k (bit 0 for +1; NaN -> 1),
 // with one shift per column k (per channel of an NHWC image viewed as
 // [pixels, C]).  Same mapping as k_pack_dense; positions >= K are +1 (0).
-template <bool VEC>
+// LDP = 4 or 8 (packed rows of that many words, C <= 256 channels): the 8
+// lane groups of a wave cover 8 / LDP rows per step, so no lane group idles
+// past the end of a short row; LDP = 0 walks any row length.
+template <bool VEC, int LDP>
 __global__ __launch_bounds__(kThreads) void k_pack_dense_rsign(
     const float* __restrict__ X, int64_t rows, int K, int64_t ldX, const float* __restrict__ beta,
     uint32_t* __restrict__ P, int64_t ldP)
@@ -310,6 +313,46 @@ __global__ __launch_bounds__(kThreads) void k_pack_dense_rsign(
     const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
     const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
     const int ldp = (int)ldP;
+    auto nibble_rs = [&](const Frag& f, int k0) {
+        uint32_t nib = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = k0 + i;
+            const bool neg = k < K && !(__uint_as_float(f.u[i]) >= beta[k]);
+            nib |= (neg ? 1u : 0u) << i;
+        }
+        return nib;
+    };
+    if constexpr (LDP > 0) {
+        // step u of a wave pass: rows r0 + RS u + grp / LDP, word grp % LDP;
+        // the lane's four columns, and so its four shifts, never change
+        constexpr int RS = 8 / (LDP > 0 ? LDP : 8);
+        const int w = grp % LDP;
+        const int k0 = 32 * w + 4 * sub;
+        float bt[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bt[i] = (k0 + i < K) ? beta[k0 + i] : 0.0f;
+        for (int64_t r0 = RS * kSteps * wave; r0 < rows; r0 += RS * kSteps * nwaves) {
+            Frag f[kSteps];
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const int64_t r = r0 + RS * u + grp / LDP;
+                f[u] = Frag{};
+                if (r < rows) f[u] = load_frag<VEC>(X + r * ldX, k0, K);
+            }
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const int64_t r = r0 + RS * u + grp / LDP;
+                uint32_t nib = 0u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    nib |= ((k0 + i < K && !(__uint_as_float(f[u].u[i]) >= bt[i])) ? 1u : 0u) << i;
+                const uint32_t word = or_reduce8_to_last(nib << (4 * sub));
+                if (sub == 7 && r < rows) P[r * ldP + w] = word;
+            }
+        }
+        return;
+    }
     for (int64_t r = wave; r < rows; r += nwaves) {
         const float* __restrict__ xr = X + r * ldX;
         uint32_t* __restrict__ pr = P + r * ldP;
@@ -321,15 +364,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_dense_rsign(
 #pragma unroll
             for (int u = 0; u < kSteps; ++u) {
                 const int w = w0 + 8 * u + grp;
-                const int k0 = 32 * w + 4 * sub;
-                uint32_t nib = 0u;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int k = k0 + i;
-                    const bool neg = k < K && !(__uint_as_float(f[u].u[i]) >= beta[k]);
-                    nib |= (neg ? 1u : 0u) << i;
-                }
-                const uint32_t word = or_reduce8_to_last(nib << (4 * sub));
+                const uint32_t word = or_reduce8_to_last(nibble_rs(f[u], 32 * w + 4 * sub) << (4 * sub));
                 if (sub == 7 && w < ldp) pr[w] = word;
             }
         }
@@ -490,9 +525,22 @@ hipError_t launch_pack_dense_rsign(const float* X, int64_t rows, int64_t K, int6
                                    uint32_t* P, int64_t ldP, hipStream_t s)
 {
     const bool vec = aligned16(X) && (ldX % 4 == 0);
-    const dim3 grid(grid_for_rows(rows)), block(kThreads);
-    if (vec) hipLaunchKernelGGL((k_pack_dense_rsign<true>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
-    else     hipLaunchKernelGGL((k_pack_dense_rsign<false>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
+    const dim3 block(kThreads);
+    if (ldP == 4 || ldP == 8) {                      // 8 / ldP rows per wave step
+        const int64_t rs = 8 / ldP;
+        const dim3 grid(grid_for_rows((rows + rs * kSteps - 1) / (rs * kSteps)));
+        if (ldP == 4) {
+            if (vec) hipLaunchKernelGGL((k_pack_dense_rsign<true, 4>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
+            else     hipLaunchKernelGGL((k_pack_dense_rsign<false, 4>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
+        } else {
+            if (vec) hipLaunchKernelGGL((k_pack_dense_rsign<true, 8>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
+            else     hipLaunchKernelGGL((k_pack_dense_rsign<false, 8>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
+        }
+        return hipGetLastError();
+    }
+    const dim3 grid(grid_for_rows(rows));
+    if (vec) hipLaunchKernelGGL((k_pack_dense_rsign<true, 0>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
+    else     hipLaunchKernelGGL((k_pack_dense_rsign<false, 0>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
     return hipGetLastError();
 }
 
