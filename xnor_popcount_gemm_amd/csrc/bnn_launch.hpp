@@ -27,6 +27,16 @@ enum : uint32_t { EPI_DOT = 1u, EPI_SCALE = 2u, EPI_RESIDUAL = 4u, EPI_THRESH = 
                   EPI_ALPHA_TENSOR = 16u, EPI_BIAS = 32u, W_TERNARY = 64u, EPI_SIGN_PACK = 128u };
 
 // Epilogue of binary weights x INT8 activations.
+// Compute units of the current device (256 if the query fails).
+inline int num_cus() {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    return cus;
+}
+
 struct EpilogueI8 {
     uint32_t flags;          // EPI_DOT, EPI_SCALE, EPI_ALPHA_TENSOR
     int32_t* D; int64_t ldD;

@@ -6,13 +6,17 @@
 // 1-bit LLMs", sign per its Notation), and the last layer reads the +1/-1
 // outputs of the last binary layer.
 //
-// First layer: 64x64 output tile per 256-thread workgroup, 4x4 per thread,
-// K staged through LDS in 16-wide slices already widened to double.  Every
-// product of two floats is exact in double and each output accumulates its
-// K products in index order with one rounding per step (an FMA of an exact
-// product equals a rounded add), so the sign decision sees the same double
-// sum as a plain sequential loop.  The signs of each row's 32-column groups
-// are folded into packed words with DPP row shifts, as in the pack kernels.
+// First layer: 64 x 8 NJ output tile per one-wave workgroup, 8 x NJ outputs
+// per lane (lane (tx, ty) owns rows 8 ty .. +7 and columns tx + 8 j), K
+// staged through LDS in 16-wide slices already widened to double: 8 + NJ LDS
+// doubles per 8 NJ FMAs, against 8 per 16 of a 4x4 tile (LDS-bound at 37% of
+// the fp64 peak).  NJ = 4 when 8-column lanes would leave fewer than two
+// waves per SIMD.  Every product of two floats is exact in double and each output
+// accumulates its K products in index order with one rounding per step (an
+// FMA of an exact product equals a rounded add), so the sign decision sees
+// the same double sum as a plain sequential loop.  The signs of each row's
+// 32-column groups are folded into packed words with DPP row shifts, as in
+// the pack kernels.
 //
 // Last layer: one workgroup per activation row, K split over its waves,
 // double accumulators, fixed-order reductions (deterministic on every run).
@@ -26,63 +30,95 @@ constexpr int kThreads = 256;
 constexpr int kTile = 64;
 constexpr int kSlice = 16;
 
-__global__ __launch_bounds__(kThreads) void k_dense_f32_sign_pack(
+template <bool VEC, int NJ>
+__global__ __launch_bounds__(64) void k_dense_f32_sign_pack(
     const float* __restrict__ X, int64_t ldX, const float* __restrict__ W, int64_t ldW,
     int M, int N, int K, uint32_t* __restrict__ Op, int64_t ldOp, int tiles_n)
 {
+    constexpr int kTN = 8 * NJ;                     // tile columns
     __shared__ double xs[kSlice][kTile];
-    __shared__ double ws[kSlice][kTile];
-    const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;
+    __shared__ double ws[kSlice][kTN];
+    const int lane = threadIdx.x;
+    const int tx = lane & 7, ty = lane >> 3;
     const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
-    const int m0 = tm * kTile, n0 = tn * kTile;
-    // staging map: thread -> (tile row, 4 consecutive k)
-    const int sr = tid >> 2, sk = (tid & 3) * 4;
+    const int m0 = tm * kTile, n0 = tn * kTN;
+    // staging: lane l widens 16 consecutive k of tile row l (of X and of W)
+    const int gm = m0 + lane, gn = n0 + lane;
+    const float* __restrict__ xrow = X + (int64_t)min(gm, M - 1) * ldX;
+    const float* __restrict__ wrow = W + (int64_t)min(min(gn, n0 + kTN - 1), N - 1) * ldW;
 
-    double acc[4][4];
+    double acc[8][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+        for (int j = 0; j < NJ; ++j) acc[i][j] = 0.0;
 
-    for (int k0 = 0; k0 < K; k0 += kSlice) {
-        {
-            const int gm = m0 + sr, gn = n0 + sr;
+    // global loads of a slice go out one slice ahead (registers), LDS reads
+    // of a k one k ahead
+    float xv[kSlice], wv[kSlice];
+    auto fetch = [&](int k0) {
+        if (VEC && k0 + kSlice <= K) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int k = k0 + sk + i;
-                xs[sk + i][sr] = (gm < M && k < K) ? (double)X[(int64_t)gm * ldX + k] : 0.0;
-                ws[sk + i][sr] = (gn < N && k < K) ? (double)W[(int64_t)gn * ldW + k] : 0.0;
+            for (int q = 0; q < kSlice / 4; ++q) {
+                const float4 x4 = *reinterpret_cast<const float4*>(xrow + k0 + 4 * q);
+                const float4 w4 = *reinterpret_cast<const float4*>(wrow + k0 + 4 * q);
+                xv[4 * q] = x4.x; xv[4 * q + 1] = x4.y; xv[4 * q + 2] = x4.z; xv[4 * q + 3] = x4.w;
+                wv[4 * q] = w4.x; wv[4 * q + 1] = w4.y; wv[4 * q + 2] = w4.z; wv[4 * q + 3] = w4.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kSlice; ++i) {
+                xv[i] = (k0 + i < K) ? xrow[k0 + i] : 0.0f;
+                wv[i] = (k0 + i < K) ? wrow[k0 + i] : 0.0f;
             }
         }
-        __syncthreads();
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += kSlice) {
+        __syncthreads();                             // the previous slice has been read
 #pragma unroll
-        for (int kk = 0; kk < kSlice; ++kk) {
-            double a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx * 4 + j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fma(a[i], b[j], acc[i][j]);
+        for (int i = 0; i < kSlice; ++i) {
+            xs[i][lane] = gm < M ? (double)xv[i] : 0.0;
+            if (lane < kTN) ws[i][lane] = gn < N ? (double)wv[i] : 0.0;
         }
         __syncthreads();
+        if (k0 + kSlice < K) fetch(k0 + kSlice);
+        double a[2][8], b[2][NJ];
+        auto rd = [&](int kk, int p) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a[p][i] = xs[kk][8 * ty + i];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) b[p][j] = ws[kk][tx + 8 * j];
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < kSlice; ++kk) {
+            if (kk + 1 < kSlice) rd(kk + 1, (kk + 1) & 1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_fma(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
+        }
     }
 
     // Padded k (k >= K) contributed exact zeros, so each acc is the in-order
-    // double sum over k < K.  Columns >= N hold 0.0 -> bit 0 (+1), the pad rule.
+    // double sum over k < K.  Columns >= N hold 0.0 -> bit 0 (+1), the pad
+    // rule.  Word h of a row (columns 32 h .. +31 of the tile) takes bit
+    // tx + 8 j' from column tx + 8 (4 h + j') of lane tx: an OR over the 8
+    // lanes of the row group.
     const int nw = (N + 31) >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t nib = 0u;
+    for (int i = 0; i < 8; ++i) {
+        const int m = m0 + 8 * ty + i;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) nib |= (acc[i][j] >= 0.0 ? 0u : 1u) << j;
-        const uint32_t word = or_reduce8_to_last(nib << (4 * (tx & 7)));
-        const int m = m0 + ty * 4 + i;
-        const int widx = (n0 >> 5) + (tx >> 3);
-        if ((tx & 7) == 7 && m < M && widx < nw) Op[(int64_t)m * ldOp + widx] = word;
+        for (int h = 0; h < NJ / 4; ++h) {
+            uint32_t bits = 0u;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) bits |= (acc[i][4 * h + jj] >= 0.0 ? 0u : 1u) << (tx + 8 * jj);
+            const uint32_t word = or_reduce8_to_last(bits);
+            const int widx = (n0 >> 5) + h;
+            if (tx == 7 && m < M && widx < nw) Op[(int64_t)m * ldOp + widx] = word;
+        }
         if (tn == tiles_n - 1 && tx == 0 && m < M)
             for (int64_t w = nw; w < ldOp; ++w) Op[(int64_t)m * ldOp + w] = 0u;
     }
@@ -151,11 +187,18 @@ hipError_t launch_dense_f32_sign_pack(const float* X, int64_t ldX, const float* 
                                       int64_t M, int64_t N, int64_t K,
                                       uint32_t* Op, int64_t ldOp, hipStream_t s)
 {
-    const int tiles_n = (int)((N + kTile - 1) / kTile);
+    const bool vec = (reinterpret_cast<uintptr_t>(X) & 15u) == 0 && (reinterpret_cast<uintptr_t>(W) & 15u) == 0 &&
+                     ldX % 4 == 0 && ldW % 4 == 0;
     const int64_t tiles_m = (M + kTile - 1) / kTile;
-    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads);
-    hipLaunchKernelGGL(k_dense_f32_sign_pack, grid, block, 0, s, X, ldX, W, ldW,
-                       (int)M, (int)N, (int)K, Op, ldOp, tiles_n);
+    const bool wide = tiles_m * ((N + 63) / 64) >= (int64_t)num_cus() * 8;   // two waves per SIMD at NJ = 8
+    const int tn_cols = wide ? 64 : 32;
+    const int tiles_n = (int)((N + tn_cols - 1) / tn_cols);
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(64);
+#define BNN_DENSE(V, NJ) hipLaunchKernelGGL((k_dense_f32_sign_pack<V, NJ>), grid, block, 0, s, X, ldX, W, ldW, \
+                                            (int)M, (int)N, (int)K, Op, ldOp, tiles_n)
+    if (vec) { if (wide) BNN_DENSE(true, 8); else BNN_DENSE(true, 4); }
+    else     { if (wide) BNN_DENSE(false, 8); else BNN_DENSE(false, 4); }
+#undef BNN_DENSE
     return hipGetLastError();
 }
 

@@ -517,15 +517,6 @@ int tile_cols_from_env() {
     return (t == 8 || t == 16 || t == 32 || t == 64) ? t : 0;
 }
 
-int num_cus() {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
-    return cus;
-}
-
 }  // namespace
 
 hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,

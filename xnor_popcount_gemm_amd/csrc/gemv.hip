@@ -27,15 +27,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-int num_cus() {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
-    return cus;
-}
-
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming load of one 16-byte weight granule: the weights are read once per
