@@ -21,7 +21,9 @@
 // is spent per weight column and amortised over the rows that share the
 // expanded fragment; each wave therefore spans all 256 rows of the
 // workgroup tile: 16 x 2 fragments, 32 MFMAs per 64-wide k-step against 2
-// weight-fragment expansions.
+// weight-fragment expansions.  (Wider wave tiles would halve the LDS reads
+// of A per MFMA but need 256 accumulator registers; as AGPRs that cost as
+// many register moves as they saved.)
 //
 // Fragment layout used for both operands: lane l holds row (A) or column (B)
 // l % 16 and the 16 consecutive k of group l / 16 within the 64-wide step.
@@ -32,10 +34,10 @@
 // 256 weight rows; wave w takes all rows and columns 32 w .. +31.  The k
 // range is walked in stages of 128 (two MFMA k-steps) with one barrier per
 // stage.  The workgroup's A tile (256 rows x 128 bytes per stage) goes
-// straight from global memory into a ring of LDS buffers (buffer loads to
-// LDS): 4 buffers issued 3 stages ahead of their use (binary weights), 2
-// buffers 1 stage ahead (ternary, whose second weight plane takes the LDS of
-// the other two); 16-byte piece j of A row r sits
+// straight from global memory into a 2-deep ring of LDS buffers (buffer
+// loads to LDS, issued one stage ahead of their use: a 4-deep ring of these
+// 32 KiB stages leaves no LDS for the ternary weights' second plane, and
+// with binary weights it ran out of registers); 16-byte piece j of A row r sits
 // at slot j ^ (r % 8) of the row's eight slots, so every 8 consecutive
 // lanes of a fragment read (8 rows of one k-group) fall on 8 distinct
 // 4-bank groups of a 32-bank window: 16-byte LDS reads are served 8 lanes
@@ -169,17 +171,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
     // the compiler can tell a load into one buffer from a read of another
     // and does not wait for the prefetch before the current stage's reads.
     __shared__ __attribute__((aligned(16))) int8_t lds_a0[kBM * kST], lds_a1[kBM * kST];
-    __shared__ __attribute__((aligned(16))) int8_t lds_a2[kNB > 2 ? kBM * kST : 16], lds_a3[kNB > 3 ? kBM * kST : 16];
     // weight chunks (two buffers): sign (or binary) plane and, ternary, the
     // nonzero plane
     __shared__ __attribute__((aligned(16))) uint32_t lds_b0[kBN * kCW], lds_b1[kBN * kCW];
     __shared__ __attribute__((aligned(16))) uint32_t lds_z0[TERN ? kBN * kCW : 4], lds_z1[TERN ? kBN * kCW : 4];
+    static_assert(kNB == 2, "the A ring is lds_a0 / lds_a1");
     auto abuf = [&](auto I) -> int8_t* {
-        constexpr int i = decltype(I)::value % kNB;
-        if constexpr (i == 0) return lds_a0;
-        else if constexpr (i == 1) return lds_a1;
-        else if constexpr (i == 2) return lds_a2;
-        else return lds_a3;
+        if constexpr (decltype(I)::value % kNB == 0) return lds_a0;
+        else return lds_a1;
     };
     auto bbuf = [&](auto I) -> uint32_t* {
         if constexpr ((decltype(I)::value & 1) == 0) return lds_b0;
@@ -361,14 +360,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Prologue: weight chunks 0 and 1, then A stages 0 .. kNB - 2.
+    // Prologue: weight chunks 0 and 1 and A stage 0, all complete before the
+    // first stage.
     issue_b(Ic<0>{}, 0);
     issue_b(Ic<1>{}, 1);
-    if (0 < stages) issue_a(Ic<0>{}, 0, 0 < full_stages);
-    if (kNB > 2 && 1 < stages) issue_a(Ic<1>{}, kST, 1 < full_stages);
-    if (kNB > 3 && 2 < stages) issue_a(Ic<2>{}, 2 * kST, 2 < full_stages);
-    if (stages >= kNB - 1 && full_stages >= kNB - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm((kNB - 2) * kA));
-    else __builtin_amdgcn_s_waitcnt(0);
+    issue_a(Ic<0>{}, 0, 0 < full_stages);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     load_bx(Ic<0>{});
 
@@ -409,7 +406,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwn_i8_gemm(
         compute(Ic<ph % kNB>{});
         if (s + 1 < stages) load_bx(Ic<(ph + 1) % 8>{});
         if (ph % kCS == kCS - 1 && s / kCS + 2 < chunks) issue_b(Ic<(ph / kCS + 2) & 1>{}, s / kCS + 2);
-        __syncthreads();                             // waits for all loads (its fence)
+        __builtin_amdgcn_s_waitcnt(0);               // every load of this lane, then the workgroup's
+        __syncthreads();
     };
     auto run8 = [&](int s0, auto body) {
         body(s0 + 0, Ic<0>{}); body(s0 + 1, Ic<1>{}); body(s0 + 2, Ic<2>{}); body(s0 + 3, Ic<3>{});
