@@ -10,6 +10,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -29,7 +31,7 @@ def hipcc() -> str:
 
 def flags() -> list:
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-ffp-contract=off",                     # alpha*D and +R stay two rounded ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-fvisibility=hidden", "-Wall",
@@ -37,13 +39,39 @@ def flags() -> list:
     ]
 
 
+def _jobs() -> int:
+    try:
+        n = int(os.environ.get("MAX_JOBS", "0"))
+    except ValueError:
+        n = 0
+    return max(1, min(n if n > 0 else (os.cpu_count() or 1), 16))
+
+
 def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip to an object (in parallel), then link libbnn.so."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + flags() + srcs + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="bnn_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in srcs]
+
+        def compile_one(so):
+            src, obj = so
+            cmd = [cc] + flags() + ["-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return subprocess.run(cmd, capture_output=True, text=True)
+
+        with ThreadPoolExecutor(max_workers=_jobs()) as pool:
+            results = list(pool.map(compile_one, zip(srcs, objs)))
+        for src, r in zip(srcs, results):
+            sys.stderr.write(r.stderr)
+            if r.returncode != 0:
+                raise subprocess.CalledProcessError(r.returncode, f"hipcc -c {src}", r.stdout, r.stderr)
+        tmp = LIB + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB
 

@@ -48,6 +48,54 @@ __device__ __forceinline__ void load_granules(uint32_t* a, const uint32_t* __res
     }
 }
 
+// Two columns' accumulators c0, c1 over NW words: c0 += popcount(a[i] ^ u[i]),
+// c1 += popcount(a[i] ^ v[i]) (u, v uniform, in SGPRs).  Each bit count is
+// separated from the xor that produces its operand by one s_nop 0, and
+// nothing else sits between the pairs.  Measured on MI355X (xor/bcnt
+// streams, 4 waves per SIMD): a v_bcnt_u32_b32 right after the VALU op that
+// writes its operand runs at ~63% of the mixed issue peak, with one nop in
+// between at ~90%, and with a second nop after the bit count at ~70%.  One
+// asm block covers NW words of both columns because the compiler puts a nop
+// of its own between consecutive asm blocks.
+#define BNN_XP(A, W, C) "v_xor_b32 %[t], " W ", " A "\n\ts_nop 0\n\tv_bcnt_u32_b32 " C ", %[t], " C "\n\t"
+#define BNN_XP2(I) BNN_XP("%[a" #I "]", "%[u" #I "]", "%[c0]") BNN_XP("%[a" #I "]", "%[v" #I "]", "%[c1]")
+#define BNN_XIN(I) [a##I] "v"(a[I]), [u##I] "s"(u[I]), [v##I] "s"(v[I])
+template <int NW>
+__device__ __forceinline__ void xor_popc_2cols(uint32_t& c0, uint32_t& c1, const uint32_t* a, const uint32_t* u,
+                                               const uint32_t* v)
+{
+    uint32_t t;
+    if constexpr (NW == 8) {
+        asm(BNN_XP2(0) BNN_XP2(1) BNN_XP2(2) BNN_XP2(3) BNN_XP2(4) BNN_XP2(5) BNN_XP2(6) BNN_XP2(7)
+            : [c0] "+v"(c0), [c1] "+v"(c1), [t] "=&v"(t)
+            : BNN_XIN(0), BNN_XIN(1), BNN_XIN(2), BNN_XIN(3), BNN_XIN(4), BNN_XIN(5), BNN_XIN(6), BNN_XIN(7));
+    } else if constexpr (NW == 4) {
+        asm(BNN_XP2(0) BNN_XP2(1) BNN_XP2(2) BNN_XP2(3)
+            : [c0] "+v"(c0), [c1] "+v"(c1), [t] "=&v"(t)
+            : BNN_XIN(0), BNN_XIN(1), BNN_XIN(2), BNN_XIN(3));
+    } else if constexpr (NW == 2) {
+        asm(BNN_XP2(0) BNN_XP2(1)
+            : [c0] "+v"(c0), [c1] "+v"(c1), [t] "=&v"(t)
+            : BNN_XIN(0), BNN_XIN(1));
+    } else {
+        static_assert(NW == 1, "blocks of 8, 4, 2 or 1 words");
+        asm(BNN_XP2(0)
+            : [c0] "+v"(c0), [c1] "+v"(c1), [t] "=&v"(t)
+            : BNN_XIN(0));
+    }
+}
+#undef BNN_XIN
+#undef BNN_XP2
+#undef BNN_XP
+
+// Ternary word: acc + popcount((a ^ s) & z), the same nop before the count.
+__device__ __forceinline__ uint32_t xor_and_popc_acc(uint32_t a, uint32_t s, uint32_t z, uint32_t acc) {
+    uint32_t r, t;
+    asm("v_xor_b32 %1, %3, %2\n\tv_and_b32 %1, %4, %1\n\ts_nop 0\n\tv_bcnt_u32_b32 %0, %1, %5"
+        : "=v"(r), "=&v"(t) : "v"(a), "s"(s), "s"(z), "v"(acc));
+    return r;
+}
+
 // Scalar loads of the KCC words of CP consecutive weight rows starting at p
 // (rows past the last live column re-read it).  MASK zeroes words >= nvalid.
 template <int CP, int KCC, bool FULLN, bool MASK>
@@ -104,13 +152,19 @@ __device__ __forceinline__ void xnor_chunk(uint32_t (&acc)[TN], const uint32_t (
         }
         __builtin_amdgcn_sched_barrier(0);
         // word-outer, column-inner: CP independent accumulator chains interleave
+        if constexpr (TERN) {
 #pragma unroll
-        for (int kk = 0; kk < KCC; ++kk)
+            for (int kk = 0; kk < KCC; ++kk)
 #pragma unroll
-            for (int c = 0; c < CP; ++c) {
-                const uint32_t t = TERN ? ((a[kk] ^ wc[c][kk]) & zc[c][kk]) : (a[kk] ^ wc[c][kk]);
-                acc[j + c] = popc_acc(t, acc[j + c]);
-            }
+                for (int c = 0; c < CP; ++c)
+                    acc[j + c] = xor_and_popc_acc(a[kk], wc[c][kk], zc[c][kk], acc[j + c]);
+        } else {
+            static_assert(CP == 2, "two columns per step");
+            constexpr int NB = KCC % 8 == 0 ? 8 : KCC % 4 == 0 ? 4 : KCC % 2 == 0 ? 2 : 1;
+#pragma unroll
+            for (int k = 0; k < KCC; k += NB)
+                xor_popc_2cols<NB>(acc[j], acc[j + 1], &a[k], &wc[0][k], &wc[1][k]);
+        }
         if (j + CP < TN) {
 #pragma unroll
             for (int c = 0; c < CP; ++c)
@@ -123,6 +177,22 @@ __device__ __forceinline__ void xnor_chunk(uint32_t (&acc)[TN], const uint32_t (
     }
 }
 
+// One dword per weight row of the tile at word offset k, loaded by the
+// vector path: it brings the row's next cache line into L2 a whole chunk
+// before the scalar loads ask for it, so a scalar-cache miss is served by L2
+// instead of waiting on memory.  Lane l takes row l % TN (ternary: the
+// nonzero plane on the second half of the lanes when TN <= 32); rows past
+// the last live column take that column.
+template <int TN, bool TERN>
+__device__ __forceinline__ uint32_t touch_w(const uint32_t* __restrict__ wbase, const uint32_t* __restrict__ zbase,
+                                            int64_t ldW, int k, int nlast)
+{
+    const int lane = threadIdx.x & 63;
+    const int r = min(lane & (TN - 1), nlast);
+    const uint32_t* base = (TERN && TN <= 32 && (lane & TN)) ? zbase : wbase;
+    return base[(int64_t)r * ldW + k];
+}
+
 template <int TN, int KC, bool FULLN, bool TERN>
 __device__ __forceinline__ void xnor_mainloop(uint32_t (&acc)[TN], const uint32_t* __restrict__ xrow,
                                               const uint32_t* __restrict__ wbase, const uint32_t* __restrict__ zbase,
@@ -133,6 +203,7 @@ __device__ __forceinline__ void xnor_mainloop(uint32_t (&acc)[TN], const uint32_
     // activation chunk double-buffered: the next chunk's vector loads are in
     // flight during this chunk's VALU work
     uint32_t a[KC], an[KC];
+    uint32_t tw = 0u;
     if (kfull > 0) load_granules(an, xrow, KC / 4);
     for (int k0 = 0; k0 < kfull; k0 += KC) {
 #pragma unroll
@@ -141,7 +212,11 @@ __device__ __forceinline__ void xnor_mainloop(uint32_t (&acc)[TN], const uint32_
         // chunk's loads go out, so no wait ever covers a fresh prefetch
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) asm volatile("" : : "v"(a[kk]));
-        if (k0 + KC < kfull) load_granules(an, xrow + k0 + KC, KC / 4);
+        asm volatile("" : : "v"(tw));
+        if (k0 + KC < kfull) {
+            load_granules(an, xrow + k0 + KC, KC / 4);
+            tw = touch_w<TN, TERN>(wbase, zbase, ldW, k0 + KC, nlast);
+        }
         xnor_chunk<TN, KC, CP, FULLN, false, TERN>(acc, a, wbase, zbase, k0, KC, ldW, nlast);
     }
     for (int k0 = kfull; k0 < Kw; k0 += 4) {     // 16-byte granules; rows hold ld >= roundup(Kw,4) words
