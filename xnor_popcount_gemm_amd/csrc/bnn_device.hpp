@@ -26,6 +26,28 @@ __device__ __forceinline__ uint32_t popc_acc(uint32_t x, uint32_t acc) {
     return r;
 }
 
+// Two accumulators over four words: c0 += sum_k popcount(x0[k] & w[k]),
+// c1 += sum_k popcount(x1[k] & w[k]), with one s_nop 0 between each v_and and
+// the bit count that reads it.  Measured on MI355X: a 32-bit VOP2 op (and,
+// xor) issued right before or after a v_bcnt_u32_b32 of the same wave costs
+// ~40% more issue time than with one nop between the two (independent or
+// not); VOP2-only chains do not pay it.  The eight pairs form one asm block
+// because the compiler separates consecutive asm blocks by a nop of its own.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void and_popc_2x4(uint32_t& c0, uint32_t& c1, u32x4_t x0, u32x4_t x1, u32x4_t w) {
+    uint32_t t;
+#define BNN_AP(X, W, C) "v_and_b32 %[t], " X ", " W "\n\ts_nop 0\n\tv_bcnt_u32_b32 " C ", %[t], " C "\n\t"
+    asm(BNN_AP("%[a0]", "%[w0]", "%[c0]") BNN_AP("%[b0]", "%[w0]", "%[c1]")
+        BNN_AP("%[a1]", "%[w1]", "%[c0]") BNN_AP("%[b1]", "%[w1]", "%[c1]")
+        BNN_AP("%[a2]", "%[w2]", "%[c0]") BNN_AP("%[b2]", "%[w2]", "%[c1]")
+        BNN_AP("%[a3]", "%[w3]", "%[c0]") BNN_AP("%[b3]", "%[w3]", "%[c1]")
+        : [c0] "+v"(c0), [c1] "+v"(c1), [t] "=&v"(t)
+        : [a0] "v"(x0.x), [a1] "v"(x0.y), [a2] "v"(x0.z), [a3] "v"(x0.w),
+          [b0] "v"(x1.x), [b1] "v"(x1.y), [b2] "v"(x1.z), [b3] "v"(x1.w),
+          [w0] "v"(w.x), [w1] "v"(w.y), [w2] "v"(w.z), [w3] "v"(w.w));
+#undef BNN_AP
+}
+
 // Sign bit of an fp32 given by its bit pattern u, per the Notation of page
 // "Extreme Quantization: Binary, Ternary & 1-bit LLMs": sign(x) = +1 for
 // x >= 0, else -1; returned as the packed bit (0 for +1, 1 for -1).

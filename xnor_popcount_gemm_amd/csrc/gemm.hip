@@ -88,14 +88,6 @@ __device__ __forceinline__ void xor_popc_2cols(uint32_t& c0, uint32_t& c1, const
 #undef BNN_XP2
 #undef BNN_XP
 
-// Ternary word: acc + popcount((a ^ s) & z), the same nop before the count.
-__device__ __forceinline__ uint32_t xor_and_popc_acc(uint32_t a, uint32_t s, uint32_t z, uint32_t acc) {
-    uint32_t r, t;
-    asm("v_xor_b32 %1, %3, %2\n\tv_and_b32 %1, %4, %1\n\ts_nop 0\n\tv_bcnt_u32_b32 %0, %1, %5"
-        : "=v"(r), "=&v"(t) : "v"(a), "s"(s), "s"(z), "v"(acc));
-    return r;
-}
-
 // Scalar loads of the KCC words of CP consecutive weight rows starting at p
 // (rows past the last live column re-read it).  MASK zeroes words >= nvalid.
 template <int CP, int KCC, bool FULLN, bool MASK>
@@ -153,11 +145,13 @@ __device__ __forceinline__ void xnor_chunk(uint32_t (&acc)[TN], const uint32_t (
         __builtin_amdgcn_sched_barrier(0);
         // word-outer, column-inner: CP independent accumulator chains interleave
         if constexpr (TERN) {
+            // (a ^ s) & z compiles to v_mov + v_bitop3; with the bit count that
+            // order already issues near the rate a nop-separated one reaches
 #pragma unroll
             for (int kk = 0; kk < KCC; ++kk)
 #pragma unroll
                 for (int c = 0; c < CP; ++c)
-                    acc[j + c] = xor_and_popc_acc(a[kk], wc[c][kk], zc[c][kk], acc[j + c]);
+                    acc[j + c] = popc_acc((a[kk] ^ wc[c][kk]) & zc[c][kk], acc[j + c]);
         } else {
             static_assert(CP == 2, "two columns per step");
             constexpr int NB = KCC % 8 == 0 ? 8 : KCC % 4 == 0 ? 4 : KCC % 2 == 0 ? 2 : 1;

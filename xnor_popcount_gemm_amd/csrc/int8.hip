@@ -274,19 +274,9 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
                     // -1 weights are S & Z, the nonzero ones Z
                     const u32x4 wn = TERN ? (w[u][i] & z[u][i]) : w[u][i];
 #pragma unroll
-                    for (int b = 0; b < 8; ++b) {
-                        const u32x4 t = xg[mr][b][i] & wn;
-                        acc[b] = popc_acc(t.x, acc[b]);
-                        acc[b] = popc_acc(t.y, acc[b]);
-                        acc[b] = popc_acc(t.z, acc[b]);
-                        acc[b] = popc_acc(t.w, acc[b]);
-                        if (TERN) {
-                            const u32x4 tz = xg[mr][b][i] & z[u][i];
-                            acz[b] = popc_acc(tz.x, acz[b]);
-                            acz[b] = popc_acc(tz.y, acz[b]);
-                            acz[b] = popc_acc(tz.z, acz[b]);
-                            acz[b] = popc_acc(tz.w, acz[b]);
-                        }
+                    for (int b = 0; b < 8; b += 2) {
+                        and_popc_2x4(acc[b], acc[b + 1], xg[mr][b][i], xg[mr][b + 1][i], wn);
+                        if (TERN) and_popc_2x4(acz[b], acz[b + 1], xg[mr][b][i], xg[mr][b + 1][i], z[u][i]);
                     }
                 }
                 // sum over the planes with their two's-complement weights:
