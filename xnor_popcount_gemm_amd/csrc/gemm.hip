@@ -345,46 +345,46 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
     for (int c0 = 0; c0 < TN; c0 += CH) {
 #pragma unroll
         for (int j = 0; j < CH; ++j) lds[lane * (CH + 1) + j] = (uint32_t)dval<TERN>(acc[c0 + j], K, e, n0 + c0 + j);
-        // The residual and alpha pieces of all passes are requested before
-        // any is used, so their latencies overlap instead of adding up.
+        // In pass q lane l covers row q * 64 / G4 + l / G4 and column group
+        // cg = l % G4 (64 is a multiple of G4), so a lane's alpha, bias and
+        // beta pieces are the same in every pass: loaded once.  The residual
+        // pieces of all passes are requested before any is used, so their
+        // latencies overlap instead of adding up.
+        const int cg = lane & (G4 - 1);
+        const int nc = n0 + c0 + 4 * cg;
+        float4 av = make_float4(0.0f, 0.0f, 0.0f, 0.0f), bv = av, tv = av;
+        if (e.flags & EPI_SCALE) {
+            if (e.flags & EPI_ALPHA_TENSOR) { const float a = e.alpha[0]; av = make_float4(a, a, a, a); }
+            else av = *reinterpret_cast<const float4*>(e.alpha + nc);
+        }
+        if (e.flags & EPI_BIAS) bv = *reinterpret_cast<const float4*>(e.bias + nc);
+        if ((e.flags & EPI_SIGN_PACK) && e.beta)
+            tv = make_float4(e.beta[nc], e.beta[nc + 1], e.beta[nc + 2], e.beta[nc + 3]);
         f32x4 rv[G4];
-        float4 av[G4], bv[G4], tv[G4];
 #pragma unroll
         for (int q = 0; q < G4; ++q) {
-            const int idx = q * 64 + lane;
-            const int r = idx / G4, cg = idx - (idx / G4) * G4;
+            const int r = q * (64 / G4) + lane / G4;
             const int m = min(wrow0 + r, M - 1);
-            const int n = n0 + c0 + 4 * cg;
-            if (e.flags & EPI_SCALE) {
-                if (e.flags & EPI_ALPHA_TENSOR) { const float a = e.alpha[0]; av[q] = make_float4(a, a, a, a); }
-                else av[q] = *reinterpret_cast<const float4*>(e.alpha + n);
-            }
-            if (e.flags & EPI_BIAS) bv[q] = *reinterpret_cast<const float4*>(e.bias + n);
-            if (e.flags & EPI_SIGN_PACK) {
-                tv[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                if (e.beta) tv[q] = make_float4(e.beta[n], e.beta[n + 1], e.beta[n + 2], e.beta[n + 3]);
-            }
             if (e.flags & EPI_RESIDUAL)
-                rv[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(e.R + (int64_t)m * e.ldR + n));
+                rv[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(e.R + (int64_t)m * e.ldR + nc));
         }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int q = 0; q < G4; ++q) {
-            const int idx = q * 64 + lane;
-            const int r = idx / G4, cg = idx - (idx / G4) * G4;
+            const int r = q * (64 / G4) + lane / G4;
             int32_t d[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) d[i] = (int32_t)lds[r * (CH + 1) + 4 * cg + i];
             const int m = wrow0 + r;
             if (m < M) {
-                const int n = n0 + c0 + 4 * cg;
+                const int n = nc;
                 if (e.flags & EPI_DOT)
                     *reinterpret_cast<int4*>(e.D + (int64_t)m * e.ldD + n) = make_int4(d[0], d[1], d[2], d[3]);
                 if (e.flags & EPI_SCALE) {
-                    const float4 a = av[q];
+                    const float4 a = av;
                     f32x4 y = {a.x * (float)d[0], a.y * (float)d[1], a.z * (float)d[2], a.w * (float)d[3]};
                     if (e.flags & EPI_BIAS) {
-                        const float4 b = bv[q];
+                        const float4 b = bv;
                         y = y + (f32x4){b.x, b.y, b.z, b.w};
                     }
                     if (e.flags & EPI_RESIDUAL) y = y + rv[q];
@@ -392,7 +392,7 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
                     if (e.flags & EPI_SIGN_PACK) {
                         // sign(y - beta_n) as bits (0 = +1), OR-ed over the G4 lanes of the
                         // row segment; the last lane stores the CH bits
-                        const float4 bt = tv[q];
+                        const float4 bt = tv;
                         const uint32_t nib = (y[0] >= bt.x ? 0u : 1u) | ((y[1] >= bt.y ? 0u : 1u) << 1) |
                                              ((y[2] >= bt.z ? 0u : 1u) << 2) | ((y[3] >= bt.w ? 0u : 1u) << 3);
                         uint32_t bits = nib << (4 * cg);
