@@ -181,8 +181,9 @@ __global__ __launch_bounds__(kThreads) void k_act_i8(
 // Bit-plane GEMV: G = 2^GLOG2 lanes share one weight row and read it in
 // consecutive 16-byte granules (coalesced), 64/G rows per wave step, CPL
 // granules per lane, U row-steps per group with all their loads issued
-// first.  Each lane keeps its granules of all 8 planes of the MR activation
-// rows in registers for the whole kernel.  Per row-step a lane does
+// first.  The 8 planes of the MR activation rows sit in LDS for the whole
+// kernel (holding them in registers took 96 VGPRs per lane at K = 11008 and
+// limited the kernel to 3 waves per SIMD).  Per row-step a lane does
 // 8 (v_and, v_bcnt) per word, 7 shift-adds to weigh the planes, and the
 // group sum takes GLOG2 DPP adds.
 // TERN: ternary weights -- Wp is the sign plane S and e.Zp the nonzero plane
@@ -201,28 +202,29 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
     const int Kw = (K + 31) >> 5;
     const int Kw4 = (Kw + 3) >> 2;
 
-    u32x4 xg[MR][8][CPL];
+    // The 8 planes of the MR activation rows, granule slot c = gl + G i of
+    // plane (mr, b) at lds_x[((mr * 8 + b) * CPL + i) * G + gl]; words >= Kw
+    // are stored as 0.  Lanes of one group read consecutive 16-byte slots
+    // (distinct banks), the groups of a wave the same slots (broadcast).
+    __shared__ u32x4 lds_x[MR * 8 * CPL * G];
+    for (int idx = threadIdx.x; idx < MR * 8 * CPL * G; idx += kThreads) {
+        const int slot = idx % (CPL * G);              // = i * G + gl
+        const int pl = idx / (CPL * G);                // = mr * 8 + b
+        const int c = (slot % G) + G * (slot / G);     // granule index gl + G i
+        u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+        if (c < Kw4) {
+            v = *reinterpret_cast<const u32x4*>(Xb + (int64_t)pl * ldXb + 4 * c);
+            v.x = (4 * c + 0 < Kw) ? v.x : 0u;
+            v.y = (4 * c + 1 < Kw) ? v.y : 0u;
+            v.z = (4 * c + 2 < Kw) ? v.z : 0u;
+            v.w = (4 * c + 3 < Kw) ? v.w : 0u;
+        }
+        lds_x[idx] = v;
+    }
+    __syncthreads();
     bool live[CPL];                               // granule inside the row
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = gl + G * i;
-        live[i] = c < Kw4;
-        u32x4 wm = (u32x4){0u, 0u, 0u, 0u};        // words >= Kw read as 0
-        if (live[i]) {
-            wm.x = (4 * c + 0 < Kw) ? ~0u : 0u;
-            wm.y = (4 * c + 1 < Kw) ? ~0u : 0u;
-            wm.z = (4 * c + 2 < Kw) ? ~0u : 0u;
-            wm.w = (4 * c + 3 < Kw) ? ~0u : 0u;
-        }
-#pragma unroll
-        for (int mr = 0; mr < MR; ++mr)
-#pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-                if (live[i]) v = *reinterpret_cast<const u32x4*>(Xb + ((int64_t)mr * 8 + b) * ldXb + 4 * c);
-                xg[mr][b][i] = v & wm;
-            }
-    }
+    for (int i = 0; i < CPL; ++i) live[i] = gl + G * i < Kw4;
     int32_t xs[MR];
     float xsc[MR];
 #pragma unroll
@@ -261,31 +263,39 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
             if ((e.flags & EPI_SCALE) && row < N) av[u] = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : row];
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = row0 + (int64_t)u * RPS;
+        for (int mr = 0; mr < MR; ++mr) {
+            // binary: count the -1 weights (bit 1); ternary: the -1 weights
+            // are S & Z, the nonzero ones Z.  Each pair of planes is read
+            // from LDS once and used for all U row-steps.
+            uint32_t acc[U][8], acz[U][8];
 #pragma unroll
-            for (int mr = 0; mr < MR; ++mr) {
-                uint32_t acc[8], acz[8];
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int b = 0; b < 8; ++b) { acc[b] = 0u; acz[b] = 0u; }
+                for (int b = 0; b < 8; ++b) { acc[u][b] = 0u; acz[u][b] = 0u; }
 #pragma unroll
-                for (int i = 0; i < CPL; ++i) {
-                    // binary: count the -1 weights (bit 1); ternary: the
-                    // -1 weights are S & Z, the nonzero ones Z
-                    const u32x4 wn = TERN ? (w[u][i] & z[u][i]) : w[u][i];
+            for (int i = 0; i < CPL; ++i) {
 #pragma unroll
-                    for (int b = 0; b < 8; b += 2) {
-                        and_popc_2x4(acc[b], acc[b + 1], xg[mr][b][i], xg[mr][b + 1][i], wn);
-                        if (TERN) and_popc_2x4(acz[b], acz[b + 1], xg[mr][b][i], xg[mr][b + 1][i], z[u][i]);
+                for (int b = 0; b < 8; b += 2) {
+                    const u32x4 x0 = lds_x[((mr * 8 + b) * CPL + i) * G + gl];
+                    const u32x4 x1 = lds_x[((mr * 8 + b + 1) * CPL + i) * G + gl];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const u32x4 wn = TERN ? (w[u][i] & z[u][i]) : w[u][i];
+                        and_popc_2x4(acc[u][b], acc[u][b + 1], x0, x1, wn);
+                        if (TERN) and_popc_2x4(acz[u][b], acz[u][b + 1], x0, x1, z[u][i]);
                     }
                 }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t row = row0 + (int64_t)u * RPS;
                 // sum over the planes with their two's-complement weights:
                 // neg = sum of q over the -1 weights, nzs = over the nonzero ones
-                uint32_t neg = acc[0], nzs = acz[0];
+                uint32_t neg = acc[u][0], nzs = acz[u][0];
 #pragma unroll
-                for (int b = 1; b < 7; ++b) { neg += acc[b] << b; if (TERN) nzs += acz[b] << b; }
-                neg -= acc[7] << 7;
-                if (TERN) nzs -= acz[7] << 7;
+                for (int b = 1; b < 7; ++b) { neg += acc[u][b] << b; if (TERN) nzs += acz[u][b] << b; }
+                neg -= acc[u][7] << 7;
+                if (TERN) nzs -= acz[u][7] << 7;
                 neg = sum_reduce_to_last_t<GLOG2>(neg);
                 if (TERN) nzs = sum_reduce_to_last_t<GLOG2>(nzs);
                 if (last && row < N) {
@@ -298,8 +308,8 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
                     }
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
