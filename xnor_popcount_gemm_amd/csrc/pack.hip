@@ -11,17 +11,17 @@
 //    section "1. Arithmetic: MAC -> XNOR + popcount".
 //  - alpha = (1/n) sum |w_i| per output row: "Extreme Quantization", eq. (1).
 //
-// Mapping: one wavefront owns one output row at a time (grid-stride over
-// rows).  Per step the 64 lanes read 64 x 16 B of consecutive source floats
-// (1 KiB, fully coalesced; the im2col variant gathers the 16-B pieces of the
-// neighbouring pixels) and each aligned group of 8 lanes folds its 32 sign
-// bits into one word with three DPP row shifts; the last lane of the group
-// stores the word.  Eight steps (four in the im2col and RSign packs) are
-// issued before any is consumed, so a wave keeps 8 KiB of loads in flight;
-// the loads are nontemporal, as every source element is read once.  alpha's
-// |w| sum stays in the wave (fp64
-// per lane, then a fixed-order butterfly), so it needs no LDS and no atomics
-// and is the same on every run.
+// Mapping: per step the 64 lanes of a wave read 64 x 16 B of consecutive
+// source floats (1 KiB, fully coalesced; the im2col variant gathers the 16-B
+// pieces of the neighbouring pixels) and each aligned group of 8 lanes folds
+// its 32 sign bits into one word with three DPP row shifts; the last lane of
+// the group stores the word.  Four steps (eight in the ternary pack) are
+// issued before any is consumed; the loads are nontemporal, as every source
+// element is read once.  The dense pack hands out 4 KiB chunks of rows (the
+// waves in flight read neighbouring chunks); the other packs give a wave one
+// output row at a time (grid-stride over rows).  alpha's |w| sum is fp64 per
+// lane, then a fixed-order butterfly per wave and a fixed-order sum over the
+// workgroup's waves: no atomics, the same result on every run.
 #include "bnn_device.hpp"
 #include "bnn_launch.hpp"
 
@@ -30,10 +30,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSteps = 4;      // 8-word steps issued back to back per wave
-constexpr int kRowSteps = 8;   // the same for the row-per-wave dense and ternary packs
-                               // (8 KiB in flight per wave: 0.222 -> 0.198 ms
-                               // for 16384 x 16384 fp32 on MI355X, with the
-                               // nontemporal loads)
+constexpr int kRowSteps = 8;   // the same for the row-per-wave ternary pack
+                               // (8 KiB in flight per wave)
+constexpr int kChunkSteps = 4; // 8-word steps per chunk of the dense pack (4 KiB
+                               // of source per chunk: 0.197 -> 0.183 ms for
+                               // 16384 x 16384 fp32 activations on MI355X)
 
 struct Frag {                  // four consecutive source elements as bit patterns
     uint32_t u[4];
@@ -67,6 +68,35 @@ __device__ __forceinline__ Frag load_frag(const float* __restrict__ row, int k, 
     return f;
 }
 
+// One chunk of a row: words w0 .. w0 + 8 kChunkSteps - 1 (clipped to ldp);
+// returns the chunk's sum of |x| in double when ALPHA.
+template <bool VEC, bool ALPHA>
+__device__ __forceinline__ double pack_chunk(const float* __restrict__ xr, uint32_t* __restrict__ pr, int w0,
+                                             int ldp, int K, int sub, int grp)
+{
+    double asum = 0.0;
+    Frag f[kChunkSteps];
+#pragma unroll
+    for (int u = 0; u < kChunkSteps; ++u)
+        f[u] = load_frag<VEC>(xr, 32 * (w0 + 8 * u + grp) + 4 * sub, K);
+#pragma unroll
+    for (int u = 0; u < kChunkSteps; ++u) {
+        const int w = w0 + 8 * u + grp;
+        const uint32_t word = or_reduce8_to_last(nibble(f[u]) << (4 * sub));
+        if (sub == 7 && w < ldp) pr[w] = word;
+        if (ALPHA) asum = abs_sum4(f[u], asum);
+    }
+    return asum;
+}
+
+// The work unit is a chunk of 8 kChunkSteps words (4 KiB of fp32 source) of a
+// row.  Without alpha the waves take the chunks in row-major order, grid
+// stride, so the waves in flight read neighbouring chunks.  With alpha a
+// workgroup owns one row at a time: its waves take the row's chunks in turn
+// and add their |w| sums through LDS in a fixed order (the same result on
+// every run).  Measured on MI355X for a 1 GiB read: waves reading
+// neighbouring blocks stream 6.6-6.8 TB/s, while waves spread over the
+// whole buffer (as with one row per wave) get 5.6-5.9.
 template <bool VEC, bool ALPHA>
 __global__ __launch_bounds__(kThreads) void k_pack_dense(
     const float* __restrict__ X, int64_t rows, int K, int64_t ldX,
@@ -76,30 +106,36 @@ __global__ __launch_bounds__(kThreads) void k_pack_dense(
     const int lane = threadIdx.x & 63;
     const int sub = lane & 7;
     const int grp = lane >> 3;
-    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
     const int ldp = (int)ldP;
-
-    for (int64_t r = wave; r < rows; r += nwaves) {
-        const float* __restrict__ xr = X + r * ldX;
-        uint32_t* __restrict__ pr = P + r * ldP;
-        double asum = 0.0;
-        for (int w0 = 0; w0 < ldp; w0 += 8 * kRowSteps) {
-            Frag f[kRowSteps];
-#pragma unroll
-            for (int u = 0; u < kRowSteps; ++u)
-                f[u] = load_frag<VEC>(xr, 32 * (w0 + 8 * u + grp) + 4 * sub, K);
-#pragma unroll
-            for (int u = 0; u < kRowSteps; ++u) {
-                const int w = w0 + 8 * u + grp;
-                const uint32_t word = or_reduce8_to_last(nibble(f[u]) << (4 * sub));
-                if (sub == 7 && w < ldp) pr[w] = word;
-                if (ALPHA) asum = abs_sum4(f[u], asum);
-            }
+    constexpr int kChunk = 8 * kChunkSteps;
+    const int nch = (ldp + kChunk - 1) / kChunk;
+    if (!ALPHA) {
+        const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+        const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+        const int64_t units = rows * nch;
+        for (int64_t u = wave; u < units; u += nwaves) {
+            const int64_t r = u / nch;
+            const int c = (int)(u - r * nch);
+            pack_chunk<VEC, false>(X + r * ldX, P + r * ldP, c * kChunk, ldp, K, sub, grp);
         }
-        if (ALPHA) {
+    } else {
+        constexpr int kW = kThreads / 64;
+        __shared__ double red[kW];
+        const int wv = threadIdx.x >> 6;
+        for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+            double asum = 0.0;
+            for (int c = wv; c < nch; c += kW)
+                asum += pack_chunk<VEC, true>(X + r * ldX, P + r * ldP, c * kChunk, ldp, K, sub, grp);
             asum = wave_sum_f64(asum);
-            if (lane == 0) alpha[r] = (float)(asum / (double)K);
+            if (lane == 0) red[wv] = asum;
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                double t = red[0];
+#pragma unroll
+                for (int i = 1; i < kW; ++i) t += red[i];
+                alpha[r] = (float)(t / (double)K);
+            }
+            __syncthreads();
         }
     }
 }
@@ -436,7 +472,13 @@ hipError_t launch_pack_dense(const float* X, int64_t rows, int64_t K, int64_t ld
                              uint32_t* P, int64_t ldP, float* alpha, hipStream_t s)
 {
     const bool vec = aligned16(X) && (ldX % 4 == 0);
-    const dim3 grid(grid_for_rows(rows)), block(kThreads);
+    // without alpha: one wave per 4 KiB chunk (grid-stride); with alpha: one
+    // workgroup per row at a time
+    const int64_t nch = (ldP + 8 * kChunkSteps - 1) / (8 * kChunkSteps);
+    int64_t blocks = alpha ? rows : (rows * nch + kThreads / 64 - 1) / (kThreads / 64);
+    const int64_t cap = 256 * 32;
+    blocks = blocks > cap ? cap : (blocks < 1 ? 1 : blocks);
+    const dim3 grid((unsigned)blocks), block(kThreads);
     const int k = (int)K;
     if (alpha) {
         if (vec) hipLaunchKernelGGL((k_pack_dense<true, true>), grid, block, 0, s, X, rows, k, ldX, P, ldP, alpha);
