@@ -195,23 +195,34 @@ __device__ __forceinline__ void xnor_mainloop(uint32_t (&acc)[TN], const uint32_
     constexpr int CP = (TN >= 2) ? 2 : 1;
     const int kfull = (Kw / KC) * KC;
     // activation chunk double-buffered: the next chunk's vector loads are in
-    // flight during this chunk's VALU work
-    uint32_t a[KC], an[KC];
+    // flight during this chunk's VALU work.  Two chunks per iteration with the
+    // buffers' roles swapped, so no register copies between chunks.
+    uint32_t a0[KC], a1[KC];
     uint32_t tw = 0u;
-    if (kfull > 0) load_granules(an, xrow, KC / 4);
-    for (int k0 = 0; k0 < kfull; k0 += KC) {
-#pragma unroll
-        for (int kk = 0; kk < KC; ++kk) a[kk] = an[kk];
-        // take delivery of this chunk (issued one chunk ago) before the next
+    if (kfull > 0) load_granules(a0, xrow, KC / 4);
+    int k0 = 0;
+    for (; k0 + 2 * KC <= kfull; k0 += 2 * KC) {
+        // take delivery of a chunk (issued one chunk ago) before the next
         // chunk's loads go out, so no wait ever covers a fresh prefetch
 #pragma unroll
-        for (int kk = 0; kk < KC; ++kk) asm volatile("" : : "v"(a[kk]));
+        for (int kk = 0; kk < KC; ++kk) asm volatile("" : : "v"(a0[kk]));
         asm volatile("" : : "v"(tw));
-        if (k0 + KC < kfull) {
-            load_granules(an, xrow + k0 + KC, KC / 4);
-            tw = touch_w<TN, TERN>(wbase, zbase, ldW, k0 + KC, nlast);
+        load_granules(a1, xrow + k0 + KC, KC / 4);
+        tw = touch_w<TN, TERN>(wbase, zbase, ldW, k0 + KC, nlast);
+        xnor_chunk<TN, KC, CP, FULLN, false, TERN>(acc, a0, wbase, zbase, k0, KC, ldW, nlast);
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) asm volatile("" : : "v"(a1[kk]));
+        asm volatile("" : : "v"(tw));
+        if (k0 + 2 * KC < kfull) {
+            load_granules(a0, xrow + k0 + 2 * KC, KC / 4);
+            tw = touch_w<TN, TERN>(wbase, zbase, ldW, k0 + 2 * KC, nlast);
         }
-        xnor_chunk<TN, KC, CP, FULLN, false, TERN>(acc, a, wbase, zbase, k0, KC, ldW, nlast);
+        xnor_chunk<TN, KC, CP, FULLN, false, TERN>(acc, a1, wbase, zbase, k0 + KC, KC, ldW, nlast);
+    }
+    if (k0 < kfull) {                             // an odd last chunk, already in a0
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) asm volatile("" : : "v"(a0[kk]));
+        xnor_chunk<TN, KC, CP, FULLN, false, TERN>(acc, a0, wbase, zbase, k0, KC, ldW, nlast);
     }
     for (int k0 = kfull; k0 < Kw; k0 += 4) {     // 16-byte granules; rows hold ld >= roundup(Kw,4) words
         const int nvalid = min(4, Kw - k0);
