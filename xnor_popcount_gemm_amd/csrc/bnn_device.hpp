@@ -17,6 +17,9 @@ typedef const __attribute__((address_space(4))) uint32_t* cptr_u32;
 typedef const __attribute__((address_space(4))) float* cptr_f32;
 typedef const __attribute__((address_space(4))) int8_t* cptr_i8;
 
+// Four 32-bit words (one 16-byte granule) as a vector.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // popcount(x) + acc as the single VALU op v_bcnt_u32_b32.  Written as asm so
 // the compiler cannot re-associate a chain of accumulations into
 // bcnt(x, 0) + v_add3 trees (one extra VALU op per two words).
@@ -33,8 +36,7 @@ __device__ __forceinline__ uint32_t popc_acc(uint32_t x, uint32_t acc) {
 // ~40% more issue time than with one nop between the two (independent or
 // not); VOP2-only chains do not pay it.  The eight pairs form one asm block
 // because the compiler separates consecutive asm blocks by a nop of its own.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void and_popc_2x4(uint32_t& c0, uint32_t& c1, u32x4_t x0, u32x4_t x1, u32x4_t w) {
+__device__ __forceinline__ void and_popc_2x4(uint32_t& c0, uint32_t& c1, u32x4 x0, u32x4 x1, u32x4 w) {
     uint32_t t;
 #define BNN_AP(X, W, C) "v_and_b32 %[t], " X ", " W "\n\ts_nop 0\n\tv_bcnt_u32_b32 " C ", %[t], " C "\n\t"
     asm(BNN_AP("%[a0]", "%[w0]", "%[c0]") BNN_AP("%[b0]", "%[w0]", "%[c1]")

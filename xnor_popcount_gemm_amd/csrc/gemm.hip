@@ -24,8 +24,13 @@
 //    into SGPRs and broadcast to all 64 lanes by the VALU's scalar operand:
 //    each output word costs exactly v_xor_b32 (SGPR ^ VGPR) + v_bcnt_u32_b32
 //    (popcount + accumulate), 2 VALU ops per 32 binary MACs, with no LDS
-//    traffic and no barriers.  Scalar loads of the next column are issued
-//    before the current column's 2*KC VALU ops (double-buffered SGPRs).
+//    traffic and no barriers.  Scalar loads of the next column pair are
+//    issued before the current pair's VALU ops (double-buffered SGPRs); one
+//    vector load per lane and K-chunk brings the next chunk's weight lines
+//    into L2 ahead of them.
+//  - The xor and the bit count of each word are separated by one s_nop (see
+//    xor_popc_2cols); the activation chunks alternate between two register
+//    buffers, two chunks per loop iteration.
 //  - Epilogue per lane: D = K - 2*acc, alpha scale, residual, or the folded
 //    BatchNorm threshold with the output bits packed along n in registers
 //    (TN/32 words per lane, no cross-lane traffic).

@@ -27,8 +27,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 // Streaming load of one 16-byte weight granule: the weights are read once per
 // call, so the load is marked nontemporal and does not displace cached data.
 __device__ __forceinline__ u32x4 load_stream(const uint32_t* p) {

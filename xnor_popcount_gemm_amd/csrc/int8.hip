@@ -31,8 +31,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 // Absmax quantization of one value (IEEE single, one rounding per step):
 // q = rint(x * inv) clamped to [-127, 127]; a NaN product gives 0.
 __device__ __forceinline__ int quant_i8(float x, float inv) {

@@ -57,8 +57,7 @@ __device__ __forceinline__ Frag load_frag(const float* __restrict__ row, int k, 
     if (VEC && k + 4 <= K) {
         // each source element is read once: nontemporal, so the stream does
         // not displace cached data
-        typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-        const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(row + k));
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + k));
         f.u[0] = v.x; f.u[1] = v.y; f.u[2] = v.z; f.u[3] = v.w;
     } else {
 #pragma unroll
