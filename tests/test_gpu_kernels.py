@@ -95,7 +95,10 @@ def _packed_pair(M, N, K, seed):
 
 GEMM_SHAPES = [(64, 256, 1000), (300, 100, 777), (257, 129, 1100), (5, 70, 4096), (1, 7, 33),
                (2, 300, 11008), (4, 33, 64), (512, 64, 576), (70, 1, 32), (1, 1, 1), (65, 96, 16),
-               (256, 512, 8192)]
+               (256, 512, 8192),
+               # 3 and 5 full 16-word chunks (the K loop takes two chunks per
+               # iteration and ends on an odd one), the second with a tail
+               (257, 64, 1536), (130, 70, 2600)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
