@@ -283,6 +283,10 @@ def test_dense_f32_sign_pack(bnn, M, N, K):
     Op = bnn.dense_f32_sign_pack(dev(X), dev(W))
     torch.cuda.synchronize()
     H = oracle.dense_f64(X, W)
+    # the kernel's double sum may run in another order: any order is within
+    # K 2^-52 sum|x w| of the exact sum, so outside that bound the sign is unique
+    bound = K * 2.0**-52 * (np.abs(X).astype(np.float64) @ np.abs(W).astype(np.float64).T)
+    assert int((np.abs(H) <= bound).sum()) == 0, "near-ties in the test data"
     s = np.where(H >= 0.0, 1, -1).astype(np.int8)
     np.testing.assert_array_equal(host_u32(Op), oracle.pack_signs(s, ld=Op.shape[1]))
 

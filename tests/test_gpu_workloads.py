@@ -98,7 +98,9 @@ def test_workload2_binary_mlp(bnn):
     acts, alphas, taus, logits = run_mlp_gpu(bnn, X, W1, hidden, W5)
     torch.cuda.synchronize()
     ref = oracle.binary_mlp(X, W1, hidden, W5)
-    # first FP layer: same in-order double sums -> identical signs; report near-ties
+    # first FP layer: a double sum of exact products in any order is within
+    # K 2^-52 sum|x w| of the exact value, so with no output inside that bound
+    # the signs are unique (and must match exactly)
     h1 = ref["h1"]
     bound = X.shape[1] * 2.0**-52 * (np.abs(X).astype(np.float64) @ np.abs(W1).astype(np.float64).T)
     assert int((np.abs(h1) <= bound).sum()) == 0, "first-layer near-ties present"

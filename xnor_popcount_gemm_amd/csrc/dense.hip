@@ -6,7 +6,9 @@
 // 1-bit LLMs", sign per its Notation), and the last layer reads the +1/-1
 // outputs of the last binary layer.
 //
-// First layer: 64 x 8 NJ output tile per one-wave workgroup, 8 x NJ outputs
+// First layer, 16-byte aligned rows: the fp64 matrix cores (see
+// k_dense_f64_mfma_sign_pack).  Other rows: 64 x 8 NJ output tile per
+// one-wave workgroup, 8 x NJ outputs
 // per lane (lane (tx, ty) owns rows 8 ty .. +7 and columns tx + 8 j), K
 // staged through LDS in 16-wide slices already widened to double: 8 + NJ LDS
 // doubles per 8 NJ FMAs, against 8 per 16 of a 4x4 tile (LDS-bound at 37% of
@@ -181,6 +183,120 @@ __global__ __launch_bounds__(kThreads) void k_dense_binact_f32(
     }
 }
 
+// First layer on the fp64 matrix cores (v_mfma_f64_16x16x4_f64): the same
+// h = X W^T with exact float products in double, for 16-byte aligned rows.
+// A wave owns a 32 x 64 tile: 2 row blocks (m) x 4 column blocks (n) of
+// 16 x 16 accumulators, 8 MFMAs per k-step.  Operands: A = a block of X
+// (lane l: row m = l % 16), B = a block of W (lane l: column n = l % 16),
+// both at k = 16 t + 4 (l / 16) + s in sub-step s of K-chunk t, so each lane
+// loads its 4 consecutive k of a chunk as one float4 and every k < K enters
+// once.  Result element r of lane l is D[4 r + l / 16][l % 16] (A's row
+// first; the lane layout measured on MI355X), i.e. h[m = 4 r + l / 16]
+// [n = l % 16] of the block, so one ballot over the 64 lanes gives
+// the sign bits of 4 rows x 16 columns in 16-bit fields.  Each output's sum
+// runs over the chunks in order; within a k-step the matrix core adds its 4
+// products in its own order, so h can differ from a sequential double sum
+// in the last bits (a sign differs only for |h| within that rounding error).
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_k4(const float* __restrict__ row, int k, int K) {
+    if (k + 4 <= K) return *reinterpret_cast<const float4*>(row + k);
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (k < K) v.x = row[k];
+    if (k + 1 < K) v.y = row[k + 1];
+    if (k + 2 < K) v.z = row[k + 2];
+    if (k + 3 < K) v.w = row[k + 3];
+    return v;
+}
+
+__device__ __forceinline__ float comp(const float4& v, int s) {
+    return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+}
+
+__global__ __launch_bounds__(kThreads) void k_dense_f64_mfma_sign_pack(
+    const float* __restrict__ X, int64_t ldX, const float* __restrict__ W, int64_t ldW,
+    int M, int N, int K, uint32_t* __restrict__ Op, int64_t ldOp, int tiles_n, int tiles)
+{
+    const int lane = threadIdx.x & 63;
+    const int tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (tile >= tiles) return;                       // no barriers below
+    const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+    const int m0 = 32 * tm, n0 = 64 * tn;
+    const int g = lane >> 4, c = lane & 15;
+    const float* xr[2];
+    const float* wr[4];
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm) xr[bm] = X + (int64_t)min(m0 + 16 * bm + c, M - 1) * ldX;
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) wr[bn] = W + (int64_t)min(n0 + 16 * bn + c, N - 1) * ldW;
+
+    v4d acc[2][4];
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = (v4d){0.0, 0.0, 0.0, 0.0};
+
+    const int nch = (K + 15) >> 4;
+    float4 xn[2], wn[4];
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm) xn[bm] = load_k4(xr[bm], 4 * g, K);
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) wn[bn] = load_k4(wr[bn], 4 * g, K);
+    for (int t = 0; t < nch; ++t) {
+        float4 xa[2], wa[4];
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm) xa[bm] = xn[bm];
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn) wa[bn] = wn[bn];
+        if (t + 1 < nch) {                           // next chunk in flight during this one
+            const int k = 16 * (t + 1) + 4 * g;
+#pragma unroll
+            for (int bm = 0; bm < 2; ++bm) xn[bm] = load_k4(xr[bm], k, K);
+#pragma unroll
+            for (int bn = 0; bn < 4; ++bn) wn[bn] = load_k4(wr[bn], k, K);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            double xd[2], wd[4];
+#pragma unroll
+            for (int bm = 0; bm < 2; ++bm) xd[bm] = (double)comp(xa[bm], s);
+#pragma unroll
+            for (int bn = 0; bn < 4; ++bn) wd[bn] = (double)comp(wa[bn], s);
+#pragma unroll
+            for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+                for (int bn = 0; bn < 4; ++bn)
+                    acc[bm][bn] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[bm], wd[bn], acc[bm][bn], 0, 0, 0);
+        }
+    }
+
+    // Sign bits: bit 1 for h < 0; columns >= N give 0 (+1, the pad rule).
+    // For block row bm and element r, ballot bn holds rows m0 + 16 bm + 4 r
+    // + q (q = 0..3) in bits 16 q .. 16 q + 15, columns n0 + 16 bn + 0..15;
+    // lanes 0..7 write the 4 rows' two words.
+    const int nw = (N + 31) >> 5;
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            uint64_t b[4];
+#pragma unroll
+            for (int bn = 0; bn < 4; ++bn)
+                b[bn] = __builtin_amdgcn_ballot_w64(acc[bm][bn][r] < 0.0 && n0 + 16 * bn + c < N);
+            if (lane < 8) {
+                const int q = lane >> 1, w = lane & 1;
+                const uint64_t lo = w ? b[2] : b[0], hi = w ? b[3] : b[1];
+                const uint32_t word = (uint32_t)((lo >> (16 * q)) & 0xFFFFu) |
+                                      ((uint32_t)((hi >> (16 * q)) & 0xFFFFu) << 16);
+                const int m = m0 + 16 * bm + 4 * r + q;
+                const int widx = (n0 >> 5) + w;
+                if (m < M && widx < nw) Op[(int64_t)m * ldOp + widx] = word;
+            }
+        }
+    if (tn == tiles_n - 1 && lane < 32 && m0 + lane < M)
+        for (int64_t w = nw; w < ldOp; ++w) Op[(int64_t)(m0 + lane) * ldOp + w] = 0u;
+}
+
 }  // namespace
 
 hipError_t launch_dense_f32_sign_pack(const float* X, int64_t ldX, const float* W, int64_t ldW,
@@ -189,6 +305,14 @@ hipError_t launch_dense_f32_sign_pack(const float* X, int64_t ldX, const float* 
 {
     const bool vec = (reinterpret_cast<uintptr_t>(X) & 15u) == 0 && (reinterpret_cast<uintptr_t>(W) & 15u) == 0 &&
                      ldX % 4 == 0 && ldW % 4 == 0;
+    if (vec) {                                       // 16-byte rows: the matrix cores
+        const int tn = (int)((N + 63) / 64);
+        const int64_t tiles = ((M + 31) / 32) * tn;
+        const dim3 g((unsigned)((tiles + kThreads / 64 - 1) / (kThreads / 64))), b(kThreads);
+        hipLaunchKernelGGL(k_dense_f64_mfma_sign_pack, g, b, 0, s, X, ldX, W, ldW, (int)M, (int)N, (int)K,
+                           Op, ldOp, tn, (int)tiles);
+        return hipGetLastError();
+    }
     const int64_t tiles_m = (M + kTile - 1) / kTile;
     const bool wide = tiles_m * ((N + 63) / 64) >= (int64_t)num_cus() * 8;   // two waves per SIMD at NJ = 8
     const int tn_cols = wide ? 64 : 32;
