@@ -275,7 +275,10 @@ def test_fused_residual_in_place(bnn):
 
 
 # ---------------------------------------------------------------- FP first / last layers
-@pytest.mark.parametrize("M,N,K", [(64, 128, 784), (100, 70, 33), (1, 32, 1), (130, 4096, 784)])
+@pytest.mark.parametrize("M,N,K", [(64, 128, 784), (100, 70, 33), (1, 32, 1), (130, 4096, 784),
+                                   # 16-byte rows (matrix-core path) with a K tail inside the
+                                   # last 16-wide chunk and partial row / column tiles
+                                   (70, 100, 36), (33, 65, 20), (1, 17, 4), (40, 64, 1000)])
 def test_dense_f32_sign_pack(bnn, M, N, K):
     X = workloads.uniform01_f32(1000 + K, (M, K))
     W = workloads.normal_f32(1001 + K, (N, K))
