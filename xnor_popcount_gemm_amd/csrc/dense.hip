@@ -22,6 +22,9 @@
 //
 // Last layer: one workgroup per activation row, K split over its waves,
 // double accumulators, fixed-order reductions (deterministic on every run).
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "bnn_device.hpp"
 #include "bnn_launch.hpp"
 
@@ -213,6 +216,7 @@ __device__ __forceinline__ float comp(const float4& v, int s) {
     return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
 }
 
+template <int BM, int BN>
 __global__ __launch_bounds__(kThreads) void k_dense_f64_mfma_sign_pack(
     const float* __restrict__ X, int64_t ldX, const float* __restrict__ W, int64_t ldW,
     int M, int N, int K, uint32_t* __restrict__ Op, int64_t ldOp, int tiles_n, int tiles)
@@ -221,51 +225,51 @@ __global__ __launch_bounds__(kThreads) void k_dense_f64_mfma_sign_pack(
     const int tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (tile >= tiles) return;                       // no barriers below
     const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
-    const int m0 = 32 * tm, n0 = 64 * tn;
+    const int m0 = 16 * BM * tm, n0 = 16 * BN * tn;
     const int g = lane >> 4, c = lane & 15;
-    const float* xr[2];
-    const float* wr[4];
+    const float* xr[BM];
+    const float* wr[BN];
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm) xr[bm] = X + (int64_t)min(m0 + 16 * bm + c, M - 1) * ldX;
+    for (int bm = 0; bm < BM; ++bm) xr[bm] = X + (int64_t)min(m0 + 16 * bm + c, M - 1) * ldX;
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) wr[bn] = W + (int64_t)min(n0 + 16 * bn + c, N - 1) * ldW;
+    for (int bn = 0; bn < BN; ++bn) wr[bn] = W + (int64_t)min(n0 + 16 * bn + c, N - 1) * ldW;
 
-    v4d acc[2][4];
+    v4d acc[BM][BN];
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
+    for (int bm = 0; bm < BM; ++bm)
 #pragma unroll
-        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = (v4d){0.0, 0.0, 0.0, 0.0};
+        for (int bn = 0; bn < BN; ++bn) acc[bm][bn] = (v4d){0.0, 0.0, 0.0, 0.0};
 
     const int nch = (K + 15) >> 4;
-    float4 xn[2], wn[4];
+    float4 xn[BM], wn[BN];
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm) xn[bm] = load_k4(xr[bm], 4 * g, K);
+    for (int bm = 0; bm < BM; ++bm) xn[bm] = load_k4(xr[bm], 4 * g, K);
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) wn[bn] = load_k4(wr[bn], 4 * g, K);
+    for (int bn = 0; bn < BN; ++bn) wn[bn] = load_k4(wr[bn], 4 * g, K);
     for (int t = 0; t < nch; ++t) {
-        float4 xa[2], wa[4];
+        float4 xa[BM], wa[BN];
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm) xa[bm] = xn[bm];
+        for (int bm = 0; bm < BM; ++bm) xa[bm] = xn[bm];
 #pragma unroll
-        for (int bn = 0; bn < 4; ++bn) wa[bn] = wn[bn];
+        for (int bn = 0; bn < BN; ++bn) wa[bn] = wn[bn];
         if (t + 1 < nch) {                           // next chunk in flight during this one
             const int k = 16 * (t + 1) + 4 * g;
 #pragma unroll
-            for (int bm = 0; bm < 2; ++bm) xn[bm] = load_k4(xr[bm], k, K);
+            for (int bm = 0; bm < BM; ++bm) xn[bm] = load_k4(xr[bm], k, K);
 #pragma unroll
-            for (int bn = 0; bn < 4; ++bn) wn[bn] = load_k4(wr[bn], k, K);
+            for (int bn = 0; bn < BN; ++bn) wn[bn] = load_k4(wr[bn], k, K);
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            double xd[2], wd[4];
+            double xd[BM], wd[BN];
 #pragma unroll
-            for (int bm = 0; bm < 2; ++bm) xd[bm] = (double)comp(xa[bm], s);
+            for (int bm = 0; bm < BM; ++bm) xd[bm] = (double)comp(xa[bm], s);
 #pragma unroll
-            for (int bn = 0; bn < 4; ++bn) wd[bn] = (double)comp(wa[bn], s);
+            for (int bn = 0; bn < BN; ++bn) wd[bn] = (double)comp(wa[bn], s);
 #pragma unroll
-            for (int bm = 0; bm < 2; ++bm)
+            for (int bm = 0; bm < BM; ++bm)
 #pragma unroll
-                for (int bn = 0; bn < 4; ++bn)
+                for (int bn = 0; bn < BN; ++bn)
                     acc[bm][bn] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[bm], wd[bn], acc[bm][bn], 0, 0, 0);
         }
     }
@@ -273,19 +277,24 @@ __global__ __launch_bounds__(kThreads) void k_dense_f64_mfma_sign_pack(
     // Sign bits: bit 1 for h < 0; columns >= N give 0 (+1, the pad rule).
     // For block row bm and element r, ballot bn holds rows m0 + 16 bm + 4 r
     // + q (q = 0..3) in bits 16 q .. 16 q + 15, columns n0 + 16 bn + 0..15;
-    // lanes 0..7 write the 4 rows' two words.
+    // lanes 0 .. 4 BN/2 - 1 write the 4 rows' BN/2 words.
+    static_assert(BN % 2 == 0, "whole 32-column words per tile");
+    constexpr int WPR = BN / 2;
     const int nw = (N + 31) >> 5;
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
+    for (int bm = 0; bm < BM; ++bm)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            uint64_t b[4];
+            uint64_t b[BN];
 #pragma unroll
-            for (int bn = 0; bn < 4; ++bn)
+            for (int bn = 0; bn < BN; ++bn)
                 b[bn] = __builtin_amdgcn_ballot_w64(acc[bm][bn][r] < 0.0 && n0 + 16 * bn + c < N);
-            if (lane < 8) {
-                const int q = lane >> 1, w = lane & 1;
-                const uint64_t lo = w ? b[2] : b[0], hi = w ? b[3] : b[1];
+            if (lane < 4 * WPR) {
+                const int q = lane / WPR, w = lane - q * WPR;
+                uint64_t lo = b[0], hi = b[1];
+#pragma unroll
+                for (int i = 1; i < WPR; ++i)
+                    if (w == i) { lo = b[2 * i]; hi = b[2 * i + 1]; }
                 const uint32_t word = (uint32_t)((lo >> (16 * q)) & 0xFFFFu) |
                                       ((uint32_t)((hi >> (16 * q)) & 0xFFFFu) << 16);
                 const int m = m0 + 16 * bm + 4 * r + q;
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void k_dense_f64_mfma_sign_pack(
                 if (m < M && widx < nw) Op[(int64_t)m * ldOp + widx] = word;
             }
         }
-    if (tn == tiles_n - 1 && lane < 32 && m0 + lane < M)
+    if (tn == tiles_n - 1 && lane < 16 * BM && m0 + lane < M)
         for (int64_t w = nw; w < ldOp; ++w) Op[(int64_t)(m0 + lane) * ldOp + w] = 0u;
 }
 
@@ -306,11 +315,25 @@ hipError_t launch_dense_f32_sign_pack(const float* X, int64_t ldX, const float* 
     const bool vec = (reinterpret_cast<uintptr_t>(X) & 15u) == 0 && (reinterpret_cast<uintptr_t>(W) & 15u) == 0 &&
                      ldX % 4 == 0 && ldW % 4 == 0;
     if (vec) {                                       // 16-byte rows: the matrix cores
-        const int tn = (int)((N + 63) / 64);
-        const int64_t tiles = ((M + 31) / 32) * tn;
+        int bm = 2, bn = 4;
+        if (const char* v = getenv("BNN_DENSE_TILE")) {  // tuning override "BM,BN" (16-row / 16-column blocks)
+            int a = 0, c = 0;
+            if (sscanf(v, "%d,%d", &a, &c) == 2 && (a == 1 || a == 2 || a == 4) && (c == 2 || c == 4)) { bm = a; bn = c; }
+        }
+        const int tn = (int)((N + 16 * bn - 1) / (16 * bn));
+        const int64_t tiles = ((M + 16 * bm - 1) / (16 * bm)) * tn;
         const dim3 g((unsigned)((tiles + kThreads / 64 - 1) / (kThreads / 64))), b(kThreads);
-        hipLaunchKernelGGL(k_dense_f64_mfma_sign_pack, g, b, 0, s, X, ldX, W, ldW, (int)M, (int)N, (int)K,
-                           Op, ldOp, tn, (int)tiles);
+#define BNN_DMF(A, C) hipLaunchKernelGGL((k_dense_f64_mfma_sign_pack<A, C>), g, b, 0, s, X, ldX, W, ldW, \
+                                         (int)M, (int)N, (int)K, Op, ldOp, tn, (int)tiles)
+        switch (bm * 8 + bn) {
+            case 1 * 8 + 2: BNN_DMF(1, 2); break;
+            case 1 * 8 + 4: BNN_DMF(1, 4); break;
+            case 2 * 8 + 2: BNN_DMF(2, 2); break;
+            case 4 * 8 + 2: BNN_DMF(4, 2); break;
+            case 4 * 8 + 4: BNN_DMF(4, 4); break;
+            default: BNN_DMF(2, 4); break;
+        }
+#undef BNN_DMF
         return hipGetLastError();
     }
     const int64_t tiles_m = (M + kTile - 1) / kTile;
