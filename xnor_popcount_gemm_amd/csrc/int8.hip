@@ -335,8 +335,9 @@ hipError_t launch_act_i8(const float* X, int64_t ldX, const int8_t* Xq_in, int64
 namespace {
 // Lane-group shape of the G-lanes GEMV for a row of K: G = 2^glog2 lanes and
 // CPL granules per lane, the fewest lane slots G * CPL covering the row's
-// ceil(Kw/4) granules (G in 16..64, CPL * M <= 4 so the planes fit in
-// registers); among equal slot counts the larger CPL (fewer group sums).
+// ceil(Kw/4) granules (G in 16..64, CPL * M <= 4, which bounds the planes'
+// LDS space to 32 KB per workgroup); among equal slot counts the larger CPL
+// (fewer group sums).
 struct I8Shape { int glog2, cpl; };
 
 bool i8_shape(int64_t M, int64_t K, I8Shape* out) {
