@@ -88,7 +88,10 @@ def _ternary_case(bnn, seed, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 300, 1000), (2, 4096, 4096), (4, 129, 333), (64, 256, 1000),
-                                   (300, 100, 577), (1000, 64, 576), (257, 130, 4096), (129, 33, 31)])
+                                   (300, 100, 577), (1000, 64, 576), (257, 130, 4096), (129, 33, 31),
+                                   # 3 and 5 full 8-word chunks (odd chunk after the two-chunk
+                                   # K loop), the second with a tail
+                                   (130, 70, 768), (257, 64, 1300)])
 def test_ternary_binary_linear_fused(bnn, M, N, K):
     T, gam, Sp, Zp, nnz, g = _ternary_case(bnn, 9100 + K, N, K)
     X = workloads.normal_f32(9200 + K, (M, K))
