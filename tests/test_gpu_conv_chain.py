@@ -41,7 +41,9 @@ def _beta(seed, C):
     return workloads.normal_f32(seed, (C,)) * np.float32(0.3)
 
 
-@pytest.mark.parametrize("M,K", [(7, 64), (100, 256), (3, 1000), (64, 33)])
+@pytest.mark.parametrize("M,K", [(7, 64), (100, 256), (3, 1000), (64, 33),
+                                 # 4-word rows with 1 or 2 data words (lane groups skip the pad)
+                                 (50, 20), (1000, 64), (17, 128)])
 def test_pack_activations_rsign(bnn, M, K):
     X = workloads.normal_f32(10000 + K, (M, K))
     X = workloads.inject_edge_values(X, 10001 + K, 0.03)

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_ternary(
 // LDP = 4 or 8 (packed rows of that many words, C <= 256 channels): the 8
 // lane groups of a wave cover 8 / LDP rows per step, so no lane group idles
 // past the end of a short row; LDP = 0 walks any row length.
-template <bool VEC, int LDP>
+template <bool VEC, int LDP, int DW = 0>
 __global__ __launch_bounds__(kThreads) void k_pack_dense_rsign(
     const float* __restrict__ X, int64_t rows, int K, int64_t ldX, const float* __restrict__ beta,
     uint32_t* __restrict__ P, int64_t ldP)
@@ -368,10 +368,15 @@ __global__ __launch_bounds__(kThreads) void k_pack_dense_rsign(
         return nib;
     };
     if constexpr (LDP > 0) {
-        // step u of a wave pass: rows r0 + RS u + grp / LDP, word grp % LDP;
+        // step u of a wave pass: rows r0 + RS u + grp / WL, word grp % WL,
+        // with WL = LDP words per row, or DW when the lane groups cover only
+        // the first DW = LDP / 2 words (the rest of the row is pad: its
+        // zeros are stored by the same lanes, with no loads spent on them);
         // the lane's four columns, and so its four shifts, never change
-        constexpr int RS = 8 / (LDP > 0 ? LDP : 8);
-        const int w = grp % LDP;
+        static_assert(DW == 0 || 2 * DW == LDP, "data words are half the row");
+        constexpr int WL = DW > 0 ? DW : (LDP > 0 ? LDP : 8);
+        constexpr int RS = 8 / WL;
+        const int w = grp % WL;
         const int k0 = 32 * w + 4 * sub;
         float bt[4];
 #pragma unroll
@@ -380,19 +385,22 @@ __global__ __launch_bounds__(kThreads) void k_pack_dense_rsign(
             Frag f[kSteps];
 #pragma unroll
             for (int u = 0; u < kSteps; ++u) {
-                const int64_t r = r0 + RS * u + grp / LDP;
+                const int64_t r = r0 + RS * u + grp / WL;
                 f[u] = Frag{};
                 if (r < rows) f[u] = load_frag<VEC>(X + r * ldX, k0, K);
             }
 #pragma unroll
             for (int u = 0; u < kSteps; ++u) {
-                const int64_t r = r0 + RS * u + grp / LDP;
+                const int64_t r = r0 + RS * u + grp / WL;
                 uint32_t nib = 0u;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     nib |= ((k0 + i < K && !(__uint_as_float(f[u].u[i]) >= bt[i])) ? 1u : 0u) << i;
                 const uint32_t word = or_reduce8_to_last(nib << (4 * sub));
-                if (sub == 7 && r < rows) P[r * ldP + w] = word;
+                if (sub == 7 && r < rows) {
+                    P[r * ldP + w] = word;
+                    if (DW > 0) P[r * ldP + w + DW] = 0u;
+                }
             }
         }
         return;
@@ -576,6 +584,13 @@ hipError_t launch_pack_dense_rsign(const float* X, int64_t rows, int64_t K, int6
 {
     const bool vec = aligned16(X) && (ldX % 4 == 0);
     const dim3 block(kThreads);
+    if (ldP == 4 && (K + 31) / 32 <= 2) {           // 2 data words + 2 pad words per row
+        const int64_t rs = 4;
+        const dim3 grid(grid_for_rows((rows + rs * kSteps - 1) / (rs * kSteps)));
+        if (vec) hipLaunchKernelGGL((k_pack_dense_rsign<true, 4, 2>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
+        else     hipLaunchKernelGGL((k_pack_dense_rsign<false, 4, 2>), grid, block, 0, s, X, rows, (int)K, ldX, beta, P, ldP);
+        return hipGetLastError();
+    }
     if (ldP == 4 || ldP == 8) {                      // 8 / ldP rows per wave step
         const int64_t rs = 8 / ldP;
         const dim3 grid(grid_for_rows((rows + rs * kSteps - 1) / (rs * kSteps)));
