@@ -51,6 +51,22 @@ def test_pack_weights_bits_and_alpha(bnn, N, K):
     assert_f32_close(host(a), a_ref, what="alpha")
 
 
+def test_pack_weights_repeatable(bnn):
+    """alpha's |w| sums are split over the waves of a workgroup and added in a
+    fixed order: repeated calls give the same bits, also on fresh buffers."""
+    N, K = 300, 16384
+    W = workloads.normal_f32(150, (N, K))
+    Wd = dev(W)
+    banner(f"pack_weights repeatability N={N} K={K}")
+    runs = [bnn.pack_weights(Wd) for _ in range(3)]
+    torch.cuda.synchronize()
+    a0, p0 = host(runs[0][1]).view(np.uint32), host_u32(runs[0][0])
+    for Wp, a in runs[1:]:
+        np.testing.assert_array_equal(host(a).view(np.uint32), a0)
+        np.testing.assert_array_equal(host_u32(Wp), p0)
+    assert_f32_close(host(runs[0][1]), oracle.alpha(W), what="alpha")
+
+
 @pytest.mark.parametrize("M,K,extra_ld", [(64, 1000, 0), (3, 70, 12), (1, 4096, 0), (1, 11008, 0),
                                           (100, 129, 4), (2, 5, 0)])
 def test_pack_activations_dense(bnn, M, K, extra_ld):
