@@ -169,6 +169,20 @@ def test_bwn_i8_gemv_matches_oracle(bnn, M, N, K):
     _check_linear(bnn, Qf, None, W, ws, a, path="gemv", per_tensor=True)
 
 
+@pytest.mark.parametrize("shape", ["5,3", "5,4", "6,2", "6,4"])
+def test_bwn_i8_gemv_every_lane_shape(bnn, shape, monkeypatch):
+    """The GEMV's lane-group shapes (BNN_I8_SHAPE "glog2,cpl") on a row that
+    each of them covers (K = 11008: 86 granules), including a ragged last row
+    group (N = 301)."""
+    monkeypatch.setenv("BNN_I8_SHAPE", shape)
+    N, K = 301, 11008
+    W, ws, a = _weights(7700, N, K)
+    X = _act_rows(7701, 1, K)
+    Q, xs = oracle.quantize_absmax_i8(X)
+    banner(f"bwn_i8 gemv lane shape {shape} N={N} K={K}")
+    _check_linear(bnn, Q, xs, W, ws, a, path="gemv")
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 64), (16, 16, 63), (64, 128, 1000), (130, 257, 100),
                                    (200, 300, 4096), (3, 1000, 11008), (129, 129, 129), (1, 64, 65),
                                    (600, 200, 1000), (513, 129, 130), (257, 385, 192)])

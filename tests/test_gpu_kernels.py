@@ -310,6 +310,24 @@ def test_dense_f32_sign_pack(bnn, M, N, K):
     np.testing.assert_array_equal(host_u32(Op), oracle.pack_signs(s, ld=Op.shape[1]))
 
 
+@pytest.mark.parametrize("tile", ["1,2", "1,4", "2,2", "2,4", "4,2", "4,4"])
+def test_dense_f32_sign_pack_every_tile(bnn, tile, monkeypatch):
+    """Every wave tile of the fp64 matrix-core first layer (BNN_DENSE_TILE
+    "BM,BN" 16-row / 16-column blocks), with partial row and column tiles."""
+    monkeypatch.setenv("BNN_DENSE_TILE", tile)
+    M, N, K = 77, 150, 784
+    X = workloads.uniform01_f32(1300, (M, K))
+    W = workloads.normal_f32(1301, (N, K))
+    banner(f"dense sign-pack tile {tile} M={M} N={N} K={K}")
+    Op = bnn.dense_f32_sign_pack(dev(X), dev(W))
+    torch.cuda.synchronize()
+    H = oracle.dense_f64(X, W)
+    bound = K * 2.0**-52 * (np.abs(X).astype(np.float64) @ np.abs(W).astype(np.float64).T)
+    assert int((np.abs(H) <= bound).sum()) == 0, "near-ties in the test data"
+    s = np.where(H >= 0.0, 1, -1).astype(np.int8)
+    np.testing.assert_array_equal(host_u32(Op), oracle.pack_signs(s, ld=Op.shape[1]))
+
+
 @pytest.mark.parametrize("M,N,K", [(64, 10, 4096), (7, 3, 33), (130, 17, 1000)])
 def test_dense_binact_f32(bnn, M, N, K):
     rng = np.random.default_rng(1100 + K)
