@@ -183,6 +183,36 @@ def test_bwn_i8_gemv_every_lane_shape(bnn, shape, monkeypatch):
     _check_linear(bnn, Q, xs, W, ws, a, path="gemv")
 
 
+@pytest.mark.parametrize("u", ["1", "2"])
+def test_bwn_i8_gemv_every_row_step_count(bnn, u, monkeypatch):
+    """Row steps per wave (BNN_GEMV_U) on a matrix tall enough that the
+    unrolled kernel runs (K = 4096: 4 rows per wave step; N = 65541 gives
+    16386 steps, a ragged last wave at U = 2).  Random packed weight words
+    with no pad bits (K is a multiple of 32); the oracle checks 400 sampled
+    rows, the bound |D| <= sum |q| holds on every row."""
+    monkeypatch.setenv("BNN_GEMV_U", u)
+    N, K = 65541, 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7900)
+    Wp = torch.randint(-2**31, 2**31 - 1, (N, K // 32), dtype=torch.int32, device="cuda", generator=g)
+    X = _act_rows(7901, 1, K)
+    Q, xs = oracle.quantize_absmax_i8(X)
+    a = workloads.uniform01_f32(7902, (N,)) + np.float32(0.5)
+    Xb, xsum = bnn.pack_act_i8(dev(Q))
+    banner(f"bwn_i8 gemv U={u} N={N} K={K}")
+    out = bnn.bwn_i8_linear(Wp, K, bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32, alpha=dev(a), xscale=dev(xs),
+                            Xb=Xb, xsum=xsum)
+    torch.cuda.synchronize()
+    d, y = host(out["D"])[0], host(out["Y"])[0]
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(N - 8, N),
+                                     np.random.default_rng(7903).integers(0, N, 384)]))
+    D_ref = oracle.dot_i8(Q, oracle.unpack_signs(host_u32(Wp)[rows], K))
+    np.testing.assert_array_equal(d[rows], D_ref[0])
+    Y_ref = oracle.scale_i8(D_ref, a[rows], xs)
+    _bits_equal(y[rows][None, :], Y_ref, "Y")
+    assert np.all(np.abs(d) <= np.abs(Q.astype(np.int64)).sum())
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 64), (16, 16, 63), (64, 128, 1000), (130, 257, 100),
                                    (200, 300, 4096), (3, 1000, 11008), (129, 129, 129), (1, 64, 65),
                                    (600, 200, 1000), (513, 129, 130), (257, 385, 192)])

@@ -153,6 +153,49 @@ def test_xnor_gemm_every_column_tile(bnn, tn, M, N, K):
     np.testing.assert_array_equal(host(D), oracle.dot(oracle.sign(X), oracle.sign(W)))
 
 
+@pytest.mark.parametrize("waves", ["4", "8", "16"])
+@pytest.mark.parametrize("M,N,K", [(1100, 100, 777), (700, 70, 5000)])
+def test_xnor_gemm_every_wave_count(bnn, waves, M, N, K, monkeypatch):
+    """Workgroups of 4, 8 and 16 waves (BNN_GEMM_WAVES) on the LDS epilogue
+    (K <= 4096) and on the direct one, with ragged row tiles (M = 1100 is one
+    full and one partial 1024-row tile at 16 waves)."""
+    monkeypatch.setenv("BNN_GEMM_WAVES", waves)
+    X, W = _packed_pair(M, N, K, 520 + M)
+    banner(f"xnor_gemm waves={waves} M={M} N={N} K={K}")
+    Wp, a = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    D, Y = bnn.xnor_gemm(Xp, Wp, K, alpha=a, want_dot=True, want_scaled=True)
+    torch.cuda.synchronize()
+    D_ref, Y_ref, _ = oracle.binary_linear(X, W)
+    np.testing.assert_array_equal(host(D), D_ref)
+    np.testing.assert_array_equal(host(Y), (host(a)[None, :] * host(D).astype(np.float32)).astype(np.float32))
+
+
+@pytest.mark.parametrize("u", ["1", "2", "4"])
+def test_gemv_every_row_step_count(bnn, u, monkeypatch):
+    """The GEMV's row steps per wave (BNN_GEMV_U) on a matrix tall enough that
+    the unrolled kernel runs (K = 16384: one row per lane group of 64; at
+    N = 32773 a wave takes 4 rows at U = 4, with a ragged last wave).  Random
+    packed words with no pad bits (K is a multiple of 32); the oracle checks
+    400 sampled rows, the invariants hold on every row."""
+    monkeypatch.setenv("BNN_GEMV_U", u)
+    N, K = 32773, 16384
+    kw = K // 32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(530)
+    Wp = torch.randint(-2**31, 2**31 - 1, (N, kw), dtype=torch.int32, device="cuda", generator=g)
+    Xp = torch.randint(-2**31, 2**31 - 1, (1, kw), dtype=torch.int32, device="cuda", generator=g)
+    banner(f"xnor_gemv U={u} N={N} K={K}")
+    D, _ = bnn.xnor_gemm(Xp, Wp, K)
+    torch.cuda.synchronize()
+    d = host(D)[0]
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(N - 8, N),
+                                     np.random.default_rng(531).integers(0, N, 384)]))
+    want = oracle.dot(oracle.unpack_signs(host_u32(Xp), K), oracle.unpack_signs(host_u32(Wp)[rows], K))[0]
+    np.testing.assert_array_equal(d[rows], want)
+    assert np.all(np.abs(d) <= K) and np.all((d - K) % 2 == 0)
+
+
 def test_xnor_gemm_strided_outputs(bnn):
     M, N, K = 130, 70, 500
     X, W = _packed_pair(M, N, K, 600)
