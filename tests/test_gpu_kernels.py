@@ -196,6 +196,28 @@ def test_gemv_every_row_step_count(bnn, u, monkeypatch):
     assert np.all(np.abs(d) <= K) and np.all((d - K) % 2 == 0)
 
 
+def test_xnor_gemm_largest_k(bnn):
+    """K = 2^24, the largest K the C ABI accepts (BNN_MAX_K): |D| reaches K,
+    which (float)D still holds exactly.  Weight rows: X's own signs (D = K),
+    their negation with zeros made negative too (D = -K), and a random row."""
+    K = 1 << 24
+    X = workloads.normal_f32(540, (2, K))
+    W = np.empty((3, K), np.float32)
+    W[0] = X[0]
+    W[1] = np.where(X[0] >= 0, np.float32(-1.0), np.float32(1.0))
+    W[2] = workloads.normal_f32(541, (1, K))[0]
+    banner(f"xnor_gemm M=2 N=3 K={K}")
+    Wp, a = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    D, Y = bnn.xnor_gemm(Xp, Wp, K, alpha=a, want_dot=True, want_scaled=True)
+    torch.cuda.synchronize()
+    D_ref, Y_ref, a_ref = oracle.binary_linear(X, W)
+    assert D_ref[0, 0] == K and D_ref[0, 1] == -K
+    np.testing.assert_array_equal(host(D), D_ref)
+    assert_f32_close(host(a), a_ref, what="alpha")
+    np.testing.assert_array_equal(host(Y), (host(a)[None, :] * host(D).astype(np.float32)).astype(np.float32))
+
+
 def test_xnor_gemm_strided_outputs(bnn):
     M, N, K = 130, 70, 500
     X, W = _packed_pair(M, N, K, 600)
