@@ -196,6 +196,24 @@ def test_gemv_every_row_step_count(bnn, u, monkeypatch):
     assert np.all(np.abs(d) <= K) and np.all((d - K) % 2 == 0)
 
 
+@pytest.mark.parametrize("M", [1, 3, 4])
+@pytest.mark.parametrize("K", [20000, 32768, 40000, 65504, 65536, 65537])
+def test_gemv_granules_per_lane(bnn, M, K):
+    """GEMV rows wider than 64 lanes x 2 granules: 4 granules per lane
+    (K = 20000, 32768) and 8 (K = 40000 up to 65536, the widest row the GEMV
+    takes); K = 65537 is one word past it and runs the GEMM instead."""
+    N = 130
+    X, W = _packed_pair(M, N, K, 560 + K + M)
+    banner(f"xnor_gemv M={M} N={N} K={K}")
+    Wp, a = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    D, Y = bnn.xnor_gemm(Xp, Wp, K, alpha=a, want_dot=True, want_scaled=True)
+    torch.cuda.synchronize()
+    D_ref, _, _ = oracle.binary_linear(X, W)
+    np.testing.assert_array_equal(host(D), D_ref)
+    np.testing.assert_array_equal(host(Y), (host(a)[None, :] * host(D).astype(np.float32)).astype(np.float32))
+
+
 def test_xnor_gemm_largest_k(bnn):
     """K = 2^24, the largest K the C ABI accepts (BNN_MAX_K): |D| reaches K,
     which (float)D still holds exactly.  Weight rows: X's own signs (D = K),
