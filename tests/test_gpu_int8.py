@@ -183,6 +183,22 @@ def test_bwn_i8_gemv_every_lane_shape(bnn, shape, monkeypatch):
     _check_linear(bnn, Q, xs, W, ws, a, path="gemv")
 
 
+@pytest.mark.parametrize("path", ["gemm", "gemm_xsum"])
+def test_bwn_i8_gemm_largest_k(bnn, path):
+    """K = 2^17, the largest K the INT8 path accepts (BNN_MAX_K_I8): an
+    all -128 activation row against an all-negative weight row gives
+    D = 128 * 2^17 = 2^24, the largest value (float)D still holds exactly."""
+    M, N, K = 3, 40, 1 << 17
+    W, _, _ = _weights(7950, N, K)
+    W[0, :] = np.float32(-1.0)
+    ws, a = oracle.sign(W), oracle.alpha(W)
+    Q = _full_range_i8(7951, M, K)
+    Q[0, :] = -128
+    assert oracle.dot_i8(Q[:1], ws[:1])[0, 0] == 1 << 24
+    banner(f"bwn_i8 {path} M={M} N={N} K={K}")
+    _check_linear(bnn, Q, None, W, ws, a, path=path)
+
+
 @pytest.mark.parametrize("u", ["1", "2"])
 def test_bwn_i8_gemv_every_row_step_count(bnn, u, monkeypatch):
     """Row steps per wave (BNN_GEMV_U) on a matrix tall enough that the
