@@ -91,7 +91,10 @@ def _ternary_case(bnn, seed, N, K):
                                    (300, 100, 577), (1000, 64, 576), (257, 130, 4096), (129, 33, 31),
                                    # 3 and 5 full 8-word chunks (odd chunk after the two-chunk
                                    # K loop), the second with a tail
-                                   (130, 70, 768), (257, 64, 1300)])
+                                   (130, 70, 768), (257, 64, 1300),
+                                   # GEMV rows of 8 granules per lane, up to the widest K
+                                   # the GEMV takes; one word past it runs the GEMM
+                                   (1, 130, 40000), (3, 130, 65536), (2, 40, 65537)])
 def test_ternary_binary_linear_fused(bnn, M, N, K):
     T, gam, Sp, Zp, nnz, g = _ternary_case(bnn, 9100 + K, N, K)
     X = workloads.normal_f32(9200 + K, (M, K))
