@@ -63,7 +63,10 @@ def _conv_ref(X, Wt, beta):
 
 
 @pytest.mark.parametrize("B,H,W,C,Cout", [(2, 5, 6, 64, 64), (1, 7, 3, 128, 100), (2, 4, 4, 256, 256),
-                                          (1, 3, 5, 512, 64), (1, 1, 1, 64, 8), (3, 6, 7, 64, 33)])
+                                          (1, 3, 5, 512, 64), (1, 1, 1, 64, 8), (3, 6, 7, 64, 33),
+                                          # one-pixel-high and one-pixel-wide strips: the rows
+                                          # or columns of taps outside are all padding
+                                          (2, 1, 9, 64, 64), (2, 9, 1, 128, 40)])
 def test_conv3x3_fused_matches_explicit(bnn, B, H, W, C, Cout):
     X = workloads.normal_f32(10100 + C, (B, H, W, C))
     Wt = workloads.normal_f32(10101 + C, (Cout, 3, 3, C))
