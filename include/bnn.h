@@ -33,7 +33,9 @@
  *    caller's next synchronization.
  *  - No global mutable state: calls may be issued from several host threads.
  *  - Sizes: 1 <= K <= 2^24 (so every dot product is exact as an fp32 and an
- *    int32).  M == 0 or N == 0 is a valid empty call (nothing launched).
+ *    int32).  M == 0 or N == 0 is a valid empty call (nothing launched); its
+ *    pointers are validated like those of any other call (non-null, aligned),
+ *    so a zero-size buffer still needs a valid base address.
  *
  * Packed layout (the "packed operand" of every call):
  *  - A packed matrix [rows, ld] of uint32 words holds row r's element k at
