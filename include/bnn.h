@@ -329,13 +329,22 @@ bnn_status bnn_bwn_i8_linear(const bnn_i8_args* args, bnn_stream_t stream);
 
 /* Fold inference BatchNorm of z = alpha[n] * D followed by sign into the
  * (tau, dir) pair consumed by BNN_EPI_THRESH_PACK.  [P1] BatchNorm around
- * binary layers; [P3] BatchNorm scales stay FP.  HOST memory, synchronous.
- *   BN(z) = gamma (z - mean) / sqrt(var + eps) + beta ; next sign = +1 iff BN >= 0.
- * With sd = sqrt(var + eps) and c = gamma*alpha (double):
- *   c > 0: dir = +1, tau = fl32((gamma*mean - beta*sd) / c)      (D >= tau)
- *   c < 0: dir = -1, tau = fl32(-(gamma*mean - beta*sd) / c)     (-D >= tau)
- *   c = 0: dir =  0, tau = 0 if beta - gamma*mean/sd >= 0 else 1 (constant)
- * Errors: NULL pointer -> BNN_ERR_NULL; N < 0 -> BNN_ERR_SHAPE. */
+ * binary layers; [P3] BatchNorm scales stay FP; [P5] eq. (4) the next layer
+ * takes the sign.  HOST memory, synchronous.
+ *   BN(z) = gamma (z - mean) / sqrt(var + eps) + beta ; next sign = +1 iff BN >= 0,
+ * taken in exact real arithmetic on the given fp32 values.  BN(alpha D) is
+ * affine in D, so over the integers the rule is one threshold:
+ *   gamma*alpha > 0: dir = +1, tau = the smallest integer D with BN >= 0
+ *   gamma*alpha < 0: dir = -1, tau = -(the largest integer D with BN >= 0)
+ *   gamma*alpha = 0: dir =  0, tau = 0 if BN (a constant) >= 0, else 1
+ * so that (float)(dir * D) >= tau holds exactly when BN(alpha D) >= 0, for
+ * every |D| <= 2^24.  tau is an integer-valued float (a boundary beyond
+ * +2^24 is stored as 2^25, one below -2^24 as -2^24).  The boundary is
+ * estimated in double and certified with exact big-integer arithmetic, so
+ * ties (BN = 0 exactly) give +1.
+ * Errors: NULL pointer (also for N == 0) -> BNN_ERR_NULL; N < 0 ->
+ * BNN_ERR_SHAPE; a non-finite parameter or var[n] + eps <= 0 ->
+ * BNN_ERR_UNSUPPORTED (nothing written). */
 bnn_status bnn_fold_bn_thresholds_host(const float* gamma, const float* beta,
                                        const float* mean, const float* var, float eps,
                                        const float* alpha, int64_t N,

@@ -13,7 +13,8 @@ the passage of the source pages it follows (page title and section/equation):
   pad bits encode +1, and the dot identity <w,x> = N - 2 popcount(w xor x).
 * "Extreme Quantization: Binary, Ternary & 1-bit LLMs": Notation (sign),
   eq. (1) (alpha = mean |w|), eq. (4)-(6) (XNOR-Net).
-* "Binary Neural Network (BNN)" glossary: scaling factors and BatchNorm.
+* "Binary Neural Network (BNN)" glossary: scaling factors and BatchNorm
+  (BatchNorm followed by the sign is decided exactly in ``batchnorm.py``).
 * "Perfected Concept", "What is binary vs not": FP first/last layers and FP
   residual streams; "State of the Art Survey", Bi-Real Net: FP shortcut.
 """
@@ -24,6 +25,8 @@ import os
 import subprocess
 
 import numpy as np
+
+from .batchnorm import bn_next_sign, bn_rule, bn_value, rule_signs  # noqa: F401  (exact BatchNorm + sign)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -81,8 +84,6 @@ def _configure(L):
         "oracle_dot": [_p, _p, _i64, _i64, _i64, _p],
         "oracle_scale": [_p, _p, _i64, _i64, _p],
         "oracle_scale_residual": [_p, _p, _p, _i64, _i64, _i64, _p],
-        "oracle_bn_fold": [_p, _p, _p, _p, ctypes.c_float, _p, _i64, _p, _p],
-        "oracle_threshold_signs": [_p, _p, _p, _i64, _i64, _p],
         "oracle_im2col_signs": [_p, _i64, _i64, _i64, _i64, _p],
         "oracle_dense_f64": [_p, _i64, _p, _i64, _i64, _i64, _i64, _p],
         "oracle_dense_pm1_f32out": [_p, _p, _i64, _i64, _i64, _i64, _p],
@@ -285,28 +286,6 @@ def scale_residual(D: np.ndarray, a: np.ndarray, R: np.ndarray) -> np.ndarray:
     return Y
 
 
-def bn_fold(gamma, beta, mean, var, eps, a):
-    """Fold inference BatchNorm of alpha*D followed by sign into (tau, dir)."""
-    gamma, beta, mean, var, a = (_c(v, np.float32) for v in (gamma, beta, mean, var, a))
-    N = a.shape[0]
-    tau = np.empty(N, dtype=np.float32)
-    d = np.empty(N, dtype=np.int8)
-    lib().oracle_bn_fold(_ptr(gamma), _ptr(beta), _ptr(mean), _ptr(var),
-                         ctypes.c_float(float(eps)), _ptr(a), N, _ptr(tau), _ptr(d))
-    return tau, d
-
-
-def threshold_signs(D: np.ndarray, tau: np.ndarray, d: np.ndarray) -> np.ndarray:
-    """Next-layer signs: +1 iff (float)(dir_n * D) >= tau_n."""
-    D = _c(D, np.int32)
-    tau = _c(tau, np.float32)
-    d = _c(d, np.int8)
-    M, N = D.shape
-    s = np.empty((M, N), dtype=np.int8)
-    lib().oracle_threshold_signs(_ptr(D), _ptr(tau), _ptr(d), M, N, _ptr(s))
-    return s
-
-
 def im2col_signs(X: np.ndarray) -> np.ndarray:
     """[B*H*W, 9*C] signs of a 3x3/stride-1/pad-1 im2col of NHWC X, pad = +1."""
     X = _c(X, np.float32)
@@ -356,21 +335,20 @@ def binary_mlp(X, W1, hidden, W5):
     layers with folded BatchNorm and sign -> FP last layer on the +1/-1 output.
 
     ``hidden`` is a list of (W, gamma, beta, mean, var, eps).  Returns a dict
-    with the first-layer pre-activations, per-layer signs, alphas, thresholds,
-    integer dots and the logits.
+    with the first-layer pre-activations, per-layer signs, alphas, integer
+    dots, the BatchNorm margins (smallest |BN(alpha D)| per channel) and the
+    logits.
     """
     h1 = dense_f64(X, W1)
     s = np.where(h1 >= 0.0, 1, -1).astype(np.int8)
-    out = dict(h1=h1, signs=[s], alphas=[], taus=[], dirs=[], dots=[])
+    out = dict(h1=h1, signs=[s], alphas=[], dots=[], bn_margins=[])
     for (W, g, b, mu, var, eps) in hidden:
         a = alpha(W)
-        tau, d = bn_fold(g, b, mu, var, eps, a)
         D = dot(s, sign(W))
-        s = threshold_signs(D, tau, d)
+        s, margin = bn_next_sign(D, a, g, b, mu, var, eps)
         out["alphas"].append(a)
-        out["taus"].append(tau)
-        out["dirs"].append(d)
         out["dots"].append(D)
+        out["bn_margins"].append(margin)
         out["signs"].append(s)
     out["logits"] = dense_pm1_f32out(s, W5)
     return out

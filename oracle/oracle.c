@@ -127,51 +127,6 @@ API void oracle_scale_residual(const int32_t* D, const float* alpha, const float
         }
 }
 
-/* [P1] BatchNorm follows the scaled binary output, and the next binary layer
- * takes its sign ([P5] eq. (4)).  Inference BatchNorm of z = alpha * D is
- *     BN(z) = gamma * (z - mean) / sqrt(var + eps) + beta,
- * and the next sign is +1 iff BN(z) >= 0.  Writing sd = sqrt(var + eps) > 0
- * and c = gamma * alpha, BN(z) >= 0 is  c * D >= gamma * mean - beta * sd.
- *   c > 0:  D >= t  with  t = (gamma * mean - beta * sd) / c   -> dir = +1, tau = t
- *   c < 0:  D <= t                                         -> dir = -1, tau = -t
- *   c = 0:  the sign is that of BN(0) = beta - gamma * mean / sd, a constant:
- *           dir = 0, tau = 0 when that constant is >= 0 (sign +1), else 1.
- * With these, the next sign is +1 iff (float)(dir * D) >= tau (see
- * oracle_threshold_signs).  Computed in double, tau rounded once to float. */
-API void oracle_bn_fold(const float* gamma, const float* beta, const float* mean, const float* var,
-                        float eps, const float* alpha, int64_t N, float* tau, int8_t* dir)
-{
-    for (int64_t n = 0; n < N; ++n) {
-        double sd = sqrt((double)var[n] + (double)eps);
-        double c = (double)gamma[n] * (double)alpha[n];
-        double rhs = (double)gamma[n] * (double)mean[n] - (double)beta[n] * sd;
-        if (c > 0.0) {
-            dir[n] = 1;
-            tau[n] = (float)(rhs / c);
-        } else if (c < 0.0) {
-            dir[n] = -1;
-            tau[n] = (float)(-(rhs / c));
-        } else {
-            double bn0 = (double)beta[n] - (double)gamma[n] * (double)mean[n] / sd;
-            dir[n] = 0;
-            tau[n] = (bn0 >= 0.0) ? 0.0f : 1.0f;
-        }
-    }
-}
-
-/* The folded BatchNorm decision: s_out = +1 iff (float)(dir * D) >= tau, else
- * -1.  D is exact as a float for |D| <= 2^24, so the comparison is exact. */
-API void oracle_threshold_signs(const int32_t* D, const float* tau, const int8_t* dir,
-                                int64_t M, int64_t N, int8_t* s_out)
-{
-    #pragma omp parallel for schedule(static)
-    for (int64_t m = 0; m < M; ++m)
-        for (int64_t n = 0; n < N; ++n) {
-            float v = (float)((int32_t)dir[n] * D[m * N + n]);
-            s_out[m * N + n] = (v >= tau[n]) ? (int8_t)1 : (int8_t)-1;
-        }
-}
-
 /* im2col of the signs of an NHWC input for a 3x3 convolution with stride 1
  * and padding 1.  Output row p = (b * H + oh) * W + ow; column
  * k = (kh * 3 + kw) * C + c (tap-major, channel-minor).  A tap that falls

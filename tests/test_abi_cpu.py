@@ -1,6 +1,7 @@
 """C-ABI checks that need no GPU: the library loads, exports every entry
 point the header declares, rejects bad arguments before any launch, and its
-host-side BatchNorm fold agrees bit for bit with the oracle's."""
+host-side BatchNorm fold gives, for every integer dot product, the decision
+that the oracle takes from the definition of BatchNorm followed by sign."""
 from __future__ import annotations
 
 import ctypes
@@ -251,19 +252,121 @@ def test_empty_calls_launch_nothing(L):
     assert L.bnn_pack_activations(A16, 0, 64, 64, None, A16, 4, None) == OK
 
 
-def test_fold_bn_thresholds_matches_oracle_bit_exact():
+def _fold_decisions(tau, d, D):
+    """The THRESH_PACK rule of the header: +1 iff (float)(dir * D) >= tau."""
+    v = (d[None, :].astype(np.int64) * np.asarray(D, np.int64)).astype(np.float32)
+    return np.where(v >= tau[None, :], 1, -1).astype(np.int8)
+
+
+def _check_fold_against_rule(tau, d, a, g, b, mu, var, eps, K, extra_D=()):
+    """The fold's decisions equal the oracle's exact rule (bisected over
+    [-K, K]) for every D in [-min(K, 4096), min(K, 4096)] and every D of
+    extra_D (all within [-K, K])."""
+    kind, bound = oracle.bn_rule(a, g, b, mu, var, eps, K)
+    N = a.shape[0]
+    span = min(K, 4096)
+    Ds = np.unique(np.concatenate([np.arange(-span, span + 1, dtype=np.int64),
+                                   np.asarray(extra_D, np.int64).reshape(-1)]))
+    assert np.abs(Ds).max() <= K
+    D = np.broadcast_to(Ds[:, None], (Ds.size, N))
+    got = _fold_decisions(tau, d, D)
+    want = oracle.rule_signs(kind, bound, D)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} decisions differ; first (D, channel) {[(int(Ds[i]), int(n)) for i, n in bad[:5]]}"
+    # tau is an integer-valued float (exact comparisons)
+    assert np.all(tau == np.rint(tau))
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_fold_bn_thresholds_exact_on_every_mlp_channel(layer):
+    """The binary MLP's three hidden layers (4096 channels each, K = 4096):
+    the fold's threshold rule equals the exact BatchNorm decision for every
+    channel and every D in [-K, K] ("Binary Neural Network (BNN)" glossary,
+    BatchNorm; "Extreme Quantization" eq. (4))."""
     import xnor_popcount_gemm_amd as bnn
-    for seed in (2001, 2002, 2003):
-        N = 4096
-        g, b, mu, var, eps = workloads.bn_params(seed, N)
-        rng = np.random.default_rng(seed)
-        g = g * np.where(rng.random(N) < 0.1, -1, 1).astype(np.float32)
-        g[:3] = 0.0
-        mu = rng.normal(0, 2, N).astype(np.float32)
-        var = (rng.random(N) * 3 + 0.01).astype(np.float32)
-        a = (rng.random(N) + 0.1).astype(np.float32)
-        a[5] = 0.0
-        t1, d1 = bnn.fold_bn_thresholds(g, b, mu, var, eps, a)
-        t2, d2 = oracle.bn_fold(g, b, mu, var, eps, a)
-        np.testing.assert_array_equal(d1, d2)
-        np.testing.assert_array_equal(t1.view(np.uint32), t2.view(np.uint32))
+    h = workloads.WORKLOADS[2]["hidden"]
+    Wh = workloads.normal_f32(workloads.seed_for(2, 2 + layer), (h, h))
+    a = oracle.alpha(Wh)
+    g, b, mu, var, eps = workloads.bn_params(workloads.seed_for(2, 10 + layer), h)
+    tau, d = bnn.fold_bn_thresholds(g, b, mu, var, eps, a)
+    _check_fold_against_rule(tau, d, a, g, b, mu, var, eps, h)
+
+
+def _hard_channels():
+    """Channels built to be hard for a threshold fold: exact ties reached
+    through a rational square root, boundaries off the data range, zero and
+    negative slopes, tiny and huge magnitudes."""
+    f = np.float32
+    rows = [  # alpha, gamma, beta, mean, var, eps
+        (0.5, 1.0, -1.0, 0.0, 1.0, 0.0),          # tie at D = 2
+        (0.5, -1.0, -1.0, 0.0, 1.0, 0.0),         # tie at D = -2, negative slope
+        (0.5, 2.0, -2.0, 0.0, 2.25, 0.0),         # sd = 1.5, tie at D = 3
+        (0.25, 1.0, 0.0, 1.5, 2.25, 0.0),         # tie at D = 6 through the mean
+        (0.25, -3.0, 0.0, 1.5, 0.0, 0.0625),      # sd = 0.25 from eps alone
+        (0.5, 0.0, 0.3, 0.0, 1.0, 1e-5),          # gamma = 0: constant +1
+        (0.0, 1.0, 0.2, 1.0, 1.0, 0.0),           # alpha = 0: constant -1
+        (0.0, 1.0, 0.0, 0.0, 1.0, 0.0),           # BN = 0 for every D: +1
+        (1e-30, 1.0, 0.0, 1e10, 1.0, 0.0),        # boundary far above 2^24: never +1
+        (1e-30, -1.0, 0.0, 1e10, 1.0, 0.0),       # ... negative slope: always +1
+        (2.0**-20, 1.0, -1.0, 0.0, 1.0, 0.0),     # boundary at 2^20
+        (2.0**-24, 1.0, -1.0, 0.0, 1.0, 0.0),     # boundary at 2^24 exactly
+        (2.0**-24, 1.0, -1.0, 2.0**-24, 1.0, 0.0),  # boundary at 2^24 + 1: never within range
+        (3.0, 1.0, 0.0, 3.0 * 16777216.0, 1.0, 0.0),  # boundary at 2^24 via the mean
+        (1.0, 1.0, 1e8, 0.0, 1.0, 0.0),           # boundary far below -2^24: always +1
+        (1e-45, 1e-45, 1e-45, 1e-45, 1e-45, 1e-45),  # denormals everywhere
+        (3e38, 3e38, -3e38, 3e38, 3e38, 0.0),     # near the top of the range
+        (0.7, 1.3, -0.9, 1e-3, 1e-6, 1e-5),       # ordinary values
+    ]
+    cols = list(zip(*rows))
+    a, g, b, mu, var = (np.array(c, np.float32) for c in cols[:5])
+    eps_vals = np.array(cols[5], np.float32)
+    return a, g, b, mu, var, eps_vals
+
+
+def test_fold_bn_thresholds_exact_on_hard_channels():
+    import xnor_popcount_gemm_amd as bnn
+    a, g, b, mu, var, eps_vals = _hard_channels()
+    K = 1 << 24        # the largest |D| the library produces
+    big = [K, K - 1, K - 2, -K, -K + 1, -K + 2, 1 << 20, (1 << 20) - 1, (1 << 20) + 1]
+    for n in range(a.shape[0]):       # eps is per call: one channel at a time
+        sl = slice(n, n + 1)
+        tau, d = bnn.fold_bn_thresholds(g[sl], b[sl], mu[sl], var[sl], eps_vals[n], a[sl])
+        _check_fold_against_rule(tau, d, a[sl], g[sl], b[sl], mu[sl], var[sl], eps_vals[n], K, extra_D=big)
+
+
+def test_fold_bn_thresholds_random_wide_parameters():
+    import xnor_popcount_gemm_amd as bnn
+    rng = np.random.default_rng(2001)
+    N = 4096
+    g, b, mu, var, eps = workloads.bn_params(2001, N)
+    g = g * np.where(rng.random(N) < 0.1, -1, 1).astype(np.float32)
+    g[:3] = 0.0
+    mu = (rng.normal(0, 1, N) * 10.0 ** rng.integers(-3, 4, N)).astype(np.float32)
+    var = (rng.random(N) * 3 + 0.01).astype(np.float32)
+    a = (rng.random(N) + 0.1).astype(np.float32)
+    a[5] = 0.0
+    tau, d = bnn.fold_bn_thresholds(g, b, mu, var, eps, a)
+    _check_fold_against_rule(tau, d, a, g, b, mu, var, eps, 2048)
+
+
+def test_fold_bn_thresholds_errors():
+    import xnor_popcount_gemm_amd as bnn
+    f = lambda *v: np.array(v, np.float32)
+    one = f(1.0)
+    with pytest.raises(bnn.BnnError) as e:
+        bnn.fold_bn_thresholds(one, one, one, f(0.0), 0.0, one)        # var + eps = 0
+    assert e.value.status == ERR_UNSUPPORTED
+    with pytest.raises(bnn.BnnError) as e:
+        bnn.fold_bn_thresholds(one, one, one, f(-2.0), 1.0, one)       # var + eps < 0
+    assert e.value.status == ERR_UNSUPPORTED
+    for bad in (np.inf, np.nan):
+        with pytest.raises(bnn.BnnError) as e:
+            bnn.fold_bn_thresholds(f(bad), one, one, one, 0.0, one)
+        assert e.value.status == ERR_UNSUPPORTED
+    with pytest.raises(bnn.BnnError) as e:
+        bnn.fold_bn_thresholds(one, one, one, one, np.inf, one)
+    assert e.value.status == ERR_UNSUPPORTED
+    L = bnn.lib()
+    fp = ctypes.c_float(0.0)
+    assert L.bnn_fold_bn_thresholds_host(None, None, None, None, fp, None, 0, None, None) == ERR_NULL
+    assert L.bnn_fold_bn_thresholds_host(A16, A16, A16, A16, fp, A16, -1, A16, A16) == ERR_SHAPE

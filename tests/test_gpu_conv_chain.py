@@ -76,17 +76,19 @@ def test_conv3x3_fused_matches_explicit(bnn, B, H, W, C, Cout):
     banner(f"conv3x3 implicit B={B} H={H} W={W} C={C} Cout={Cout}")
     Ximg = bnn.pack_activations_rsign(dev(X.reshape(M, C)), dev(beta))
     Wp, ad = bnn.pack_weights(dev(np.ascontiguousarray(Wt.reshape(Cout, 9 * C))))
-    out = bnn.conv3x3_fused(Ximg, Wp, (B, H, W, C), bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32, alpha=ad)
+    # the oracle's alpha drives the GPU epilogue; the GPU's alpha is checked apart
+    out = bnn.conv3x3_fused(Ximg, Wp, (B, H, W, C), bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32, alpha=dev(a))
     torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(ad).view(np.uint32), a.view(np.uint32))
     np.testing.assert_array_equal(host(out["D"]), D_ref)
-    _bits_equal(host(out["Y"]), oracle.scale(D_ref, host(ad)), "Y")
-    # thresholds (BatchNorm fold) on the implicit path too
+    _bits_equal(host(out["Y"]), oracle.scale(D_ref, a), "Y")
+    # BatchNorm + sign on the implicit path too (the library's fold of the oracle's alpha)
     g, b, mu, var, eps = workloads.bn_params(10103 + C, Cout)
-    tau, dirv = oracle.bn_fold(g, b, mu, var, eps, host(ad))
+    tau, dirv = bnn.fold_bn_thresholds(g, b, mu, var, eps, a)
     th = bnn.conv3x3_fused(Ximg, Wp, (B, H, W, C), bnn.EPI_THRESH_PACK, tau=dev(tau), dir=dev(dirv))
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(host_u32(th["Op"]),
-                                  oracle.pack_signs(oracle.threshold_signs(D_ref, tau, dirv), ld=th["Op"].shape[1]))
+    s_ref, _ = oracle.bn_next_sign(D_ref, a, g, b, mu, var, eps)
+    np.testing.assert_array_equal(host_u32(th["Op"]), oracle.pack_signs(s_ref, ld=th["Op"].shape[1]))
 
 
 @pytest.mark.parametrize("tn", [8, 16, 32, 64])
@@ -123,10 +125,12 @@ def test_dense_sign_pack_epilogue(bnn):
     bt = _beta(10302, N)
     Xp = bnn.pack_activations(dev(X))
     Wp, ad = bnn.pack_weights(dev(W))
+    a_ref = oracle.alpha(W)
     banner("dense sign-pack")
-    out = bnn.linear_fused(Xp, Wp, K, bnn.EPI_SCALE_F32 | bnn.EPI_SIGN_PACK, alpha=ad, beta=dev(bt))
+    out = bnn.linear_fused(Xp, Wp, K, bnn.EPI_SCALE_F32 | bnn.EPI_SIGN_PACK, alpha=dev(a_ref), beta=dev(bt))
     torch.cuda.synchronize()
-    Y_ref = oracle.scale(oracle.dot(oracle.sign(X), oracle.sign(W)), host(ad))
+    np.testing.assert_array_equal(host(ad).view(np.uint32), a_ref.view(np.uint32))
+    Y_ref = oracle.scale(oracle.dot(oracle.sign(X), oracle.sign(W)), a_ref)
     _bits_equal(host(out["Y"]), Y_ref, "Y")
     np.testing.assert_array_equal(host_u32(out["Op"]), oracle.pack_signs(oracle.rsign(Y_ref, bt), ld=out["Op"].shape[1]))
 

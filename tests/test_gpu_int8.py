@@ -208,9 +208,8 @@ def test_bwn_i8_gemv_every_row_step_count(bnn, u, monkeypatch):
     rows, the bound |D| <= sum |q| holds on every row."""
     monkeypatch.setenv("BNN_GEMV_U", u)
     N, K = 65541, 4096
-    g = torch.Generator(device="cuda")
-    g.manual_seed(7900)
-    Wp = torch.randint(-2**31, 2**31 - 1, (N, K // 32), dtype=torch.int32, device="cuda", generator=g)
+    Wh = workloads.random_words(7900, (N, K // 32))
+    Wp = dev(Wh.view(np.int32))
     X = _act_rows(7901, 1, K)
     Q, xs = oracle.quantize_absmax_i8(X)
     a = workloads.uniform01_f32(7902, (N,)) + np.float32(0.5)
@@ -222,7 +221,7 @@ def test_bwn_i8_gemv_every_row_step_count(bnn, u, monkeypatch):
     d, y = host(out["D"])[0], host(out["Y"])[0]
     rows = np.unique(np.concatenate([np.arange(8), np.arange(N - 8, N),
                                      np.random.default_rng(7903).integers(0, N, 384)]))
-    D_ref = oracle.dot_i8(Q, oracle.unpack_signs(host_u32(Wp)[rows], K))
+    D_ref = oracle.dot_i8(Q, oracle.unpack_signs(Wh[rows], K))
     np.testing.assert_array_equal(d[rows], D_ref[0])
     Y_ref = oracle.scale_i8(D_ref, a[rows], xs)
     _bits_equal(y[rows][None, :], Y_ref, "Y")

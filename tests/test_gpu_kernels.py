@@ -181,17 +181,16 @@ def test_gemv_every_row_step_count(bnn, u, monkeypatch):
     monkeypatch.setenv("BNN_GEMV_U", u)
     N, K = 32773, 16384
     kw = K // 32
-    g = torch.Generator(device="cuda")
-    g.manual_seed(530)
-    Wp = torch.randint(-2**31, 2**31 - 1, (N, kw), dtype=torch.int32, device="cuda", generator=g)
-    Xp = torch.randint(-2**31, 2**31 - 1, (1, kw), dtype=torch.int32, device="cuda", generator=g)
+    Wh = workloads.random_words(530, (N, kw))
+    Xh = workloads.random_words(532, (1, kw))
+    Wp, Xp = dev(Wh.view(np.int32)), dev(Xh.view(np.int32))
     banner(f"xnor_gemv U={u} N={N} K={K}")
     D, _ = bnn.xnor_gemm(Xp, Wp, K)
     torch.cuda.synchronize()
     d = host(D)[0]
     rows = np.unique(np.concatenate([np.arange(8), np.arange(N - 8, N),
                                      np.random.default_rng(531).integers(0, N, 384)]))
-    want = oracle.dot(oracle.unpack_signs(host_u32(Xp), K), oracle.unpack_signs(host_u32(Wp)[rows], K))[0]
+    want = oracle.dot(oracle.unpack_signs(Xh, K), oracle.unpack_signs(Wh[rows], K))[0]
     np.testing.assert_array_equal(d[rows], want)
     assert np.all(np.abs(d) <= K) and np.all((d - K) % 2 == 0)
 
@@ -277,7 +276,7 @@ def test_fused_threshold_pack(bnn, M, N, K):
     Wp, a = bnn.pack_weights(dev(W))
     Xp = bnn.pack_activations(dev(X))
     a_ref = oracle.alpha(W)
-    tau, d = oracle.bn_fold(g, b, mu, var, eps, a_ref)   # the same tau/dir feed both sides
+    tau, d = bnn.fold_bn_thresholds(g, b, mu, var, eps, a_ref)   # the library's fold of the oracle's alpha
     ldo = bnn.padded_ld(N) + 4
     Op = torch.full((M, ldo), -1, dtype=torch.int32, device="cuda")
     out = bnn.linear_fused(Xp, Wp, K, bnn.EPI_THRESH_PACK | bnn.EPI_DOT_I32,
@@ -285,8 +284,9 @@ def test_fused_threshold_pack(bnn, M, N, K):
     torch.cuda.synchronize()
     D_ref = oracle.dot(oracle.sign(X), oracle.sign(W))
     np.testing.assert_array_equal(host(out["D"]), D_ref)
-    want = oracle.pack_signs(oracle.threshold_signs(D_ref, tau, d), ld=ldo)
-    np.testing.assert_array_equal(host_u32(Op), want)
+    s_ref, _ = oracle.bn_next_sign(D_ref, a_ref, g, b, mu, var, eps)   # BatchNorm then sign, exactly
+    np.testing.assert_array_equal(host_u32(Op), oracle.pack_signs(s_ref, ld=ldo))
+    np.testing.assert_array_equal(host(a).view(np.uint32), a_ref.view(np.uint32))
 
 
 @pytest.mark.parametrize("tn", ["8", "16", "32", "64"])
@@ -296,7 +296,8 @@ def test_fused_threshold_pack_every_column_tile(bnn, tn, M, N, K):
     g, b, mu, var, eps = workloads.bn_params(751 + N, N)
     Wp, a = bnn.pack_weights(dev(W))
     Xp = bnn.pack_activations(dev(X))
-    tau, d = oracle.bn_fold(g, b, mu, var, eps, oracle.alpha(W))
+    a_ref = oracle.alpha(W)
+    tau, d = bnn.fold_bn_thresholds(g, b, mu, var, eps, a_ref)
     ldo = bnn.padded_ld(N) + 4
     Op = torch.full((M, ldo), -1, dtype=torch.int32, device="cuda")
     old = os.environ.get("BNN_GEMM_TN")
@@ -311,7 +312,8 @@ def test_fused_threshold_pack_every_column_tile(bnn, tn, M, N, K):
         else:
             os.environ["BNN_GEMM_TN"] = old
     D_ref = oracle.dot(oracle.sign(X), oracle.sign(W))
-    np.testing.assert_array_equal(host_u32(Op), oracle.pack_signs(oracle.threshold_signs(D_ref, tau, d), ld=ldo))
+    s_ref, _ = oracle.bn_next_sign(D_ref, a_ref, g, b, mu, var, eps)
+    np.testing.assert_array_equal(host_u32(Op), oracle.pack_signs(s_ref, ld=ldo))
 
 
 @pytest.mark.parametrize("tn", ["8", "16", "32", "64"])
@@ -335,8 +337,10 @@ def test_fused_epilogue_every_column_tile(bnn, tn, M, N, K):
         else:
             os.environ["BNN_GEMM_TN"] = old
     D_ref = oracle.dot(oracle.sign(X), oracle.sign(W))
+    a_ref = oracle.alpha(W)
     np.testing.assert_array_equal(host(out["D"]), D_ref)
-    np.testing.assert_array_equal(host(out["Y"]), oracle.scale_residual(D_ref, host(a), R))
+    np.testing.assert_array_equal(host(a).view(np.uint32), a_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(out["Y"]), oracle.scale_residual(D_ref, a_ref, R))
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 64, 576), (50, 256, 2304), (2, 64, 576), (129, 70, 333)])
@@ -355,8 +359,9 @@ def test_fused_scale_residual(bnn, M, N, K):
     Y_ref = oracle.scale_residual(D_ref, a_ref, R)
     scale = np.abs(a_ref[None, :] * D_ref) + np.abs(R)
     assert_f32_close(host(out["Y"]), Y_ref, scale=scale, what="Y residual")
-    # with the GPU's own alpha the result is exact
-    np.testing.assert_array_equal(host(out["Y"]), oracle.scale_residual(D_ref, host(a), R))
+    # alpha and Y are in fact bit-exact
+    np.testing.assert_array_equal(host(a).view(np.uint32), a_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(out["Y"]).view(np.uint32), Y_ref.view(np.uint32))
 
 
 def test_fused_residual_in_place(bnn):
@@ -370,7 +375,9 @@ def test_fused_residual_in_place(bnn):
     bnn.linear_fused(Xp, Wp, K, bnn.EPI_SCALE_F32 | bnn.EPI_RESIDUAL_F32, alpha=a, R=Rd, Y=Rd)
     torch.cuda.synchronize()
     D_ref = oracle.dot(oracle.sign(X), oracle.sign(W))
-    np.testing.assert_array_equal(host(Rd), oracle.scale_residual(D_ref, host(a), R))
+    a_ref = oracle.alpha(W)
+    np.testing.assert_array_equal(host(a).view(np.uint32), a_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(Rd), oracle.scale_residual(D_ref, a_ref, R))
 
 
 # ---------------------------------------------------------------- FP first / last layers

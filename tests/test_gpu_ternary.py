@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import require_gpu, banner, dev, host, host_u32, assert_f32_close
+from gpu_util import require_gpu, banner, dev, host, host_u32
 
 pytestmark = pytest.mark.gpu
 
@@ -57,13 +57,13 @@ def test_pack_weights_ternary(bnn, N, K, mode):
     if mode == "roundclip":
         Wf = W.copy()
         Wf[~np.isfinite(Wf)] = 0.0                  # a finite gamma
+        gam = oracle.alpha_tensor(Wf)               # the oracle's gamma feeds the GPU pack
         Wd = dev(Wf)
-        g = bnn.weight_scale_tensor(Wd)
-        Sp, Zp, nnz = bnn.pack_weights_ternary(Wd, gamma=g)
+        Sp, Zp, nnz = bnn.pack_weights_ternary(Wd, gamma=dev(np.array([gam], np.float32)))
+        g_gpu = bnn.weight_scale_tensor(Wd)         # and the GPU's own gamma is checked apart
         torch.cuda.synchronize()
-        gam = float(host(g)[0])
-        assert_f32_close(np.float32(gam), oracle.alpha_tensor(Wf), what="gamma")
-        T = oracle.ternary_roundclip(Wf, gam)       # the same gamma on both sides
+        np.testing.assert_array_equal(host(g_gpu).view(np.uint32), np.array([gam], np.float32).view(np.uint32))
+        T = oracle.ternary_roundclip(Wf, gam)
     else:
         delta = {"threshold": 0.5, "threshold_zero": 0.0, "threshold_neg": -0.25}[mode]
         Sp, Zp, nnz = bnn.pack_weights_ternary(Wd, delta=delta)
@@ -77,12 +77,16 @@ def test_pack_weights_ternary(bnn, N, K, mode):
 
 # ---------------------------------------------------------------- ternary x binary activations
 def _ternary_case(bnn, seed, N, K):
+    """Ternary weights from the oracle's gamma (eq. (9)): the GPU packs with
+    that gamma; the GPU's own gamma is checked against it bit for bit."""
     W = _weights(seed, N, K, edges=False)
+    gam = oracle.alpha_tensor(W)
     Wd = dev(W)
-    g = bnn.weight_scale_tensor(Wd)
+    g = dev(np.array([gam], np.float32))
     Sp, Zp, nnz = bnn.pack_weights_ternary(Wd, gamma=g)
+    g_gpu = bnn.weight_scale_tensor(Wd)
     torch.cuda.synchronize()
-    gam = np.float32(host(g)[0])
+    np.testing.assert_array_equal(host(g_gpu).view(np.uint32), np.array([gam], np.float32).view(np.uint32))
     T = oracle.ternary_roundclip(W, gam)
     return T, gam, Sp, Zp, nnz, g
 
@@ -105,7 +109,7 @@ def test_ternary_binary_linear_fused(bnn, M, N, K):
     bias = workloads.normal_f32(9400 + N, (N,))
     gma, beta, mean, var, eps = workloads.bn_params(9500 + N, N)
     alpha_vec = np.full(N, gam, np.float32)
-    tau, dirv = oracle.bn_fold(gma, beta, mean, var, eps, alpha_vec)
+    tau, dirv = bnn.fold_bn_thresholds(gma, beta, mean, var, eps, alpha_vec)
     f = bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32 | bnn.EPI_ALPHA_TENSOR | bnn.W_TERNARY
     banner(f"ternary x binary fused M={M} N={N} K={K}")
     out = bnn.linear_fused(Xp, Sp, K, f | bnn.EPI_BIAS_F32 | bnn.EPI_RESIDUAL_F32, alpha=g, bias=dev(bias),
@@ -116,8 +120,8 @@ def test_ternary_binary_linear_fused(bnn, M, N, K):
     np.testing.assert_array_equal(host(out["D"]), D_ref)
     _bits_equal(host(out["Y"]), oracle.scale_bias_residual(D_ref, np.atleast_1d(gam), bias, R), "Y")
     ld = th["Op"].shape[1]
-    np.testing.assert_array_equal(host_u32(th["Op"]),
-                                  oracle.pack_signs(oracle.threshold_signs(D_ref, tau, dirv), ld=ld))
+    s_ref, _ = oracle.bn_next_sign(D_ref, alpha_vec, gma, beta, mean, var, eps)
+    np.testing.assert_array_equal(host_u32(th["Op"]), oracle.pack_signs(s_ref, ld=ld))
 
 
 @pytest.mark.parametrize("tn", [8, 16, 32, 64])
@@ -183,10 +187,10 @@ def test_ternary_b158_decode_chain(bnn):
         out = bnn.bwn_i8_linear(Sp, K, bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32 | bnn.EPI_ALPHA_TENSOR | bnn.W_TERNARY,
                                 Xb=q["Xb"], xscale=q["xscale"], alpha=g, Zp=Zp)
         torch.cuda.synchronize()
-        gam = np.float32(host(g)[0])
+        gam = oracle.alpha_tensor(W)          # the oracle's own chain, end to end
         T = oracle.ternary_roundclip(W, gam)
         Q, xs = oracle.quantize_absmax_i8(X)
         D_ref = oracle.dot_i8(Q, T)
+        np.testing.assert_array_equal(host(g).view(np.uint32), np.array([gam], np.float32).view(np.uint32))
         np.testing.assert_array_equal(host(out["D"]), D_ref)
         _bits_equal(host(out["Y"]), oracle.scale_i8(D_ref, np.atleast_1d(gam), xs), "Y")
-        assert_f32_close(gam, oracle.alpha_tensor(W), what="gamma")

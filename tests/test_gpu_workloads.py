@@ -1,10 +1,12 @@
 """GPU parity on the five workloads at their full sizes, against the CPU oracle.
 
-Where the oracle cannot compute every output in seconds, sampled rows are
-compared element by element (first/last rows, rows at 256-row tile
-boundaries and seeded random rows), and every output is checked for the
-properties that hold at any size (D = K mod 2, |D| <= K, Y = fl32(alpha*D)).
-The launch configurations are the ones ``bench.py`` times."""
+Every output is compared element by element with the oracle: packed
+operands, int32 dot products and alpha-scaled fp32 outputs bit-exact, the
+binary MLP's packed BatchNorm-then-sign outputs against the oracle's exact
+decisions.  The properties that hold at any size (D = K mod 2, |D| <= K) are
+checked as well.  The launch configurations are the ones ``bench.py`` times.
+The largest case (16384^3) costs the oracle about half a minute on 16 host
+threads."""
 from __future__ import annotations
 
 import numpy as np
@@ -26,14 +28,15 @@ def bnn():
     return m
 
 
-def _sample_rows(M, seed, n_random=6):
-    rng = np.random.default_rng(seed)
-    rows = {0, 1, M - 1, M - 2}
-    for b in (255, 256, 257, 4095, 4096, 8191, 8192):
-        if b < M:
-            rows.add(b)
-    rows.update(int(r) for r in rng.integers(0, M, n_random))
-    return np.array(sorted(rows))
+def _equal(got: np.ndarray, want: np.ndarray, what: str):
+    """Element-by-element equality of two large arrays (bit patterns for
+    floats), reporting the count and the first mismatches."""
+    if got.dtype == np.float32:
+        got, want = got.view(np.uint32), np.asarray(want, np.float32).view(np.uint32)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)
+        raise AssertionError(f"{what}: {len(bad)} of {got.size} differ; first {bad[:5].tolist()}")
 
 
 def _check_dot_properties(D: torch.Tensor, K: int):
@@ -93,6 +96,9 @@ def run_mlp_gpu(bnn, X, W1, hidden, W5):
 
 
 def test_workload2_binary_mlp(bnn):
+    """The library path (GPU alpha -> host BatchNorm fold -> THRESH_PACK) against
+    the oracle's BatchNorm-then-sign decided exactly from its definition
+    ("Binary Neural Network (BNN)" glossary; "Extreme Quantization" eq. (4))."""
     X, W1, hidden, W5 = _mlp_inputs()
     banner("workload2 binary MLP batch 1024")
     acts, alphas, taus, logits = run_mlp_gpu(bnn, X, W1, hidden, W5)
@@ -106,11 +112,12 @@ def test_workload2_binary_mlp(bnn):
     assert int((np.abs(h1) <= bound).sum()) == 0, "first-layer near-ties present"
     for i, act in enumerate(acts):
         want = oracle.pack_signs(ref["signs"][i], ld=act.shape[1])
-        np.testing.assert_array_equal(host_u32(act), want, err_msg=f"layer {i + 1} packed signs")
+        if i > 0:
+            margin = float(ref["bn_margins"][i - 1].min())
+            print(f"[workload2] layer {i + 1}: smallest |BN(alpha D)| of any output {margin:.3g}", flush=True)
+        _equal(host_u32(act), want, f"layer {i + 1} packed signs")
         if i < len(alphas):
-            np.testing.assert_array_equal(host(alphas[i]).view(np.uint32), ref["alphas"][i].view(np.uint32))
-            np.testing.assert_array_equal(taus[i][0].view(np.uint32), ref["taus"][i].view(np.uint32))
-            np.testing.assert_array_equal(taus[i][1], ref["dirs"][i])
+            _equal(host(alphas[i]), ref["alphas"][i], f"layer {i + 2} alpha")
     W5sum = np.abs(W5).sum(axis=1)[None, :]
     assert_f32_close(host(logits), ref["logits"], scale=1e-3 * W5sum, what="logits")
 
@@ -157,7 +164,8 @@ def test_workload3_gemv_streaming_stack(bnn, shape):
 
 # ---------------------------------------------------------------- workload 4
 @pytest.mark.parametrize("shape", workloads.WORKLOADS[4]["shapes"], ids=lambda s: f"M{s['M']}")
-def test_workload4_large_gemm_sampled(bnn, shape):
+def test_workload4_large_gemm_full(bnn, shape):
+    """Every element of D, Y and both packed operands against the oracle."""
     M, N, K = shape["M"], shape["N"], shape["K"]
     X = workloads.normal_f32(workloads.seed_for(4, 0) + M, (M, K))
     W = workloads.normal_f32(workloads.seed_for(4, 1) + M, (N, K))
@@ -169,26 +177,26 @@ def test_workload4_large_gemm_sampled(bnn, shape):
     D, Y = bnn.xnor_gemm(Xp, Wp, K, alpha=a, want_scaled=True)
     torch.cuda.synchronize()
     _check_dot_properties(D, K)
-    assert bool((Y == a[None, :] * D.to(torch.float32)).all()), "Y != fl32(alpha * D)"
-    rows = _sample_rows(M, 4242 + M)
-    ws = oracle.sign(W)
+    Dh, Yh, Xph, Wph, ah = host(D), host(Y), host_u32(Xp), host_u32(Wp), host(a)
+    del D, Y, Xp, Wp
+    torch.cuda.empty_cache()
+    banner(f"workload4 oracle M={M} N={N} K={K} on {oracle.num_threads()} threads")
+    xs, ws = oracle.sign(X), oracle.sign(W)
+    del X
+    _equal(Wph, oracle.pack_signs(ws, ld=Wph.shape[1]), "packed W")
+    _equal(Xph, oracle.pack_signs(xs, ld=Xph.shape[1]), "packed X")
     a_ref = oracle.alpha(W)
-    np.testing.assert_array_equal(host(a).view(np.uint32), a_ref.view(np.uint32))
-    D_ref = oracle.dot(oracle.sign(X[rows]), ws)
-    np.testing.assert_array_equal(host(D[torch.from_numpy(rows).cuda()]), D_ref)
-    Y_ref = oracle.scale(D_ref, a_ref)
-    np.testing.assert_array_equal(host(Y[torch.from_numpy(rows).cuda()]).view(np.uint32), Y_ref.view(np.uint32))
-    # packed operands: sampled rows bit-exact
-    np.testing.assert_array_equal(host_u32(Xp[torch.from_numpy(rows).cuda()]),
-                                  oracle.pack_signs(oracle.sign(X[rows]), ld=Xp.shape[1]))
-    cols = _sample_rows(N, 77 + N)
-    np.testing.assert_array_equal(host_u32(Wp[torch.from_numpy(cols).cuda()]),
-                                  oracle.pack_signs(ws[cols], ld=Wp.shape[1]))
+    _equal(ah, a_ref, "alpha")
+    D_ref = oracle.dot(xs, ws)
+    del xs, ws
+    _equal(Dh, D_ref, "D")
+    _equal(Yh, oracle.scale(D_ref, a_ref), "Y")
 
 
 # ---------------------------------------------------------------- workload 5
 @pytest.mark.parametrize("shape", workloads.WORKLOADS[5]["shapes"], ids=lambda s: f"H{s['H']}_C{s['C']}")
-def test_workload5_conv_block_sampled_images(bnn, shape):
+def test_workload5_conv_block_full(bnn, shape):
+    """All 256 images: the packed im2col matrix, D and Y = fl32(fl32(alpha D) + R)."""
     B, H, Wd, C, Co = shape["B"], shape["H"], shape["W"], shape["C"], shape["Cout"]
     X = workloads.normal_f32(workloads.seed_for(5, 0) + C, (B, H, Wd, C))
     Wt = workloads.normal_f32(workloads.seed_for(5, 1) + C, (Co, 3, 3, C))
@@ -198,15 +206,15 @@ def test_workload5_conv_block_sampled_images(bnn, shape):
     Wp, a = bnn.pack_weights(dev(Wt.reshape(Co, K)))
     Xp = bnn.pack_activations(Xd, conv3x3=True)
     R = Xd.reshape(B * H * Wd, C)
+    # the launch the benchmark times (Y only), then the same GEMM with D as well
     out = bnn.linear_fused(Xp, Wp, K, bnn.EPI_SCALE_F32 | bnn.EPI_RESIDUAL_F32, alpha=a, R=R)
+    out_d = bnn.linear_fused(Xp, Wp, K, bnn.EPI_DOT_I32, alpha=a)
     torch.cuda.synchronize()
-    Y = out["Y"]
-    a_ref = oracle.alpha(Wt.reshape(Co, K))
-    np.testing.assert_array_equal(host(a).view(np.uint32), a_ref.view(np.uint32))
-    P = H * Wd
-    for b in (0, 1, B - 1):
-        Db, Yb, _ = oracle.conv_block(X[b:b + 1], Wt)
-        sl = slice(b * P, (b + 1) * P)
-        np.testing.assert_array_equal(host(Y[sl]).view(np.uint32), Yb.view(np.uint32), err_msg=f"image {b}")
-        want_p = oracle.pack_signs(oracle.im2col_signs(X[b:b + 1]), ld=Xp.shape[1])
-        np.testing.assert_array_equal(host_u32(Xp[sl]), want_p, err_msg=f"im2col image {b}")
+    _check_dot_properties(out_d["D"], K)
+    Dh, Yh, Xph, ah = host(out_d["D"]), host(out["Y"]), host_u32(Xp), host(a)
+    banner(f"workload5 oracle B={B} H={H} W={Wd} C={C}")
+    D_ref, Y_ref, a_ref = oracle.conv_block(X, Wt)
+    _equal(ah, a_ref, "alpha")
+    _equal(Dh, D_ref, "D")
+    _equal(Yh, Y_ref, "Y")
+    _equal(Xph, oracle.pack_signs(oracle.im2col_signs(X), ld=Xph.shape[1]), "packed im2col")

@@ -9,6 +9,7 @@ accepts would mean the pins do not constrain that part of the oracle.
 """
 from __future__ import annotations
 
+import importlib.util
 import os
 import tempfile
 
@@ -18,6 +19,7 @@ import oracle
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
+BN_SRC = os.path.join(os.path.dirname(SRC), "batchnorm.py")
 
 MUTATIONS = [
     ("sign: zero maps to -1",
@@ -50,15 +52,6 @@ MUTATIONS = [
     ("residual: fused multiply-add",
      "float z = alpha[n] * (float)D[m * N + n];\n            Y[m * N + n] = z + R[m * ldr + n];",
      "Y[m * N + n] = fmaf(alpha[n], (float)D[m * N + n], R[m * ldr + n]);"),
-    ("bn fold: sign of beta flipped",
-     "double rhs = (double)gamma[n] * (double)mean[n] - (double)beta[n] * sd;",
-     "double rhs = (double)gamma[n] * (double)mean[n] + (double)beta[n] * sd;"),
-    ("bn fold: negative direction not flipped",
-     "tau[n] = (float)(-(rhs / c));", "tau[n] = (float)(rhs / c);"),
-    ("bn fold: eps ignored",
-     "double sd = sqrt((double)var[n] + (double)eps);", "double sd = sqrt((double)var[n]);"),
-    ("threshold: strict comparison at the tie",
-     "s_out[m * N + n] = (v >= tau[n])", "s_out[m * N + n] = (v > tau[n])"),
     ("im2col: pad pixels encode -1",
      "int8_t v = 1;\n                    if (inside)", "int8_t v = -1;\n                    if (inside)"),
     ("im2col: tap order transposed",
@@ -129,13 +122,38 @@ MUTATIONS = [
 ]
 
 
+# Mistakes planted in the exact BatchNorm + sign module (oracle/batchnorm.py).
+BN_MUTATIONS = [
+    ("bn: strict comparison at the tie",
+     "return u * u >= b * b * self.s", "return u * u > b * b * self.s"),
+    ("bn: zero sum with zero beta read as negative",
+     "if u >= 0 and b >= 0:", "if u > 0 and b >= 0:"),
+    ("bn: eps ignored",
+     'self.s = _exact(var, "var") + _exact(eps, "eps")', 'self.s = _exact(var, "var")'),
+    ("bn: sign of beta flipped",
+     "        b = self.b\n        if u >= 0", "        b = -self.b\n        if u >= 0"),
+    ("bn: mean added instead of subtracted",
+     "u = self.g * (self.a * int(D) - self.mu)\n        b = self.b",
+     "u = self.g * (self.a * int(D) + self.mu)\n        b = self.b"),
+    ("bn: negative slope treated as positive",
+     "if ch.slope_sign > 0:       # decisions False", "if ch.slope_sign != 0:      # decisions False"),
+    ("bn rule: boundary of a negative slope off by one",
+     "-K + _first_true(lambda d: not ch.nonneg(d), ints) - 1", "-K + _first_true(lambda d: not ch.nonneg(d), ints)"),
+    ("bn: margin from one side of the boundary only",
+     "for j in (i - 1, i) if", "for j in (i,) if"),
+]
+_BN_NAMES = ("bn_next_sign", "bn_rule", "bn_value", "rule_signs")
+
+
 def _pin_calls():
     """The pin suite; parametrized pins run with their own parameter lists
-    (the random-K identity with a representative subset)."""
+    (the random-K identity with a representative subset).  The full-size pins
+    (test_full_*) are left out of the sweep for time; smaller pins cover the
+    same code."""
     calls = []
     for name in sorted(dir(pins)):
         fn = getattr(pins, name)
-        if not (name.startswith("test_") and callable(fn)):
+        if not (name.startswith("test_") and callable(fn)) or name.startswith("test_full_"):
             continue
         marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
         if not marks:
@@ -184,4 +202,31 @@ def test_each_planted_mistake_fails_a_pin(workdir, label, old, new):
                 failed.append(name)
     finally:
         oracle.use_library(None)
+    assert failed, f"no pin caught the planted mistake: {label}"
+
+
+@pytest.mark.parametrize("label,old,new", BN_MUTATIONS, ids=[m[0] for m in BN_MUTATIONS])
+def test_each_planted_batchnorm_mistake_fails_a_pin(workdir, label, old, new):
+    src = open(BN_SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique or missing: {label}"
+    tag = "".join(ch if ch.isalnum() else "_" for ch in label)
+    path = os.path.join(workdir, f"{tag}.py")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"bn_mutant_{tag}", path)
+    mutant = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mutant)
+    saved = {n: getattr(oracle, n) for n in _BN_NAMES}
+    failed = []
+    try:
+        for n in _BN_NAMES:
+            setattr(oracle, n, getattr(mutant, n))
+        for name, call in _pin_calls():
+            try:
+                call()
+            except Exception:
+                failed.append(name)
+    finally:
+        for n, v in saved.items():
+            setattr(oracle, n, v)
     assert failed, f"no pin caught the planted mistake: {label}"

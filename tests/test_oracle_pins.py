@@ -235,72 +235,166 @@ def test_scale_residual_two_roundings():
             assert f32_bits(Y[m, n]) == f32_bits(want)
 
 
-# ---------------------------------------------------------------- BatchNorm fold
-def _exact_bn_sign(D, a, g, b, mu, var, eps):
-    """sign(BN(alpha*D)) decided exactly: BN >= 0  iff  g*(a*D - mu) >= -b*sd,
-    sd = sqrt(var + eps), decided by squaring with sign cases."""
-    a, g, b, mu = (Fraction(float(v)) for v in (a, g, b, mu))
-    v2 = Fraction(float(var)) + Fraction(float(eps))
-    L = g * (a * D - mu)
-    R0 = -b          # right side is R0 * sd, sd > 0
-    if R0 <= 0 and L >= 0:
-        return 1
-    if R0 >= 0 and L < 0:
-        return -1
-    if R0 > 0:       # L >= 0: L >= R0*sd  iff  L^2 >= R0^2 v2
-        return 1 if L * L >= R0 * R0 * v2 else -1
-    # R0 < 0, L < 0: L >= R0*sd  iff  |L| <= |R0| sd  iff  L^2 <= R0^2 v2
-    return 1 if L * L <= R0 * R0 * v2 else -1
+# ---------------------------------------------------------------- BatchNorm + sign
+# Page "Binary Neural Network (BNN)" glossary (BatchNorm around the binary
+# layers) and page "Extreme Quantization", eq. (4) (the next layer takes the
+# sign, +1 for >= 0).  The oracle decides sign(BN(alpha D)) exactly; these pins
+# check it against an evaluation of the formula in 80-digit decimal arithmetic
+# (square root included, no rearrangement) and against closed-form ties.
+def _bn_decimal(D, a, g, b, mu, var, eps, digits=80):
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = digits
+        q = lambda v: Decimal(float(np.float32(v)))          # exact value of the fp32
+        sd = (q(var) + q(eps)).sqrt()
+        return q(g) * (q(a) * int(D) - q(mu)) / sd + q(b)
 
 
-def test_bn_fold_exact_ties_and_directions():
-    one = np.ones(1, np.float32)
-    zero = np.zeros(1, np.float32)
-    # gamma=1, alpha=0.5, beta=-1, mean=0, var=1, eps=0: BN = 0.5 D - 1, tie at D=2
-    tau, d = oracle.bn_fold(one, -one, zero, one, 0.0, 0.5 * one)
-    assert d[0] == 1 and tau[0] == 2.0
-    D = np.array([[1], [2], [3]], np.int32)          # M=3 rows, one channel
-    np.testing.assert_array_equal(oracle.threshold_signs(D, tau, d)[:, 0], [-1, 1, 1])
+def _decided_sign(D, a, g, b, mu, var, eps):
+    """+1 / -1 from the decimal value; None when it is too close to call
+    (the 80-digit evaluation is good to ~1e-75 relative to the terms)."""
+    v = _bn_decimal(D, a, g, b, mu, var, eps)
+    scale = abs(float(g) * float(a) * D) + abs(float(g) * float(mu)) + abs(float(b)) + 1e-300
+    if abs(v) <= scale * 1e-70:
+        return None
+    return 1 if v > 0 else -1
+
+
+def test_bn_sign_closed_form_ties_and_directions():
+    f = np.float32
+    col = lambda *v: np.array(v, np.int32)[:, None]
+    # gamma=1, alpha=0.5, beta=-1, mean=0, var=1, eps=0: BN = 0.5 D - 1, tie at D=2 -> +1
+    s, m = oracle.bn_next_sign(col(1, 2, 3), f(0.5), f(1), f(-1), f(0), f(1), f(0))
+    assert s[:, 0].tolist() == [-1, 1, 1] and m[0] == 0.0
     # gamma=-1: BN = -0.5 D - 1 >= 0 iff D <= -2 (tie at -2 -> +1)
-    tau, d = oracle.bn_fold(-one, -one, zero, one, 0.0, 0.5 * one)
-    assert d[0] == -1
-    D = np.array([[-3], [-2], [-1]], np.int32)
-    np.testing.assert_array_equal(oracle.threshold_signs(D, tau, d)[:, 0], [1, 1, -1])
-    # gamma=0: constant sign of beta
+    s, _ = oracle.bn_next_sign(col(-3, -2, -1), f(0.5), f(-1), f(-1), f(0), f(1), f(0))
+    assert s[:, 0].tolist() == [1, 1, -1]
+    # gamma=0: the constant sign of beta (beta=0 is a tie -> +1)
     for beta, want in ((0.3, 1), (-0.3, -1), (0.0, 1)):
-        tau, d = oracle.bn_fold(zero, beta * one, zero, one, 1e-5, 0.5 * one)
-        assert d[0] == 0
-        got = oracle.threshold_signs(np.array([[-7], [0], [9]], np.int32), tau, d)[:, 0]
-        np.testing.assert_array_equal(got, [want] * 3)
-    # alpha=0 (all-zero weight row): BN(0) = beta - gamma*mean/sd
-    tau, d = oracle.bn_fold(one, 0.2 * one, one, one, 0.0, zero)
-    assert d[0] == 0
-    assert oracle.threshold_signs(np.array([[5]], np.int32), tau, d)[0, 0] == -1
-    # eps enters sd = sqrt(var + eps): var=0, eps=4 -> sd=2, BN = 0.5 D - 2, tie at D=4
-    tau, d = oracle.bn_fold(one, -one, zero, zero, 4.0, 0.5 * one)
-    assert d[0] == 1 and tau[0] == 4.0
-    D = np.array([[2], [3], [4], [5]], np.int32)
-    np.testing.assert_array_equal(oracle.threshold_signs(D, tau, d)[:, 0], [-1, -1, 1, 1])
+        s, _ = oracle.bn_next_sign(col(-7, 0, 9), f(0.5), f(0), f(beta), f(0), f(1), f(1e-5))
+        assert s[:, 0].tolist() == [want] * 3
+    # alpha=0 (all-zero weight row): BN = beta - gamma*mean/sd = 0.2 - 1 < 0
+    s, _ = oracle.bn_next_sign(col(5, -5), f(0), f(1), f(0.2), f(1), f(1), f(0))
+    assert s[:, 0].tolist() == [-1, -1]
+    # eps enters sd = sqrt(var + eps): var=0, eps=4 -> sd=2, BN = 0.5 D/2 - 1, tie at D=4
+    s, _ = oracle.bn_next_sign(col(2, 3, 4, 5), f(0.5), f(1), f(-1), f(0), f(0), f(4))
+    assert s[:, 0].tolist() == [-1, -1, 1, 1]
+    # the mean shifts the tie: BN = (0.25 D - 1.5)/1.5 + 0 -> tie at D = 6
+    s, _ = oracle.bn_next_sign(col(5, 6, 7), f(0.25), f(1), f(0), f(1.5), f(2.25), f(0))
+    assert s[:, 0].tolist() == [-1, 1, 1]
+    # a tie reached through sqrt: var+eps = 2.25 -> sd = 1.5; BN = 2(0.5 D - 0)/1.5 - 2 -> tie at D = 3
+    s, _ = oracle.bn_next_sign(col(2, 3, 4), f(0.5), f(2), f(-2), f(0), f(2.25), f(0))
+    assert s[:, 0].tolist() == [-1, 1, 1]
+
+
+def test_bn_sign_rejects_undefined_parameters():
+    f = np.float32
+    D = np.zeros((1, 1), np.int32)
+    with pytest.raises(ValueError):        # sqrt(var + eps) = 0
+        oracle.bn_next_sign(D, f(1), f(1), f(0), f(0), f(0), f(0))
+    with pytest.raises(ValueError):
+        oracle.bn_next_sign(D, f(1), f(np.inf), f(0), f(0), f(1), f(0))
+
+
+def _bn_random_channels(seed, N):
+    rng = np.random.default_rng(seed)
+    g, b, mu, var, eps = workloads.bn_params(seed, N)
+    g = g * np.where(np.arange(N) % 5 == 0, -1, 1).astype(np.float32)   # both directions
+    g[7] = 0.0
+    mu = rng.normal(0, 3, N).astype(np.float32)
+    var = (rng.random(N) * 2 + 0.1).astype(np.float32)
+    a = (rng.random(N) + 0.2).astype(np.float32)
+    a[11] = 0.0
+    return a, g, b, mu, var, eps
 
 
 @pytest.mark.parametrize("eps_scale", [1.0, 1e4])
-def test_bn_fold_decisions_match_exact_rational(eps_scale):
-    rng = np.random.default_rng(12)
-    N = 64
-    g, b, mu, var, eps = workloads.bn_params(2001, N)
-    eps = np.float32(eps * eps_scale)        # 1e-5, and 0.1 where eps moves the thresholds
-    g = g * np.where(np.arange(N) % 5 == 0, -1, 1).astype(np.float32)   # both directions
-    mu = (rng.normal(0, 3, N)).astype(np.float32)
-    var = (rng.random(N) * 2 + 0.1).astype(np.float32)
-    a = (rng.random(N) + 0.2).astype(np.float32)
-    tau, d = oracle.bn_fold(g, b, mu, var, eps, a)
-    # D values around every threshold, both parities
-    Dn = np.rint(tau.astype(np.float64) * d).astype(np.int64)
-    D = (Dn[None, :] + np.arange(-3, 4)[:, None]).astype(np.int32)
-    s = oracle.threshold_signs(D, tau, d)
-    for i in range(D.shape[0]):
+def test_bn_sign_matches_decimal_evaluation(eps_scale):
+    N = 48
+    a, g, b, mu, var, eps = _bn_random_channels(12, N)
+    eps = np.float32(eps * eps_scale)        # 1e-5, and 0.1 where eps moves the boundaries
+    K = 64
+    rng = np.random.default_rng(13)
+    D = rng.integers(-K, K + 1, size=(40, N)).astype(np.int32)
+    s, margin = oracle.bn_next_sign(D, a, g, b, mu, var, eps)
+    undecided = 0
+    for m in range(D.shape[0]):
         for n in range(N):
-            assert s[i, n] == _exact_bn_sign(int(D[i, n]), a[n], g[n], b[n], mu[n], var[n], eps), (i, n)
+            want = _decided_sign(int(D[m, n]), a[n], g[n], b[n], mu[n], var[n], eps)
+            if want is None:
+                undecided += 1
+                continue
+            assert s[m, n] == want, (m, n)
+    assert undecided == 0
+    for n in range(N):   # the reported margin is the smallest |BN| of the column
+        mins = min(abs(float(_bn_decimal(int(d), a[n], g[n], b[n], mu[n], var[n], eps))) for d in D[:, n])
+        assert margin[n] == pytest.approx(mins, rel=1e-12, abs=1e-300)
+
+
+def test_bn_rule_boundaries_by_decimal_evaluation():
+    """Each channel's integer boundary: the decimal value changes sign there."""
+    N = 48
+    a, g, b, mu, var, eps = _bn_random_channels(14, N)
+    K = 200
+    kind, bound = oracle.bn_rule(a, g, b, mu, var, eps, K)
+    for n in range(N):
+        args = (a[n], g[n], b[n], mu[n], var[n], eps)
+        if kind[n] == 0:
+            assert g[n] == 0 or a[n] == 0
+            assert all(_decided_sign(d, *args) == bound[n] for d in (-K, 0, K))
+        elif kind[n] > 0:
+            if -K < bound[n] <= K:
+                assert _decided_sign(int(bound[n]), *args) == 1
+                assert _decided_sign(int(bound[n]) - 1, *args) == -1
+        else:
+            if -K <= bound[n] < K:
+                assert _decided_sign(int(bound[n]), *args) == 1
+                assert _decided_sign(int(bound[n]) + 1, *args) == -1
+    # the rule applied to every D agrees with the per-output decisions
+    Dall = np.broadcast_to(np.arange(-K, K + 1, dtype=np.int32)[:, None], (2 * K + 1, N))
+    s, _ = oracle.bn_next_sign(Dall, a, g, b, mu, var, eps)
+    np.testing.assert_array_equal(oracle.rule_signs(kind, bound, Dall), s)
+
+
+def test_bn_brute_force_tiny_layer():
+    """Every decision of a small binary layer against the decimal value."""
+    rng = np.random.default_rng(15)
+    M, N, K = 12, 14, 37
+    xs, ws = _rand_signs(rng, (M, K)), _rand_signs(rng, (N, K))
+    D = oracle.dot(xs, ws)
+    a, g, b, mu, var, eps = _bn_random_channels(16, N)
+    mu = (a * rng.integers(-3, 4, N)).astype(np.float32)   # boundaries near the data
+    s, _ = oracle.bn_next_sign(D, a, g, b, mu, var, eps)
+    for m in range(M):
+        for n in range(N):
+            assert s[m, n] == _decided_sign(int(D[m, n]), a[n], g[n], b[n], mu[n], var[n], eps)
+
+
+def _mlp_layer_params(i):
+    c = workloads.WORKLOADS[2]
+    h = c["hidden"]
+    Wh = workloads.normal_f32(workloads.seed_for(2, 2 + i), (h, h))
+    return (oracle.alpha(Wh),) + workloads.bn_params(workloads.seed_for(2, 10 + i), h)
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_full_bn_rule_every_mlp_channel(layer):
+    """The binary MLP's hidden layers (batch 1024, 4096 -> 4096, K = 4096):
+    for every one of the 4096 channels, the oracle's exact boundary is where
+    the 80-digit value of BN(alpha D) changes sign.  Decisions on both sides
+    of each boundary are also far from their ties (reported margin)."""
+    a, g, b, mu, var, eps = _mlp_layer_params(layer)
+    K = workloads.WORKLOADS[2]["hidden"]
+    kind, bound = oracle.bn_rule(a, g, b, mu, var, eps, K)
+    assert (kind == 1).all()              # gamma > 0 and alpha > 0 on every channel
+    closest = np.inf
+    for n in range(K):
+        args = (a[n], g[n], b[n], mu[n], var[n], eps)
+        hi = _bn_decimal(int(bound[n]), *args)
+        lo = _bn_decimal(int(bound[n]) - 1, *args)
+        assert hi >= 0 > lo, n
+        closest = min(closest, float(hi), -float(lo))
+    assert closest > 1e-6, f"a decision lies within {closest:.3g} of its tie"
 
 
 # ---------------------------------------------------------------- conv im2col
@@ -401,7 +495,7 @@ def test_mlp_chain_small_composition():
         np.testing.assert_array_equal(r["dots"][i], D)
         for m in range(0, 16, 5):
             for n in range(64):
-                want = _exact_bn_sign(int(D[m, n]), r["alphas"][i][n], g[n], b[n], mu[n], var[n], eps)
+                want = _decided_sign(int(D[m, n]), r["alphas"][i][n], g[n], b[n], mu[n], var[n], eps)
                 assert r["signs"][i + 1][m, n] == want
         s = r["signs"][i + 1]
     assert r["logits"].shape == (16, 10)

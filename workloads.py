@@ -14,7 +14,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "normal_f32", "uniform01_f32", "bn_params", "edge_values", "inject_edge_values",
+    "normal_f32", "uniform01_f32", "random_words", "bn_params", "edge_values", "inject_edge_values",
     "WORKLOADS", "seed_for",
 ]
 
@@ -31,6 +31,12 @@ def normal_f32(seed: int, shape) -> np.ndarray:
 def uniform01_f32(seed: int, shape) -> np.ndarray:
     """fp32 samples of U(0, 1)."""
     return np.random.default_rng(seed).random(shape, dtype=np.float32)
+
+
+def random_words(seed: int, shape) -> np.ndarray:
+    """Uniformly random 32-bit words (uint32): packed operands with every bit
+    pattern, for cases where the bits themselves are the input."""
+    return np.random.default_rng(seed).integers(0, 2**32, size=shape, dtype=np.uint32)
 
 
 def bn_params(seed: int, n: int):

@@ -400,32 +400,6 @@ bnn_status bnn_bwn_i8_linear(const bnn_i8_args* args, bnn_stream_t stream)
                                             args->M, args->N, args->K, e, s));
 }
 
-bnn_status bnn_fold_bn_thresholds_host(const float* gamma, const float* beta,
-                                       const float* mean, const float* var, float eps,
-                                       const float* alpha, int64_t N, float* tau, int8_t* dir)
-{
-    if (N < 0) return BNN_ERR_SHAPE;
-    if (N == 0) return BNN_OK;
-    if (!gamma || !beta || !mean || !var || !alpha || !tau || !dir) return BNN_ERR_NULL;
-    for (int64_t n = 0; n < N; ++n) {
-        const double sd = sqrt((double)var[n] + (double)eps);
-        const double c = (double)gamma[n] * (double)alpha[n];
-        const double rhs = (double)gamma[n] * (double)mean[n] - (double)beta[n] * sd;
-        if (c > 0.0) {
-            dir[n] = 1;
-            tau[n] = (float)(rhs / c);
-        } else if (c < 0.0) {
-            dir[n] = -1;
-            tau[n] = (float)(-(rhs / c));
-        } else {
-            const double bn0 = (double)beta[n] - (double)gamma[n] * (double)mean[n] / sd;
-            dir[n] = 0;
-            tau[n] = bn0 >= 0.0 ? 0.0f : 1.0f;
-        }
-    }
-    return BNN_OK;
-}
-
 bnn_status bnn_dense_f32_sign_pack(const float* X, int64_t ldX, const float* W, int64_t ldW,
                                    int64_t M, int64_t N, int64_t K,
                                    uint32_t* Op, int64_t ldOp, bnn_stream_t stream)
