@@ -31,7 +31,9 @@
  *    means nothing was launched and no memory was touched.  BNN_ERR_HIP means
  *    the HIP runtime refused a launch.  Faults inside kernels surface at the
  *    caller's next synchronization.
- *  - No global mutable state: calls may be issued from several host threads.
+ *  - No global mutable state, except the per-GPU scratch array of
+ *    bnn_weight_scale_tensor_noalloc: calls may be issued from several host
+ *    threads (that one entry point's calls must not overlap on one GPU).
  *  - Sizes: 1 <= K <= 2^24 (so every dot product is exact as an fp32 and an
  *    int32).  M == 0 or N == 0 is a valid empty call (nothing launched); its
  *    pointers are validated like those of any other call (non-null, aligned),
@@ -282,6 +284,23 @@ bnn_status bnn_pack_weights_ternary(const float* W, int64_t N, int64_t K, int64_
  *  N >= 1.  Errors: NULL -> BNN_ERR_NULL; sizes -> BNN_ERR_SHAPE / _LD. */
 bnn_status bnn_weight_scale_tensor(const float* W, int64_t N, int64_t K, int64_t ldW,
                                    double* work, float* alpha, bnn_stream_t stream);
+
+/* The same scale as bnn_weight_scale_tensor with no workspace argument and
+ * no allocation, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The N per-row partial sums live in a static device array of
+ * BNN_NOALLOC_MAX_ROWS doubles (512 KiB), one per GPU, held until the
+ * process ends; its address is looked up once per device, on the first call
+ * made with that device current.  Every call on a GPU uses that GPU's one
+ * array: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be ordered by the caller.  Each call writes all N partial
+ * sums before reading them, so nothing from an earlier call is read.
+ *  W fp32 [N, ldW] (ldW >= K, 4-byte aligned); alpha: device fp32 [1].
+ *  1 <= N <= BNN_NOALLOC_MAX_ROWS, else BNN_ERR_SHAPE; NULL -> BNN_ERR_NULL;
+ *  BNN_ERR_HIP if the array's device address cannot be obtained. */
+#define BNN_NOALLOC_MAX_ROWS 65536
+bnn_status bnn_weight_scale_tensor_noalloc(const float* W, int64_t N, int64_t K, int64_t ldW,
+                                           float* alpha, bnn_stream_t stream);
 
 /* Quantize fp32 activations to INT8, one scale per row, [P5] "BitNet"
  * item 2 (activations at INT8; the quantizer is not given there, this is

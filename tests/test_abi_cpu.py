@@ -370,3 +370,18 @@ def test_fold_bn_thresholds_errors():
     fp = ctypes.c_float(0.0)
     assert L.bnn_fold_bn_thresholds_host(None, None, None, None, fp, None, 0, None, None) == ERR_NULL
     assert L.bnn_fold_bn_thresholds_host(A16, A16, A16, A16, fp, A16, -1, A16, A16) == ERR_SHAPE
+
+
+def test_weight_scale_tensor_noalloc_validation(L):
+    f = L.bnn_weight_scale_tensor_noalloc      # W, N, K, ldW, alpha, stream
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    lim = 1 << 16
+    assert f(A16, lim + 1, 64, 64, A16, None) == ERR_SHAPE      # beyond the static scratch
+    assert f(A16, 0, 64, 64, A16, None) == ERR_SHAPE
+    assert f(A16, 4, 0, 64, A16, None) == ERR_SHAPE
+    assert f(0, 4, 64, 64, A16, None) == ERR_NULL
+    assert f(A16, 4, 64, 64, 0, None) == ERR_NULL
+    assert f(A16, 4, 64, 63, A16, None) == ERR_LD
+    assert f(A2, 4, 64, 64, A16, None) == ERR_ALIGN
+    assert f(A16, 4, 64, 64, A2, None) == ERR_ALIGN

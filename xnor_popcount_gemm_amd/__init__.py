@@ -25,7 +25,7 @@ __all__ = [
     "xnor_gemm", "linear_fused", "fold_bn_thresholds", "dense_f32_sign_pack",
     "dense_binact_f32", "EPI_DOT_I32", "EPI_SCALE_F32", "EPI_RESIDUAL_F32",
     "EPI_THRESH_PACK", "EPI_ALPHA_TENSOR", "EPI_BIAS_F32", "LIB_PATH",
-    "weight_scale_tensor", "quantize_act_i8", "pack_act_i8", "bwn_i8_linear", "MAX_K_I8",
+    "weight_scale_tensor", "weight_scale_tensor_noalloc", "NOALLOC_MAX_ROWS", "quantize_act_i8", "pack_act_i8", "bwn_i8_linear", "MAX_K_I8",
     "W_TERNARY", "pack_weights_ternary", "EPI_SIGN_PACK", "pack_activations_rsign", "conv3x3_fused",
 ]
 
@@ -40,6 +40,7 @@ EPI_BIAS_F32 = 32
 W_TERNARY = 64
 EPI_SIGN_PACK = 128
 MAX_K_I8 = 1 << 17
+NOALLOC_MAX_ROWS = 1 << 16
 
 _STATUS = {
     0: "BNN_OK", 1: "BNN_ERR_NULL", 2: "BNN_ERR_SHAPE", 3: "BNN_ERR_LD",
@@ -118,6 +119,7 @@ def lib() -> ctypes.CDLL:
             "bnn_dense_f32_sign_pack": [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp],
             "bnn_dense_binact_f32": [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp],
             "bnn_weight_scale_tensor": [_vp, _i64, _i64, _i64, _vp, _vp, _vp],
+            "bnn_weight_scale_tensor_noalloc": [_vp, _i64, _i64, _i64, _vp, _vp],
             "bnn_quantize_act_i8": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp],
             "bnn_pack_act_i8": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
             "bnn_bwn_i8_linear": [ctypes.POINTER(_I8Args), _vp],
@@ -368,6 +370,19 @@ def weight_scale_tensor(W: torch.Tensor, *, out: torch.Tensor | None = None) -> 
     _check(lib().bnn_weight_scale_tensor(_ptr(W), N, K, _ld(W), _ptr(work), _ptr(a),
                                          _stream(W.device)), "bnn_weight_scale_tensor")
     return a
+
+
+def weight_scale_tensor_noalloc(W: torch.Tensor, *, out: torch.Tensor) -> torch.Tensor:
+    """The scale of weight_scale_tensor through the entry point that allocates
+    nothing: the caller passes the output, the library's static per-GPU
+    scratch holds the row sums (N <= NOALLOC_MAX_ROWS; overlapping calls on
+    one GPU race)."""
+    _dev(W, torch.float32, "W")
+    _dev(out, torch.float32, "out")
+    N, K = W.shape
+    _check(lib().bnn_weight_scale_tensor_noalloc(_ptr(W), N, K, _ld(W), _ptr(out), _stream(W.device)),
+           "bnn_weight_scale_tensor_noalloc")
+    return out
 
 
 def i8_ld(K: int) -> int:

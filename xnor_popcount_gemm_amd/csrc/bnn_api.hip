@@ -4,8 +4,17 @@
 // documented (with their sources on the pages) in include/bnn.h.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "bnn.h"
 #include "bnn_launch.hpp"
+
+// Device scratch of bnn_weight_scale_tensor_noalloc: one fp64 partial sum per
+// weight row.  Each GPU holds its own copy for the life of the process; host
+// code reaches it only through the address hipGetSymbolAddress returns for
+// that device (the array's name in host code is a host-side stand-in).
+static __device__ __align__(256) double scratch[BNN_NOALLOC_MAX_ROWS];
 
 namespace {
 
@@ -348,6 +357,49 @@ bnn_status bnn_weight_scale_tensor(const float* W, int64_t N, int64_t K, int64_t
     if (ldW < K) return BNN_ERR_LD;
     if (misaligned4(W) || misaligned4(alpha) || (reinterpret_cast<uintptr_t>(work) & 7u) != 0)
         return BNN_ERR_ALIGN;
+    return from_hip(bnn::launch_alpha_tensor(W, N, K, ldW, work, alpha, as_stream(stream)));
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<double*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch array's device address on the current device, looked up once
+// per device (with that device current) and kept; nullptr on failure.
+double* scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    double* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void* addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+        p = static_cast<double*>(addr);
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
+bnn_status bnn_weight_scale_tensor_noalloc(const float* W, int64_t N, int64_t K, int64_t ldW,
+                                           float* alpha, bnn_stream_t stream)
+{
+    bnn_status st;
+    if ((st = check_rows(N)) != BNN_OK) return st;
+    if ((st = check_k(K)) != BNN_OK) return st;
+    if (N < 1 || N > BNN_NOALLOC_MAX_ROWS) return BNN_ERR_SHAPE;
+    if (!W || !alpha) return BNN_ERR_NULL;
+    if (ldW < K) return BNN_ERR_LD;
+    if (misaligned4(W) || misaligned4(alpha)) return BNN_ERR_ALIGN;
+    double* work = scratch_on_current_device();
+    if (!work) return BNN_ERR_HIP;
+    // every row's partial sum is written before the second pass reads it, so
+    // the scratch needs no clearing between calls
     return from_hip(bnn::launch_alpha_tensor(W, N, K, ldW, work, alpha, as_stream(stream)));
 }
 
