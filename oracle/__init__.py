@@ -82,6 +82,7 @@ def _configure(L):
         "oracle_unpack_signs": [_p, _i64, _i64, _i64, _p],
         "oracle_alpha": [_p, _i64, _i64, _i64, _p],
         "oracle_dot": [_p, _p, _i64, _i64, _i64, _p],
+        "oracle_dot_packed": [_p, _i64, _p, _i64, _i64, _i64, _i64, _p],
         "oracle_scale": [_p, _p, _i64, _i64, _p],
         "oracle_scale_residual": [_p, _p, _p, _i64, _i64, _i64, _p],
         "oracle_im2col_signs": [_p, _i64, _i64, _i64, _i64, _p],
@@ -171,6 +172,20 @@ def dot(xs: np.ndarray, ws: np.ndarray) -> np.ndarray:
     assert K == K2
     D = np.empty((M, N), dtype=np.int32)
     lib().oracle_dot(_ptr(xs), _ptr(ws), M, N, K, _ptr(D))
+    return D
+
+
+def dot_packed(xw: np.ndarray, ww: np.ndarray, K: int) -> np.ndarray:
+    """D = K - 2 sum popcount(x xor w) over packed rows (the identity of
+    "First Principles" section "1. Arithmetic" / "Extreme Quantization"
+    eq. (6)); CPU-baseline context, not an expected-value source."""
+    xw = _c(xw, np.uint32)
+    ww = _c(ww, np.uint32)
+    M, ldx = xw.shape
+    N, ldw = ww.shape
+    assert min(ldx, ldw) >= (K + 31) // 32
+    D = np.empty((M, N), dtype=np.int32)
+    lib().oracle_dot_packed(_ptr(xw), ldx, _ptr(ww), ldw, M, N, K, _ptr(D))
     return D
 
 

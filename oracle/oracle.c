@@ -104,6 +104,27 @@ API void oracle_dot(const int8_t* xs, const int8_t* ws, int64_t M, int64_t N, in
     }
 }
 
+/* [P2] section "1. Arithmetic" and [P5] eq. (6): the same dot products
+ * through the packed identity, D = K - 2 * sum_w popcount(x_w xor w_w) over
+ * the Kw = ceil(K/32) words of each packed row (pad bits equal on both
+ * operands contribute nothing).  Not used for any expected value: it is
+ * timed next to oracle_dot as context for the CPU baseline, and pinned to
+ * oracle_dot by the tests.  xw is [M, ldx] words, ww is [N, ldw] words. */
+__attribute__((target("popcnt")))
+API void oracle_dot_packed(const uint32_t* xw, int64_t ldx, const uint32_t* ww, int64_t ldw,
+                           int64_t M, int64_t N, int64_t K, int32_t* D)
+{
+    const int64_t Kw = (K + 31) / 32;
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t ones = 0;
+            for (int64_t w = 0; w < Kw; ++w)
+                ones += __builtin_popcount(xw[m * ldx + w] ^ ww[n * ldw + w]);
+            D[m * N + n] = (int32_t)(K - 2 * ones);
+        }
+}
+
 /* [P5] eq. (1): y = alpha * (w_b^T x_b), one rounded single multiply. */
 API void oracle_scale(const int32_t* D, const float* alpha, int64_t M, int64_t N, float* Y)
 {

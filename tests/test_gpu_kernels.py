@@ -171,6 +171,59 @@ def test_xnor_gemm_every_wave_count(bnn, waves, M, N, K, monkeypatch):
     np.testing.assert_array_equal(host(Y), (host(a)[None, :] * host(D).astype(np.float32)).astype(np.float32))
 
 
+@pytest.mark.parametrize("epi", ["direct", "staged"])
+@pytest.mark.parametrize("tn", ["8", "16", "32", "64"])
+@pytest.mark.parametrize("M,N,K", [(300, 128, 576), (257, 192, 2304), (130, 64, 4200), (70, 96, 100)])
+def test_xnor_gemm_every_epilogue_mode(bnn, epi, tn, M, N, K, monkeypatch):
+    """The two epilogue modes (BNN_GEMM_EPI: from registers, staged through
+    LDS) on every column tile, with D, Y = fl32(fl32(alpha D) + bias) + R; K tails of
+    an 8-word chunk (576: 16 + 2, 4200: 128 + 8 + 2 words) and of single
+    granules.  The oracle's alpha drives the epilogue."""
+    monkeypatch.setenv("BNN_GEMM_EPI", epi)
+    monkeypatch.setenv("BNN_GEMM_TN", tn)
+    X, W = _packed_pair(M, N, K, 560 + M + K)
+    R = workloads.normal_f32(561 + K, (M, N))
+    bias = workloads.normal_f32(562 + N, (N,))
+    a_ref = oracle.alpha(W)
+    Wp, _ = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    banner(f"xnor_gemm epilogue={epi} TN={tn} M={M} N={N} K={K}")
+    out = bnn.linear_fused(Xp, Wp, K, bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32 | bnn.EPI_BIAS_F32 | bnn.EPI_RESIDUAL_F32,
+                           alpha=dev(a_ref), bias=dev(bias), R=dev(R))
+    plain = bnn.linear_fused(Xp, Wp, K, bnn.EPI_SCALE_F32, alpha=dev(a_ref))
+    torch.cuda.synchronize()
+    D_ref = oracle.dot(oracle.sign(X), oracle.sign(W))
+    np.testing.assert_array_equal(host(out["D"]), D_ref)
+    np.testing.assert_array_equal(host(out["Y"]).view(np.uint32),
+                                  oracle.scale_bias_residual(D_ref, a_ref, bias, R).view(np.uint32))
+    np.testing.assert_array_equal(host(plain["Y"]).view(np.uint32), oracle.scale(D_ref, a_ref).view(np.uint32))
+
+
+@pytest.mark.parametrize("epi", ["direct", "staged"])
+@pytest.mark.parametrize("C", [64, 128, 256, 512])
+def test_conv3x3_every_epilogue_mode(bnn, epi, C, monkeypatch):
+    """The implicit-im2col conv with each epilogue mode (C = 512: K = 4608,
+    144 words per row)."""
+    monkeypatch.setenv("BNN_GEMM_EPI", epi)
+    B, H, Wd, Co = 2, 5, 7, 96
+    X = workloads.normal_f32(570 + C, (B, H, Wd, C))
+    Wt = workloads.normal_f32(571 + C, (Co, 3, 3, C))
+    R = workloads.normal_f32(572 + C, (B * H * Wd, Co))
+    M, K = B * H * Wd, 9 * C
+    Wf = np.ascontiguousarray(Wt.reshape(Co, K))
+    a_ref = oracle.alpha(Wf)
+    S = oracle.sign(X.reshape(M, C)).reshape(X.shape)
+    D_ref = oracle.dot(oracle.im2col_pm1(S), oracle.sign(Wf))
+    Ximg = bnn.pack_activations(dev(X.reshape(M, C)))
+    Wp, _ = bnn.pack_weights(dev(Wf))
+    banner(f"conv3x3 epilogue={epi} C={C}")
+    out = bnn.conv3x3_fused(Ximg, Wp, (B, H, Wd, C), bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32 | bnn.EPI_RESIDUAL_F32,
+                            alpha=dev(a_ref), R=dev(R))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out["D"]), D_ref)
+    np.testing.assert_array_equal(host(out["Y"]).view(np.uint32), oracle.scale_residual(D_ref, a_ref, R).view(np.uint32))
+
+
 @pytest.mark.parametrize("u", ["1", "2", "4"])
 def test_gemv_every_row_step_count(bnn, u, monkeypatch):
     """The GEMV's row steps per wave (BNN_GEMV_U) on a matrix tall enough that

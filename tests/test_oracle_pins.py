@@ -137,6 +137,17 @@ def test_identity_random_K(K):
         D.astype(np.int64), _popcount_identity(oracle.pack_signs(xs), oracle.pack_signs(ws), K))
 
 
+@pytest.mark.parametrize("K", [1, 31, 32, 33, 100, 1000, 4096])
+def test_packed_identity_routine_equals_dot(K):
+    """The oracle's packed routine (K - 2 popcount(x xor w)) against its plain
+    +1/-1 multiply-add, with wider rows (pad words) on one side."""
+    rng = np.random.default_rng(90 + K)
+    xs, ws = _rand_signs(rng, (7, K)), _rand_signs(rng, (5, K))
+    xw = oracle.pack_signs(xs, ld=(K + 31) // 32 + 4)
+    ww = oracle.pack_signs(ws)
+    np.testing.assert_array_equal(oracle.dot_packed(xw, ww, K), oracle.dot(xs, ws))
+
+
 def test_dot_matches_float64_matmul():
     rng = np.random.default_rng(11)
     for (M, N, K) in ((64, 256, 1000), (7, 9, 4096), (33, 17, 11008)):

@@ -1,7 +1,9 @@
-"""Build libbnn.so (the gfx950 HIP kernels and their C ABI) with hipcc.
+"""Build libbnn.so (the gfx950 HIP kernels and their C ABI) with hipcc, and
+libbnn_calib.so (the VALU issue-rate probes the benchmark runs for its
+roofline; not part of the product library).
 
 Run as ``python -m xnor_popcount_gemm_amd.build``; ``__graft_entry__.build()``
-calls :func:`build`.  The library is built in-tree, next to this file.
+calls :func:`build`.  The libraries are built in-tree, next to this file.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbnn.so")
+CALIB_SRC = os.path.join(HERE, "calib", "valu_rate.hip")
+CALIB_LIB = os.path.join(HERE, "libbnn_calib.so")
 ARCH = "gfx950"
 
 
@@ -47,8 +51,23 @@ def _jobs() -> int:
     return max(1, min(n if n > 0 else (os.cpu_count() or 1), 16))
 
 
+def build_calib(verbose: bool = False) -> str:
+    """Compile the issue-rate probes into libbnn_calib.so."""
+    tmp = CALIB_LIB + ".tmp"
+    cmd = [hipcc()] + [f for f in flags() if not f.startswith("-I")] + ["-shared", CALIB_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    sys.stderr.write(r.stderr)
+    if r.returncode != 0:
+        raise subprocess.CalledProcessError(r.returncode, f"hipcc {CALIB_SRC}", r.stdout, r.stderr)
+    os.replace(tmp, CALIB_LIB)
+    return CALIB_LIB
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip to an object (in parallel), then link libbnn.so."""
+    """Compile every csrc/*.hip to an object (in parallel), then link libbnn.so;
+    then build the probe library."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="bnn_build_") as tmpdir:
@@ -73,6 +92,7 @@ def build(verbose: bool = False) -> str:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_calib(verbose)
     return LIB
 
 
