@@ -196,7 +196,8 @@ def test_workload4_large_gemm_full(bnn, shape):
 # ---------------------------------------------------------------- workload 5
 @pytest.mark.parametrize("shape", workloads.WORKLOADS[5]["shapes"], ids=lambda s: f"H{s['H']}_C{s['C']}")
 def test_workload5_conv_block_full(bnn, shape):
-    """All 256 images: the packed im2col matrix, D and Y = fl32(fl32(alpha D) + R)."""
+    """All 256 images: the packed im2col matrix, the packed sign image, D, and
+    Y = fl32(fl32(alpha D) + R) by the explicit and the implicit im2col."""
     B, H, Wd, C, Co = shape["B"], shape["H"], shape["W"], shape["C"], shape["Cout"]
     X = workloads.normal_f32(workloads.seed_for(5, 0) + C, (B, H, Wd, C))
     Wt = workloads.normal_f32(workloads.seed_for(5, 1) + C, (Co, 3, 3, C))
@@ -206,15 +207,21 @@ def test_workload5_conv_block_full(bnn, shape):
     Wp, a = bnn.pack_weights(dev(Wt.reshape(Co, K)))
     Xp = bnn.pack_activations(Xd, conv3x3=True)
     R = Xd.reshape(B * H * Wd, C)
-    # the launch the benchmark times (Y only), then the same GEMM with D as well
+    # the launches the benchmark times (Y only): explicit im2col + GEMM, and the
+    # packed sign image + implicit-im2col conv; then the GEMM with D as well
     out = bnn.linear_fused(Xp, Wp, K, bnn.EPI_SCALE_F32 | bnn.EPI_RESIDUAL_F32, alpha=a, R=R)
+    img = bnn.pack_activations(R)
+    out_i = bnn.conv3x3_fused(img, Wp, (B, H, Wd, C), bnn.EPI_SCALE_F32 | bnn.EPI_RESIDUAL_F32, alpha=a, R=R)
     out_d = bnn.linear_fused(Xp, Wp, K, bnn.EPI_DOT_I32, alpha=a)
     torch.cuda.synchronize()
     _check_dot_properties(out_d["D"], K)
     Dh, Yh, Xph, ah = host(out_d["D"]), host(out["Y"]), host_u32(Xp), host(a)
+    Yih, imgh = host(out_i["Y"]), host_u32(img)
     banner(f"workload5 oracle B={B} H={H} W={Wd} C={C}")
     D_ref, Y_ref, a_ref = oracle.conv_block(X, Wt)
     _equal(ah, a_ref, "alpha")
     _equal(Dh, D_ref, "D")
     _equal(Yh, Y_ref, "Y")
+    _equal(Yih, Y_ref, "Y (implicit im2col)")
     _equal(Xph, oracle.pack_signs(oracle.im2col_signs(X), ld=Xph.shape[1]), "packed im2col")
+    _equal(imgh, oracle.pack_signs(oracle.sign(X.reshape(B * H * Wd, C)), ld=imgh.shape[1]), "packed image")
