@@ -68,7 +68,11 @@ def test_pack_weights_repeatable(bnn):
 
 
 @pytest.mark.parametrize("M,K,extra_ld", [(64, 1000, 0), (3, 70, 12), (1, 4096, 0), (1, 11008, 0),
-                                          (100, 129, 4), (2, 5, 0)])
+                                          (100, 129, 4), (2, 5, 0),
+                                          # short rows (ld 4 or 8): several rows per wave step,
+                                          # with and without pad words stored apart, ragged row counts
+                                          (1000, 64, 0), (333, 33, 0), (5, 1, 0), (257, 100, 0),
+                                          (130, 256, 0), (77, 200, 0), (65, 60, 4), (3, 128, 4)])
 def test_pack_activations_dense(bnn, M, K, extra_ld):
     X = _signs_with_edges(200 + K, (M, K))
     ld = bnn.padded_ld(K) + extra_ld
@@ -79,10 +83,10 @@ def test_pack_activations_dense(bnn, M, K, extra_ld):
     np.testing.assert_array_equal(host_u32(out), oracle.pack_signs(oracle.sign(X), ld=ld))
 
 
-def test_pack_unaligned_source_rows(bnn):
+@pytest.mark.parametrize("M,K", [(37, 301), (1000, 64), (129, 250)])
+def test_pack_unaligned_source_rows(bnn, M, K):
     # ld of the fp32 source not a multiple of 4 -> the scalar-load path
-    M, K = 37, 301
-    big = workloads.normal_f32(250, (M, K + 3))
+    big = workloads.normal_f32(250 + K, (M, K + 3))
     Xt = dev(big)[:, :K]
     assert Xt.stride(0) == K + 3
     banner("pack_activations scalar path")
@@ -176,9 +180,9 @@ def test_xnor_gemm_every_wave_count(bnn, waves, M, N, K, monkeypatch):
 @pytest.mark.parametrize("M,N,K", [(300, 128, 576), (257, 192, 2304), (130, 64, 4200), (70, 96, 100)])
 def test_xnor_gemm_every_epilogue_mode(bnn, epi, tn, M, N, K, monkeypatch):
     """The two epilogue modes (BNN_GEMM_EPI: from registers, staged through
-    LDS) on every column tile, with D, Y = fl32(fl32(alpha D) + bias) + R; K tails of
-    an 8-word chunk (576: 16 + 2, 4200: 128 + 8 + 2 words) and of single
-    granules.  The oracle's alpha drives the epilogue."""
+    LDS) on every column tile, with D, Y = fl32(fl32(alpha D) + bias) + R; K
+    tails of an 8-word chunk (576: 16 + 2, 4200: 128 + 8 + 2 words) and of
+    single granules.  The oracle's alpha drives the epilogue."""
     monkeypatch.setenv("BNN_GEMM_EPI", epi)
     monkeypatch.setenv("BNN_GEMM_TN", tn)
     X, W = _packed_pair(M, N, K, 560 + M + K)
@@ -199,13 +203,37 @@ def test_xnor_gemm_every_epilogue_mode(bnn, epi, tn, M, N, K, monkeypatch):
     np.testing.assert_array_equal(host(plain["Y"]).view(np.uint32), oracle.scale(D_ref, a_ref).view(np.uint32))
 
 
+@pytest.mark.parametrize("K", [32767, 32768, 40000])
+def test_xnor_gemm_staged_long_rows(bnn, K):
+    """The staged epilogue with rows past 2^15 bits; rows of all +1 or all -1
+    reach |D| = K."""
+    M, N = 130, 64
+    X, W = _packed_pair(M, N, K, 590 + K)
+    X[0, :] = 1.0
+    X[1, :] = -1.0
+    W[0, :] = 1.0
+    a_ref = oracle.alpha(W)
+    Wp, _ = bnn.pack_weights(dev(W))
+    Xp = bnn.pack_activations(dev(X))
+    banner(f"xnor_gemm staged K={K}")
+    out = bnn.linear_fused(Xp, Wp, K, bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32, alpha=dev(a_ref))
+    torch.cuda.synchronize()
+    D_ref = oracle.dot(oracle.sign(X), oracle.sign(W))
+    assert D_ref[0, 0] == K and D_ref[1, 0] == -K
+    np.testing.assert_array_equal(host(out["D"]), D_ref)
+    np.testing.assert_array_equal(host(out["Y"]).view(np.uint32), oracle.scale(D_ref, a_ref).view(np.uint32))
+
+
+@pytest.mark.parametrize("prefetch", ["1", "0"])
 @pytest.mark.parametrize("epi", ["direct", "staged"])
-@pytest.mark.parametrize("C", [64, 128, 256, 512])
-def test_conv3x3_every_epilogue_mode(bnn, epi, C, monkeypatch):
-    """The implicit-im2col conv with each epilogue mode (C = 512: K = 4608,
-    144 words per row)."""
+@pytest.mark.parametrize("C,B,H,Wd,Co", [(64, 2, 5, 7, 96), (128, 2, 5, 7, 96), (256, 2, 5, 7, 96),
+                                         (512, 2, 5, 7, 96), (64, 3, 9, 11, 80), (256, 3, 9, 11, 64)])
+def test_conv3x3_every_epilogue_mode(bnn, epi, prefetch, C, B, H, Wd, Co, monkeypatch):
+    """The implicit-im2col conv with each epilogue mode, with and without the
+    residual prefetch (C = 512: K = 4608, 144 words per row; 297 pixels: two
+    row tiles, the second ragged)."""
     monkeypatch.setenv("BNN_GEMM_EPI", epi)
-    B, H, Wd, Co = 2, 5, 7, 96
+    monkeypatch.setenv("BNN_CONV_PREFETCH", prefetch)
     X = workloads.normal_f32(570 + C, (B, H, Wd, C))
     Wt = workloads.normal_f32(571 + C, (Co, 3, 3, C))
     R = workloads.normal_f32(572 + C, (B * H * Wd, Co))
@@ -216,7 +244,7 @@ def test_conv3x3_every_epilogue_mode(bnn, epi, C, monkeypatch):
     D_ref = oracle.dot(oracle.im2col_pm1(S), oracle.sign(Wf))
     Ximg = bnn.pack_activations(dev(X.reshape(M, C)))
     Wp, _ = bnn.pack_weights(dev(Wf))
-    banner(f"conv3x3 epilogue={epi} C={C}")
+    banner(f"conv3x3 epilogue={epi} prefetch={prefetch} C={C} B={B} H={H} W={Wd} Co={Co}")
     out = bnn.conv3x3_fused(Ximg, Wp, (B, H, Wd, C), bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32 | bnn.EPI_RESIDUAL_F32,
                             alpha=dev(a_ref), R=dev(R))
     torch.cuda.synchronize()

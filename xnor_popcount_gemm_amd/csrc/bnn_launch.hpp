@@ -24,7 +24,10 @@ struct Epilogue {
 };
 
 enum : uint32_t { EPI_DOT = 1u, EPI_SCALE = 2u, EPI_RESIDUAL = 4u, EPI_THRESH = 8u,
-                  EPI_ALPHA_TENSOR = 16u, EPI_BIAS = 32u, W_TERNARY = 64u, EPI_SIGN_PACK = 128u };
+                  EPI_ALPHA_TENSOR = 16u, EPI_BIAS = 32u, W_TERNARY = 64u, EPI_SIGN_PACK = 128u,
+                  // set by the launchers only (never by a caller): touch the residual
+                  // tile at the start of the K loop
+                  EPI_PREFETCH_R = 1u << 30 };
 
 // Epilogue of binary weights x INT8 activations.
 // Compute units of the current device (256 if the query fails).

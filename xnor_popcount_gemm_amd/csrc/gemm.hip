@@ -12,12 +12,7 @@ hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
     // segments (row-per-lane stores from registers write partial lines:
     // 1.29x the algorithmic bytes at 16384^3, and 9% slower at 8192^3).
     // THRESH_PACK stores its bits from registers.
-    int epi = EPI_DIRECT;
-    if ((e.flags & (EPI_DOT | EPI_SCALE)) && !(e.flags & EPI_THRESH)) {
-        epi = EPI_STAGED;
-        const int ov = epilogue_from_env();
-        if (ov >= 0) epi = ov;
-    }
+    const int epi = pick_epilogue(e);
     // Waves per workgroup: all waves of a workgroup read the same TN weight
     // rows through the CU's scalar cache, so bigger workgroups put fewer
     // distinct weight streams on a CU.  Measured on MI355X: 8 waves for
@@ -25,7 +20,7 @@ hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp,
     // otherwise (8 waves lose 8% on the 64-wide tiles of 16384^3 and 15% on
     // the 14x14x256 conv GEMM, K = 2304).
     const int64_t kw = (K + 31) / 32;
-    int waves = (tn == 32 && epi == EPI_STAGED && kw > 128) ? 8 : 4;
+    int waves = (tn == 32 && epi != EPI_DIRECT && kw > 128) ? 8 : 4;
     if (const char* v = getenv("BNN_GEMM_WAVES")) {       // tuning override: 4, 8 or 16
         const int w = atoi(v);
         if (w == 4 || w == 8 || w == 16) waves = w;

@@ -267,41 +267,77 @@ __device__ __forceinline__ void xnor_mainloop(uint32_t (&acc)[TN], const uint32_
 // the CW words of each of its 9 neighbours (tap t = 3 kh + kw; k = t C + c,
 // the layout of the explicit im2col and of OHWI weights).  Taps outside the
 // image are +1, i.e. zero words ("First Principles", section "1.
-// Arithmetic": pad bits encode +1).  toff[t] is the neighbour's word offset
-// or -1 outside.  The 9 CW words run through the same 16-word chunks as the
-// dense loop (TPC = 16/CW taps per chunk; the last 9 CW % 16 words form a
-// short tail chunk); the next chunk's neighbour loads are in flight during
-// the current chunk's VALU work.
+// Arithmetic": pad bits encode +1).  The neighbour of tap t sits at word
+// offset base + (t/3 - 1) rowstep + (t%3 - 1) ldx (the last two terms are
+// uniform, so only base and the in-image bit mask take vector registers).
+// The 9 CW words run through KC-word chunks (TPC = KC/CW taps per chunk;
+// the last 9 CW % KC words form a short tail chunk); the next chunk's
+// neighbour loads are in flight during the current chunk's VALU work.
+struct Taps {
+    int base;        // word offset of the lane's own pixel
+    uint32_t in;     // bit t: tap t lies inside the image
+    int rowstep;     // words per image row (W ldx)
+    int ldx;         // words per pixel
+    __device__ __forceinline__ int off(int t) const { return base + (t / 3 - 1) * rowstep + (t % 3 - 1) * ldx; }
+    __device__ __forceinline__ bool inside(int t) const { return (in >> t) & 1u; }
+};
+// Branch-free: a tap outside the image loads row 0 of the image, and
+// conv_chunk_mask zeroes its words when the chunk is consumed (not at the
+// load, which would wait for the data at once).  Every load is issued on
+// every path, so the waits on the vector-memory counter stay exact (a branch
+// around a load makes the compiler wait for all loads in flight).
 template <int CW>
 __device__ __forceinline__ void conv_chunk_load(uint32_t* a, const uint32_t* __restrict__ Xp,
-                                                const int (&toff)[9], int t0, int ntaps)
+                                                const Taps& tp, int t0, int ntaps)
 {
 #pragma unroll
     for (int t = 0; t < ntaps; ++t) {
-        const int o = toff[t0 + t];
+        const uint32_t* __restrict__ src = Xp + (tp.inside(t0 + t) ? tp.off(t0 + t) : 0);
         if (CW >= 4) {
 #pragma unroll
             for (int q = 0; q < CW / 4; ++q) {
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (o >= 0) v = *reinterpret_cast<const uint4*>(Xp + o + 4 * q);
+                const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * q);
                 a[t * CW + 4 * q] = v.x; a[t * CW + 4 * q + 1] = v.y;
                 a[t * CW + 4 * q + 2] = v.z; a[t * CW + 4 * q + 3] = v.w;
             }
         } else {
-            uint2 v = make_uint2(0u, 0u);
-            if (o >= 0) v = *reinterpret_cast<const uint2*>(Xp + o);
+            const uint2 v = *reinterpret_cast<const uint2*>(src);
             a[t * CW] = v.x; a[t * CW + 1] = v.y;
         }
     }
 }
 
-template <int TN, int CW, bool FULLN>
+template <int CW>
+__device__ __forceinline__ void conv_chunk_mask(uint32_t* a, const Taps& tp, int t0, int ntaps)
+{
+#pragma unroll
+    for (int t = 0; t < ntaps; ++t) {
+        const bool in = tp.inside(t0 + t);
+#pragma unroll
+        for (int i = 0; i < CW; ++i) a[t * CW + i] = in ? a[t * CW + i] : 0u;
+    }
+}
+
+// pfr: the lane's row of the residual tile, touched once per 128-byte line
+// once the last chunk's data has arrived, so the tile streams in during the
+// last chunk's VALU work with no wait placed on it before the epilogue; pf
+// receives the loaded words (to be consumed).  Without a prefetch pfr is any
+// valid word and cmask 0 (the same loads, all of that word): no branch, so
+// the compiler's waits on the vector-memory counter stay exact.
+template <int TN>
+__device__ __forceinline__ void touch_residual(uint32_t& pf, const float* __restrict__ pfr, int cmask) {
+#pragma unroll
+    for (int c = 0; c < TN; c += 32) pf |= __float_as_uint(pfr[c & cmask]);
+}
+
+template <int TN, int CW, int KC, bool FULLN>
 __device__ __forceinline__ void conv_mainloop(uint32_t (&acc)[TN], const uint32_t* __restrict__ Xp,
-                                              const int (&toff)[9], const uint32_t* __restrict__ wbase,
-                                              int64_t ldW, int nlast)
+                                              const Taps& tp, const uint32_t* __restrict__ wbase,
+                                              int64_t ldW, int nlast, uint32_t& pf, const float* __restrict__ pfr,
+                                              int pfmask)
 {
     constexpr int CP = (TN >= 2) ? 2 : 1;
-    constexpr int KC = 16;
+    static_assert(KC % CW == 0, "whole taps per chunk");
     constexpr int TPC = KC / CW;                  // taps per chunk
     constexpr int NCH = 9 / TPC;                  // full chunks
     constexpr int TT = 9 - NCH * TPC;             // taps in the tail chunk
@@ -309,18 +345,23 @@ __device__ __forceinline__ void conv_mainloop(uint32_t (&acc)[TN], const uint32_
     constexpr int TW = TT > 0 ? TT * CW : 1;
     uint32_t t[TW];
     // the tail taps are requested with the first chunk: no exposed load at the end
-    if (TT > 0) conv_chunk_load<CW>(t, Xp, toff, NCH * TPC, TT);
-    if (NCH > 0) conv_chunk_load<CW>(an, Xp, toff, 0, TPC);
+    if (TT > 0) conv_chunk_load<CW>(t, Xp, tp, NCH * TPC, TT);
+    if (NCH > 0) conv_chunk_load<CW>(an, Xp, tp, 0, TPC);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) a[kk] = an[kk];
+        conv_chunk_mask<CW>(a, tp, c * TPC, TPC);
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) asm volatile("" : : "v"(a[kk]));
-        if (c + 1 < NCH) conv_chunk_load<CW>(an, Xp, toff, (c + 1) * TPC, TPC);
+        if (c + 1 < NCH) conv_chunk_load<CW>(an, Xp, tp, (c + 1) * TPC, TPC);
+        else touch_residual<TN>(pf, pfr, pfmask);
         xnor_chunk<TN, KC, CP, FULLN, false, false>(acc, a, wbase, wbase, c * KC, KC, ldW, nlast);
     }
-    if (TT > 0) xnor_chunk<TN, TW, CP, FULLN, false, false>(acc, t, wbase, wbase, NCH * KC, TW, ldW, nlast);
+    if (TT > 0) {
+        conv_chunk_mask<CW>(t, tp, NCH * TPC, TT);
+        xnor_chunk<TN, TW, CP, FULLN, false, false>(acc, t, wbase, wbase, NCH * KC, TW, ldW, nlast);
+    }
 }
 
 // Packed sign bits of a lane's TN outputs (bit j = column n0 + j), stored
@@ -376,11 +417,14 @@ __device__ __forceinline__ int32_t dval(uint32_t acc, int K, const Epilogue& e, 
 // slower) and RH rows at a time (all 64: staging the rows in two halves of
 // 32 to halve the LDS footprint measured 10% slower at 16384^3 and 12-29%
 // on the conv GEMMs).
+// (Staging D as int16 pairs, half the LDS, measured no faster on MI355X:
+// 57.9 -> 60.0 us on the 14x14x256 conv GEMM, 94.5 -> 97.5 us on 56x56x64.)
 template <int TN>
 struct Stage {
     static constexpr int CH = TN < 32 ? TN : 32;
     static constexpr int RH = 64;
-    static constexpr int words = RH * (CH + 1);
+    static constexpr int RW = CH + 1;             // words per staged row (odd: no bank conflicts)
+    static constexpr int words = RH * RW;
 };
 
 template <int TN, bool TERN>
@@ -389,6 +433,7 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
 {
     constexpr int CH = Stage<TN>::CH;
     constexpr int RH = Stage<TN>::RH;
+    constexpr int RW = Stage<TN>::RW;
     constexpr int G4 = CH / 4;
     constexpr int RPP = 64 / G4;                  // rows per read pass
     constexpr int GLOG = G4 == 8 ? 3 : G4 == 4 ? 2 : G4 == 2 ? 1 : 0;
@@ -415,15 +460,22 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
             if (lane / RH == h) {
 #pragma unroll
                 for (int j = 0; j < CH; ++j)
-                    lds[(lane % RH) * (CH + 1) + j] = (uint32_t)dval<TERN>(acc[c0 + j], K, e, n0 + c0 + j);
+                    lds[(lane % RH) * RW + j] = (uint32_t)dval<TERN>(acc[c0 + j], K, e, n0 + c0 + j);
             }
+            // the accumulators are dead from here: keep the residual loads
+            // below so the two sets are never live together
+            __builtin_amdgcn_sched_barrier(0);
             constexpr int NP = RH / RPP;          // read passes per half
             f32x4 rv[NP];
+            if (e.flags & EPI_RESIDUAL) {
 #pragma unroll
-            for (int q = 0; q < NP; ++q) {
-                const int m = min(wrow0 + h * RH + q * RPP + lane / G4, M - 1);
-                if (e.flags & EPI_RESIDUAL)
+                for (int q = 0; q < NP; ++q) {
+                    const int m = min(wrow0 + h * RH + q * RPP + lane / G4, M - 1);
                     rv[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(e.R + (int64_t)m * e.ldR + nc));
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < NP; ++q) rv[q] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
             }
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -431,7 +483,7 @@ __device__ __forceinline__ void epilogue_lds(const uint32_t (&acc)[TN], uint32_t
                 const int r = q * RPP + lane / G4;
                 int32_t d[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) d[i] = (int32_t)lds[r * (CH + 1) + 4 * cg + i];
+                for (int i = 0; i < 4; ++i) d[i] = (int32_t)lds[r * RW + 4 * cg + i];
                 const int m = wrow0 + h * RH + r;
                 if (m < M) {
                     const int n = nc;
@@ -496,8 +548,8 @@ __device__ __forceinline__ bool staged_ok(const Epilogue& e, bool full) {
 template <int TN>
 struct MinWaves { static constexpr int value = TN >= 64 ? 3 : TN == 32 ? 5 : 8; };
 
-template <int TN, int KC, int EPI, int WAVES, bool TERN, int CW>
-__global__ __launch_bounds__(WAVES * 64, MinWaves<TN>::value) void k_xnor_gemm(
+template <int TN, int KC, int EPI, int WAVES, bool TERN, int CW, int MW = MinWaves<TN>::value>
+__global__ __launch_bounds__(WAVES * 64, MW) void k_xnor_gemm(
     const uint32_t* __restrict__ Xp, int64_t ldX, const uint32_t* __restrict__ Wp, int64_t ldW,
     int M, int N, int K, int tiles_n, Epilogue e, int convH, int convW)
 {
@@ -522,27 +574,39 @@ __global__ __launch_bounds__(WAVES * 64, MinWaves<TN>::value) void k_xnor_gemm(
     const bool full = (ncols == TN);
     const bool staged = EPI_LDS && staged_ok(e, full);
 
+    // Residual prefetch (the conv loop): the lane's row of the residual tile
+    uint32_t pf = 0u;
+    const bool pfon = staged && (e.flags & EPI_PREFETCH_R) && (e.flags & EPI_RESIDUAL);
+    const float* __restrict__ pfr = pfon ? e.R + (int64_t)min(m, M - 1) * e.ldR + n0
+                                         : reinterpret_cast<const float*>(Xp);
+    const int pfmask = pfon ? -1 : 0;
+
     uint32_t acc[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[j] = 0u;
     if (CW > 0) {
-        // neighbour word offsets of this lane's output pixel (m = (b H + oh) W + ow)
+        // the taps of this lane's output pixel (m = (b H + oh) W + ow)
         const int mc = min(m, M - 1);
         const int ow = mc % convW, oh = (mc / convW) % convH;
-        int toff[9];
+        Taps tp;
+        tp.base = mc * (int)ldX;
+        tp.rowstep = convW * (int)ldX;
+        tp.ldx = (int)ldX;
+        tp.in = 0u;
 #pragma unroll
         for (int t = 0; t < 9; ++t) {
             const int dh = t / 3 - 1, dw = t % 3 - 1;
             const bool inside = oh + dh >= 0 && oh + dh < convH && ow + dw >= 0 && ow + dw < convW;
-            toff[t] = inside ? (mc + dh * convW + dw) * (int)ldX : -1;
+            tp.in |= (inside ? 1u : 0u) << t;
         }
-        if (n0 + TN <= N) conv_mainloop<TN, (CW > 0 ? CW : 2), true>(acc, Xp, toff, wbase, ldW, nlast);
-        else              conv_mainloop<TN, (CW > 0 ? CW : 2), false>(acc, Xp, toff, wbase, ldW, nlast);
+        if (n0 + TN <= N) conv_mainloop<TN, (CW > 0 ? CW : 2), KC, true>(acc, Xp, tp, wbase, ldW, nlast, pf, pfr, pfmask);
+        else              conv_mainloop<TN, (CW > 0 ? CW : 2), KC, false>(acc, Xp, tp, wbase, ldW, nlast, pf, pfr, pfmask);
     } else {
         if (n0 + TN <= N) xnor_mainloop<TN, KC, true, TERN>(acc, xrow, wbase, zbase, Kw, ldW, nlast);
         else              xnor_mainloop<TN, KC, false, TERN>(acc, xrow, wbase, zbase, Kw, ldW, nlast);
     }
 
+    asm volatile("" : : "v"(pf));
     if (staged) {
         epilogue_lds<TN, TERN>(acc, lds_epi + wave * kLdsWords, wrow0, M, n0, K, e);
         if ((e.flags & EPI_SIGN_PACK) && tn == tiles_n - 1 && m < M) {
@@ -672,6 +736,15 @@ int epilogue_from_env() {
     if (v[0] == 'd') return EPI_DIRECT;
     if (v[0] == 's') return EPI_STAGED;
     return -1;
+}
+
+// The epilogue of a launch: staged through LDS for D and Y outputs (whole
+// row segments per store), direct for THRESH_PACK (its bits leave from
+// registers).
+int pick_epilogue(const Epilogue& e) {
+    if (!(e.flags & (EPI_DOT | EPI_SCALE)) || (e.flags & EPI_THRESH)) return EPI_DIRECT;
+    const int ov = epilogue_from_env();
+    return ov >= 0 ? ov : EPI_STAGED;
 }
 
 // Column tile: 64-wide tiles (the most reuse of each activation chunk) once
