@@ -69,7 +69,7 @@ def parse_args():
     p.add_argument("--size", type=int, default=16384, help="M = N = K of the headline GEMM step")
     p.add_argument("--no-secondary", action="store_true", help="skip the GEMV / MLP / conv / 8192 runs")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv", "i8", "tern"], default=None,
+    p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv", "i8", "tern", "f16"], default=None,
                    help="run one workload only (for profiler runs); prints its JSON")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--cpu-child", nargs=5, default=None, help=argparse.SUPPRESS)
@@ -346,6 +346,66 @@ def i8_gemv_bench(bnn, torch, N, K, reps=20):
         # 8 (v_and, v_bcnt) pairs per weight word: the VALU share of the same time
         stream_valu_frac=16.0 * Nt * kw / t_stream / PEAK_INT_OPS,
         decode_call_us_quantize_plus_gemv=1e3 * per_call_ms,
+    )
+    del Wst, ast, Wp, a, Y, graph
+    torch.cuda.empty_cache()
+    return res
+
+
+def f16_gemv_bench(bnn, torch, N, K, reps=20):
+    """Binary weights x fp16 activations at the decode shape: one launch
+    streaming 191 stacked weight copies, and exact-shape calls on cold copies
+    from a HIP graph."""
+    import workloads
+    log(f"f16 gemv N={N} K={K}: {GEMV_COPIES} stacked copies")
+    W = torch.from_numpy(workloads.normal_f32(workloads.seed_for(3, 0) + K, (N, K))).cuda()
+    x = torch.from_numpy(workloads.normal_f32(workloads.seed_for(3, 1) + K, (1, K))).cuda().half()
+    Wp, a = bnn.pack_weights(W)
+    del W
+    G = GEMV_COPIES
+    Wst = Wp.repeat(G, 1)
+    ast = a.repeat(G)
+    Nt = G * N
+    Y = torch.empty((1, Nt), dtype=torch.float32, device="cuda")
+    kw = (K + 31) // 32
+    clock_warmup(torch, lambda: bnn.bwn_f16_gemv(Wst, K, x, ast, Y=Y))
+    ts = [Ev() for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in ts:
+        e.start()
+        bnn.bwn_f16_gemv(Wst, K, x, ast, Y=Y)
+        e.stop()
+    torch.cuda.synchronize()
+    ms = [e.ms() for e in ts]
+    # weights + fp16 activations + alpha + y
+    bytes_stream = 4.0 * Nt * kw + 2.0 * K + 4.0 * Nt + 4.0 * Nt
+    t_stream = statistics.mean(ms) * 1e-3
+    ys = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    order = [(i * 37) % G for i in range(2 * G)]
+
+    def seq():
+        for g in order:
+            bnn.bwn_f16_gemv(Wst[g * N:(g + 1) * N], K, x, ast[g * N:(g + 1) * N], Y=ys)
+    seq()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        seq()
+    graph.replay()
+    torch.cuda.synchronize()
+    e = Ev()
+    e.start()
+    graph.replay()
+    e.stop()
+    torch.cuda.synchronize()
+    per_call_ms = e.ms() / len(order)
+    res = dict(
+        N=N, K=K, copies=G, stream_ms_mean=statistics.mean(ms), stream_ms_median=median(ms),
+        stream_bytes=bytes_stream, stream_GBps=bytes_stream / t_stream / 1e9,
+        stream_frac_hbm=bytes_stream / t_stream / PEAK_HBM,
+        # per weight word and lane: 15 shifts, 16 bit-selects, 16 dot2 (47 VALU lane-ops)
+        stream_valu_frac=47.0 * Nt * kw / t_stream / PEAK_INT_OPS,
+        exact_shape_cold_us_per_call=1e3 * per_call_ms,
     )
     del Wst, ast, Wp, a, Y, graph
     torch.cuda.empty_cache()
@@ -837,6 +897,8 @@ def main():
             r = mlp_bench(bnn, torch)
         elif args.only == "tern":
             r = ternary_bench(bnn, torch)
+        elif args.only == "f16":
+            r = [f16_gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]]
         elif args.only == "i8":
             r = {"gemv": [i8_gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]],
                  "gemm": i8_gemm_bench(bnn, torch, 8192, 8192, 8192)}
@@ -944,6 +1006,16 @@ def main():
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": round(min(r["stream_frac_hbm"] for r in iv), 4)},
             "shapes": iv,
+        }
+        fv = [f16_gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]]
+        sec["f16act_gemv_batch1"] = {
+            "metric": "binary weights x fp16 activations, batch-1 GEMV HBM GB/s (191 stacked copies)",
+            "value": round(min(r["stream_GBps"] for r in fv), 1),
+            "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(min(r["stream_GBps"] for r in fv), 1),
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": round(min(r["stream_frac_hbm"] for r in fv), 4)},
+            "shapes": fv,
         }
         ig = i8_gemm_bench(bnn, torch, 8192, 8192, 8192)
         idig = source_digest("xnor_popcount_gemm_amd/csrc/i8gemm.hip", "xnor_popcount_gemm_amd/csrc/bnn_device.hpp")

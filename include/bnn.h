@@ -92,6 +92,7 @@ typedef enum bnn_status {
 
 /* Longest row of the INT8-activation calls: |D| <= 128 K stays exact in fp32. */
 #define BNN_MAX_K_I8 ((int64_t)1 << 17)
+#define BNN_MAX_K_F16 ((int64_t)16384)
 
 /* Geometry of a binary 3x3 convolution lowered to a GEMM by im2col.
  * Input NHWC [B, H, W, C] fp32, contiguous.  Only R = S = 3, stride 1,
@@ -345,6 +346,29 @@ bnn_status bnn_pack_act_i8(const int8_t* Xq, int64_t M, int64_t K, int64_t ldXq,
  *  DOT_I32, SCALE_F32, ALPHA_TENSOR and W_TERNARY -> BNN_ERR_UNSUPPORTED;
  *  neither usable activation form -> BNN_ERR_NULL. */
 bnn_status bnn_bwn_i8_linear(const bnn_i8_args* args, bnn_stream_t stream);
+
+/* Binary weights x fp16 activations (BinaryConnect / BWN), [P5] "Binary
+ * Neural Networks" eq. (1)-(2): real activations, +1/-1 weights, so each
+ * weight adds or subtracts its activation:
+ *     S[m,n] = sum_{k<K} s(n,k) * x[m,k]        (s = +1 for bit 0)
+ *     Y[m,n] = fl32(alpha_n * S[m,n])
+ *  The products +-x are exact; S is summed in fp32 in a fixed order of the
+ *  kernel's: no term passes through more than n = 128 ceil(ceil(K/128) / G)
+ *  + 6 rounded additions (G = lanes per weight row: the smallest power of
+ *  two >= ceil(K/128), at most 64), so |S - S_exact| <= n u / (1 - n u) *
+ *  sum_k |x[m,k]| with u = 2^-24.
+ *  One launch per activation row: the packed weights stream once per row
+ *  (the batch-1 decode case of [P2] "Bandwidth math").
+ *  X     fp16 bit patterns [M, ldX]: 16-byte aligned, ldX % 8 == 0, ldX >= K;
+ *  Wp    packed weights [N, ldWp] (packed layout, ldWp % 4 == 0);
+ *  alpha fp32 [N], or [1] with BNN_EPI_ALPHA_TENSOR;
+ *  Y     fp32 [M, ldY], ldY >= N, 4-byte aligned.
+ *  epilogue: BNN_EPI_SCALE_F32 [| BNN_EPI_ALPHA_TENSOR]; anything else ->
+ *  BNN_ERR_UNSUPPORTED.  1 <= K <= BNN_MAX_K_F16 (the activations of a lane
+ *  stay in registers). */
+bnn_status bnn_bwn_f16_gemv(const uint16_t* X, int64_t ldX, const uint32_t* Wp, int64_t ldWp,
+                            int64_t M, int64_t N, int64_t K, uint32_t epilogue,
+                            const float* alpha, float* Y, int64_t ldY, bnn_stream_t stream);
 
 /* Fold inference BatchNorm of z = alpha[n] * D followed by sign into the
  * (tau, dir) pair consumed by BNN_EPI_THRESH_PACK.  [P1] BatchNorm around

@@ -103,6 +103,8 @@ def _configure(L):
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = None
+    L.oracle_bwn_f16.argtypes = [_p, _i64, _p, _i64, _i64, _i64, _p]
+    L.oracle_bwn_f16.restype = ctypes.c_int
     L.oracle_alpha_tensor.argtypes = [_p, _i64, _i64, _i64]
     L.oracle_alpha_tensor.restype = ctypes.c_float
     L.oracle_num_threads.argtypes = []
@@ -201,6 +203,33 @@ def dot_i8(xq: np.ndarray, ws: np.ndarray) -> np.ndarray:
     D = np.empty((M, N), dtype=np.int32)
     lib().oracle_dot_i8(_ptr(xq), _ptr(ws), M, N, K, _ptr(D))
     return D
+
+
+def bwn_f16_units(x16: np.ndarray, ws: np.ndarray) -> np.ndarray:
+    """S[m, n] = sum_k ws[n, k] * x[m, k] with fp16 activations and +1/-1
+    weights ("Extreme Quantization" eq. (1)-(2), BinaryConnect / BWN), taken
+    exactly: int64 [M, N] in units of 2^-24 (S = units * 2^-24).  x16 holds
+    fp16 values (np.float16) or their bit patterns (np.uint16); all finite."""
+    x16 = np.ascontiguousarray(x16)
+    bits = x16.view(np.uint16) if x16.dtype == np.float16 else _c(x16, np.uint16)
+    ws = _c(ws, np.int8)
+    M, K = bits.shape
+    N, K2 = ws.shape
+    assert K == K2 and K <= 1 << 14
+    S = np.empty((M, N), dtype=np.int64)
+    if lib().oracle_bwn_f16(_ptr(bits), K, _ptr(ws), M, N, K, _ptr(S)):
+        raise ValueError("fp16 activations must be finite")
+    return S
+
+
+def bwn_f16(x16: np.ndarray, W: np.ndarray, a: np.ndarray):
+    """Binary weights x fp16 activations, y = alpha_n * sum_k s(W[n, k]) x[m, k]
+    (eq. (1)-(2)): returns (S float64 [M, N], y float64 [M, N]) with S exact
+    up to its final rounding to double and y = alpha * S in double (the
+    reference a tolerance is measured against)."""
+    U = bwn_f16_units(x16, sign(W))
+    S = U.astype(np.float64) * 2.0 ** -24
+    return S, np.asarray(a, np.float64)[None, :] * S
 
 
 def quantize_absmax_i8(X: np.ndarray):

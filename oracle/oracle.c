@@ -227,6 +227,46 @@ API void oracle_dot_i8(const int8_t* xq, const int8_t* ws, int64_t M, int64_t N,
         }
 }
 
+/* IEEE half precision (binary16) as an exact multiple of 2^-24, decoded from
+ * the format's definition: sign bit 15, biased exponent e = bits 14..10,
+ * fraction f = bits 9..0.  Normal (1 <= e <= 30): (1024 + f) * 2^(e - 25)
+ * = (1024 + f) * 2^(e - 1) units of 2^-24; subnormal or zero (e = 0):
+ * f units.  Returns 0 and sets *bad for infinities and NaNs (e = 31). */
+static int64_t half_units(uint16_t h, int* bad)
+{
+    const int64_t e = (h >> 10) & 0x1F, f = h & 0x3FF;
+    int64_t u;
+    if (e == 31) { *bad = 1; return 0; }
+    if (e == 0) u = f;
+    else u = (1024 + f) << (e - 1);
+    return (h & 0x8000) ? -u : u;
+}
+
+/* [P5] "Binary Neural Networks" eq. (1)-(2) with real activations
+ * (BinaryConnect / BWN): each +1/-1 weight adds or subtracts its activation,
+ * S[m, n] = sum_k s[n, k] * x[m, k].  x is fp16 (bit patterns, [M, ldx]); the
+ * sum is taken exactly, in integer units of 2^-24 (every fp16 value is one:
+ * |x| < 2^16, so |S| < 2^54 units for K <= 2^14 and int64 cannot overflow).
+ * S_units[m * N + n] = S[m, n] * 2^24.  Returns 1 if any x is not finite. */
+API int oracle_bwn_f16(const uint16_t* x, int64_t ldx, const int8_t* ws, int64_t M, int64_t N, int64_t K,
+                       int64_t* S_units)
+{
+    int bad = 0;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) (void)half_units(x[m * ldx + k], &bad);
+    if (bad) return 1;
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int dummy = 0;
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (int64_t)ws[n * K + k] * half_units(x[m * ldx + k], &dummy);
+            S_units[m * N + n] = acc;
+        }
+    return 0;
+}
+
 /* [P5] "BitNet: 1-bit Transformer", item 2 (activations quantized to INT8).
  * The page names no quantizer; the reading taken is symmetric per-row absmax:
  *   amax = max_k |x[m,k]| (NaN elements skipped),

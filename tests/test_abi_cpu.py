@@ -244,6 +244,31 @@ def test_pack_weights_ternary_validation(L):
     assert p(A16, 4, 0, 64, None, f, A16, A16, 4, A16, None) == ERR_SHAPE
 
 
+def test_bwn_f16_gemv_validation(L):
+    # X, ldX, Wp, ldWp, M, N, K, epilogue, alpha, Y, ldY, stream
+    g = L.bnn_bwn_f16_gemv
+    SC, AT, DOT = 2, 16, 1
+    assert g(A16, 104, A16, 4, 0, 8, 100, SC, A16, A16, 8, None) == OK            # M == 0: nothing to do
+    assert g(A16, 104, A16, 4, 2, 0, 100, SC, A16, A16, 8, None) == OK            # N == 0
+    assert g(0, 104, A16, 4, 1, 8, 100, SC, A16, A16, 8, None) == ERR_NULL
+    assert g(A16, 104, 0, 4, 1, 8, 100, SC, A16, A16, 8, None) == ERR_NULL
+    assert g(A16, 104, A16, 4, 1, 8, 100, SC, 0, A16, 8, None) == ERR_NULL
+    assert g(A16, 104, A16, 4, 1, 8, 100, SC, A16, 0, 8, None) == ERR_NULL
+    assert g(A16, 104, A16, 4, 1, 8, 100, DOT, A16, A16, 8, None) == ERR_UNSUPPORTED
+    assert g(A16, 104, A16, 4, 1, 8, 100, SC | DOT, A16, A16, 8, None) == ERR_UNSUPPORTED
+    assert g(A16, 104, A16, 4, 1, 8, 100, AT, A16, A16, 8, None) == ERR_UNSUPPORTED   # no SCALE
+    assert g(A16, 104, A16, 4, 1, 8, 0, SC, A16, A16, 8, None) == ERR_SHAPE
+    assert g(A16, 16384, A16, 512, 1, 8, 16385, SC, A16, A16, 8, None) == ERR_SHAPE
+    assert g(A16, 96, A16, 4, 1, 8, 100, SC, A16, A16, 8, None) == ERR_LD         # ldX < K
+    assert g(A16, 104, A16, 4, 1, 8, 100, SC, A16, A16, 7, None) == ERR_LD        # ldY < N
+    assert g(A16, 104, A16, 3, 1, 8, 100, SC, A16, A16, 8, None) == ERR_LD        # ldWp < ceil(K/32)
+    assert g(A4, 104, A16, 4, 1, 8, 100, SC, A16, A16, 8, None) == ERR_ALIGN      # X not 16-byte aligned
+    assert g(A16, 100, A16, 4, 1, 8, 100, SC, A16, A16, 8, None) == ERR_ALIGN     # ldX % 8 != 0
+    assert g(A16, 104, A4, 4, 1, 8, 100, SC, A16, A16, 8, None) == ERR_ALIGN      # Wp not 16-byte aligned
+    assert g(A16, 104, A16, 4, 1, 8, 100, SC, A2, A16, 8, None) == ERR_ALIGN
+    assert g(A16, 104, A16, 4, 1, 8, 100, SC, A16, A2, 8, None) == ERR_ALIGN
+
+
 def test_empty_calls_launch_nothing(L):
     # M == 0 or N == 0 is a valid empty call that returns before any launch.
     assert L.bnn_xnor_gemm(A16, 4, A16, 4, 0, 8, 100, A16, 8, None, None, 0, None) == OK

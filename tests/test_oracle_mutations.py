@@ -117,6 +117,18 @@ MUTATIONS = [
     ("RSign im2col: pad taps -1",
      "inside ? S[((b * H + ih) * W + iw) * C + c] : (int8_t)1;",
      "inside ? S[((b * H + ih) * W + iw) * C + c] : (int8_t)-1;"),
+    ("half: exponent bias off by one",
+     "else u = (1024 + f) << (e - 1);", "else u = (1024 + f) << e;"),
+    ("half: sign bit ignored",
+     "return (h & 0x8000) ? -u : u;", "return u;"),
+    ("half: subnormals given the implicit leading one",
+     "if (e == 0) u = f;", "if (e == 0) u = 1024 + f;"),
+    ("fp16 activations: last term dropped",
+     "for (int64_t k = 0; k < K; ++k)\n                acc += (int64_t)ws[n * K + k] * half_units",
+     "for (int64_t k = 0; k + 1 < K; ++k)\n                acc += (int64_t)ws[n * K + k] * half_units"),
+    ("fp16 activations: weight sign ignored",
+     "acc += (int64_t)ws[n * K + k] * half_units(x[m * ldx + k], &dummy);",
+     "acc += half_units(x[m * ldx + k], &dummy);"),
     ("ternary pack: zeros counted as nonzero",
      "if (t != 0) {\n                Z[n * ld + k / 32]", "if (t != 2) {\n                Z[n * ld + k / 32]"),
 ]

@@ -542,6 +542,63 @@ def test_dot_i8_add_subtract_reading():
             assert int(D[m, n]) == acc
 
 
+def test_half_decode_every_finite_pattern():
+    # the oracle decodes fp16 from the format's definition; numpy's IEEE
+    # binary16 conversion is the independent reading of the same standard
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> 10) & 0x1F) != 0x1F
+    bits = bits[finite]
+    U = oracle.bwn_f16_units(bits.reshape(-1, 1), np.ones((1, 1), np.int8))[:, 0]
+    want = bits.view(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(U.astype(np.float64) * 2.0 ** -24, want)
+    with pytest.raises(ValueError):
+        oracle.bwn_f16_units(np.array([[0x7C00]], np.uint16), np.ones((1, 1), np.int8))
+
+
+def test_bwn_f16_pm1_activations_equal_dot():
+    # eq. (1)-(2) with +1/-1 activations is the binary dot product (eq. (6))
+    rng = np.random.default_rng(73)
+    for K in (1, 31, 33, 1000, 4096):
+        xs = _rand_signs(rng, (3, K))
+        ws = _rand_signs(rng, (5, K))
+        U = oracle.bwn_f16_units(xs.astype(np.float16), ws)
+        np.testing.assert_array_equal(U, oracle.dot(xs, ws).astype(np.int64) << 24)
+
+
+def test_bwn_f16_exact_rational_sums():
+    # brute force in exact rationals over values of every fp16 class
+    # (subnormals, zeros of both signs, the largest finite value)
+    rng = np.random.default_rng(74)
+    x = (rng.standard_normal((4, 57)) * np.exp2(rng.integers(-26, 17, size=(4, 57)))).astype(np.float16)
+    x[0, :5] = np.array([0.0, -0.0, 65504.0, -65504.0, 2.0 ** -24], np.float16)
+    x[~np.isfinite(x)] = np.float16(1.5)
+    W = rng.standard_normal((6, 57)).astype(np.float32)
+    W[0, :3] = [0.0, -0.0, 1e-40]                # sign(0) = sign(-0) = +1, a denormal weight +1
+    S, _ = oracle.bwn_f16(x, W, np.ones(6, np.float32))
+    U = oracle.bwn_f16_units(x, oracle.sign(W))
+    for m in range(4):
+        for n in range(6):
+            exact = sum((Fraction(float(x[m, k])) * (1 if (W[n, k] >= 0) else -1) for k in range(57)), Fraction(0))
+            assert Fraction(int(U[m, n]), 1 << 24) == exact
+            assert S[m, n] == float(exact)
+
+
+def test_bwn_f16_invariants():
+    rng = np.random.default_rng(75)
+    x = rng.standard_normal((3, 300)).astype(np.float16)
+    W = rng.standard_normal((7, 300)).astype(np.float32)
+    W[W == 0] = 1.0
+    U = oracle.bwn_f16_units(x, oracle.sign(W))
+    np.testing.assert_array_equal(oracle.bwn_f16_units(x, oracle.sign(-W)), -U)          # negate weights
+    np.testing.assert_array_equal(oracle.bwn_f16_units(-x, oracle.sign(W)), -U)          # negate activations
+    ones = np.ones((1, 300), np.int8)
+    tot = oracle.bwn_f16_units(x, ones)[:, 0]
+    np.testing.assert_array_equal(tot.astype(np.float64) * 2.0 ** -24,
+                                  x.astype(np.float64).sum(axis=1))     # all +1: the plain sum (exact here)
+    _, y = oracle.bwn_f16(x, W, np.full(7, 0.5, np.float32))
+    np.testing.assert_array_equal(y, 0.5 * U.astype(np.float64) * 2.0 ** -24)
+
+
 def test_dot_i8_extremes_and_invariants():
     K = 1000
     lo = np.full((1, K), -128, np.int8)

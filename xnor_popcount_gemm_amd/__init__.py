@@ -25,7 +25,7 @@ __all__ = [
     "xnor_gemm", "linear_fused", "fold_bn_thresholds", "dense_f32_sign_pack",
     "dense_binact_f32", "EPI_DOT_I32", "EPI_SCALE_F32", "EPI_RESIDUAL_F32",
     "EPI_THRESH_PACK", "EPI_ALPHA_TENSOR", "EPI_BIAS_F32", "LIB_PATH",
-    "weight_scale_tensor", "weight_scale_tensor_noalloc", "NOALLOC_MAX_ROWS", "quantize_act_i8", "pack_act_i8", "bwn_i8_linear", "MAX_K_I8",
+    "weight_scale_tensor", "weight_scale_tensor_noalloc", "NOALLOC_MAX_ROWS", "quantize_act_i8", "pack_act_i8", "bwn_i8_linear", "MAX_K_I8", "bwn_f16_gemv", "MAX_K_F16",
     "W_TERNARY", "pack_weights_ternary", "EPI_SIGN_PACK", "pack_activations_rsign", "conv3x3_fused",
 ]
 
@@ -40,6 +40,7 @@ EPI_BIAS_F32 = 32
 W_TERNARY = 64
 EPI_SIGN_PACK = 128
 MAX_K_I8 = 1 << 17
+MAX_K_F16 = 16384
 NOALLOC_MAX_ROWS = 1 << 16
 
 _STATUS = {
@@ -123,6 +124,7 @@ def lib() -> ctypes.CDLL:
             "bnn_quantize_act_i8": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp],
             "bnn_pack_act_i8": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
             "bnn_bwn_i8_linear": [ctypes.POINTER(_I8Args), _vp],
+            "bnn_bwn_f16_gemv": [_vp, _i64, _vp, _i64, _i64, _i64, _i64, ctypes.c_uint32, _vp, _vp, _i64, _vp],
             "bnn_pack_weights_ternary": [_vp, _i64, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _i64, _vp, _vp],
             "bnn_pack_activations_rsign": [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp],
             "bnn_conv3x3_fused": [ctypes.POINTER(_FusedArgs), ctypes.POINTER(_ConvGeom), _vp],
@@ -471,6 +473,23 @@ def bwn_i8_linear(Wp: torch.Tensor, K: int, epilogue: int, *, Xb=None, xsum=None
         a.Zp = Zp.data_ptr()
     _check(lib().bnn_bwn_i8_linear(ctypes.byref(a), _stream(dev)), "bnn_bwn_i8_linear")
     return {"D": D, "Y": Y}
+
+
+def bwn_f16_gemv(Wp: torch.Tensor, K: int, X: torch.Tensor, alpha: torch.Tensor, *,
+                 alpha_tensor: bool = False, Y: torch.Tensor | None = None):
+    """Binary weights x fp16 activations: Y = fl32(alpha * sum_k s x_k) with
+    an fp32 sum (bnn_bwn_f16_gemv).  X float16 [M, ldX >= K] (ldX % 8 == 0),
+    alpha fp32 [N] (or [1] with ``alpha_tensor``).  Returns Y fp32 [M, N]."""
+    _dev(Wp, torch.int32, "Wp")
+    _dev(X, torch.float16, "X")
+    _dev(alpha, torch.float32, "alpha")
+    M, N = X.shape[0], Wp.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=Wp.device)
+    fl = EPI_SCALE_F32 | (EPI_ALPHA_TENSOR if alpha_tensor else 0)
+    _check(lib().bnn_bwn_f16_gemv(X.data_ptr(), _ld(X), Wp.data_ptr(), _ld(Wp), M, N, int(K), fl,
+                                  alpha.data_ptr(), Y.data_ptr(), _ld(Y), _stream(Wp.device)), "bnn_bwn_f16_gemv")
+    return Y
 
 
 def pack_weights_ternary(W: torch.Tensor, *, gamma: torch.Tensor | None = None, delta: float = 0.0):

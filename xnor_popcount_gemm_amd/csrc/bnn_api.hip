@@ -452,6 +452,30 @@ bnn_status bnn_bwn_i8_linear(const bnn_i8_args* args, bnn_stream_t stream)
                                             args->M, args->N, args->K, e, s));
 }
 
+bnn_status bnn_bwn_f16_gemv(const uint16_t* X, int64_t ldX, const uint32_t* Wp, int64_t ldWp,
+                            int64_t M, int64_t N, int64_t K, uint32_t epilogue,
+                            const float* alpha, float* Y, int64_t ldY, bnn_stream_t stream)
+{
+    bnn_status st;
+    if ((st = check_rows(M)) != BNN_OK) return st;
+    if ((st = check_rows(N)) != BNN_OK) return st;
+    if (K < 1 || K > BNN_MAX_K_F16 || K > bnn::f16_gemv_max_k()) return BNN_ERR_SHAPE;
+    if (epilogue & ~(uint32_t)(BNN_EPI_SCALE_F32 | BNN_EPI_ALPHA_TENSOR)) return BNN_ERR_UNSUPPORTED;
+    if (!(epilogue & BNN_EPI_SCALE_F32)) return BNN_ERR_UNSUPPORTED;
+    if ((st = check_packed(Wp, K, ldWp)) != BNN_OK) return st;
+    if (!X || !alpha || !Y) return BNN_ERR_NULL;
+    if (ldX < K || ldY < N) return BNN_ERR_LD;
+    if (misaligned16(X) || ldX % 8 != 0 || misaligned4(alpha) || misaligned4(Y)) return BNN_ERR_ALIGN;
+    if (M == 0 || N == 0) return BNN_OK;
+    hipStream_t s = as_stream(stream);
+    const bool at = (epilogue & BNN_EPI_ALPHA_TENSOR) != 0;
+    for (int64_t m = 0; m < M; ++m) {
+        const hipError_t e = bnn::launch_bwn_f16_gemv(X + m * ldX, Wp, ldWp, N, K, alpha, at, Y + m * ldY, s);
+        if (e != hipSuccess) return BNN_ERR_HIP;
+    }
+    return BNN_OK;
+}
+
 bnn_status bnn_dense_f32_sign_pack(const float* X, int64_t ldX, const float* W, int64_t ldW,
                                    int64_t M, int64_t N, int64_t K,
                                    uint32_t* Op, int64_t ldOp, bnn_stream_t stream)
