@@ -51,6 +51,7 @@ VALU_LANES_PER_CLK = 128
 PEAK_INT_OPS = NUM_CU * CLOCK_HZ * VALU_LANES_PER_CLK      # 78.64e12 lane-ops/s
 PEAK_HBM = 8.0e12                                    # bytes/s
 PEAK_INT8_MFMA = 5.0e15                              # dense int8 matrix-core ops/s (MAC = 2 ops)
+PEAK_FP4_MFMA = 10.1e15                              # dense fp4 (e2m1) matrix-core ops/s (MAC = 2 ops)
 GEMM_SOURCES = ("xnor_popcount_gemm_amd/csrc/gemm.hip", "xnor_popcount_gemm_amd/csrc/gemm_kernel.hpp",
                 "xnor_popcount_gemm_amd/csrc/bnn_device.hpp")
 METRIC = "binary GEMM ops/s (TOPS, % int-VALU peak) + batch-1 GEMV HBM GB/s"
@@ -69,7 +70,7 @@ def parse_args():
     p.add_argument("--size", type=int, default=16384, help="M = N = K of the headline GEMM step")
     p.add_argument("--no-secondary", action="store_true", help="skip the GEMV / MLP / conv / 8192 runs")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv", "i8", "tern", "f16"], default=None,
+    p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv", "i8", "tern", "f16", "mfma"], default=None,
                    help="run one workload only (for profiler runs); prints its JSON")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--cpu-child", nargs=5, default=None, help=argparse.SUPPRESS)
@@ -159,7 +160,7 @@ def read_traffic(kernel_key: str, digest: str):
 
 
 # ---------------------------------------------------------------- workloads
-def gemm_step_bench(bnn, torch, M, N, K, steps, warmup, seed_base, warm_ms=0.0):
+def gemm_step_bench(bnn, torch, M, N, K, steps, warmup, seed_base, warm_ms=0.0, mfma=False):
     import workloads
     log(f"gemm {M}x{N}x{K}: generating inputs")
     X = torch.from_numpy(workloads.normal_f32(workloads.seed_for(4, 0) + seed_base, (M, K))).cuda()
@@ -180,7 +181,7 @@ def gemm_step_bench(bnn, torch, M, N, K, steps, warmup, seed_base, warm_ms=0.0):
         if record: e["pack_x"].stop(); e["pack_w"].start()
         bnn.pack_weights(W, out=Wp, alpha_out=a)
         if record: e["pack_w"].stop(); e["gemm"].start()
-        bnn.xnor_gemm(Xp, Wp, K, alpha=a, want_scaled=True, D=D, Y=Y)
+        (bnn.xnor_gemm_mfma if mfma else bnn.xnor_gemm)(Xp, Wp, K, alpha=a, want_scaled=True, D=D, Y=Y)
         if record: e["gemm"].stop()
         return e
 
@@ -410,6 +411,24 @@ def f16_gemv_bench(bnn, torch, N, K, reps=20):
     del Wst, ast, Wp, a, Y, graph
     torch.cuda.empty_cache()
     return res
+
+
+def mfma_lines(bnn, torch, args):
+    """The XNOR GEMM step on the fp4 matrix cores (exact +-1 products), at the
+    headline size and at 8192^3, against the dense fp4 matrix-core peak."""
+    out = {}
+    for n, steps in ((args.size, args.steps), (8192, max(5, args.steps // 2))):
+        g = gemm_step_bench(bnn, torch, n, n, n, steps, 2, seed_base=n, warm_ms=80.0, mfma=True)
+        ops = g["binops_per_step"]
+        out[f"gemm_{n}"] = {
+            "binary_tops_step": round(ops / (g["ms_per_step"] * 1e-3) / 1e12, 2),
+            "gemm_ms": round(g["gemm_ms_mean"], 4), "ms_per_step": round(g["ms_per_step"], 4),
+            "roofline": {"bound": "mfma", "achieved": round(ops / (g["gemm_ms_mean"] * 1e-3) / 1e12, 1),
+                         "peak": PEAK_FP4_MFMA / 1e12, "unit": "T binary ops/s (fp4 MFMA dense)",
+                         "frac": round(ops / (g["gemm_ms_mean"] * 1e-3) / PEAK_FP4_MFMA, 4)},
+            "pack_x_ms": round(g["pack_x_ms"], 4), "pack_w_ms": round(g["pack_w_ms"], 4),
+        }
+    return out
 
 
 def i8_gemm_bench(bnn, torch, M, N, K, reps=10, warmup=2):
@@ -897,6 +916,8 @@ def main():
             r = mlp_bench(bnn, torch)
         elif args.only == "tern":
             r = ternary_bench(bnn, torch)
+        elif args.only == "mfma":
+            r = mfma_lines(bnn, torch, args)
         elif args.only == "f16":
             r = [f16_gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]]
         elif args.only == "i8":
@@ -1007,6 +1028,9 @@ def main():
                          "frac": round(min(r["stream_frac_hbm"] for r in iv), 4)},
             "shapes": iv,
         }
+        sec["xnor_gemm_fp4_mfma"] = dict(
+            metric="binary GEMM ops/s with the GEMM on the fp4 matrix cores (exact +-1 in e2m1), the same step",
+            **mfma_lines(bnn, torch, args))
         fv = [f16_gemv_bench(bnn, torch, s["N"], s["K"]) for s in workloads.WORKLOADS[3]["shapes"]]
         sec["f16act_gemv_batch1"] = {
             "metric": "binary weights x fp16 activations, batch-1 GEMV HBM GB/s (191 stacked copies)",

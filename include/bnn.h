@@ -206,6 +206,20 @@ bnn_status bnn_xnor_gemm(const uint32_t* Xp, int64_t ldXp,
                          const float* alpha, float* Y, int64_t ldY,
                          bnn_stream_t stream);
 
+/* The same D and Y as bnn_xnor_gemm, computed on the matrix cores: every sign
+ * becomes the FP4 (e2m1) value +1.0 or -1.0, so each product is exactly +-1
+ * and the fp32 accumulation of integers below 2^24 is exact (K <= 2^24):
+ * D[m,n] = sum_k s(X[m,k]) s(W[n,k]) bit for bit, the integer of [P2]
+ * section "1. Arithmetic" and [P5] eq. (6) (not an approximation).  One
+ * kernel for every M (no batch-1 GEMV path); arguments, layouts, limits and
+ * errors as bnn_xnor_gemm. */
+bnn_status bnn_xnor_gemm_mfma(const uint32_t* Xp, int64_t ldXp,
+                              const uint32_t* Wp, int64_t ldWp,
+                              int64_t M, int64_t N, int64_t K,
+                              int32_t* D, int64_t ldD,
+                              const float* alpha, float* Y, int64_t ldY,
+                              bnn_stream_t stream);
+
 /* The XNOR-popcount GEMM with a fused epilogue (see BNN_EPI_*):
  *  DOT_I32      D as in bnn_xnor_gemm.
  *  SCALE_F32    Y = fl32(alpha[n] * D)                               [P5] eq. (1)

@@ -244,6 +244,22 @@ def test_pack_weights_ternary_validation(L):
     assert p(A16, 4, 0, 64, None, f, A16, A16, 4, A16, None) == ERR_SHAPE
 
 
+def test_xnor_gemm_mfma_validation(L):
+    # Xp, ldXp, Wp, ldWp, M, N, K, D, ldD, alpha, Y, ldY, stream: the checks of bnn_xnor_gemm
+    g = L.bnn_xnor_gemm_mfma
+    assert g(A16, 4, A16, 4, 0, 8, 100, A16, 8, None, None, 0, None) == OK
+    assert g(A16, 4, A16, 4, 3, 0, 100, A16, 8, None, None, 0, None) == OK
+    assert g(A16, 4, A16, 4, 3, 8, 100, None, 8, None, None, 0, None) == ERR_NULL        # no output
+    assert g(0, 4, A16, 4, 3, 8, 100, A16, 8, None, None, 0, None) == ERR_NULL
+    assert g(A16, 4, A16, 4, 3, 8, 100, None, 0, None, A16, 8, None) == ERR_NULL         # Y without alpha
+    assert g(A16, 4, A16, 4, 3, 8, 0, A16, 8, None, None, 0, None) == ERR_SHAPE
+    assert g(A16, 4, A16, 4, 3, 8, (1 << 24) + 1, A16, 8, None, None, 0, None) == ERR_SHAPE
+    assert g(A16, 3, A16, 4, 3, 8, 100, A16, 8, None, None, 0, None) == ERR_LD
+    assert g(A16, 4, A16, 4, 3, 8, 100, A16, 7, None, None, 0, None) == ERR_LD
+    assert g(A4, 4, A16, 4, 3, 8, 100, A16, 8, None, None, 0, None) == ERR_ALIGN
+    assert g(A16, 4, A16, 6, 3, 8, 100, A16, 8, None, None, 0, None) == ERR_ALIGN
+
+
 def test_bwn_f16_gemv_validation(L):
     # X, ldX, Wp, ldWp, M, N, K, epilogue, alpha, Y, ldY, stream
     g = L.bnn_bwn_f16_gemv

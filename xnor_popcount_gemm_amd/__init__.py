@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "BnnError", "lib", "packed_words", "padded_ld", "pack_weights", "pack_activations",
-    "xnor_gemm", "linear_fused", "fold_bn_thresholds", "dense_f32_sign_pack",
+    "xnor_gemm", "xnor_gemm_mfma", "linear_fused", "fold_bn_thresholds", "dense_f32_sign_pack",
     "dense_binact_f32", "EPI_DOT_I32", "EPI_SCALE_F32", "EPI_RESIDUAL_F32",
     "EPI_THRESH_PACK", "EPI_ALPHA_TENSOR", "EPI_BIAS_F32", "LIB_PATH",
     "weight_scale_tensor", "weight_scale_tensor_noalloc", "NOALLOC_MAX_ROWS", "quantize_act_i8", "pack_act_i8", "bwn_i8_linear", "MAX_K_I8", "bwn_f16_gemv", "MAX_K_F16",
@@ -115,6 +115,7 @@ def lib() -> ctypes.CDLL:
             "bnn_pack_weights": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
             "bnn_pack_activations": [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp],
             "bnn_xnor_gemm": [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp],
+            "bnn_xnor_gemm_mfma": [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp],
             "bnn_linear_fused": [ctypes.POINTER(_FusedArgs), _vp],
             "bnn_fold_bn_thresholds_host": [_vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _vp, _vp],
             "bnn_dense_f32_sign_pack": [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp],
@@ -241,6 +242,29 @@ def xnor_gemm(Xp: torch.Tensor, Wp: torch.Tensor, K: int, *, alpha: torch.Tensor
                                _ptr(D), _ld(D) if D is not None else 0, _ptr(alpha),
                                _ptr(Y), _ld(Y) if Y is not None else 0,
                                _stream(Xp.device)), "bnn_xnor_gemm")
+    return D, Y
+
+
+def xnor_gemm_mfma(Xp: torch.Tensor, Wp: torch.Tensor, K: int, *, alpha: torch.Tensor | None = None,
+                   want_dot: bool = True, want_scaled: bool = False,
+                   D: torch.Tensor | None = None, Y: torch.Tensor | None = None):
+    """The same D and Y as ``xnor_gemm``, computed on the fp4 matrix cores
+    (bnn_xnor_gemm_mfma: exact +-1 products)."""
+    _dev(Xp, torch.int32, "Xp")
+    _dev(Wp, torch.int32, "Wp")
+    M, N = Xp.shape[0], Wp.shape[0]
+    if want_dot and D is None:
+        D = torch.empty((M, N), dtype=torch.int32, device=Xp.device)
+    if want_scaled and Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=Xp.device)
+    if not want_dot:
+        D = None
+    if not want_scaled:
+        Y = None
+    _check(lib().bnn_xnor_gemm_mfma(_ptr(Xp), _ld(Xp), _ptr(Wp), _ld(Wp), M, N, int(K),
+                                    _ptr(D), _ld(D) if D is not None else 0, _ptr(alpha),
+                                    _ptr(Y), _ld(Y) if Y is not None else 0,
+                                    _stream(Xp.device)), "bnn_xnor_gemm_mfma")
     return D, Y
 
 

@@ -282,6 +282,24 @@ bnn_status bnn_xnor_gemm(const uint32_t* Xp, int64_t ldXp, const uint32_t* Wp, i
     return run_fused(&a, as_stream(stream));
 }
 
+bnn_status bnn_xnor_gemm_mfma(const uint32_t* Xp, int64_t ldXp, const uint32_t* Wp, int64_t ldWp,
+                              int64_t M, int64_t N, int64_t K,
+                              int32_t* D, int64_t ldD, const float* alpha, float* Y, int64_t ldY,
+                              bnn_stream_t stream)
+{
+    if (!D && !Y) return BNN_ERR_NULL;
+    bnn_fused_args a = {};
+    a.Xp = Xp; a.ldXp = ldXp; a.Wp = Wp; a.ldWp = ldWp;
+    a.M = M; a.N = N; a.K = K;
+    a.epilogue = (D ? BNN_EPI_DOT_I32 : 0u) | (Y ? BNN_EPI_SCALE_F32 : 0u);
+    a.D = D; a.ldD = ldD; a.alpha = alpha; a.Y = Y; a.ldY = ldY;
+    const bnn_status st = validate_fused(&a);
+    if (st != BNN_OK) return st;
+    if (M == 0 || N == 0) return BNN_OK;
+    return from_hip(bnn::launch_xnor_gemm_fp4(Xp, ldXp, Wp, ldWp, M, N, K, D, ldD, alpha, false, Y, ldY,
+                                              as_stream(stream)));
+}
+
 bnn_status bnn_linear_fused(const bnn_fused_args* args, bnn_stream_t stream)
 {
     const bnn_status st = validate_fused(args);

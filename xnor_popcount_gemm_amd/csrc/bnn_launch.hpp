@@ -96,6 +96,11 @@ hipError_t launch_act_i8(const float* X, int64_t ldX, const int8_t* Xq_in, int64
                          float* xscale, hipStream_t s);
 
 // True when the bit-plane GEMV serves binary weights x INT8 activations.
+// The XNOR GEMM on the fp4 matrix cores (exact +-1 products): D and/or Y = alpha * D.
+hipError_t launch_xnor_gemm_fp4(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
+                                int64_t M, int64_t N, int64_t K, int32_t* D, int64_t ldD,
+                                const float* alpha, bool alpha_tensor, float* Y, int64_t ldY, hipStream_t s);
+
 // Binary weights x fp16 activations, one activation row: y = alpha * sum_k s x_k.
 int64_t f16_gemv_max_k();
 hipError_t launch_bwn_f16_gemv(const uint16_t* X, const uint32_t* Wp, int64_t ldW, int64_t N, int64_t K,
