@@ -59,6 +59,20 @@ def test_xnor_gemm_mfma_matches_oracle(bnn, M, N, K):
     np.testing.assert_array_equal(host(Y).view(np.uint32), oracle.scale(D_ref, a).view(np.uint32))
 
 
+@pytest.mark.parametrize("tile", ["8x4", "4x8", "8x8"])
+@pytest.mark.parametrize("M,N,K", [(300, 100, 777), (257, 129, 1100), (130, 513, 16385), (1, 7, 33)])
+def test_xnor_gemm_mfma_every_tile(bnn, tile, M, N, K, monkeypatch):
+    """The tuning override BNN_MFMA_TILE (MFMA blocks per wave) changes no result."""
+    monkeypatch.setenv("BNN_MFMA_TILE", tile)
+    xs, ws, Xp, Wp, a = _case(8200 + K + M, M, N, K)
+    banner(f"xnor_gemm_mfma tile={tile} M={M} N={N} K={K}")
+    D, Y = bnn.xnor_gemm_mfma(Xp, Wp, K, alpha=dev(a), want_dot=True, want_scaled=True)
+    torch.cuda.synchronize()
+    D_ref = oracle.dot(xs, ws)
+    np.testing.assert_array_equal(host(D), D_ref)
+    np.testing.assert_array_equal(host(Y).view(np.uint32), oracle.scale(D_ref, a).view(np.uint32))
+
+
 def test_xnor_gemm_mfma_wide_ld_and_strided_outputs(bnn):
     """Leading dimensions past the data words (their pad words are the
     packed layout's zeros), outputs with ld > N, D alone and Y alone."""
