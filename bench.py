@@ -609,6 +609,40 @@ def mlp_bench(bnn, torch, reps=20, warmup=3):
     kw = (h + 31) // 32
     hidden_ops = 2.0 * B * h * kw
     hid_ms = [median(per[i]) for i in (1, 2, 3)]
+    # The same step replayed from a HIP graph (no per-launch host work): the
+    # whole step, and each hidden layer as a graph of `reps` back-to-back
+    # launches (time per launch = replay time / reps); the replayed logits
+    # must equal the eager ones bit for bit.
+    ref = logits.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(None)
+    graph.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(logits, ref))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall_g = time.perf_counter() - t0
+    same = same and bool(torch.equal(logits, ref))
+    hid_ms_g = []
+    for i, (Wp, tau, d) in enumerate(layers):
+        gl = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gl):
+            for _ in range(reps):
+                bnn.linear_fused(acts[i], Wp, h, bnn.EPI_THRESH_PACK, tau=tau, dir=d, Op=acts[i + 1])
+        gl.replay()
+        ev = [Ev() for _ in range(3)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e.start()
+            gl.replay()
+            e.stop()
+        torch.cuda.synchronize()
+        hid_ms_g.append(median([e.ms() for e in ev]) / reps)
+        del gl
+    del graph
     return dict(
         batch=B, step_ms=1e3 * wall / reps, images_per_s=B * reps / wall,
         first_layer_ms=median(per[0]),
@@ -616,6 +650,10 @@ def mlp_bench(bnn, torch, reps=20, warmup=3):
         hidden_layer_ms=hid_ms,
         hidden_layer_int_valu_frac=[hidden_ops / (t * 1e-3) / PEAK_INT_OPS for t in hid_ms],
         last_layer_ms=median(per[4]),
+        graph_step_ms=1e3 * wall_g / reps, graph_images_per_s=B * reps / wall_g,
+        graph_hidden_layer_ms=hid_ms_g,
+        graph_hidden_layer_int_valu_frac=[hidden_ops / (t * 1e-3) / PEAK_INT_OPS for t in hid_ms_g],
+        graph_replay_matches_eager=same,
     )
 
 
@@ -1063,6 +1101,8 @@ def main():
             mlp = sec["binary_mlp_batch1024"]
             mlp["hidden_layer_frac_of_probe_mix"] = [round(f * PEAK_INT_OPS / mix, 4)
                                                      for f in mlp["hidden_layer_int_valu_frac"]]
+            mlp["graph_hidden_layer_frac_of_probe_mix"] = [round(f * PEAK_INT_OPS / mix, 4)
+                                                           for f in mlp["graph_hidden_layer_int_valu_frac"]]
             for c in sec["conv_block"] + sec["conv_chain"]:
                 lane_ops = 2.0 * c["M"] * c.get("Cout", c["C"]) * (9 * c["C"] // 32)
                 c["block_bound_achievable_ms"] = 1e3 * max(c["block_bytes"] / PEAK_HBM, lane_ops / mix)

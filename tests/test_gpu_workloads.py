@@ -122,6 +122,46 @@ def test_workload2_binary_mlp(bnn):
     assert_f32_close(host(logits), ref["logits"], scale=1e-3 * W5sum, what="logits")
 
 
+def test_workload2_mlp_graph_replay(bnn):
+    """The MLP forward (first layer, three THRESH_PACK layers, last layer)
+    captured once in a HIP graph and replayed three times, with eager work and
+    synchronisation between the replays: every replay's packed activations and
+    logits equal the eager run's bit for bit."""
+    X, W1, hidden, W5 = _mlp_inputs()
+    h = W1.shape[0]
+    banner("workload2 MLP graph replay")
+    acts_e, _, taus, logits_e = run_mlp_gpu(bnn, X, W1, hidden, W5)
+    Xd, W1d, W5d = dev(X), dev(W1), dev(W5)
+    layers = []
+    for (Wh, *_), (tau, d) in zip(hidden, taus):
+        Wp, _ = bnn.pack_weights(dev(Wh))
+        layers.append((Wp, dev(tau), dev(d)))
+    ld = bnn.padded_ld(h)
+    acts = [torch.empty((X.shape[0], ld), dtype=torch.int32, device="cuda") for _ in range(4)]
+    logits = torch.empty((X.shape[0], W5.shape[0]), dtype=torch.float32, device="cuda")
+
+    def step():
+        bnn.dense_f32_sign_pack(Xd, W1d, out=acts[0])
+        for i, (Wp, tau, d) in enumerate(layers):
+            bnn.linear_fused(acts[i], Wp, h, bnn.EPI_THRESH_PACK, tau=tau, dir=d, Op=acts[i + 1])
+        bnn.dense_binact_f32(acts[3], W5d, h, out=logits)
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        for t in acts + [logits]:
+            t.fill_(-1)                            # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(4):
+            _equal(host_u32(acts[i]), host_u32(acts_e[i]), f"replay {r} layer {i + 1} packed signs")
+        _equal(host(logits).view(np.uint32), host(logits_e).view(np.uint32), f"replay {r} logits")
+
+
 # ---------------------------------------------------------------- workload 3
 @pytest.mark.parametrize("shape", workloads.WORKLOADS[3]["shapes"], ids=lambda s: f"N{s['N']}_K{s['K']}")
 def test_workload3_gemv_exact_shape(bnn, shape):
