@@ -99,7 +99,11 @@ def _ternary_case(bnn, seed, N, K):
                                    # GEMV rows of 8 granules per lane, up to the widest K
                                    # the GEMV takes; one word past it runs the GEMM
                                    (1, 130, 40000), (3, 130, 65536), (2, 40, 65537)])
-def test_ternary_binary_linear_fused(bnn, M, N, K):
+@pytest.mark.parametrize("kernel", ["wlane", "rows"])
+def test_ternary_binary_linear_fused(bnn, kernel, M, N, K, monkeypatch):
+    """Both GEMM kernels (one weight row per lane, one activation row per
+    lane); small M takes the GEMV either way."""
+    monkeypatch.setenv("BNN_TERN_KERNEL", kernel)
     T, gam, Sp, Zp, nnz, g = _ternary_case(bnn, 9100 + K, N, K)
     X = workloads.normal_f32(9200 + K, (M, K))
     xs = oracle.sign(X)
@@ -111,7 +115,7 @@ def test_ternary_binary_linear_fused(bnn, M, N, K):
     alpha_vec = np.full(N, gam, np.float32)
     tau, dirv = bnn.fold_bn_thresholds(gma, beta, mean, var, eps, alpha_vec)
     f = bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32 | bnn.EPI_ALPHA_TENSOR | bnn.W_TERNARY
-    banner(f"ternary x binary fused M={M} N={N} K={K}")
+    banner(f"ternary x binary fused kernel={kernel} M={M} N={N} K={K}")
     out = bnn.linear_fused(Xp, Sp, K, f | bnn.EPI_BIAS_F32 | bnn.EPI_RESIDUAL_F32, alpha=g, bias=dev(bias),
                            R=dev(R), Zp=Zp, nnz=nnz)
     th = bnn.linear_fused(Xp, Sp, K, bnn.EPI_THRESH_PACK | bnn.W_TERNARY, tau=dev(tau), dir=dev(dirv),
@@ -124,8 +128,38 @@ def test_ternary_binary_linear_fused(bnn, M, N, K):
     np.testing.assert_array_equal(host_u32(th["Op"]), oracle.pack_signs(s_ref, ld=ld))
 
 
+@pytest.mark.parametrize("M,N,K", [(33, 1, 100), (64, 63, 64), (31, 65, 1000), (97, 255, 2049),
+                                   (40, 256, 4096), (70, 257, 300), (130, 300, 31)])
+def test_ternary_gemm_weight_row_lanes(bnn, M, N, K):
+    """The GEMM with one weight row per lane: ragged row tiles (M not a
+    multiple of 32), waves past N and a partial last wave (N around 64 and
+    256), K tails below one chunk and one word; per-row alpha, D, Y with bias
+    and residual, and SIGN_PACK whose pad bits and pad words start non-zero."""
+    T, gam, Sp, Zp, nnz, g = _ternary_case(bnn, 9800 + K + N, N, K)
+    X = workloads.normal_f32(9801 + K, (M, K))
+    D_ref = oracle.dot_i8(oracle.sign(X), T)
+    a = np.abs(workloads.normal_f32(9802 + N, (N,))) + np.float32(0.1)
+    bias = workloads.normal_f32(9803 + N, (N,))
+    R = workloads.normal_f32(9804 + N, (M, N))
+    b1 = workloads.normal_f32(9805 + N, (N,)) * np.float32(0.5)
+    Xp = bnn.pack_activations(dev(X))
+    ld = bnn.padded_ld(N)
+    Op = torch.full((M, ld), -1, dtype=torch.int32, device="cuda")
+    f = (bnn.EPI_DOT_I32 | bnn.EPI_SCALE_F32 | bnn.EPI_BIAS_F32 | bnn.EPI_RESIDUAL_F32 | bnn.EPI_SIGN_PACK
+         | bnn.W_TERNARY)
+    banner(f"ternary gemm weight-row lanes M={M} N={N} K={K}")
+    out = bnn.linear_fused(Xp, Sp, K, f, alpha=dev(a), bias=dev(bias), R=dev(R), beta=dev(b1), Op=Op,
+                           Zp=Zp, nnz=nnz)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out["D"]), D_ref)
+    Y_ref = oracle.scale_bias_residual(D_ref, a, bias, R)
+    _bits_equal(host(out["Y"]), Y_ref, "Y")
+    np.testing.assert_array_equal(host_u32(Op), oracle.pack_signs(oracle.rsign(Y_ref, b1), ld=ld))
+
+
 @pytest.mark.parametrize("tn", [8, 16, 32, 64])
 def test_ternary_gemm_every_column_tile(bnn, tn, monkeypatch):
+    monkeypatch.setenv("BNN_TERN_KERNEL", "rows")
     M, N, K = 300, 130, 1000
     T, gam, Sp, Zp, nnz, g = _ternary_case(bnn, 9600, N, K)
     X = workloads.normal_f32(9601, (M, K))
