@@ -132,6 +132,8 @@ bnn_status run_fused(const bnn_fused_args* a, hipStream_t s) {
     e.beta = a->beta;
     if (bnn::gemv_eligible(a->M, a->K, e.flags))
         return from_hip(bnn::launch_xnor_gemv(a->Xp, a->ldXp, a->Wp, a->ldWp, a->M, a->N, a->K, e, s));
+    if ((e.flags & bnn::W_TERNARY) && bnn::tern_gemm_t_eligible())
+        return from_hip(bnn::launch_tern_gemm_t(a->Xp, a->ldXp, a->Wp, a->ldWp, a->M, a->N, a->K, e, s));
     return from_hip(bnn::launch_xnor_gemm(a->Xp, a->ldXp, a->Wp, a->ldWp, a->M, a->N, a->K, e, s));
 }
 

@@ -81,7 +81,8 @@ hipError_t launch_xnor_conv3x3(const uint32_t* Xp, int64_t ldX, const uint32_t* 
                                const Epilogue& e, hipStream_t s);
 
 // Ternary weights (e.Zp, e.nnz) x binary activations with one weight row per
-// lane; tern_gemm_t_eligible says whether launch_xnor_gemm takes it.
+// lane; tern_gemm_t_eligible says whether it serves a ternary GEMM (else the
+// ternary mode of launch_xnor_gemm).
 bool tern_gemm_t_eligible();
 hipError_t launch_tern_gemm_t(const uint32_t* Xp, int64_t ldX, const uint32_t* Sp, int64_t ldW,
                               int64_t M, int64_t N, int64_t K, const Epilogue& e, hipStream_t s);

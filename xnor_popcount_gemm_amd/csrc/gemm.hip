@@ -7,7 +7,6 @@ namespace bnn {
 hipError_t launch_xnor_gemm(const uint32_t* Xp, int64_t ldX, const uint32_t* Wp, int64_t ldW,
                             int64_t M, int64_t N, int64_t K, const Epilogue& e, hipStream_t s)
 {
-    if ((e.flags & W_TERNARY) && tern_gemm_t_eligible()) return launch_tern_gemm_t(Xp, ldX, Wp, ldW, M, N, K, e, s);
     const int tn = pick_tile_cols(M, N);
     // Epilogue: D and Y staged through LDS, so that stores cover whole row
     // segments (row-per-lane stores from registers write partial lines:

@@ -93,14 +93,17 @@ __device__ __forceinline__ void tern_chunk(uint32_t (&acc)[kTM], const uint32_t 
 {
     int64_t ldx = ldX;
     asm volatile("" : "+s"(ldx));   // keep the row offsets out of the loop preheader
+    // full tiles walk the rows with one running pointer (two 64-bit adds per
+    // pair, not a multiply per row); a partial tile clamps each row
+    cptr_u32 pr = (cptr_u32)(xbase + k0);
     auto load_x = [&](uint32_t (&u)[2][KCC], int j) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const int r = FULLM ? j + c : min(j + c, mlast);
-            const cptr_u32 p = (cptr_u32)(xbase + (int64_t)r * ldx + k0);
+            const cptr_u32 p = FULLM ? pr + c * ldx : (cptr_u32)(xbase + (int64_t)min(j + c, mlast) * ldx + k0);
 #pragma unroll
             for (int kk = 0; kk < KCC; ++kk) u[c][kk] = p[kk];
         }
+        if (FULLM) pr += 2 * ldx;
     };
     uint32_t xc[2][KCC];
     load_x(xc, 0);
