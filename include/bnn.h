@@ -371,15 +371,16 @@ bnn_status bnn_bwn_i8_linear(const bnn_i8_args* args, bnn_stream_t stream);
  *  + 6 rounded additions (G = lanes per weight row: the smallest power of
  *  two >= ceil(K/128), at most 64), so |S - S_exact| <= n u / (1 - n u) *
  *  sum_k |x[m,k]| with u = 2^-24.
- *  One launch per activation row: the packed weights stream once per row
- *  (the batch-1 decode case of [P2] "Bandwidth math").
+ *  (The default kernel's sums are shallower: at most 22 additions.)
+ *  One launch per activation row (two for K > 8192: the first leaves its
+ *  partial sum in Y): the packed weights stream once per row (the batch-1
+ *  decode case of [P2] "Bandwidth math").
  *  X     fp16 bit patterns [M, ldX]: 16-byte aligned, ldX % 8 == 0, ldX >= K;
  *  Wp    packed weights [N, ldWp] (packed layout, ldWp % 4 == 0);
  *  alpha fp32 [N], or [1] with BNN_EPI_ALPHA_TENSOR;
  *  Y     fp32 [M, ldY], ldY >= N, 4-byte aligned.
  *  epilogue: BNN_EPI_SCALE_F32 [| BNN_EPI_ALPHA_TENSOR]; anything else ->
- *  BNN_ERR_UNSUPPORTED.  1 <= K <= BNN_MAX_K_F16 (the activations of a lane
- *  stay in registers). */
+ *  BNN_ERR_UNSUPPORTED.  1 <= K <= BNN_MAX_K_F16. */
 bnn_status bnn_bwn_f16_gemv(const uint16_t* X, int64_t ldX, const uint32_t* Wp, int64_t ldWp,
                             int64_t M, int64_t N, int64_t K, uint32_t epilogue,
                             const float* alpha, float* Y, int64_t ldY, bnn_stream_t stream);

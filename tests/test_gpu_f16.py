@@ -83,7 +83,10 @@ def _within_bound(Y, x16, S, a, K, what):
 
 
 SHAPES = [(1, 11008, 4096), (1, 4096, 11008), (2, 300, 1000), (1, 7, 1), (1, 130, 33), (1, 64, 16384),
-          (2, 257, 16383), (1, 1, 128), (3, 65, 129), (1, 33, 8200)]
+          (2, 257, 16383), (1, 1, 128), (3, 65, 129), (1, 33, 8200),
+          # the table kernel's size classes and K pieces: 64 KiB / 128 KiB tables,
+          # one pass up to K = 8192, a second pass of one element after it
+          (1, 70, 4097), (2, 129, 8192), (1, 65, 8193), (1, 3, 2049)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -138,3 +141,26 @@ def test_f16_gemv_many_rows_random_words(bnn, N, K):
     ws = oracle.unpack_signs(words[rows], K)
     S = oracle.bwn_f16_units(x, ws).astype(np.float64) * U
     _within_bound(Y[:, rows], x, S, a[rows], K, "Y")
+
+
+@pytest.mark.parametrize("variant", [{"BNN_F16_KERNEL": "regs"}, {"BNN_F16_PIECE": "4096"}])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 1000), (1, 257, 4096), (2, 129, 11008), (1, 65, 16384), (1, 9, 8193)])
+def test_f16_gemv_variants(bnn, variant, M, N, K, monkeypatch):
+    """The register-held-activation kernel (BNN_F16_KERNEL=regs) and the
+    table kernel in 4096-wide K pieces (BNN_F16_PIECE=4096), both within the
+    stated bound, and bit-exact for integer activations."""
+    for k, v in variant.items():
+        monkeypatch.setenv(k, v)
+    rng = np.random.default_rng(9300 + K)
+    W = workloads.normal_f32(9301 + N, (N, K))
+    a = oracle.alpha(W)
+    Wp = _packed(W)
+    banner(f"bwn f16 gemv {variant} M={M} N={N} K={K}")
+    xi = rng.integers(-8, 9, size=(M, K)).astype(np.float16)
+    Y = _run(bnn, Wp, K, xi, a)
+    S32 = (oracle.bwn_f16_units(xi, oracle.sign(W)) >> 24).astype(np.float32)
+    np.testing.assert_array_equal(Y.view(np.uint32), (a[None, :] * S32).astype(np.float32).view(np.uint32))
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    Y = _run(bnn, Wp, K, x, a)
+    S, _ = oracle.bwn_f16(x, W, np.ones(N, np.float32))
+    _within_bound(Y, x, S, a, K, "Y")

@@ -13,26 +13,44 @@
 //    Principles", sections "The cost of a neural network step" and
 //    "Bandwidth math".
 //
-// Arithmetic.  A weight word W covers activations x[32w .. 32w+31].  They sit
-// in a lane's registers as 16 fp16 pairs, pair p = (x[32w+p], x[32w+p+16]),
-// so the two sign bits of pair p are bits p and p+16 of W, and one shift by
-// 15-p moves them onto the two fp16 sign bits (15 and 31):
+// Two kernels compute S = sum_k s_k x_k (s_k = +1 for bit 0, -1 for bit 1)
+// with exact products and fp32 additions in a fixed order; Y = fl32(alpha S).
+//
+// Table kernel (the default, every K).  The signs of 4 consecutive
+// activations are one nibble of a weight word, so S is a sum of one of 16
+// signed sums per nibble.  A workgroup writes all 16 sums of every group of
+// 4 activations into LDS (512 bytes per weight word), then streams weight
+// rows: per nibble one shift, one and-or (the LDS address), one LDS read and
+// one fp32 add -- 24 VALU ops and 8 LDS reads per weight word.  The entries
+// of one table sit in one bank and the lanes of a read use distinct banks,
+// so a read costs what a conflict-free one does.  Rows longer than 8192 run
+// as passes over 8192-wide K pieces (the tables of a piece fill 128 KiB).
+//
+// Register kernel (BNN_F16_KERNEL=regs).  A weight word W covers
+// activations x[32w .. 32w+31].  They sit in a lane's registers as 16 fp16
+// pairs, pair p = (x[32w+p], x[32w+p+16]), so the two sign bits of pair p
+// are bits p and p+16 of W, and one shift by 15-p moves them onto the two
+// fp16 sign bits (15 and 31):
 //     flip_p = (W << (15 - p)) & 0x80008000
 //     acc    = dot2(pair_p XOR flip_p, (1.0, 1.0), acc)     (v_dot2_f32_f16)
-// The products are +-x exactly; only the fp32 additions round.  Activations
-// past K are 0, so the weights' pad bits add nothing.
+// 47 VALU ops per weight word.
+//
+// In both, activations past K are 0, so the weights' pad bits add nothing.
 //
 // Mapping (as the binary GEMV): G lanes (a power of two covering the row's
 // 16-byte weight granules, at most 64) share one weight row, 64/G rows per
 // wave step, U row-steps' weight loads in flight before the first is used.
-// A lane keeps its granules' 128 activations per granule as 64 pair
-// registers for the whole kernel and sums a row in four dot2 chains (one per
-// word of a granule, added pairwise at the end); the G partial sums of a
-// row meet in a fixed DPP tree and the group's last lane writes y.  The
-// deepest term passes through 2 * 16 CPL additions of its chain (a dot2 may
-// round twice), 2 of the pairwise sum and GLOG2 <= 6 of the tree: within
-// the 128 CPL + 6 the interface states.
+// The register kernel keeps a lane's 128 activations per granule as 64 pair
+// registers and sums a row in four dot2 chains (one per word of a granule,
+// added pairwise at the end); the G partial sums of a row meet in a fixed
+// DPP tree and the group's last lane writes y.  The deepest term passes
+// through 2 * 16 CPL additions of its chain (a dot2 may round twice), 2 of
+// the pairwise sum and GLOG2 <= 6 of the tree: within the 128 CPL + 6 the
+// interface states.  The table kernel's depth is smaller (see
+// k_bwn_f16_lut).
 #include <stdlib.h>
+
+#include <algorithm>
 
 #include "bnn_device.hpp"
 #include "bnn_launch.hpp"
@@ -158,9 +176,200 @@ __global__ __launch_bounds__(kThreads) void k_bwn_f16_gemv(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Table variant.  Each weight nibble (4 consecutive bits of a word, i.e. the
+// signs of 4 consecutive activations) selects one of 16 signed sums of those
+// activations; a workgroup computes all of them once into LDS and then each
+// nibble of each weight row costs one LDS read and one fp32 add instead of
+// 4 sign flips and 2 dot2 halves.
+//   entry(w, i, nib) = ((s0 x0 + s1 x1) + s2 x2) + s3 x3,  x_q = x[32w+4i+q],
+//   s_q = -1 if bit q of nib is set, else +1 (activations past K are 0).
+// Layout: the 16 entries of one (w, i) table sit in one LDS bank, 32 words
+// apart, and the bank is the lane's: slot s = c % 32 for the word's 16-byte
+// granule c when a row has >= 32 lanes, else (row copy) G + c, with the
+// tables stored once per row copy.  So the 64 lanes of a read touch each
+// bank from at most 2 lanes, whatever the nibbles.  A block of 512 words
+// holds the 32 slots' tables of one (granule group c / 32, word j of the
+// granule, nibble i): block ((c / 32) 4 + j) 8 + i, word nib 32 + s.
+// A lane sums 4 chains (one per word of its granule), each adding the 8
+// entries of its word in nibble order: a term passes through at most 3 (its
+// entry) + 8 (its chain) + 2 (the pairwise sum) + GLOG2 <= 6 (the lane
+// tree) rounded additions, plus one per later K piece (at most 3), i.e. at
+// most 22 -- below the 128 ceil(ceil(K/128) / G) + 6 >= 134 of the
+// register variant, which the interface states.
+// A long row runs in passes over K pieces (mode: 0 single pass, Y = alpha S;
+// 1 first pass, Y = S; 3 middle pass, Y = Y + S; 2 last pass,
+// Y = alpha (Y + S)), X and Wp then pointing at the piece.
+template <int GLOG2, int U, int TBLOCKS>
+__global__ __launch_bounds__(1024) void k_bwn_f16_lut(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wp, int64_t ldW, int N, int K,
+    const float* __restrict__ alpha, int astr, float* __restrict__ Y, int mode)
+{
+    constexpr int G = 1 << GLOG2;
+    constexpr int RPS = 64 / G;                   // rows per wave step
+    static_assert(G >= 32 || TBLOCKS == 32, "narrow rows: one granule group, row copies");
+    __shared__ float tab[TBLOCKS * 512];
+    const int Kw = (K + 31) >> 5;
+    const int Kw4 = (Kw + 3) >> 2;
+
+    // one thread per (w, i) table: its 4 activations in one 8-byte load, the
+    // 16 entries by extending the 2, 4 and 8 partial sums of the first 1, 2
+    // and 3 terms (28 additions, each entry in the order above)
+    for (int tix = threadIdx.x; tix < TBLOCKS * 32; tix += blockDim.x) {
+        const int blk = tix >> 5, sl = tix & 31;
+        const int i = blk & 7, j = (blk >> 3) & 3;
+        const int c = G >= 32 ? (blk >> 5) * 32 + sl : (sl & (G - 1));
+        const int k0 = 32 * (4 * c + j) + 4 * i;
+        float x[4];
+        if (k0 + 4 <= K) {
+            const uint2 v = *reinterpret_cast<const uint2*>(X + k0);
+            x[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.x & 0xFFFFu));
+            x[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.x >> 16));
+            x[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.y & 0xFFFFu));
+            x[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.y >> 16));
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[q] = (k0 + q < K) ? (float)__builtin_bit_cast(_Float16, X[k0 + q]) : 0.0f;
+        }
+        float p[16];
+        p[0] = x[0]; p[1] = -x[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) {
+#pragma unroll
+            for (int n = (1 << q) - 1; n >= 0; --n) {      // bit q of the entry index: the sign of x[q]
+                p[n + (1 << q)] = p[n] - x[q];
+                p[n] = p[n] + x[q];
+            }
+        }
+#pragma unroll
+        for (int nib = 0; nib < 16; ++nib) tab[blk * 512 + nib * 32 + sl] = p[nib];
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int gl = lane & (G - 1);
+    const int go = lane >> GLOG2;
+    // byte offset of the lane's tables for word j of its granule (nibble i
+    // adds i * 2048 bytes, nib * 128); granules past the row's read zeros
+    const int sl = G >= 32 ? (gl & 31) : (((go * G) & 31) | gl);
+    uint32_t L[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) L[j] = (uint32_t)(((G >= 32 ? (gl >> 5) * 4 : 0) + j) * 8 * 2048 + sl * 4);
+    const char* tb = reinterpret_cast<const char*>(tab);
+    (void)Kw4;
+
+    const int64_t nsteps = ((int64_t)N + RPS - 1) / RPS;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t s0 = wave * U; s0 < nsteps; s0 += nwaves * U) {
+        u32x4 wv[U];
+        float av[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = (s0 + u) * RPS + go;
+            wv[u] = (u32x4){0u, 0u, 0u, 0u};
+            if (row < N && gl < Kw4)
+                wv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wp + row * ldW + 4 * gl));
+            av[u] = row < N ? alpha[row * astr] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = (s0 + u) * RPS + go;
+            float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            const uint32_t wj[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t t = (i <= 1) ? (wj[j] << (7 - 4 * i)) : (wj[j] >> (4 * i - 7));
+                    const uint32_t a = (t & 0x780u) | L[j];
+                    acc4[j] += *reinterpret_cast<const float*>(tb + a + i * 2048);
+                }
+            }
+            float acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+            acc = fsum_to_last<GLOG2>(acc);
+            if (gl == G - 1 && row < N) {
+                if (mode == 0) Y[row] = av[u] * acc;
+                else if (mode == 1) Y[row] = acc;
+                else if (mode == 3) Y[row] = Y[row] + acc;
+                else Y[row] = av[u] * (Y[row] + acc);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 }  // namespace
 
 int64_t f16_gemv_max_k() { return 64 * 2 * 128; }
+
+namespace {
+
+// Tuning override: BNN_F16_KERNEL=regs keeps the register variant for every K.
+bool f16_regs_from_env() {
+    const char* v = getenv("BNN_F16_KERNEL");
+    return v && v[0] == 'r';
+}
+
+// The table variant: 32 blocks of 2 KiB per group of 32 granules (64 KiB
+// up to K = 4096, two 1024-thread workgroups per CU; 128 KiB up to 8192,
+// one).  Longer rows run as passes over pieces of 8192 (at most two: K is
+// at most 16384), the first leaving its raw sum in Y.
+hipError_t launch_lut_piece(const uint16_t* X, const uint32_t* Wp, int64_t ldW, int64_t N, int64_t K,
+                            const float* alpha, int astr, float* Y, int mode, hipStream_t s, int cus)
+{
+    const int64_t kw4 = ((K + 31) / 32 + 3) / 4;
+    int glog2 = 0;
+    while ((1 << glog2) < kw4 && glog2 < 6) ++glog2;
+    const int rps = 64 >> glog2;
+    const int64_t steps = (N + rps - 1) / rps;
+    const int tblocks = kw4 <= 32 ? 32 : 64;
+    const int per_cu = tblocks == 32 ? 2 : 1;
+    const bool unroll = steps >= (int64_t)cus * per_cu * 16 * 8;
+    const int U = unroll ? 4 : 1;
+    const int64_t waves = (steps + U - 1) / U;
+    int64_t blocks = (waves + 15) / 16;
+    const int64_t cap = (int64_t)cus * per_cu;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    const dim3 grid((unsigned)blocks), block(1024);
+    const int n = (int)N, k = (int)K;
+#define BNN_LUT(GL, UU, TB) hipLaunchKernelGGL((k_bwn_f16_lut<GL, UU, TB>), grid, block, 0, s, X, Wp, ldW, n, k, alpha, astr, Y, mode)
+#define BNN_LUT_U(GL, TB) do { if (U == 1) BNN_LUT(GL, 1, TB); else BNN_LUT(GL, 4, TB); } while (0)
+    switch (glog2) {
+        case 0: BNN_LUT_U(0, 32); break;
+        case 1: BNN_LUT_U(1, 32); break;
+        case 2: BNN_LUT_U(2, 32); break;
+        case 3: BNN_LUT_U(3, 32); break;
+        case 4: BNN_LUT_U(4, 32); break;
+        case 5: BNN_LUT_U(5, 32); break;
+        default: BNN_LUT_U(6, 64); break;
+    }
+#undef BNN_LUT_U
+#undef BNN_LUT
+    return hipGetLastError();
+}
+
+hipError_t launch_lut(const uint16_t* X, const uint32_t* Wp, int64_t ldW, int64_t N, int64_t K,
+                      const float* alpha, bool alpha_tensor, float* Y, hipStream_t s, int cus)
+{
+    int64_t piece = 8192;                         // 64 granules: the 128 KiB table
+    if (const char* v = getenv("BNN_F16_PIECE")) {          // tuning override: 4096 or 8192
+        const int64_t p = atoll(v);
+        if (p == 4096 || p == 8192) piece = p;
+    }
+    const int astr = alpha_tensor ? 0 : 1;
+    if (K <= piece) return launch_lut_piece(X, Wp, ldW, N, K, alpha, astr, Y, 0, s, cus);
+    for (int64_t k0 = 0; k0 < K; k0 += piece) {
+        const int mode = k0 == 0 ? 1 : (k0 + piece >= K ? 2 : 3);
+        const hipError_t e = launch_lut_piece(X + k0, Wp + k0 / 32, ldW, N, std::min(piece, K - k0), alpha, astr, Y,
+                                              mode, s, cus);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
 
 hipError_t launch_bwn_f16_gemv(const uint16_t* X, const uint32_t* Wp, int64_t ldW, int64_t N, int64_t K,
                                const float* alpha, bool alpha_tensor, float* Y, hipStream_t s)
@@ -173,6 +382,7 @@ hipError_t launch_bwn_f16_gemv(const uint16_t* X, const uint32_t* Wp, int64_t ld
     const int rps = 64 / G;
     const int64_t steps = (N + rps - 1) / rps;
     const int cus = num_cus();
+    if (!f16_regs_from_env()) return launch_lut(X, Wp, ldW, N, K, alpha, alpha_tensor, Y, s, cus);
     const bool unroll = steps >= (int64_t)cus * 4 * 8 * 4;
     const int U = unroll ? (cpl == 1 ? 4 : 2) : 1;
     const int64_t waves = (steps + U - 1) / U;
