@@ -404,9 +404,9 @@ def f16_gemv_bench(bnn, torch, N, K, reps=20):
         N=N, K=K, copies=G, stream_ms_mean=statistics.mean(ms), stream_ms_median=median(ms),
         stream_bytes=bytes_stream, stream_GBps=bytes_stream / t_stream / 1e9,
         stream_frac_hbm=bytes_stream / t_stream / PEAK_HBM,
-        # per weight word and lane (table kernel): 8 shifts, 8 and-ors (LDS
-        # addresses), 8 fp32 adds of the 8 table entries read from LDS
-        stream_valu_frac=24.0 * Nt * kw / t_stream / PEAK_INT_OPS,
+        # per weight word and lane (table kernel): 8 SDWA ops writing the
+        # nibbles into LDS addresses, 8 fp32 adds of the table entries read
+        stream_valu_frac=16.0 * Nt * kw / t_stream / PEAK_INT_OPS,
         exact_shape_cold_us_per_call=1e3 * per_call_ms,
     )
     del Wst, ast, Wp, a, Y, graph

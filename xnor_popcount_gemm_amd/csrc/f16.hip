@@ -180,17 +180,21 @@ __global__ __launch_bounds__(kThreads) void k_bwn_f16_gemv(
 // Table variant.  Each weight nibble (4 consecutive bits of a word, i.e. the
 // signs of 4 consecutive activations) selects one of 16 signed sums of those
 // activations; a workgroup computes all of them once into LDS and then each
-// nibble of each weight row costs one LDS read and one fp32 add instead of
-// 4 sign flips and 2 dot2 halves.
+// nibble of each weight row costs one address op, one LDS read and one fp32
+// add instead of 4 sign flips and 2 dot2 halves.
 //   entry(w, i, nib) = ((s0 x0 + s1 x1) + s2 x2) + s3 x3,  x_q = x[32w+4i+q],
 //   s_q = -1 if bit q of nib is set, else +1 (activations past K are 0).
-// Layout: the 16 entries of one (w, i) table sit in one LDS bank, 32 words
-// apart, and the bank is the lane's: slot s = c % 32 for the word's 16-byte
-// granule c when a row has >= 32 lanes, else (row copy) G + c, with the
-// tables stored once per row copy.  So the 64 lanes of a read touch each
-// bank from at most 2 lanes, whatever the nibbles.  A block of 512 words
-// holds the 32 slots' tables of one (granule group c / 32, word j of the
-// granule, nibble i): block ((c / 32) 4 + j) 8 + i, word nib 32 + s.
+// Layout (byte address of an entry):
+//   h 65536 + (g / 2) 4096 + nib 256 + (g % 2) 128 + s 4
+// for word j of 16-byte granule c (w = 4c + j), nibble i, g = 8 j + i; with
+// >= 32 lanes per row s = c % 32 and h = c / 32, with fewer (row copies)
+// s = (row group * G) % 32 + c and h = 0, the tables stored once per copy.
+//  - The 16 entries of one table sit in one bank (s), and the lanes of a read
+//    use distinct banks but for pairs: any nibbles cost a conflict-free read.
+//  - A lane's address register holds h, nib and s; g is the read's immediate
+//    offset, so per nibble one SDWA op writes the nibble into byte 1 of the
+//    register (the other bytes stay): an and with 15 of byte k of the weight
+//    word for nibble 2k, a shift right by 4 of it for nibble 2k + 1.
 // A lane sums 4 chains (one per word of its granule), each adding the 8
 // entries of its word in nibble order: a term passes through at most 3 (its
 // entry) + 8 (its chain) + 2 (the pairwise sum) + GLOG2 <= 6 (the lane
@@ -200,25 +204,60 @@ __global__ __launch_bounds__(kThreads) void k_bwn_f16_gemv(
 // A long row runs in passes over K pieces (mode: 0 single pass, Y = alpha S;
 // 1 first pass, Y = S; 3 middle pass, Y = Y + S; 2 last pass,
 // Y = alpha (Y + S)), X and Wp then pointing at the piece.
-template <int GLOG2, int U, int TBLOCKS>
+#define BNN_NIB_LO(K) "v_and_b32_sdwa %0, 15, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_" #K
+#define BNN_NIB_HI(K) "v_lshrrev_b32_sdwa %0, 4, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:BYTE_" #K
+template <int I>
+__device__ __forceinline__ void nib_to_byte1(uint32_t& a, uint32_t w) {
+    if constexpr (I == 0) asm(BNN_NIB_LO(0) : "+v"(a) : "v"(w));
+    else if constexpr (I == 1) asm(BNN_NIB_HI(0) : "+v"(a) : "v"(w));
+    else if constexpr (I == 2) asm(BNN_NIB_LO(1) : "+v"(a) : "v"(w));
+    else if constexpr (I == 3) asm(BNN_NIB_HI(1) : "+v"(a) : "v"(w));
+    else if constexpr (I == 4) asm(BNN_NIB_LO(2) : "+v"(a) : "v"(w));
+    else if constexpr (I == 5) asm(BNN_NIB_HI(2) : "+v"(a) : "v"(w));
+    else if constexpr (I == 6) asm(BNN_NIB_LO(3) : "+v"(a) : "v"(w));
+    else asm(BNN_NIB_HI(3) : "+v"(a) : "v"(w));
+}
+#undef BNN_NIB_LO
+#undef BNN_NIB_HI
+
+template <int I, int J>
+__device__ __forceinline__ float lut_read(const char* tb, uint32_t a) {
+    constexpr int g = 8 * J + I;
+    return *reinterpret_cast<const float*>(tb + a + (g >> 1) * 4096 + (g & 1) * 128);
+}
+
+template <int I>
+__device__ __forceinline__ void lut_nibble(float (&acc4)[4], uint32_t (&A)[2][4], const uint32_t (&wj)[4],
+                                           const char* tb) {
+    nib_to_byte1<I>(A[I & 1][0], wj[0]);
+    nib_to_byte1<I>(A[I & 1][1], wj[1]);
+    nib_to_byte1<I>(A[I & 1][2], wj[2]);
+    nib_to_byte1<I>(A[I & 1][3], wj[3]);
+    acc4[0] += lut_read<I, 0>(tb, A[I & 1][0]);
+    acc4[1] += lut_read<I, 1>(tb, A[I & 1][1]);
+    acc4[2] += lut_read<I, 2>(tb, A[I & 1][2]);
+    acc4[3] += lut_read<I, 3>(tb, A[I & 1][3]);
+}
+
+template <int GLOG2, int U, int NH>
 __global__ __launch_bounds__(1024) void k_bwn_f16_lut(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Wp, int64_t ldW, int N, int K,
     const float* __restrict__ alpha, int astr, float* __restrict__ Y, int mode)
 {
     constexpr int G = 1 << GLOG2;
     constexpr int RPS = 64 / G;                   // rows per wave step
-    static_assert(G >= 32 || TBLOCKS == 32, "narrow rows: one granule group, row copies");
-    __shared__ float tab[TBLOCKS * 512];
+    static_assert(G >= 32 || NH == 1, "narrow rows: one granule group, row copies");
+    __shared__ float tab[NH * 16384];
     const int Kw = (K + 31) >> 5;
     const int Kw4 = (Kw + 3) >> 2;
 
     // one thread per (w, i) table: its 4 activations in one 8-byte load, the
     // 16 entries by extending the 2, 4 and 8 partial sums of the first 1, 2
     // and 3 terms (28 additions, each entry in the order above)
-    for (int tix = threadIdx.x; tix < TBLOCKS * 32; tix += blockDim.x) {
-        const int blk = tix >> 5, sl = tix & 31;
-        const int i = blk & 7, j = (blk >> 3) & 3;
-        const int c = G >= 32 ? (blk >> 5) * 32 + sl : (sl & (G - 1));
+    for (int tix = threadIdx.x; tix < NH * 1024; tix += blockDim.x) {
+        const int h = tix >> 10, g = (tix >> 5) & 31, sl = tix & 31;
+        const int j = g >> 3, i = g & 7;
+        const int c = G >= 32 ? h * 32 + sl : (sl & (G - 1));
         const int k0 = 32 * (4 * c + j) + 4 * i;
         float x[4];
         if (k0 + 4 <= K) {
@@ -241,22 +280,24 @@ __global__ __launch_bounds__(1024) void k_bwn_f16_lut(
                 p[n] = p[n] + x[q];
             }
         }
+        float* t = tab + h * 16384 + (g >> 1) * 1024 + (g & 1) * 32 + sl;
 #pragma unroll
-        for (int nib = 0; nib < 16; ++nib) tab[blk * 512 + nib * 32 + sl] = p[nib];
+        for (int nib = 0; nib < 16; ++nib) t[nib * 64] = p[nib];
     }
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
     const int gl = lane & (G - 1);
     const int go = lane >> GLOG2;
-    // byte offset of the lane's tables for word j of its granule (nibble i
-    // adds i * 2048 bytes, nib * 128); granules past the row's read zeros
-    const int sl = G >= 32 ? (gl & 31) : (((go * G) & 31) | gl);
-    uint32_t L[4];
+    const uint32_t sl = G >= 32 ? (uint32_t)(gl & 31) : (uint32_t)(((go * G) & 31) | gl);
+    const uint32_t h = G >= 32 ? (uint32_t)(gl >> 5) : 0u;
+    // address registers (byte 1 rewritten per nibble): [nibble parity][word]
+    uint32_t A[2][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) L[j] = (uint32_t)(((G >= 32 ? (gl >> 5) * 4 : 0) + j) * 8 * 2048 + sl * 4);
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A[q][j] = (h << 16) | (sl << 2);
     const char* tb = reinterpret_cast<const char*>(tab);
-    (void)Kw4;
 
     const int64_t nsteps = ((int64_t)N + RPS - 1) / RPS;
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -277,15 +318,14 @@ __global__ __launch_bounds__(1024) void k_bwn_f16_lut(
             const int64_t row = (s0 + u) * RPS + go;
             float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             const uint32_t wj[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t t = (i <= 1) ? (wj[j] << (7 - 4 * i)) : (wj[j] >> (4 * i - 7));
-                    const uint32_t a = (t & 0x780u) | L[j];
-                    acc4[j] += *reinterpret_cast<const float*>(tb + a + i * 2048);
-                }
-            }
+            lut_nibble<0>(acc4, A, wj, tb);
+            lut_nibble<1>(acc4, A, wj, tb);
+            lut_nibble<2>(acc4, A, wj, tb);
+            lut_nibble<3>(acc4, A, wj, tb);
+            lut_nibble<4>(acc4, A, wj, tb);
+            lut_nibble<5>(acc4, A, wj, tb);
+            lut_nibble<6>(acc4, A, wj, tb);
+            lut_nibble<7>(acc4, A, wj, tb);
             float acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
             acc = fsum_to_last<GLOG2>(acc);
             if (gl == G - 1 && row < N) {
@@ -323,8 +363,8 @@ hipError_t launch_lut_piece(const uint16_t* X, const uint32_t* Wp, int64_t ldW, 
     while ((1 << glog2) < kw4 && glog2 < 6) ++glog2;
     const int rps = 64 >> glog2;
     const int64_t steps = (N + rps - 1) / rps;
-    const int tblocks = kw4 <= 32 ? 32 : 64;
-    const int per_cu = tblocks == 32 ? 2 : 1;
+    const int nh = kw4 <= 32 ? 1 : 2;                  // 64 KiB of tables per 32 granules
+    const int per_cu = nh == 1 ? 2 : 1;
     const bool unroll = steps >= (int64_t)cus * per_cu * 16 * 8;
     const int U = unroll ? 4 : 1;
     const int64_t waves = (steps + U - 1) / U;
@@ -334,16 +374,16 @@ hipError_t launch_lut_piece(const uint16_t* X, const uint32_t* Wp, int64_t ldW, 
     if (blocks < 1) blocks = 1;
     const dim3 grid((unsigned)blocks), block(1024);
     const int n = (int)N, k = (int)K;
-#define BNN_LUT(GL, UU, TB) hipLaunchKernelGGL((k_bwn_f16_lut<GL, UU, TB>), grid, block, 0, s, X, Wp, ldW, n, k, alpha, astr, Y, mode)
-#define BNN_LUT_U(GL, TB) do { if (U == 1) BNN_LUT(GL, 1, TB); else BNN_LUT(GL, 4, TB); } while (0)
+#define BNN_LUT(GL, UU, NHH) hipLaunchKernelGGL((k_bwn_f16_lut<GL, UU, NHH>), grid, block, 0, s, X, Wp, ldW, n, k, alpha, astr, Y, mode)
+#define BNN_LUT_U(GL, NHH) do { if (U == 1) BNN_LUT(GL, 1, NHH); else BNN_LUT(GL, 4, NHH); } while (0)
     switch (glog2) {
-        case 0: BNN_LUT_U(0, 32); break;
-        case 1: BNN_LUT_U(1, 32); break;
-        case 2: BNN_LUT_U(2, 32); break;
-        case 3: BNN_LUT_U(3, 32); break;
-        case 4: BNN_LUT_U(4, 32); break;
-        case 5: BNN_LUT_U(5, 32); break;
-        default: BNN_LUT_U(6, 64); break;
+        case 0: BNN_LUT_U(0, 1); break;
+        case 1: BNN_LUT_U(1, 1); break;
+        case 2: BNN_LUT_U(2, 1); break;
+        case 3: BNN_LUT_U(3, 1); break;
+        case 4: BNN_LUT_U(4, 1); break;
+        case 5: BNN_LUT_U(5, 1); break;
+        default: BNN_LUT_U(6, 2); break;
     }
 #undef BNN_LUT_U
 #undef BNN_LUT
