@@ -891,9 +891,10 @@ def cpu_baseline(M, N, K, target_s):
 
 def valu_probe():
     """The issue-rate probes of libbnn_calib.so (register-only loops of the
-    XOR-popcount mix, v_xor only and v_bcnt only, at 4 and 8 waves per SIMD):
-    lane-ops per second, the engine clock the probe ran at, and lane-ops per
-    clock per CU."""
+    XOR-popcount mix, v_xor only and v_bcnt only, at 4 and 8 waves per SIMD;
+    the mix at 2 waves per SIMD, and the mix with the xor's uniform operand
+    in a VGPR): lane-ops per second, the engine clock the probe ran at, and
+    lane-ops per clock per CU."""
     import ctypes
     path = os.path.join(ROOT, "xnor_popcount_gemm_amd", "libbnn_calib.so")
     if not os.path.exists(path):
@@ -904,9 +905,10 @@ def valu_probe():
                   ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int64)]
     f.restype = ctypes.c_int
     out = {}
-    for mode, name in ((0, "xor_nop_bcnt_mix"), (1, "xor_only"), (2, "bcnt_only")):
+    for mode, name, bpcs in ((0, "xor_nop_bcnt_mix", (4, 8)), (1, "xor_only", (4, 8)), (2, "bcnt_only", (4, 8)),
+                             (0, "xor_nop_bcnt_mix_2_waves", (2,)), (3, "xor_vgpr_operand_mix", (4, 8))):
         best = None
-        for bpc in (4, 8):
+        for bpc in bpcs:
             sec, cyc, tck, wg = ctypes.c_double(), ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_int64()
             iters = 20000
             rc = f(mode, bpc, iters, ctypes.byref(sec), ctypes.byref(cyc), ctypes.byref(tck), ctypes.byref(wg))
@@ -1104,6 +1106,10 @@ def main():
                                                      for f in mlp["hidden_layer_int_valu_frac"]]
             mlp["graph_hidden_layer_frac_of_probe_mix"] = [round(f * PEAK_INT_OPS / mix, 4)
                                                            for f in mlp["graph_hidden_layer_int_valu_frac"]]
+            # the layer runs 2 waves per SIMD: against the mix probed at that occupancy
+            mix2 = probe["xor_nop_bcnt_mix_2_waves"]["lane_ops_per_s"]
+            mlp["graph_hidden_layer_frac_of_probe_mix_2_waves"] = [
+                round(f * PEAK_INT_OPS / mix2, 4) for f in mlp["graph_hidden_layer_int_valu_frac"]]
             for c in sec["conv_block"] + sec["conv_chain"]:
                 lane_ops = 2.0 * c["M"] * c.get("Cout", c["C"]) * (9 * c["C"] // 32)
                 c["block_bound_achievable_ms"] = 1e3 * max(c["block_bytes"] / PEAK_HBM, lane_ops / mix)
