@@ -499,7 +499,10 @@ def test_dense_f32_sign_pack_every_tile(bnn, tile, monkeypatch):
     np.testing.assert_array_equal(host_u32(Op), oracle.pack_signs(s, ld=Op.shape[1]))
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 10, 4096), (7, 3, 33), (130, 17, 1000)])
+# 4 rows per workgroup (ragged M: 7, 130, 5, 1), 16 columns per pass (N = 17,
+# 33: a second and third pass), K slices of 64 per wave (ragged K, K < 64)
+@pytest.mark.parametrize("M,N,K", [(64, 10, 4096), (7, 3, 33), (130, 17, 1000), (1, 10, 4096), (5, 33, 257),
+                                   (3, 1, 4), (1024, 10, 4096)])
 def test_dense_binact_f32(bnn, M, N, K):
     rng = np.random.default_rng(1100 + K)
     s = np.where(rng.random((M, K)) < 0.5, 1, -1).astype(np.int8)

@@ -129,28 +129,43 @@ __global__ __launch_bounds__(64) void k_dense_f32_sign_pack(
     }
 }
 
-// Last layer: one workgroup per activation row; its 4 waves take interleaved
-// 256-element slices of K (lane: 4 consecutive k), every lane keeps one
-// double per output column (NB per pass), each wave reduces with a
-// fixed-order butterfly and wave 0 adds the 4 wave sums in order.
+// Last layer: a workgroup of 16 waves owns 4 activation rows.  In each wave the 16
+// lanes of row group g (lanes 16 g .. 16 g + 15) take row 4 b + g, lane
+// 16 g + l the 4 consecutive k = 64 (w + 16 t) + 4 l of wave w, t = 0, 1, ...
+// The 4 row groups read the same weight addresses, which the memory
+// pipeline serves once per instruction, so each weight travels from L2 once
+// per 4 rows.  Per k: acc += s * (double)w with s = +1.0 / -1.0 from the
+// row's bit: an fma with an exact product, i.e. the exactly rounded
+// acc +- w.  Each output's lane sums meet in a fixed 16-lane butterfly,
+// then the 16 waves' sums are added in wave order; NB columns per pass.
+// (With 4 waves per workgroup, 16 K steps per wave, one wave per SIMD: 48
+// us for the binary MLP's 1024 x 4096 -> 10 layer, latency-bound.)
+constexpr int kBinactThreads = 1024;
 template <int NB, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_dense_binact_f32(
+__global__ __launch_bounds__(kBinactThreads) void k_dense_binact_f32(
     const uint32_t* __restrict__ Xp, int64_t ldXp, const float* __restrict__ W, int64_t ldW,
     int M, int N, int K, float* __restrict__ Y, int64_t ldY)
 {
-    __shared__ double part[4][NB];
+    constexpr int RB = 4;                         // rows per workgroup (one per 16-lane group)
+    constexpr int WPG = kBinactThreads / 64;      // waves per workgroup
+    __shared__ double part[WPG][RB][NB];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t m = blockIdx.x;
-    const uint32_t* __restrict__ xr = Xp + m * ldXp;
+    const int rg = lane >> 4, li = lane & 15;
+    const int64_t m0 = (int64_t)blockIdx.x * RB;
+    const int64_t mc = min(m0 + rg, (int64_t)M - 1);
+    const uint32_t* __restrict__ xr = Xp + mc * ldXp;
     for (int n0 = 0; n0 < N; n0 += NB) {
         double acc[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[j] = 0.0;
-        for (int kb = 256 * wave; kb < K; kb += 1024) {
-            const int k = kb + 4 * lane;
+        for (int kb = 64 * wave; kb < K; kb += 64 * WPG) {
+            const int k = kb + 4 * li;
             if (k < K) {
                 const uint32_t bits = xr[k >> 5] >> (k & 31);
+                double sg[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sg[i] = ((bits >> i) & 1u) ? -1.0 : 1.0;
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     if (n0 + j < N) {
@@ -164,23 +179,30 @@ __global__ __launch_bounds__(kThreads) void k_dense_binact_f32(
                             for (int i = 0; i < 4; ++i) w[i] = (k + i < K) ? wr[i] : 0.0f;
                         }
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const double d = (double)w[i];
-                            acc[j] = ((bits >> i) & 1u) ? acc[j] - d : acc[j] + d;
-                        }
+                        for (int i = 0; i < 4; ++i) acc[j] = __builtin_fma(sg[i], (double)w[i], acc[j]);
                     }
                 }
             }
         }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const double tot = wave_sum_f64(acc[j]);
-            if (lane == 0) part[wave][j] = tot;
+            if (n0 + j < N) {
+                double v = acc[j];
+#pragma unroll
+                for (int sft = 8; sft >= 1; sft >>= 1) v += __shfl_xor(v, sft, 64);
+                if (li == 0) part[wave][rg][j] = v;
+            }
         }
         __syncthreads();
-        if (threadIdx.x < NB && n0 + (int)threadIdx.x < N) {
-            const int j = threadIdx.x;
-            Y[m * ldY + n0 + j] = (float)(((part[0][j] + part[1][j]) + part[2][j]) + part[3][j]);
+        if (threadIdx.x < RB * NB) {
+            const int r = threadIdx.x / NB, j = threadIdx.x % NB;
+            const int64_t m = m0 + r;
+            if (m < M && n0 + j < N) {
+                double t = part[0][r][j];
+#pragma unroll
+                for (int w = 1; w < WPG; ++w) t += part[w][r][j];
+                Y[m * ldY + n0 + j] = (float)t;
+            }
         }
         __syncthreads();
     }
@@ -353,7 +375,7 @@ hipError_t launch_dense_binact_f32(const uint32_t* Xp, int64_t ldXp, const float
                                    int64_t M, int64_t N, int64_t K,
                                    float* Y, int64_t ldY, hipStream_t s)
 {
-    const dim3 grid((unsigned)M), block(kThreads);
+    const dim3 grid((unsigned)((M + 3) / 4)), block(kBinactThreads);
     const bool vec = (reinterpret_cast<uintptr_t>(W) & 15u) == 0 && ldW % 4 == 0;
     if (vec) hipLaunchKernelGGL((k_dense_binact_f32<16, true>), grid, block, 0, s, Xp, ldXp, W, ldW,
                                 (int)M, (int)N, (int)K, Y, ldY);
