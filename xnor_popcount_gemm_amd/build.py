@@ -65,6 +65,14 @@ def build_calib(verbose: bool = False) -> str:
     return CALIB_LIB
 
 
+# Per-source flags.  dense.hip: MFMA results in VGPRs (the VGPR form of
+# v_mfma_f64_16x16x4_f64).  Left to choose, the compiler kept the fp64 first
+# layer's loop-carried accumulators in VGPRs but let the MFMAs write AGPRs,
+# and copied all 64 accumulator registers across and back every K chunk
+# (4 VALU ops per MFMA in a loop of 32 MFMAs).
+FILE_FLAGS = {"dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose: bool = False) -> str:
     """Compile every csrc/*.hip to an object (in parallel), then link libbnn.so;
     then build the probe library."""
@@ -75,7 +83,7 @@ def build(verbose: bool = False) -> str:
 
         def compile_one(so):
             src, obj = so
-            cmd = [cc] + flags() + ["-c", src, "-o", obj]
+            cmd = [cc] + flags() + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             return subprocess.run(cmd, capture_output=True, text=True)

@@ -262,25 +262,21 @@ __global__ __launch_bounds__(kThreads) void k_dense_f64_mfma_sign_pack(
 #pragma unroll
         for (int bn = 0; bn < BN; ++bn) acc[bm][bn] = (v4d){0.0, 0.0, 0.0, 0.0};
 
-    const int nch = (K + 15) >> 4;
-    float4 xn[BM], wn[BN];
+    // Full 16-k chunks run with unguarded loads and only uniform branches
+    // (guarded loads inside the loop made the compiler move the accumulators
+    // between AGPRs and VGPRs around every chunk: 4 extra VALU ops per MFMA);
+    // the two operand buffers swap roles each chunk (no register copies).
+    // A last partial chunk (K % 16 != 0) takes guarded loads after the loop.
+    const int nfull = K >> 4;
+    float4 x0[BM], w0[BN], x1[BM], w1[BN];
+    auto ld_full = [&](float4 (&xv)[BM], float4 (&wv)[BN], int t) {
+        const int k = 16 * t + 4 * g;
 #pragma unroll
-    for (int bm = 0; bm < BM; ++bm) xn[bm] = load_k4(xr[bm], 4 * g, K);
+        for (int bm = 0; bm < BM; ++bm) xv[bm] = *reinterpret_cast<const float4*>(xr[bm] + k);
 #pragma unroll
-    for (int bn = 0; bn < BN; ++bn) wn[bn] = load_k4(wr[bn], 4 * g, K);
-    for (int t = 0; t < nch; ++t) {
-        float4 xa[BM], wa[BN];
-#pragma unroll
-        for (int bm = 0; bm < BM; ++bm) xa[bm] = xn[bm];
-#pragma unroll
-        for (int bn = 0; bn < BN; ++bn) wa[bn] = wn[bn];
-        if (t + 1 < nch) {                           // next chunk in flight during this one
-            const int k = 16 * (t + 1) + 4 * g;
-#pragma unroll
-            for (int bm = 0; bm < BM; ++bm) xn[bm] = load_k4(xr[bm], k, K);
-#pragma unroll
-            for (int bn = 0; bn < BN; ++bn) wn[bn] = load_k4(wr[bn], k, K);
-        }
+        for (int bn = 0; bn < BN; ++bn) wv[bn] = *reinterpret_cast<const float4*>(wr[bn] + k);
+    };
+    auto mma_chunk = [&](const float4 (&xa)[BM], const float4 (&wa)[BN]) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             double xd[BM], wd[BN];
@@ -294,6 +290,23 @@ __global__ __launch_bounds__(kThreads) void k_dense_f64_mfma_sign_pack(
                 for (int bn = 0; bn < BN; ++bn)
                     acc[bm][bn] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[bm], wd[bn], acc[bm][bn], 0, 0, 0);
         }
+    };
+    if (nfull > 0) ld_full(x0, w0, 0);
+    int t = 0;
+    for (; t + 2 <= nfull; t += 2) {              // chunk t from buffer 0, t + 1 from buffer 1
+        ld_full(x1, w1, t + 1);
+        mma_chunk(x0, w0);
+        if (t + 2 < nfull) ld_full(x0, w0, t + 2);
+        mma_chunk(x1, w1);
+    }
+    if (t < nfull) mma_chunk(x0, w0);             // an odd last full chunk, already loaded
+    if (K & 15) {                                 // the partial chunk: k >= K reads as 0
+        const int k = 16 * nfull + 4 * g;
+#pragma unroll
+        for (int bm = 0; bm < BM; ++bm) x1[bm] = load_k4(xr[bm], k, K);
+#pragma unroll
+        for (int bn = 0; bn < BN; ++bn) w1[bn] = load_k4(wr[bn], k, K);
+        mma_chunk(x1, w1);
     }
 
     // Sign bits: bit 1 for h < 0; columns >= N give 0 (+1, the pad rule).
