@@ -70,7 +70,7 @@ def parse_args():
     p.add_argument("--size", type=int, default=16384, help="M = N = K of the headline GEMM step")
     p.add_argument("--no-secondary", action="store_true", help="skip the GEMV / MLP / conv / 8192 runs")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv", "i8", "tern", "f16", "mfma"], default=None,
+    p.add_argument("--only", choices=["gemm", "gemv", "mlp", "conv", "i8", "tern", "f16", "mfma", "probe"], default=None,
                    help="run one workload only (for profiler runs); prints its JSON")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--cpu-child", nargs=5, default=None, help=argparse.SUPPRESS)
@@ -943,6 +943,12 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name}, {props.multi_processor_count} CUs")
 
+    if args.only == "probe":
+        # the issue-rate probes alone: register-only loops whose VALU
+        # instruction count is known exactly (per dispatch: workgroups x 4
+        # waves x iterations x 32), for checking the VALU counters
+        print(json.dumps({"only": "probe", "result": valu_probe()}))
+        return
     if args.only == "gemm":
         g = gemm_step_bench(bnn, torch, args.size, args.size, args.size, args.steps, args.warmup, seed_base=args.size)
         if args.copy_calib:
