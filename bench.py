@@ -924,6 +924,32 @@ def valu_probe():
     return out
 
 
+def read_stream_probe(gib=2, reps=5):
+    """The HBM read-stream ceiling as measured context for the 8.0 TB/s spec:
+    libbnn_calib.so reads a fresh 2 GiB buffer once per launch (16-byte
+    nontemporal loads, neighbouring 4 KiB chunks in flight); the best of
+    `reps` launches at 4, 8 and 16 workgroups per CU, in GB/s."""
+    import ctypes
+    path = os.path.join(ROOT, "xnor_popcount_gemm_amd", "libbnn_calib.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    f = L.bnn_calib_read_stream
+    f.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    f.restype = ctypes.c_int
+    nbytes = gib << 30
+    best = None
+    for bpc in (4, 8, 16):
+        sec = ctypes.c_double()
+        rc = f(nbytes, bpc, reps, ctypes.byref(sec))
+        if rc != 0:
+            raise RuntimeError(f"read-stream probe failed with HIP error {rc}")
+        if best is None or sec.value < best[1]:
+            best = (bpc, sec.value)
+    return dict(bytes=nbytes, workgroups_per_cu=best[0], seconds=best[1], GBps=nbytes / best[1] / 1e9,
+                frac_of_spec=nbytes / best[1] / PEAK_HBM)
+
+
 def main():
     args = parse_args()
     if args.cpu_child:
@@ -947,7 +973,7 @@ def main():
         # the issue-rate probes alone: register-only loops whose VALU
         # instruction count is known exactly (per dispatch: workgroups x 4
         # waves x iterations x 32), for checking the VALU counters
-        print(json.dumps({"only": "probe", "result": valu_probe()}))
+        print(json.dumps({"only": "probe", "result": {"valu": valu_probe(), "hbm_read_stream": read_stream_probe()}}))
         return
     if args.only == "gemm":
         g = gemm_step_bench(bnn, torch, args.size, args.size, args.size, args.steps, args.warmup, seed_base=args.size)
@@ -1058,6 +1084,13 @@ def main():
                          "frac": round(min(r["stream_frac_hbm"] for r in gv), 4)},
             "shapes": gv,
         }
+        log("HBM read-stream probe")
+        rs = read_stream_probe()
+        if rs:
+            # context for the spec peak: a plain read of 2 GiB, and the GEMV against it
+            sec["gemv_batch1"]["roofline"]["measured_read_stream_GBps"] = round(rs["GBps"], 1)
+            sec["gemv_batch1"]["roofline"]["frac_of_measured_read_stream"] = round(
+                min(r["stream_GBps"] for r in gv) / rs["GBps"], 4)
         g8 = gemm_step_bench(bnn, torch, 8192, 8192, 8192, max(5, args.steps // 2), 2, seed_base=8192,
                              warm_ms=80.0)
         sec["gemm_8192"] = {

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbnn.so")
-CALIB_SRC = os.path.join(HERE, "calib", "valu_rate.hip")
+CALIB_SRCS = [os.path.join(HERE, "calib", "valu_rate.hip"), os.path.join(HERE, "calib", "hbm_stream.hip")]
 CALIB_LIB = os.path.join(HERE, "libbnn_calib.so")
 ARCH = "gfx950"
 
@@ -54,13 +54,13 @@ def _jobs() -> int:
 def build_calib(verbose: bool = False) -> str:
     """Compile the issue-rate probes into libbnn_calib.so."""
     tmp = CALIB_LIB + ".tmp"
-    cmd = [hipcc()] + [f for f in flags() if not f.startswith("-I")] + ["-shared", CALIB_SRC, "-o", tmp]
+    cmd = [hipcc()] + [f for f in flags() if not f.startswith("-I")] + ["-shared"] + CALIB_SRCS + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     sys.stderr.write(r.stderr)
     if r.returncode != 0:
-        raise subprocess.CalledProcessError(r.returncode, f"hipcc {CALIB_SRC}", r.stdout, r.stderr)
+        raise subprocess.CalledProcessError(r.returncode, f"hipcc {' '.join(CALIB_SRCS)}", r.stdout, r.stderr)
     os.replace(tmp, CALIB_LIB)
     return CALIB_LIB
 
