@@ -20,7 +20,8 @@
 // 32-column groups are folded into packed words with DPP row shifts, as in
 // the pack kernels.
 //
-// Last layer: one workgroup per activation row, K split over its waves,
+// Last layer: 4 activation rows per workgroup (one per 16-lane group of
+// each wave, the groups sharing every weight load), K split over the waves,
 // double accumulators, fixed-order reductions (deterministic on every run).
 #include <stdio.h>
 #include <stdlib.h>

@@ -20,8 +20,8 @@
 // activations are one nibble of a weight word, so S is a sum of one of 16
 // signed sums per nibble.  A workgroup writes all 16 sums of every group of
 // 4 activations into LDS (512 bytes per weight word), then streams weight
-// rows: per nibble one shift, one and-or (the LDS address), one LDS read and
-// one fp32 add -- 24 VALU ops and 8 LDS reads per weight word.  The entries
+// rows: per nibble one SDWA op (the nibble into the LDS address), one LDS
+// read and one fp32 add -- 16 VALU ops and 8 LDS reads per weight word.  The entries
 // of one table sit in one bank and the lanes of a read use distinct banks,
 // so a read costs what a conflict-free one does.  Rows longer than 8192 run
 // as passes over 8192-wide K pieces (the tables of a piece fill 128 KiB).
