@@ -137,11 +137,28 @@ __global__ __launch_bounds__(64) void k_dense_f32_sign_pack(
 // pipeline serves once per instruction, so each weight travels from L2 once
 // per 4 rows.  Per k: acc += s * (double)w with s = +1.0 / -1.0 from the
 // row's bit: an fma with an exact product, i.e. the exactly rounded
-// acc +- w.  Each output's lane sums meet in a fixed 16-lane butterfly,
+// acc +- w.  Each output's lane sums meet in a fixed 16-lane DPP scan,
 // then the 16 waves' sums are added in wave order; NB columns per pass.
 // (With 4 waves per workgroup, 16 K steps per wave, one wave per SIMD: 48
 // us for the binary MLP's 1024 x 4096 -> 10 layer, latency-bound.)
 constexpr int kBinactThreads = 1024;
+
+// Sum of a double over each aligned 16-lane row, complete in the row's last
+// lane: an inclusive scan by DPP row shifts of 1, 2, 4, 8 (both 32-bit
+// halves moved, lanes shifted in from outside the row read +0.0), a fixed
+// order with no LDS traffic.
+__device__ __forceinline__ double dsum16_to_last(double v) {
+#define BNN_DSTEP(CTRL)                                                                              \
+    {                                                                                                \
+        const uint64_t b = (uint64_t)__double_as_longlong(v);                                        \
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, true); \
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true); \
+        v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));                          \
+    }
+    BNN_DSTEP(0x111) BNN_DSTEP(0x112) BNN_DSTEP(0x114) BNN_DSTEP(0x118)
+#undef BNN_DSTEP
+    return v;
+}
 template <int NB, bool VEC>
 __global__ __launch_bounds__(kBinactThreads) void k_dense_binact_f32(
     const uint32_t* __restrict__ Xp, int64_t ldXp, const float* __restrict__ W, int64_t ldW,
@@ -188,10 +205,8 @@ __global__ __launch_bounds__(kBinactThreads) void k_dense_binact_f32(
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             if (n0 + j < N) {
-                double v = acc[j];
-#pragma unroll
-                for (int sft = 8; sft >= 1; sft >>= 1) v += __shfl_xor(v, sft, 64);
-                if (li == 0) part[wave][rg][j] = v;
+                const double v = dsum16_to_last(acc[j]);
+                if (li == 15) part[wave][rg][j] = v;
             }
         }
         __syncthreads();
