@@ -117,11 +117,21 @@ __global__ __launch_bounds__(NT, MINW) void k_xnor_gemm_fp4(
         lb[u] = row * RS + 4 * qb[u];
     }
     u32x4 ra[GA], rb[GB];
+    // a step whose 16 words all lie inside the rows (every step but a last,
+    // partial one; a uniform test) loads without the per-granule guards, so
+    // the loop carries no exec-masked branches
     auto gload = [&](int t) {
+        if (16 * t + 16 <= Kw) {
 #pragma unroll
-        for (int u = 0; u < GA; ++u) ra[u] = granule(gpa[u], 16 * t + 4 * qa[u], Kw);
+            for (int u = 0; u < GA; ++u) ra[u] = *reinterpret_cast<const u32x4*>(gpa[u] + 16 * t + 4 * qa[u]);
 #pragma unroll
-        for (int u = 0; u < GB; ++u) rb[u] = granule(gpb[u], 16 * t + 4 * qb[u], Kw);
+            for (int u = 0; u < GB; ++u) rb[u] = *reinterpret_cast<const u32x4*>(gpb[u] + 16 * t + 4 * qb[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < GA; ++u) ra[u] = granule(gpa[u], 16 * t + 4 * qa[u], Kw);
+#pragma unroll
+            for (int u = 0; u < GB; ++u) rb[u] = granule(gpb[u], 16 * t + 4 * qb[u], Kw);
+        }
     };
     auto swrite = [&](int b) {
 #pragma unroll
