@@ -220,9 +220,14 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
         lds_x[idx] = v;
     }
     __syncthreads();
-    bool live[CPL];                               // granule inside the row
+    // Weight loads are branch-free: a lane's granule past the row reads the
+    // row's last granule instead (the activation planes of that slot are 0 in
+    // LDS, so it adds nothing) and a row past N reads row N - 1 (its result is
+    // not stored).  With the loads under a per-lane branch, the exec-masked
+    // blocks sat in the streaming loop.
+    int coff[CPL];                                // word offset of granule slot i in a row
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) live[i] = gl + G * i < Kw4;
+    for (int i = 0; i < CPL; ++i) coff[i] = 4 * min(gl + G * i, Kw4 - 1);
     int32_t xs[MR];
     float xsc[MR];
 #pragma unroll
@@ -235,27 +240,19 @@ __global__ __launch_bounds__(kThreads) void k_bwn_i8_gemv(
     const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
     const int64_t stride = (((int64_t)gridDim.x * kThreads) >> 6) * U;
     const bool last = gl == G - 1;
-    const int64_t step_words = (int64_t)RPS * ldW;     // one row-step further down
     for (int64_t s0 = wave * U; s0 < nsteps; s0 += stride) {
         const int64_t row0 = s0 * RPS + go;
-        const uint32_t* __restrict__ wp0 = Wp + row0 * ldW + 4 * gl;
         u32x4 w[U][CPL], z[U][CPL];
         float av[U];
-        const uint32_t* __restrict__ zp0 = TERN ? e.Zp + (wp0 - Wp) : wp0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = row0 + (int64_t)u * RPS;
+            const int64_t roff = min(row, (int64_t)N - 1) * ldW;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
-                w[u][i] = (u32x4){0u, 0u, 0u, 0u};
+                w[u][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wp + roff + coff[i]));
                 z[u][i] = (u32x4){0u, 0u, 0u, 0u};
-                if (row < N && live[i]) {
-                    w[u][i] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4*>(wp0 + u * step_words + 4 * G * i));
-                    if (TERN)
-                        z[u][i] = __builtin_nontemporal_load(
-                            reinterpret_cast<const u32x4*>(zp0 + u * step_words + 4 * G * i));
-                }
+                if (TERN) z[u][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(e.Zp + roff + coff[i]));
             }
             av[u] = 0.0f;
             if ((e.flags & EPI_SCALE) && row < N) av[u] = e.alpha[(e.flags & EPI_ALPHA_TENSOR) ? 0 : row];
